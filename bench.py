@@ -1,0 +1,295 @@
+"""Benchmark of the quantized conv / GEMM hot path on one MI355X.
+
+Default workload: the ResNet-50 conv trunk at batch 256 (224x224x3 input), one
+step = quantize the fp32 input (resident in HBM) -> 53 fused quantized convs
+(Conv_Relu / Conv / Conv_Add_Relu) + one max pooling -> dequantize the output.
+`value` is whole-step throughput in TOPS (2*M*N*K of every conv, K = KH*KW*C_in
+without padding) over exactly --steps timed steps.
+
+The JSON line also carries
+  roofline      the implicit-GEMM conv kernel (all its launches in the timed
+                steps, timed with HIP events on the launch stream): algorithmic
+                bytes or ops per launch / average launch duration, against the
+                MI355X peak that binds at the kernel's arithmetic intensity;
+  cpu_baseline  the CPU oracle (plain C, OpenMP) timed on the host on a bounded
+                sample of the same workload (whole images), scaled to TOPS; the
+                GPU output of those images is compared with it byte for byte.
+
+Other workloads (--workload) time a single layer for the kernel tables.
+Only one GPU is supported: --gpus N with N > 1 exits with a message.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "int8/int4 quantized conv+GEMM TOPS and % of int8 MFMA peak, bit-exact"
+PEAK_INT8_OPS = 5.0e15      # MI355X dense int8 MFMA, ops/s
+PEAK_HBM = 8.0e12           # MI355X HBM3E, bytes/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qconv_igemm_traffic.md")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_tag():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("qconv.hip", "iqnn_internal.h"):
+        with open(os.path.join(ROOT, "integer_quantized_nn_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from committed rocprofv3 PMC runs, if the kernel source is
+    unchanged since they were taken; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    tag = kernel_source_tag()
+    for line in open(TRAFFIC_FILE):
+        if line.startswith("TRAFFIC "):
+            rec = json.loads(line[len("TRAFFIC "):])
+            if rec.get("workload") == workload and rec.get("kernel_source") == tag:
+                return rec.get("bytes_per_launch")
+    return None
+
+
+# ---------------------------------------------------------------- trunk
+
+
+def cpu_baseline_trunk(tr, gpu_final_codes, budget_s):
+    """Oracle chain on whole images until ~budget_s of wall time; returns the record."""
+    import oracle as O
+    w = {l.name: O.quantize(l.case.w, l.case.s_w, 0, O.INT8, axis=0) for l in tr.layers}
+    per_img_ops = tr.ops() / tr.batch
+    final = tr.layers[-1].out
+    s_f, z_f = tr.qparams[final]
+    t0 = time.perf_counter()
+    n_img, exact = 0, True
+    while n_img < tr.batch:
+        i = n_img
+        x = O.quantize(tr.x[i:i + 1], tr.s_in, tr.z_in, O.UINT8)
+        acts = {"input": x}
+        for layer in tr.layers:
+            c = layer.case
+            res = acts[layer.res_src] if layer.res_src is not None else None
+            acts[layer.out] = O.qconv(acts[layer.src], c.z_in, c.s_in, w[layer.name], c.s_w, c.bias, c.s_out,
+                                      c.z_out, O.UINT8, c.epi, c.stride, c.pad, res, c.s_res, c.z_res)
+            if layer.name == "stem":
+                acts["pool"] = O.maxpool2d(acts["stem"], 3, 2, 1)
+        O.dequantize(acts[final], s_f, z_f)
+        n_img += 1
+        exact = exact and np.array_equal(O.pack(acts[final], O.UINT8)[0], gpu_final_codes[i])
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": per_img_ops * n_img / dt / 1e12, "unit": "TOPS", "cores": O.num_threads(), "kind": "oracle",
+            "sample": "%d of %d images through the whole step (quantize, 53 convs, max pooling, dequantize), "
+                      "%.1f s wall; weight quantization excluded" % (n_img, tr.batch, dt),
+            "bit_exact_vs_gpu": bool(exact)}
+
+
+def bench_trunk(args):
+    import torch
+    from integer_quantized_nn_amd import synth
+    from integer_quantized_nn_amd.resnet50 import QuantResNet50Trunk
+
+    t0 = time.perf_counter()
+    tr = synth.resnet50_trunk(seed=0, batch=args.batch)
+    log("synthetic trunk ready in %.1f s" % (time.perf_counter() - t0))
+    net = QuantResNet50Trunk(tr)
+    x = torch.from_numpy(tr.x).cuda()
+    torch.cuda.synchronize()
+    launches = net.launches()
+    conv_launches = [l for l in launches if l[0].startswith("qconv:")]
+    step_ops = sum(l[1] for l in conv_launches)
+    log("prepacked %d convs; %.1f GOP per step" % (len(conv_launches), step_ops / 1e9))
+
+    for _ in range(args.warmup):
+        net.step(x)
+    torch.cuda.synchronize()
+
+    # per-launch events around every conv of every timed step, on the launch stream
+    stream = torch.cuda.current_stream()
+    n_conv = len(tr.layers)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_conv)]
+          for _ in range(args.steps)]
+
+    def timed_step(evs):
+        from integer_quantized_nn_amd import binding as B
+        from integer_quantized_nn_amd.layers import dequantize, maxpool2d, quantize
+        b = net.bufs
+        quantize(x, net.in_scale, net.in_zp, B.UINT8, out=b["input"])
+        for i, layer in enumerate(tr.layers):
+            conv = net.convs[layer.name]
+            res = b[layer.res_src] if layer.res_src is not None else None
+            evs[i][0].record(stream)
+            conv(b[layer.src], res=res, out=b[layer.out])
+            evs[i][1].record(stream)
+            if layer.name == "stem":
+                n, h, w, c = net.shapes["stem"]
+                maxpool2d(b["stem"], n, h, w, c, 3, 2, 1, B.UINT8, out=b["pool"])
+        dequantize(b[net.final], net.shapes[net.final], net.final_scale, net.final_zp, B.UINT8, out=net.out_f32)
+
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        timed_step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+
+    dur = np.array([[a.elapsed_time(b) * 1e-3 for (a, b) in row] for row in ev])   # seconds [steps][conv]
+    conv_ops = np.array([l[1] for l in conv_launches], np.float64)
+    conv_bytes = np.array([l[2] for l in conv_launches], np.float64)
+    avg_dur = dur.mean()                                  # average launch duration
+    ops_per_launch = conv_ops.mean()
+    bytes_per_launch = conv_bytes.mean()
+    ai = conv_ops.sum() / conv_bytes.sum()
+    if ai < PEAK_INT8_OPS / PEAK_HBM:
+        roof = {"bound": "hbm", "achieved": bytes_per_launch / avg_dur / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": ops_per_launch / avg_dur / 1e12, "peak": PEAK_INT8_OPS / 1e12,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    tr_bytes = measured_traffic("resnet50_trunk_b%d" % args.batch)
+    roof["traffic"] = tr_bytes
+    roof["kernel"] = "qconv_igemm (all instantiations; %d launches per step)" % n_conv
+    roof["algorithmic_bytes_per_launch"] = bytes_per_launch
+    roof["algorithmic_ops_per_launch"] = ops_per_launch
+    roof["avg_launch_us"] = avg_dur * 1e6
+    roof["mfma_frac"] = ops_per_launch / avg_dur / PEAK_INT8_OPS
+
+    value = step_ops / (ms_per_step * 1e-3) / 1e12
+    per_layer = {}
+    for i, layer in enumerate(tr.layers):
+        t = float(np.median(dur[:, i]))
+        per_layer[layer.name] = [round(t * 1e6, 1), round(conv_ops[i] / t / 1e12, 1)]
+
+    rec = {
+        "metric": METRIC, "value": value, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": "resnet50_trunk_b%d" % args.batch, "batch": args.batch, "image_hw": 224,
+                   "convs": n_conv, "ops_per_step": step_ops,
+                   "activations": "uint8 asymmetric per-tensor", "weights": "int8 per-channel symmetric",
+                   "step": "quantize fp32 input, 53 fused convs + max pooling, dequantize output"},
+        "pct_int8_mfma_peak": value * 1e12 / PEAK_INT8_OPS,
+        "roofline": roof,
+        "conv_time_share": float(dur.sum() / wall),
+        "per_layer_us_tops": per_layer,
+    }
+    if not args.no_cpu_baseline:
+        final_codes = net.bufs[net.final].cpu().numpy()
+        rec["cpu_baseline"] = cpu_baseline_trunk(tr, final_codes, args.cpu_seconds)
+    else:
+        rec["cpu_baseline"] = None
+    return rec
+
+
+# --------------------------------------------------------- single layers
+
+
+def bench_layer(args):
+    import torch
+    import oracle as O
+    from integer_quantized_nn_amd import synth
+    from integer_quantized_nn_amd.layers import QConv, QGemm, quantize
+
+    wl = args.workload
+    if wl in ("conv3x3_int8", "conv3x3_4bit"):
+        c = synth.conv3x3_int8() if wl == "conv3x3_int8" else synth.conv3x3_4bit()
+        n, h, w, ci = c.x.shape
+        co = c.c_out
+        wq = quantize(torch.from_numpy(c.w).cuda(), c.s_w, 0, c.w_type, axis=0).cpu().numpy()
+        layer = QConv(n, h, w, ci, co, 3, c.stride, c.pad, c.x_type, c.w_type, c.y_type, c.epi, c.z_in, c.z_out,
+                      wq, c.bias, c.s_in, c.s_w, c.s_out, res_type=c.res_type, z_res=c.z_res, s_res=c.s_res)
+        xd = quantize(torch.from_numpy(c.x).cuda(), c.s_in, c.z_in, c.x_type)
+        rd = quantize(torch.from_numpy(c.res).cuda(), c.s_res, c.z_res, c.res_type) if c.res is not None else None
+        ops = c.ops(n, h, w)
+        oh, ow = layer.out_shape[1:3]
+        w_bytes = co * 9 * ci // (2 if c.w_type in (synth.UINT4, synth.INT4) else 1)
+        y_bytes = n * oh * ow * co // (2 if c.y_type in (synth.UINT4, synth.INT4) else 1)
+        nbytes = xd.numel() + w_bytes + y_bytes + (rd.numel() if rd is not None else 0)
+        run = lambda: layer(xd, res=rd)
+    elif wl in ("vitl_fc1", "gemm_int8_256"):
+        g = synth.vitl_fc1() if wl == "vitl_fc1" else synth.gemm_int8_256()
+        m, n, k = g.shape
+        if g.b_codes is not None:
+            b_bytes = O.pack(g.b_codes, O.INT8)
+            a_dev = torch.from_numpy(O.pack(g.a_codes, O.INT8)).cuda()
+        else:
+            b_bytes = quantize(torch.from_numpy(g.b).cuda(), g.s_b, 0, g.b_type, axis=0).cpu().numpy()
+            a_dev = quantize(torch.from_numpy(g.a).cuda(), g.s_a, g.z_a, g.a_type)
+        layer = QGemm(m, n, k, g.a_type, g.b_type, g.c_type, g.epi, g.z_a, g.z_out, b_bytes, g.bias, g.s_a, g.s_b,
+                      g.s_out)
+        ops = 2 * m * n * k
+        nbytes = m * k + n * k + m * n
+        run = lambda: layer(a_dev)
+    else:
+        raise SystemExit("unknown workload " + wl)
+    for _ in range(max(args.warmup, 1)):
+        run()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    stream = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dur = np.array([a.elapsed_time(b) * 1e-3 for a, b in evs])
+    avg = dur.mean()
+    ai = ops / nbytes
+    if ai < PEAK_INT8_OPS / PEAK_HBM:
+        roof = {"bound": "hbm", "achieved": nbytes / avg / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": ops / avg / 1e12, "peak": PEAK_INT8_OPS / 1e12, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(wl)
+    roof["avg_launch_us"] = avg * 1e6
+    roof["mfma_frac"] = ops / avg / PEAK_INT8_OPS
+    return {"metric": METRIC, "value": ops / avg / 1e12, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+            "config": {"workload": wl, "ops": ops, "algorithmic_bytes": nbytes, "cache": "warm (inputs reused)"},
+            "pct_int8_mfma_peak": ops / avg / PEAK_INT8_OPS, "roofline": roof, "cpu_baseline": None}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--batch", type=int, default=256)
+    ap.add_argument("--workload", default="resnet50_trunk",
+                    choices=["resnet50_trunk", "conv3x3_int8", "conv3x3_4bit", "vitl_fc1", "gemm_int8_256"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    from integer_quantized_nn_amd import binding
+    binding.lib()
+    rec = bench_trunk(args) if args.workload == "resnet50_trunk" else bench_layer(args)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

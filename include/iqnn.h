@@ -1,0 +1,242 @@
+/*
+ * iqnn.h -- C ABI of libiqnn: integer-quantized convolution and GEMM on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What the library computes (sources are cited by page title and section):
+ *   - Linear quantization q = clip(round(x / S) + Z, Q_MIN, Q_MAX) and its inverse
+ *     x = (q - Z) * S, per tensor or per channel, symmetric (Z = 0) or asymmetric
+ *     ("Quantization" blog, sections 量化算子 / 反量化算子 / 量化模式 /
+ *     tensor量化与通道量化; MegEngine 4-bit article, section 背景, Fig. 1 and 2).
+ *   - Quantized convolution as an implicit GEMM with int32 accumulation, the
+ *     zero-point terms that are known before inference folded into an int32 bias,
+ *     and the fused Conv / Conv_Relu / Conv_Add_Relu epilogue (MegEngine 4-bit
+ *     article, sections 緩解精度下降, 算子融合優化 and conv 算子優化;
+ *     "Quantization" blog, sections 量化乘法, 量化加法, 量化激活函数, 量化矩阵乘).
+ *   - Quantized GEMM, the same operator with a 1x1 kernel (Horizon J5 lecture:
+ *     Linear is a 1x1 conv).
+ *   - Max pooling on codes, a passive operator ("Quantization" blog, 量化激活函数).
+ *
+ * Conventions shared by every entry point
+ *   Status     Every call returns an iqnn_status.  On error nothing is launched,
+ *              no output byte is written, and iqnn_last_error() (thread-local)
+ *              describes the failure.  Nothing aborts or prints.
+ *   Memory     The caller owns all memory.  Pointers named *_dev are device
+ *              pointers (hipMalloc / PyTorch CUDA tensors); *_host are host
+ *              pointers.  No forward entry point allocates device memory.
+ *   Streams    `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *              Forward / quantize / dequantize / maxpool calls are asynchronous on
+ *              it; prepack is blocking (it returns after its copy completes).
+ *   Layouts    Activations are NHWC with C innermost.  Conv weights are OHWI
+ *              [C_out][KH][KW][C_in] codes.  GEMM: A [M][K] row-major, B [N][K]
+ *              row-major (weight layout), C = A * B^T stored [M][N].  4-bit tensors
+ *              pack two consecutive elements of the flattened tensor per byte:
+ *              element 2j in bits 0-3, element 2j+1 in bits 4-7; INT4 is two's
+ *              complement.  Weights are symmetric (Z_w = 0).
+ *   Rounding   Every round is round-half-to-even ("Quantization" blog, 量化算子).
+ *              Floating point is IEEE binary32, one rounding per operation, no
+ *              fused multiply-add, so results are bit-exact and reproducible.
+ *   Threading  The library keeps no mutable global state; calls on different
+ *              streams or threads are independent.
+ */
+#ifndef IQNN_H
+#define IQNN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define IQNN_ABI_VERSION 1
+
+typedef enum {
+    IQNN_OK = 0,
+    IQNN_ERR_INVALID_ARG = 1,  /* a size, type, zero point, scale or pointer is invalid */
+    IQNN_ERR_UNSUPPORTED = 2,  /* valid, but a combination this build does not implement */
+    IQNN_ERR_ALIGNMENT = 3,    /* a pointer or row does not meet the documented alignment */
+    IQNN_ERR_OVERFLOW = 4,     /* folded bias or accumulator bound would leave int32 */
+    IQNN_ERR_HIP = 5           /* the HIP runtime reported an error */
+} iqnn_status;
+
+/* Element types.  Code ranges: INT8 [-128,127], UINT8 [0,255], INT4 [-8,7],
+ * UINT4 [0,15] (MegEngine 4-bit article, Fig. 1 / Fig. 2). */
+typedef enum {
+    IQNN_INT8 = 0,
+    IQNN_UINT8 = 1,
+    IQNN_INT4 = 2,
+    IQNN_UINT4 = 3,
+    IQNN_INT32 = 4   /* raw accumulator output only */
+} iqnn_dtype;
+
+/* Fused epilogues (MegEngine 4-bit article, section 算子融合優化: Conv_Relu and
+ * Conv_Add_Relu; "Quantization" blog, 常见计算图优化: conv-add fusion).
+ * With a = acc + folded bias (int32), M[c] = S_in*S_w[c]/S_out, M_res = S_res/S_out:
+ *   t = float(a) * M[c]
+ *   ADD, ADD_RELU:  t = t + float(r - Z_res) * M_res
+ *   RELU, ADD_RELU: t = max(t, 0)
+ *   y = clip(rne(t) + Z_out, Q_MIN, Q_MAX)
+ * RAW_INT32 stores a itself (y_type must be IQNN_INT32). */
+typedef enum {
+    IQNN_EPI_NONE = 0,
+    IQNN_EPI_RELU = 1,
+    IQNN_EPI_ADD = 2,
+    IQNN_EPI_ADD_RELU = 3,
+    IQNN_EPI_RAW_INT32 = 4
+} iqnn_epilogue;
+
+/* Convolution descriptor.  Dilation 1, groups 1.  Output size
+ * OH = (H + 2*pad_h - KH)/stride_h + 1, OW likewise.
+ * x_type: INT8, UINT8, INT4 or UINT4.  w_type: INT8 or INT4 (symmetric).
+ * y_type: INT8, UINT8, INT4, UINT4, or INT32 with IQNN_EPI_RAW_INT32.
+ * res_type: type of the residual for ADD / ADD_RELU (8- or 4-bit), else ignored.
+ * z_in / z_out / z_res: zero points, within the code range of their type.
+ * 4-bit activations need C_in % 16 == 0; 8-bit activations with C_in % 16 != 0
+ * take a slower element-gather path (e.g. the 3-channel stem). */
+typedef struct {
+    int32_t n, h, w, c_in, c_out;
+    int32_t kh, kw, stride_h, stride_w, pad_h, pad_w;
+    int32_t x_type, w_type, y_type, res_type;
+    int32_t epilogue;
+    int32_t z_in, z_out, z_res;
+} iqnn_conv_desc;
+
+/* GEMM descriptor: C[M][N] = epilogue(A[M][K] * B[N][K]^T).  a_type is the
+ * activation type (8- or 4-bit, zero point z_a), b_type the weight type (INT8 or
+ * INT4), c_type / res_type / epilogue / z_out / z_res as for convolution. */
+typedef struct {
+    int64_t m, n, k;
+    int32_t a_type, b_type, c_type, res_type;
+    int32_t epilogue;
+    int32_t z_a, z_out, z_res;
+} iqnn_gemm_desc;
+
+/* ---------------------------------------------------------------- misc */
+
+/* Returns IQNN_ABI_VERSION of the built library. */
+int iqnn_abi_version(void);
+
+/* Static string naming a status code. */
+const char *iqnn_status_str(iqnn_status status);
+
+/* Message for the last failed call on this thread ("" if none).  The pointer
+ * stays valid until the next library call on the same thread. */
+const char *iqnn_last_error(void);
+
+/* ------------------------------------------------------- quantize / dequantize */
+
+/* Quantize fp32 -> codes.  x viewed as [outer][ch][inner]; with per_channel the
+ * scale and zero point of element (o, c, i) are scale_dev[c], zp_dev[c], else
+ * scale_dev[0], zp_dev[0].  q = clip(rne(x / S) + Z, Q_MIN, Q_MAX) with one IEEE
+ * division ("Quantization" blog, 量化算子 and 量化模式).  qtype: INT8, UINT8, INT4,
+ * UINT4; 4-bit output packs element pairs of the flattened tensor, so
+ * outer*ch*inner must be even.  Infinities saturate; NaN inputs give unspecified
+ * codes.  Scales and zero points are read on the device at run time; they must
+ * be positive finite floats and zero points within the code range.
+ * Alignment: x_dev 16 bytes, q_dev 16 bytes (8-bit) or 8 bytes (4-bit). */
+iqnn_status iqnn_quantize(const float *x_dev, void *q_dev, int64_t outer, int64_t ch,
+                          int64_t inner, const float *scale_dev, const int32_t *zp_dev,
+                          int per_channel, int32_t qtype, void *stream);
+
+/* Dequantize codes -> fp32: x = float(q - Z) * S ("Quantization" blog, 反量化算子;
+ * MegEngine 4-bit article, 背景).  Same views, types and alignment as quantize. */
+iqnn_status iqnn_dequantize(const void *q_dev, float *x_dev, int64_t outer, int64_t ch,
+                            int64_t inner, const float *scale_dev, const int32_t *zp_dev,
+                            int per_channel, int32_t qtype, void *stream);
+
+/* ---------------------------------------------------------------- convolution */
+
+/* Bytes of device memory the prepacked form of this layer needs. 0 if the
+ * descriptor is invalid (iqnn_last_error says why). */
+size_t iqnn_qconv_packed_size(const iqnn_conv_desc *desc);
+
+/* Prepack one conv layer (blocking; not for the hot path).
+ * w_host: OHWI weight codes, one byte per code (INT8) or packed nibbles (INT4,
+ *   C_in even).  bias_host: fp32 [C_out] or NULL.  s_in: input scale.  s_w_host:
+ *   weight scales, [C_out] when per_channel else [1].  s_out: output scale.
+ *   s_res: residual scale (ADD / ADD_RELU; ignored otherwise).
+ * Computes, once: bias_q[c] = rne(B[c] / (S_in*S_w[c])) (MegEngine 4-bit article,
+ *   緩解精度下降: terms known before inference go into the bias), the folded int32
+ *   bias bias_q[c] - Z_in*sum(W[c]) (plus the kernel-private shift term for uint8
+ *   activations), M[c] = (S_in*S_w[c])/S_out and M_res = S_res/S_out in binary32
+ *   ("Quantization" blog, 量化乘法: the combined scale is precomputed), and the
+ *   weights reordered for the kernel (output channels permuted so each lane stores
+ *   contiguous channels: MegEngine 4-bit article, conv 算子優化, Fig. 8).
+ * packed_dev: device buffer of iqnn_qconv_packed_size() bytes, 256-byte aligned.
+ * Errors: INVALID_ARG (bad desc, code out of range, non-positive/non-finite scale,
+ *   multiplier not a normal float), OVERFLOW (folded bias or accumulator bound
+ *   outside int32). */
+iqnn_status iqnn_qconv_prepack(const iqnn_conv_desc *desc, const void *w_host,
+                               const float *bias_host, float s_in, const float *s_w_host,
+                               int per_channel, float s_out, float s_res, void *packed_dev,
+                               size_t packed_bytes, void *stream);
+
+/* Host-side prepack: writes into packed_host (iqnn_qconv_packed_size bytes) exactly
+ * the bytes iqnn_qconv_prepack copies to the device, and makes no HIP call.  For
+ * callers that prepack without a device, cache packed layers, or upload them on
+ * their own stream.  Same arguments and errors as iqnn_qconv_prepack.
+ * The packed form, with OCP = C_out rounded up to 256 and KP = K rounded up to 64
+ * (K = KH*KW*C_in), is:
+ *   int32 bias[OCP]     folded bias per physical output channel
+ *   float mult[OCP]     requant multiplier M[c] (1.0 for RAW_INT32)
+ *   float m_res; zero padding to 8*OCP + 256 bytes
+ *   int8  w[OCP][KP]    weight codes; row packed_row(c) holds channel c, where for
+ *                       c = 64b + 16g + 4t + r, packed_row(c) = 64b + 16t + 4g + r;
+ *                       for 4-bit activations the K positions inside every group of
+ *                       16 are ordered 0,2,4,6,1,3,5,7,8,10,12,14,9,11,13,15
+ *                       (the order the kernel unpacks nibbles in); zero padding.
+ * The folded bias is rne(B[c]/(S_in*S_w[c])) - (Z_in - s)*sum_k W[c][k] with s = 128
+ * for UINT8 activations (the kernel stages them as q - 128) and 0 otherwise. */
+iqnn_status iqnn_qconv_prepack_host(const iqnn_conv_desc *desc, const void *w_host,
+                                    const float *bias_host, float s_in, const float *s_w_host,
+                                    int per_channel, float s_out, float s_res, void *packed_host,
+                                    size_t packed_bytes);
+
+/* Quantized conv forward: y = epilogue(conv(x, W) + folded bias).
+ * x_dev: NHWC codes of x_type.  packed_dev: from iqnn_qconv_prepack with the same
+ * descriptor.  res_dev: NHWC [N][OH][OW][C_out] codes of res_type for ADD /
+ * ADD_RELU, NULL otherwise.  y_dev: NHWC [N][OH][OW][C_out] of y_type.
+ * Padding positions hold the real value 0 (code Z_in).  Implicit GEMM: no im2col
+ * buffer, no workspace.  Alignment: x, y, res 16 bytes. */
+iqnn_status iqnn_qconv_fwd(const iqnn_conv_desc *desc, const void *x_dev,
+                           const void *packed_dev, const void *res_dev, void *y_dev,
+                           void *stream);
+
+/* ---------------------------------------------------------------------- GEMM */
+
+size_t iqnn_qgemm_packed_size(const iqnn_gemm_desc *desc);
+
+/* As iqnn_qconv_prepack, for B [N][K] codes (INT8 bytes or INT4 nibbles, K even),
+ * s_b_host [N] (per_channel) or [1]. */
+iqnn_status iqnn_qgemm_prepack(const iqnn_gemm_desc *desc, const void *b_host,
+                               const float *bias_host, float s_a, const float *s_b_host,
+                               int per_channel, float s_out, float s_res, void *packed_dev,
+                               size_t packed_bytes, void *stream);
+
+/* Host-side GEMM prepack; see iqnn_qconv_prepack_host (B rows play the role of
+ * output channels, K of KH*KW*C_in). */
+iqnn_status iqnn_qgemm_prepack_host(const iqnn_gemm_desc *desc, const void *b_host,
+                                    const float *bias_host, float s_a, const float *s_b_host,
+                                    int per_channel, float s_out, float s_res, void *packed_host,
+                                    size_t packed_bytes);
+
+/* C[M][N] = epilogue(A[M][K] * B^T + folded bias) ("Quantization" blog, 量化矩阵乘:
+ * int8 in, int32 accumulate, requantize to int8 out).  res_dev [M][N] or NULL. */
+iqnn_status iqnn_qgemm_fwd(const iqnn_gemm_desc *desc, const void *a_dev,
+                           const void *packed_dev, const void *res_dev, void *c_dev,
+                           void *stream);
+
+/* -------------------------------------------------------------------- pooling */
+
+/* Max pooling k x k, stride s, padding p over NHWC codes of dtype INT8 or UINT8;
+ * taps outside the image are skipped (requires 2p <= k-1).  Passive: the output
+ * keeps the input's scale and zero point ("Quantization" blog, 量化激活函数).
+ * Alignment: x, y 16 bytes; C % 16 == 0. */
+iqnn_status iqnn_maxpool2d(const void *x_dev, void *y_dev, int32_t n, int32_t h, int32_t w,
+                           int32_t c, int32_t k, int32_t stride, int32_t pad, int32_t dtype,
+                           void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* IQNN_H */

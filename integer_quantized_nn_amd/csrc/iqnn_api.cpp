@@ -1,0 +1,455 @@
+// iqnn_api.cpp -- the extern "C" entry points of libiqnn: argument validation,
+// layer prepacking (folded bias, multipliers, reordered weights) and kernel
+// dispatch.  Declarations and full contracts are in include/iqnn.h.
+#include <hip/hip_runtime.h>
+
+#include <cfenv>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <string>
+#include <vector>
+
+#include "iqnn.h"
+#include "iqnn_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace iqnn {
+
+PackGeom pack_geom(int64_t c_out, int64_t k) {
+    PackGeom g;
+    g.ocp = (int32_t)((c_out + kOcPad - 1) / kOcPad * kOcPad);
+    g.kp = (int32_t)((k + kKPad - 1) / kKPad * kKPad);
+    g.w_off = (int64_t)g.ocp * 8 + 256;
+    g.bytes = g.w_off + (int64_t)g.ocp * g.kp;
+    return g;
+}
+
+}  // namespace iqnn
+
+using namespace iqnn;
+
+namespace {
+
+thread_local std::string g_err;
+
+iqnn_status fail(iqnn_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+iqnn_status ok() {
+    g_err.clear();
+    return IQNN_OK;
+}
+
+bool code_range(int32_t t, int32_t* lo, int32_t* hi) {
+    switch (t) {
+    case T_INT8: *lo = -128; *hi = 127; return true;
+    case T_UINT8: *lo = 0; *hi = 255; return true;
+    case T_INT4: *lo = -8; *hi = 7; return true;
+    case T_UINT4: *lo = 0; *hi = 15; return true;
+    default: return false;
+    }
+}
+bool is_code_type(int32_t t) { int32_t a, b; return code_range(t, &a, &b); }
+bool is_4bit(int32_t t) { return t == T_INT4 || t == T_UINT4; }
+bool in_range(int32_t t, int32_t z) {
+    int32_t lo, hi;
+    return code_range(t, &lo, &hi) && z >= lo && z <= hi;
+}
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.0f; }
+bool normal_ok(float s) { return std::isfinite(s) && s >= std::numeric_limits<float>::min(); }
+
+// A conv or GEMM layer in one normalized form.
+struct Layer {
+    int64_t n, h, w, c, c_out, oh, ow, m, k;
+    int32_t kh, kw, sh, sw, ph, pw;
+    int32_t x_type, w_type, y_type, res_type, epi, z_in, z_out, z_res;
+    bool gemm;
+};
+
+iqnn_status check_layer(const Layer& L) {
+    if (L.n <= 0 || L.h <= 0 || L.w <= 0 || L.c <= 0 || L.c_out <= 0)
+        return fail(IQNN_ERR_INVALID_ARG, "sizes must be positive (n=%lld h=%lld w=%lld c_in=%lld c_out=%lld)",
+                    (long long)L.n, (long long)L.h, (long long)L.w, (long long)L.c, (long long)L.c_out);
+    if (L.kh <= 0 || L.kw <= 0 || L.sh <= 0 || L.sw <= 0 || L.ph < 0 || L.pw < 0)
+        return fail(IQNN_ERR_INVALID_ARG, "kernel, stride must be positive and padding non-negative");
+    if (L.h + 2 * (int64_t)L.ph < L.kh || L.w + 2 * (int64_t)L.pw < L.kw || L.oh <= 0 || L.ow <= 0)
+        return fail(IQNN_ERR_INVALID_ARG, "kernel larger than the padded input");
+    if (L.c_out > (1 << 24) || L.k > (1 << 24))
+        return fail(IQNN_ERR_UNSUPPORTED, "C_out or K above 2^24");
+    if (!is_code_type(L.x_type)) return fail(IQNN_ERR_INVALID_ARG, "activation type %d is not a code type", L.x_type);
+    if (L.w_type != T_INT8 && L.w_type != T_INT4)
+        return fail(IQNN_ERR_INVALID_ARG, "weight type must be INT8 or INT4 (symmetric)");
+    if (L.epi < E_NONE || L.epi > E_RAW) return fail(IQNN_ERR_INVALID_ARG, "unknown epilogue %d", L.epi);
+    if ((L.epi == E_RAW) != (L.y_type == T_INT32))
+        return fail(IQNN_ERR_INVALID_ARG, "INT32 output goes with the RAW_INT32 epilogue and only with it");
+    if (L.epi != E_RAW && !is_code_type(L.y_type))
+        return fail(IQNN_ERR_INVALID_ARG, "output type %d is not a code type", L.y_type);
+    const bool add = L.epi == E_ADD || L.epi == E_ADD_RELU;
+    if (add && !is_code_type(L.res_type))
+        return fail(IQNN_ERR_INVALID_ARG, "residual type %d is not a code type", L.res_type);
+    if (!in_range(L.x_type, L.z_in)) return fail(IQNN_ERR_INVALID_ARG, "z_in %d outside the input code range", L.z_in);
+    if (L.epi != E_RAW && !in_range(L.y_type, L.z_out))
+        return fail(IQNN_ERR_INVALID_ARG, "z_out %d outside the output code range", L.z_out);
+    if (add && !in_range(L.res_type, L.z_res))
+        return fail(IQNN_ERR_INVALID_ARG, "z_res %d outside the residual code range", L.z_res);
+    if (is_4bit(L.x_type) && L.c % 16 != 0)
+        return fail(IQNN_ERR_UNSUPPORTED, "4-bit activations need C_in %% 16 == 0 (C_in=%lld)", (long long)L.c);
+    if ((is_4bit(L.y_type) || (add && is_4bit(L.res_type))) && L.c_out % 2 != 0)
+        return fail(IQNN_ERR_INVALID_ARG, "4-bit outputs / residuals need an even C_out");
+    if (L.w_type == T_INT4 && L.c % 2 != 0)
+        return fail(IQNN_ERR_INVALID_ARG, "INT4 weights need an even C_in (nibble pairs)");
+    if (!is_4bit(L.x_type) && L.c % 16 != 0 && L.w > 0x7FFFFFFF)
+        return fail(IQNN_ERR_UNSUPPORTED, "element-gather path limited to 2^31 columns");
+    if (L.m > ((int64_t)1 << 40)) return fail(IQNN_ERR_UNSUPPORTED, "too many output pixels");
+    return IQNN_OK;
+}
+
+iqnn_status conv_layer(const iqnn_conv_desc* d, Layer* L) {
+    if (!d) return fail(IQNN_ERR_INVALID_ARG, "null descriptor");
+    L->gemm = false;
+    L->n = d->n; L->h = d->h; L->w = d->w; L->c = d->c_in; L->c_out = d->c_out;
+    L->kh = d->kh; L->kw = d->kw; L->sh = d->stride_h; L->sw = d->stride_w; L->ph = d->pad_h; L->pw = d->pad_w;
+    L->x_type = d->x_type; L->w_type = d->w_type; L->y_type = d->y_type; L->res_type = d->res_type;
+    L->epi = d->epilogue; L->z_in = d->z_in; L->z_out = d->z_out; L->z_res = d->z_res;
+    L->oh = L->sh > 0 ? (L->h + 2 * (int64_t)L->ph - L->kh) / L->sh + 1 : 0;
+    L->ow = L->sw > 0 ? (L->w + 2 * (int64_t)L->pw - L->kw) / L->sw + 1 : 0;
+    L->m = L->n * L->oh * L->ow;
+    L->k = (int64_t)L->kh * L->kw * L->c;
+    return check_layer(*L);
+}
+
+iqnn_status gemm_layer(const iqnn_gemm_desc* d, Layer* L) {
+    if (!d) return fail(IQNN_ERR_INVALID_ARG, "null descriptor");
+    L->gemm = true;
+    L->n = 1; L->h = 1; L->w = d->m; L->c = d->k; L->c_out = d->n;
+    L->kh = L->kw = L->sh = L->sw = 1; L->ph = L->pw = 0;
+    L->x_type = d->a_type; L->w_type = d->b_type; L->y_type = d->c_type; L->res_type = d->res_type;
+    L->epi = d->epilogue; L->z_in = d->z_a; L->z_out = d->z_out; L->z_res = d->z_res;
+    L->oh = 1; L->ow = d->m; L->m = d->m; L->k = d->k;
+    if (d->m <= 0 || d->n <= 0 || d->k <= 0) return fail(IQNN_ERR_INVALID_ARG, "GEMM sizes must be positive");
+    return check_layer(*L);
+}
+
+int64_t packed_size(const Layer& L) { return pack_geom(L.c_out, L.k).bytes; }
+
+// Staged K position of logical K index k.  4-bit activations are unpacked in
+// 16-element segments as [0,2,4,6, 1,3,5,7, 8,10,12,14, 9,11,13,15] (low nibbles of
+// four bytes, then their high nibbles); the weights are stored in the same order
+// so both MFMA operands see one consistent K permutation.
+int64_t staged_k(int64_t k, bool act4) {
+    if (!act4) return k;
+    static const int pos_of_elem[16] = {0, 4, 1, 5, 2, 6, 3, 7, 8, 12, 9, 13, 10, 14, 11, 15};
+    return (k & ~(int64_t)15) | pos_of_elem[k & 15];
+}
+
+// Writes the packed layer (layout in PackGeom) into host memory `dst` of g.bytes.
+iqnn_status prepack_into(const Layer& L, const void* w_host, const float* bias_host, float s_in,
+                         const float* s_w_host, int per_channel, float s_out, float s_res, uint8_t* dst) {
+    const PackGeom g = pack_geom(L.c_out, L.k);
+    if (!scale_ok(s_in)) return fail(IQNN_ERR_INVALID_ARG, "input scale must be positive and finite");
+    const bool raw = L.epi == E_RAW;
+    const bool add = L.epi == E_ADD || L.epi == E_ADD_RELU;
+    if (!raw && !scale_ok(s_out)) return fail(IQNN_ERR_INVALID_ARG, "output scale must be positive and finite");
+    if (add && !scale_ok(s_res)) return fail(IQNN_ERR_INVALID_ARG, "residual scale must be positive and finite");
+    if (std::fegetround() != FE_TONEAREST) return fail(IQNN_ERR_INVALID_ARG, "host rounding mode is not nearest-even");
+
+    std::memset(dst, 0, (size_t)g.bytes);
+    int32_t* bias = reinterpret_cast<int32_t*>(dst);
+    float* mult = reinterpret_cast<float*>(dst + (size_t)g.ocp * 4);
+    float* mres = reinterpret_cast<float*>(dst + (size_t)g.ocp * 8);
+    int8_t* wp = reinterpret_cast<int8_t*>(dst + g.w_off);
+
+    const bool act4 = is_4bit(L.x_type);
+    const int64_t shift = L.x_type == T_UINT8 ? 128 : 0;   // kernel stages q - 128 for UINT8
+    const int64_t mx = L.x_type == T_UINT4 ? 15 : (L.x_type == T_INT4 ? 8 : 128);
+    const uint8_t* wb = static_cast<const uint8_t*>(w_host);
+    std::vector<int32_t> row((size_t)L.k);
+
+    for (int64_t oc = 0; oc < L.c_out; ++oc) {
+        int64_t sum = 0, abs_sum = 0;
+        for (int64_t k = 0; k < L.k; ++k) {
+            int64_t e = oc * L.k + k;
+            int32_t v;
+            if (L.w_type == T_INT8) {
+                v = (int8_t)wb[e];
+            } else {
+                uint8_t byte = wb[e >> 1];
+                v = (e & 1) ? (byte >> 4) : (byte & 0xF);
+                if (v >= 8) v -= 16;
+            }
+            row[(size_t)k] = v;
+            sum += v;
+            abs_sum += v < 0 ? -v : v;
+        }
+        const float s_w = per_channel ? s_w_host[oc] : s_w_host[0];
+        if (!scale_ok(s_w)) return fail(IQNN_ERR_INVALID_ARG, "weight scale of channel %lld is not positive finite", (long long)oc);
+        const float sw_in = s_in * s_w;
+        int64_t bias_q = 0;
+        if (bias_host) {
+            const float b = bias_host[oc];
+            if (!std::isfinite(b)) return fail(IQNN_ERR_INVALID_ARG, "bias of channel %lld is not finite", (long long)oc);
+            const float rb = std::nearbyint(b / sw_in);
+            if (!(rb >= -2147483648.0f && rb <= 2147483520.0f))
+                return fail(IQNN_ERR_OVERFLOW, "quantized bias of channel %lld leaves int32", (long long)oc);
+            bias_q = (int64_t)rb;
+        }
+        const int64_t fold = bias_q + (shift - L.z_in) * sum;
+        if (fold < INT32_MIN || fold > INT32_MAX)
+            return fail(IQNN_ERR_OVERFLOW, "folded bias of channel %lld leaves int32", (long long)oc);
+        if (mx * abs_sum + (fold < 0 ? -fold : fold) > INT32_MAX)
+            return fail(IQNN_ERR_OVERFLOW, "accumulator of channel %lld may leave int32", (long long)oc);
+        bias[oc] = (int32_t)fold;
+        if (!raw) {
+            const float m = sw_in / s_out;
+            if (!normal_ok(m))
+                return fail(IQNN_ERR_INVALID_ARG, "requant multiplier of channel %lld is not a normal float", (long long)oc);
+            mult[oc] = m;
+        } else {
+            mult[oc] = 1.0f;
+        }
+        int8_t* dst = wp + (int64_t)packed_row_of_channel((int32_t)oc) * g.kp;
+        for (int64_t k = 0; k < L.k; ++k) dst[staged_k(k, act4)] = (int8_t)row[(size_t)k];
+    }
+    if (add) {
+        const float m = s_res / s_out;
+        if (!normal_ok(m)) return fail(IQNN_ERR_INVALID_ARG, "residual multiplier is not a normal float");
+        mres[0] = m;
+    }
+    return ok();
+}
+
+iqnn_status prepack_host(const Layer& L, const void* w_host, const float* bias_host, float s_in,
+                         const float* s_w_host, int per_channel, float s_out, float s_res, void* packed_host,
+                         size_t packed_bytes) {
+    if (!w_host || !s_w_host || !packed_host) return fail(IQNN_ERR_INVALID_ARG, "null weight, scale or output pointer");
+    const PackGeom g = pack_geom(L.c_out, L.k);
+    if ((int64_t)packed_bytes < g.bytes)
+        return fail(IQNN_ERR_INVALID_ARG, "packed buffer has %zu bytes, needs %lld", packed_bytes, (long long)g.bytes);
+    return prepack_into(L, w_host, bias_host, s_in, s_w_host, per_channel, s_out, s_res,
+                        static_cast<uint8_t*>(packed_host));
+}
+
+iqnn_status prepack_dev(const Layer& L, const void* w_host, const float* bias_host, float s_in,
+                        const float* s_w_host, int per_channel, float s_out, float s_res, void* packed_dev,
+                        size_t packed_bytes, hipStream_t stream) {
+    if (!w_host || !s_w_host || !packed_dev) return fail(IQNN_ERR_INVALID_ARG, "null weight, scale or output pointer");
+    const PackGeom g = pack_geom(L.c_out, L.k);
+    if ((int64_t)packed_bytes < g.bytes)
+        return fail(IQNN_ERR_INVALID_ARG, "packed buffer has %zu bytes, needs %lld", packed_bytes, (long long)g.bytes);
+    if (!aligned(packed_dev, 256)) return fail(IQNN_ERR_ALIGNMENT, "packed buffer must be 256-byte aligned");
+    std::vector<uint8_t> buf((size_t)g.bytes);
+    iqnn_status s = prepack_into(L, w_host, bias_host, s_in, s_w_host, per_channel, s_out, s_res, buf.data());
+    if (s != IQNN_OK) return s;
+    hipError_t e = hipMemcpyAsync(packed_dev, buf.data(), buf.size(), hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(IQNN_ERR_HIP, "copy of the packed layer failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+iqnn_status forward(const Layer& L, const void* x, const void* packed, const void* res, void* y, hipStream_t stream) {
+    const bool add = L.epi == E_ADD || L.epi == E_ADD_RELU;
+    if (!x || !packed || !y) return fail(IQNN_ERR_INVALID_ARG, "null input, packed or output pointer");
+    if (add && !res) return fail(IQNN_ERR_INVALID_ARG, "ADD / ADD_RELU epilogue needs a residual");
+    if (!aligned(x, 16) || !aligned(y, 16) || (add && !aligned(res, 16)))
+        return fail(IQNN_ERR_ALIGNMENT, "activation, output and residual pointers must be 16-byte aligned");
+    if (!aligned(packed, 256)) return fail(IQNN_ERR_ALIGNMENT, "packed buffer must be 256-byte aligned");
+    const PackGeom g = pack_geom(L.c_out, L.k);
+
+    ConvParams p;
+    std::memset(&p, 0, sizeof p);
+    p.x = static_cast<const uint8_t*>(x);
+    p.w = reinterpret_cast<const int8_t*>(static_cast<const uint8_t*>(packed) + g.w_off);
+    p.bias = static_cast<const int32_t*>(packed);
+    p.mult = reinterpret_cast<const float*>(static_cast<const uint8_t*>(packed) + (size_t)g.ocp * 4);
+    p.m_res = reinterpret_cast<const float*>(static_cast<const uint8_t*>(packed) + (size_t)g.ocp * 8);
+    p.res = add ? static_cast<const uint8_t*>(res) : nullptr;
+    p.y = static_cast<uint8_t*>(y);
+    p.m = L.m;
+    p.h = (int32_t)L.h;
+    p.w_in = (int32_t)(L.w > 0x7FFFFFFF ? 0x7FFFFFFF : L.w);
+    p.c = (int32_t)L.c;
+    p.oh = (int32_t)(L.oh > 0x7FFFFFFF ? 0x7FFFFFFF : L.oh);
+    p.ow = (int32_t)(L.ow > 0x7FFFFFFF ? 0x7FFFFFFF : L.ow);
+    p.kh = L.kh; p.kw = L.kw; p.sh = L.sh; p.sw = L.sw; p.ph = L.ph; p.pw = L.pw;
+    p.k = (int32_t)L.k;
+    p.kp = g.kp;
+    p.c_out = (int32_t)L.c_out;
+    const uint32_t pad_byte = (L.x_type == T_UINT8) ? ((uint32_t)L.z_in ^ 0x80u) & 0xFF : (uint32_t)L.z_in & 0xFF;
+    p.pad_word = pad_byte * 0x01010101u;
+    p.x_xor = L.x_type == T_UINT8 ? 0x80808080u : 0u;
+    p.x_signed4 = L.x_type == T_INT4;
+    p.y_type = L.y_type;
+    p.res_type = L.res_type;
+    p.epi = L.epi;
+    p.z_out = L.z_out;
+    p.z_res = L.z_res;
+    if (L.epi != E_RAW) {
+        int32_t lo, hi;
+        code_range(L.y_type, &lo, &hi);
+        p.lo = (float)(lo - L.z_out);
+        p.hi = (float)(hi - L.z_out);
+    }
+    p.vec_store = L.c_out % 16 == 0;
+    const int gather = is_4bit(L.x_type) ? GATHER_B4 : (L.c % 16 == 0 ? GATHER_B8 : GATHER_B8_ELEM);
+    const bool is_1x1 = gather != GATHER_B8_ELEM && L.kh == 1 && L.kw == 1 && L.sh == 1 && L.sw == 1 &&
+                        L.ph == 0 && L.pw == 0;
+    hipError_t e = launch_qconv(p, gather, is_1x1, stream);
+    if (e != hipSuccess) return fail(IQNN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int iqnn_abi_version(void) { return IQNN_ABI_VERSION; }
+
+const char* iqnn_status_str(iqnn_status s) {
+    switch (s) {
+    case IQNN_OK: return "IQNN_OK";
+    case IQNN_ERR_INVALID_ARG: return "IQNN_ERR_INVALID_ARG";
+    case IQNN_ERR_UNSUPPORTED: return "IQNN_ERR_UNSUPPORTED";
+    case IQNN_ERR_ALIGNMENT: return "IQNN_ERR_ALIGNMENT";
+    case IQNN_ERR_OVERFLOW: return "IQNN_ERR_OVERFLOW";
+    case IQNN_ERR_HIP: return "IQNN_ERR_HIP";
+    }
+    return "IQNN_ERR_UNKNOWN";
+}
+
+const char* iqnn_last_error(void) { return g_err.c_str(); }
+
+iqnn_status iqnn_quantize(const float* x_dev, void* q_dev, int64_t outer, int64_t ch, int64_t inner,
+                          const float* scale_dev, const int32_t* zp_dev, int per_channel, int32_t qtype,
+                          void* stream) {
+    int32_t lo, hi;
+    if (!code_range(qtype, &lo, &hi)) return fail(IQNN_ERR_INVALID_ARG, "quantize: type %d is not a code type", qtype);
+    if (outer < 0 || ch <= 0 || inner <= 0) return fail(IQNN_ERR_INVALID_ARG, "quantize: bad view sizes");
+    const int64_t total = outer * ch * inner;
+    if (total > 0 && (!x_dev || !q_dev || !scale_dev || !zp_dev))
+        return fail(IQNN_ERR_INVALID_ARG, "quantize: null pointer");
+    if (is_4bit(qtype) && total % 2) return fail(IQNN_ERR_INVALID_ARG, "quantize: 4-bit output needs an even element count");
+    if (!aligned(x_dev, 16) || !aligned(q_dev, is_4bit(qtype) ? 8 : 16))
+        return fail(IQNN_ERR_ALIGNMENT, "quantize: misaligned pointer");
+    QuantParams p{x_dev, static_cast<uint8_t*>(q_dev), scale_dev, zp_dev, total, ch, inner,
+                  per_channel ? 1 : 0, qtype, lo, hi};
+    hipError_t e = launch_quantize(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(IQNN_ERR_HIP, "quantize launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+iqnn_status iqnn_dequantize(const void* q_dev, float* x_dev, int64_t outer, int64_t ch, int64_t inner,
+                            const float* scale_dev, const int32_t* zp_dev, int per_channel, int32_t qtype,
+                            void* stream) {
+    if (!is_code_type(qtype)) return fail(IQNN_ERR_INVALID_ARG, "dequantize: type %d is not a code type", qtype);
+    if (outer < 0 || ch <= 0 || inner <= 0) return fail(IQNN_ERR_INVALID_ARG, "dequantize: bad view sizes");
+    const int64_t total = outer * ch * inner;
+    if (total > 0 && (!x_dev || !q_dev || !scale_dev || !zp_dev))
+        return fail(IQNN_ERR_INVALID_ARG, "dequantize: null pointer");
+    if (is_4bit(qtype) && total % 2) return fail(IQNN_ERR_INVALID_ARG, "dequantize: 4-bit input needs an even element count");
+    if (!aligned(x_dev, 16) || !aligned(q_dev, is_4bit(qtype) ? 8 : 16))
+        return fail(IQNN_ERR_ALIGNMENT, "dequantize: misaligned pointer");
+    DequantParams p{static_cast<const uint8_t*>(q_dev), x_dev, scale_dev, zp_dev, total, ch, inner,
+                    per_channel ? 1 : 0, qtype};
+    hipError_t e = launch_dequantize(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(IQNN_ERR_HIP, "dequantize launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t iqnn_qconv_packed_size(const iqnn_conv_desc* desc) {
+    Layer L;
+    if (conv_layer(desc, &L) != IQNN_OK) return 0;
+    ok();
+    return (size_t)packed_size(L);
+}
+
+iqnn_status iqnn_qconv_prepack(const iqnn_conv_desc* desc, const void* w_host, const float* bias_host, float s_in,
+                               const float* s_w_host, int per_channel, float s_out, float s_res, void* packed_dev,
+                               size_t packed_bytes, void* stream) {
+    Layer L;
+    iqnn_status s = conv_layer(desc, &L);
+    if (s != IQNN_OK) return s;
+    return prepack_dev(L, w_host, bias_host, s_in, s_w_host, per_channel, s_out, s_res, packed_dev, packed_bytes,
+                       static_cast<hipStream_t>(stream));
+}
+
+iqnn_status iqnn_qconv_prepack_host(const iqnn_conv_desc* desc, const void* w_host, const float* bias_host,
+                                    float s_in, const float* s_w_host, int per_channel, float s_out, float s_res,
+                                    void* packed_host, size_t packed_bytes) {
+    Layer L;
+    iqnn_status s = conv_layer(desc, &L);
+    if (s != IQNN_OK) return s;
+    return prepack_host(L, w_host, bias_host, s_in, s_w_host, per_channel, s_out, s_res, packed_host, packed_bytes);
+}
+
+iqnn_status iqnn_qconv_fwd(const iqnn_conv_desc* desc, const void* x_dev, const void* packed_dev,
+                           const void* res_dev, void* y_dev, void* stream) {
+    Layer L;
+    iqnn_status s = conv_layer(desc, &L);
+    if (s != IQNN_OK) return s;
+    return forward(L, x_dev, packed_dev, res_dev, y_dev, static_cast<hipStream_t>(stream));
+}
+
+size_t iqnn_qgemm_packed_size(const iqnn_gemm_desc* desc) {
+    Layer L;
+    if (gemm_layer(desc, &L) != IQNN_OK) return 0;
+    ok();
+    return (size_t)packed_size(L);
+}
+
+iqnn_status iqnn_qgemm_prepack(const iqnn_gemm_desc* desc, const void* b_host, const float* bias_host, float s_a,
+                               const float* s_b_host, int per_channel, float s_out, float s_res, void* packed_dev,
+                               size_t packed_bytes, void* stream) {
+    Layer L;
+    iqnn_status s = gemm_layer(desc, &L);
+    if (s != IQNN_OK) return s;
+    return prepack_dev(L, b_host, bias_host, s_a, s_b_host, per_channel, s_out, s_res, packed_dev, packed_bytes,
+                       static_cast<hipStream_t>(stream));
+}
+
+iqnn_status iqnn_qgemm_prepack_host(const iqnn_gemm_desc* desc, const void* b_host, const float* bias_host,
+                                    float s_a, const float* s_b_host, int per_channel, float s_out, float s_res,
+                                    void* packed_host, size_t packed_bytes) {
+    Layer L;
+    iqnn_status s = gemm_layer(desc, &L);
+    if (s != IQNN_OK) return s;
+    return prepack_host(L, b_host, bias_host, s_a, s_b_host, per_channel, s_out, s_res, packed_host, packed_bytes);
+}
+
+iqnn_status iqnn_qgemm_fwd(const iqnn_gemm_desc* desc, const void* a_dev, const void* packed_dev,
+                           const void* res_dev, void* c_dev, void* stream) {
+    Layer L;
+    iqnn_status s = gemm_layer(desc, &L);
+    if (s != IQNN_OK) return s;
+    return forward(L, a_dev, packed_dev, res_dev, c_dev, static_cast<hipStream_t>(stream));
+}
+
+iqnn_status iqnn_maxpool2d(const void* x_dev, void* y_dev, int32_t n, int32_t h, int32_t w, int32_t c, int32_t k,
+                           int32_t stride, int32_t pad, int32_t dtype, void* stream) {
+    if (dtype != T_INT8 && dtype != T_UINT8) return fail(IQNN_ERR_UNSUPPORTED, "maxpool: 8-bit codes only");
+    if (n <= 0 || h <= 0 || w <= 0 || c <= 0 || k <= 0 || stride <= 0 || pad < 0)
+        return fail(IQNN_ERR_INVALID_ARG, "maxpool: sizes must be positive");
+    if (2 * pad > k - 1) return fail(IQNN_ERR_INVALID_ARG, "maxpool: padding must satisfy 2*pad <= k-1");
+    if (c % 16 != 0) return fail(IQNN_ERR_UNSUPPORTED, "maxpool: C %% 16 != 0");
+    if (h + 2 * pad < k || w + 2 * pad < k) return fail(IQNN_ERR_INVALID_ARG, "maxpool: window larger than input");
+    if (!x_dev || !y_dev) return fail(IQNN_ERR_INVALID_ARG, "maxpool: null pointer");
+    if (!aligned(x_dev, 16) || !aligned(y_dev, 16)) return fail(IQNN_ERR_ALIGNMENT, "maxpool: misaligned pointer");
+    PoolParams p{static_cast<const uint8_t*>(x_dev), static_cast<uint8_t*>(y_dev), n, h, w, c, k, stride, pad,
+                 (h + 2 * pad - k) / stride + 1, (w + 2 * pad - k) / stride + 1, dtype == T_INT8};
+    hipError_t e = launch_maxpool(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(IQNN_ERR_HIP, "maxpool launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+"""ResNet-50 convolution trunk on libiqnn: every layer a fused quantized conv.
+
+The schedule follows the fused ResNet-50 graph of the MegEngine 4-bit article
+(section 算子融合優化, Fig. 3 and 4): Conv_Relu for the stem and the first two
+convs of each bottleneck, Conv_Add_Relu for the third (the residual add and ReLU
+absorbed into the conv), a plain Conv for the stride-s 1x1 downsample of each
+stage's first block, and a passive max pooling after the stem ("Quantization"
+blog, 量化激活函数).  One forward step is: quantize the fp32 input, 53 convs and
+one max pooling on one stream, dequantize the final output.  Every activation
+tensor keeps its own HBM buffer (the trunk needs a few GB at batch 256).
+"""
+import numpy as np
+import torch
+
+from . import binding as B
+from .layers import QConv, dequantize, empty_codes, maxpool2d, quantize
+
+
+class QuantResNet50Trunk:
+    def __init__(self, trunk, device="cuda", weight_codes=None, stream=None):
+        """trunk: synth.Trunk.  weight_codes: optional {layer name: OHWI int8 bytes};
+        by default the float weights are quantized per output channel on the GPU."""
+        self.trunk = trunk
+        self.device = device
+        n = trunk.batch
+        self.convs = {}
+        self.shapes = {"input": (n,) + trunk.x.shape[1:]}
+        for layer in trunk.layers:
+            c = layer.case
+            co, kh, kw, ci = c.w.shape
+            if weight_codes is not None:
+                w_bytes = np.ascontiguousarray(weight_codes[layer.name]).view(np.uint8)
+            else:
+                w_dev = torch.from_numpy(c.w).to(device)
+                w_bytes = quantize(w_dev, c.s_w, 0, B.INT8, axis=0, stream=stream).cpu().numpy()
+            h, w = layer.in_hw
+            conv = QConv(n, h, w, ci, co, kh, c.stride, c.pad, B.UINT8, B.INT8, B.UINT8, c.epi, c.z_in, c.z_out,
+                         w_bytes, c.bias, c.s_in, c.s_w, c.s_out, res_type=B.UINT8, z_res=c.z_res,
+                         s_res=c.s_res, device=device, stream=stream)
+            self.convs[layer.name] = conv
+            self.shapes[layer.out] = conv.out_shape
+            if layer.name == "stem":
+                oh, ow = conv.out_shape[1:3]
+                self.shapes["pool"] = (n, (oh + 2 - 3) // 2 + 1, (ow + 2 - 3) // 2 + 1, co)
+        self.bufs = {name: empty_codes(shape, B.UINT8, device) for name, shape in self.shapes.items()}
+        self.final = trunk.layers[-1].out
+        s_f, z_f = trunk.qparams[self.final]
+        self.final_scale = torch.tensor([s_f], dtype=torch.float32, device=device)
+        self.final_zp = torch.tensor([z_f], dtype=torch.int32, device=device)
+        self.in_scale = torch.tensor([trunk.s_in], dtype=torch.float32, device=device)
+        self.in_zp = torch.tensor([trunk.z_in], dtype=torch.int32, device=device)
+        self.out_f32 = torch.empty(self.shapes[self.final], dtype=torch.float32, device=device)
+
+    def run_codes(self, stream=None):
+        """53 convs + max pooling on the codes already in bufs['input']."""
+        b = self.bufs
+        for layer in self.trunk.layers:
+            conv = self.convs[layer.name]
+            res = b[layer.res_src] if layer.res_src is not None else None
+            conv(b[layer.src], res=res, out=b[layer.out], stream=stream)
+            if layer.name == "stem":
+                n, h, w, c = self.shapes["stem"]
+                maxpool2d(b["stem"], n, h, w, c, 3, 2, 1, B.UINT8, out=b["pool"], stream=stream)
+        return b[self.final]
+
+    def step(self, x_f32, stream=None):
+        """One full forward: quantize -> trunk -> dequantize.  Returns fp32 NHWC output."""
+        quantize(x_f32, self.in_scale, self.in_zp, B.UINT8, out=self.bufs["input"], stream=stream)
+        self.run_codes(stream)
+        dequantize(self.bufs[self.final], self.shapes[self.final], self.final_scale, self.final_zp, B.UINT8,
+                   out=self.out_f32, stream=stream)
+        return self.out_f32
+
+    def launches(self):
+        """(kernel family, algorithmic ops, algorithmic bytes) of every launch in one step."""
+        out = []
+        n_in = int(np.prod(self.shapes["input"]))
+        out.append(("quantize", 0, n_in * 4 + n_in))
+        for layer in self.trunk.layers:
+            conv = self.convs[layer.name]
+            d = conv.desc
+            oh, ow = d.out_hw()
+            ops = 2 * d.n * oh * ow * d.c_out * d.kh * d.kw * d.c_in
+            by = d.n * d.h * d.w * d.c_in + d.c_out * d.kh * d.kw * d.c_in + d.n * oh * ow * d.c_out
+            if layer.res_src is not None:
+                by += d.n * oh * ow * d.c_out
+            out.append(("qconv:" + layer.name, ops, by))
+            if layer.name == "stem":
+                n, h, w, c = self.shapes["stem"]
+                out.append(("maxpool", 0, n * h * w * c + int(np.prod(self.shapes["pool"]))))
+        n_out = int(np.prod(self.shapes[self.final]))
+        out.append(("dequantize", 0, n_out + 4 * n_out))
+        return out

@@ -1,0 +1,171 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/iqnn.h declares, rejects invalid arguments with the documented status
+before any device work, and its host prepack computes the folded bias,
+multipliers and weight layout the oracle's own qparam functions imply."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from integer_quantized_nn_amd import binding as B
+from parity_util import otype, to_bytes
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libiqnn.so is not built (run __graft_entry__.build())")
+    return B.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    header = open(os.path.join(ROOT, "include", "iqnn.h")).read()
+    names = set(re.findall(r"\b(iqnn_[a-z0-9_]+)\s*\(", header))
+    assert len(names) >= 14
+    raw = ctypes.CDLL(B.LIB_PATH)
+    missing = [n for n in sorted(names) if not hasattr(raw, n)]
+    assert not missing, missing
+
+
+def test_version_and_status_strings(lib):
+    assert B.iqnn_abi_version() == 1
+    assert lib.iqnn_status_str(0) == b"IQNN_OK"
+    assert lib.iqnn_status_str(4) == b"IQNN_ERR_OVERFLOW"
+
+
+def conv_desc(**kw):
+    d = B.ConvDesc()
+    base = dict(n=1, h=8, w=8, c_in=16, c_out=32, kh=3, kw=3, stride_h=1, stride_w=1, pad_h=1, pad_w=1,
+                x_type=B.UINT8, w_type=B.INT8, y_type=B.UINT8, res_type=B.UINT8, epilogue=B.EPI_RELU,
+                z_in=3, z_out=5, z_res=0)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=0), 1), (dict(c_out=0), 1), (dict(kh=11, pad_h=0), 1), (dict(x_type=7), 1),
+    (dict(w_type=B.UINT8), 1), (dict(y_type=B.INT32), 1), (dict(epilogue=B.EPI_RAW_INT32), 1),
+    (dict(z_in=300), 1), (dict(z_out=-1), 1), (dict(x_type=B.UINT4, c_in=8, z_in=3), 2),
+    (dict(epilogue=B.EPI_ADD, res_type=9), 1), (dict(y_type=B.UINT4, c_out=33, z_out=1), 1),
+    (dict(stride_h=0), 1), (dict(pad_w=-1), 1),
+])
+def test_invalid_descriptors_are_rejected(lib, kw, status):
+    d = conv_desc(**kw)
+    assert lib.iqnn_qconv_packed_size(ctypes.byref(d)) == 0
+    assert B.lib().iqnn_last_error().decode() != ""
+    rc = lib.iqnn_qconv_fwd(ctypes.byref(d), ctypes.c_void_p(4096), ctypes.c_void_p(4096), None,
+                            ctypes.c_void_p(4096), None)
+    assert rc == status
+
+
+def test_forward_argument_errors_before_launch(lib):
+    d = conv_desc(epilogue=B.EPI_ADD_RELU)
+    P = ctypes.c_void_p
+    assert lib.iqnn_qconv_fwd(ctypes.byref(d), P(4096), P(4096), None, P(4096), None) == 1   # no residual
+    d = conv_desc()
+    assert lib.iqnn_qconv_fwd(ctypes.byref(d), P(4097), P(4096), None, P(4096), None) == 3   # misaligned x
+    assert lib.iqnn_qconv_fwd(ctypes.byref(d), P(4096), P(4112), None, P(4096), None) == 3   # packed not 256-aligned
+    assert lib.iqnn_qconv_fwd(ctypes.byref(d), None, P(4096), None, P(4096), None) == 1
+    assert "null" in lib.iqnn_last_error().decode()
+
+
+def test_quantize_and_pool_argument_errors(lib):
+    P = ctypes.c_void_p
+    assert lib.iqnn_quantize(P(4096), P(4096), 1, 3, 1, P(4096), P(4096), 0, 9, None) == 1
+    assert lib.iqnn_quantize(P(4096), P(4096), 1, 3, 1, P(4096), P(4096), 0, B.UINT4, None) == 1   # odd count
+    assert lib.iqnn_quantize(P(4100), P(4096), 1, 4, 1, P(4096), P(4096), 0, B.INT8, None) == 3
+    assert lib.iqnn_dequantize(P(4096), P(4096), 1, 0, 1, P(4096), P(4096), 0, B.INT8, None) == 1
+    assert lib.iqnn_maxpool2d(P(4096), P(4096), 1, 8, 8, 16, 3, 2, 2, B.UINT8, None) == 1   # 2p > k-1
+    assert lib.iqnn_maxpool2d(P(4096), P(4096), 1, 8, 8, 12, 3, 2, 1, B.UINT8, None) == 2   # C % 16
+    assert lib.iqnn_maxpool2d(P(4096), P(4096), 1, 8, 8, 16, 3, 2, 1, B.UINT4, None) == 2
+
+
+def _host_pack(d, w_codes, wt, bias, s_in, s_w, s_out, s_res=1.0):
+    size = B.iqnn_qconv_packed_size(d)
+    buf = np.zeros(size, np.uint8)
+    B.iqnn_qconv_prepack_host(d, to_bytes(w_codes, wt), bias, s_in, s_w, np.size(s_w) > 1, s_out, s_res, buf)
+    return buf
+
+
+def _unpack_layout(buf, c_out, k, act4):
+    ocp = (c_out + 255) // 256 * 256
+    kp = (k + 63) // 64 * 64
+    bias = buf[:4 * ocp].view(np.int32)
+    mult = buf[4 * ocp:8 * ocp].view(np.float32)
+    mres = buf[8 * ocp:8 * ocp + 4].view(np.float32)[0]
+    w = buf[8 * ocp + 256:8 * ocp + 256 + ocp * kp].view(np.int8).reshape(ocp, kp)
+    rows = []
+    for c in range(c_out):
+        b, r64 = divmod(c, 64)
+        g, t, r = r64 // 16, (r64 // 4) % 4, r64 % 4
+        rows.append(64 * b + 16 * t + 4 * g + r)
+    w = w[rows][:, :k]
+    if act4:
+        order = [0, 2, 4, 6, 1, 3, 5, 7, 8, 10, 12, 14, 9, 11, 13, 15]
+        logical = np.empty_like(w)
+        for s0 in range(0, k, 16):
+            for p, e in enumerate(order):
+                logical[:, s0 + e] = w[:, s0 + p]
+        w = logical
+    return bias[:c_out], mult[:c_out], mres, w
+
+
+@pytest.mark.parametrize("x_type,w_type,c_in,c_out,epi", [
+    (B.UINT8, B.INT8, 16, 96, B.EPI_RELU),
+    (B.INT8, B.INT8, 32, 64, B.EPI_NONE),
+    (B.UINT4, B.INT4, 32, 48, B.EPI_ADD_RELU),
+    (B.INT4, B.INT4, 16, 16, B.EPI_ADD),
+    (B.UINT8, B.INT8, 3, 64, B.EPI_RELU),
+])
+def test_host_prepack_matches_oracle_qparams(lib, x_type, w_type, c_in, c_out, epi):
+    rng = np.random.default_rng(c_in * 1000 + c_out)
+    lo, hi = O.qrange(otype(w_type))
+    w = rng.integers(lo, hi + 1, size=(c_out, 3, 3, c_in)).astype(np.int32)
+    xlo, xhi = O.qrange(otype(x_type))
+    z_in = int(rng.integers(xlo, xhi + 1)) if x_type in (B.UINT8, B.UINT4) else 0
+    s_in = np.float32(0.013)
+    s_w = rng.uniform(0.001, 0.01, c_out).astype(np.float32)
+    bias = rng.normal(0, 0.3, c_out).astype(np.float32)
+    s_out, s_res = np.float32(0.07), np.float32(0.031)
+    y_type = B.UINT8 if x_type == B.UINT8 else (B.INT8 if x_type == B.INT8 else B.UINT4)
+    d = conv_desc(x_type=x_type, w_type=w_type, y_type=y_type, c_in=c_in, c_out=c_out, epilogue=epi, z_in=z_in,
+                  z_out=1, res_type=B.UINT4, z_res=2)
+    buf = _host_pack(d, w, w_type, bias, s_in, s_w, s_out, s_res)
+    act4 = x_type in (B.UINT4, B.INT4)
+    fold, mult, mres, wl = _unpack_layout(buf, c_out, 9 * c_in, act4)
+    # weights: exactly the codes, back in OHWI order after undoing the documented permutations
+    assert np.array_equal(wl.astype(np.int32), w.reshape(c_out, -1))
+    # multipliers: the oracle's requant_multiplier / residual_multiplier
+    assert np.array_equal(mult, O.requant_multiplier(s_in, s_w, s_out))
+    if epi in (B.EPI_ADD, B.EPI_ADD_RELU):
+        assert mres == O.residual_multiplier(s_res, s_out)
+    # folded bias: the oracle's bias quantization minus the zero-point term, checked through
+    # the fold identity on a one-pixel input where every tap reads the input value q:
+    # sum_k (q - Z) w + bias_q == sum_k (q - shift) w + fold.
+    shift = 128 if x_type == B.UINT8 else 0
+    bq = O.quantize_bias(bias, s_in, s_w).astype(np.int64)
+    for q in (xlo, z_in, xhi):
+        lhs = (q - z_in) * w.reshape(c_out, -1).astype(np.int64).sum(1) + bq
+        rhs = (q - shift) * w.reshape(c_out, -1).astype(np.int64).sum(1) + fold.astype(np.int64)
+        assert np.array_equal(lhs, rhs)
+
+
+def test_prepack_overflow_and_bad_scales(lib):
+    d = conv_desc(c_in=16, c_out=16)
+    w = np.full((16, 3, 3, 16), 127, np.int32)
+    with pytest.raises(B.IqnnError) as e:
+        _host_pack(d, w, B.INT8, np.full(16, 1e9, np.float32), np.float32(1e-3), np.full(16, 1e-3, np.float32), 1.0)
+    assert e.value.status == 4
+    with pytest.raises(B.IqnnError) as e:
+        _host_pack(d, w, B.INT8, None, np.float32(-1.0), np.full(16, 1e-3, np.float32), 1.0)
+    assert e.value.status == 1
+    with pytest.raises(B.IqnnError) as e:   # multiplier underflows to a denormal
+        _host_pack(d, w, B.INT8, None, np.float32(1e-20), np.full(16, 1e-20, np.float32), 1e10)
+    assert e.value.status == 1

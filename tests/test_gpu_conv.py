@@ -1,0 +1,104 @@
+"""GPU parity of the implicit-GEMM quantized conv: every output byte equals the
+oracle's (direct 7-loop conv, explicit zero-point subtraction, strict fp32
+requant).  Small shapes cover several tiles, ragged pixel / channel tails, every
+epilogue, activation / weight / output type and the stride / padding / kernel
+sizes of the workloads; the two standalone conv workloads run at full size and
+are compared on whole sampled images (batch elements are independent)."""
+import numpy as np
+import pytest
+
+import oracle as O
+from integer_quantized_nn_amd import synth
+from parity_util import (assert_bytes_equal, conv_codes, gpu_conv, oracle_conv, otype, require_gpu,
+                         to_bytes)
+
+pytestmark = pytest.mark.gpu
+
+U8, I8, U4, I4, I32 = synth.UINT8, synth.INT8, synth.UINT4, synth.INT4, synth.INT32
+NONE, RELU, ADD, ADD_RELU, RAW = synth.EPI_NONE, synth.EPI_RELU, synth.EPI_ADD, synth.EPI_ADD_RELU, synth.EPI_RAW
+
+SMALL = [
+    # n, h, w, c_in, c_out, k, stride, pad, x_type, w_type, y_type, epi, res_type
+    (2, 9, 11, 64, 64, 3, 1, 1, U8, I8, U8, RELU, U8),
+    (3, 7, 7, 32, 128, 3, 2, 1, U8, I8, U8, ADD_RELU, U8),
+    (1, 13, 5, 16, 80, 1, 1, 0, I8, I8, I8, NONE, U8),
+    (2, 6, 9, 48, 192, 1, 2, 0, U8, I8, U8, NONE, U8),
+    (1, 10, 10, 128, 48, 3, 1, 1, U8, I8, I32, RAW, U8),
+    (2, 8, 8, 32, 64, 3, 1, 1, U4, I4, U4, ADD_RELU, U4),
+    (1, 9, 7, 64, 96, 1, 1, 0, U4, I4, U4, RELU, U4),
+    (2, 5, 5, 16, 32, 3, 2, 1, I4, I4, I8, ADD, I8),
+    (1, 12, 12, 32, 64, 3, 1, 1, U4, I8, U8, ADD_RELU, U4),
+    (2, 15, 15, 3, 64, 7, 2, 3, U8, I8, U8, RELU, U8),
+    (1, 8, 8, 8, 24, 3, 1, 1, U8, I8, U8, RELU, U8),
+    (1, 4, 4, 256, 256, 3, 1, 1, U8, I8, U8, RELU, U8),
+    (1, 3, 3, 64, 40, 3, 1, 2, U8, I8, U8, NONE, U8),
+    (1, 1, 1, 1024, 2048, 1, 1, 0, U8, I8, U8, ADD_RELU, U8),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "n%dh%dw%dci%dco%dk%ds%dp%d_x%dw%dy%de%d" % c[:12])
+def test_conv_small_shapes(case):
+    require_gpu()
+    n, h, w, ci, co, k, s, p, xt, wt, yt, epi, rt = case
+    c = synth.conv_case(hash(case) % 2 ** 31, n, h, w, ci, co, k, s, p, xt, wt, yt, epi, res_type=rt)
+    x, wc, res = conv_codes(c)
+    want = to_bytes(oracle_conv(c, x, wc, res), yt)
+    got = gpu_conv(c, x, wc, res)
+    assert_bytes_equal(got, want, str(case))
+
+
+def test_conv_adversarial_codes_and_padding():
+    # every code of each type, including -128 / 255 / -8 / 15, on tiny images where
+    # most taps read padding
+    require_gpu()
+    rng = np.random.default_rng(42)
+    for (xt, wt, yt, rt, ci) in [(U8, I8, U8, U8, 32), (I8, I8, I8, I8, 16), (U4, I4, U4, U4, 32), (I4, I4, I4, I4, 16)]:
+        c = synth.conv_case(7, 3, 2, 3, ci, 64, 3, 1, 2, xt, wt, yt, ADD_RELU, res_type=rt)
+        xlo, xhi = O.qrange(otype(xt))
+        wlo, whi = O.qrange(otype(wt))
+        rlo, rhi = O.qrange(otype(rt))
+        x = rng.integers(xlo, xhi + 1, size=c.x.shape).astype(np.int32)
+        w = rng.integers(wlo, whi + 1, size=c.w.shape).astype(np.int32)
+        r = rng.integers(rlo, rhi + 1, size=c.res.shape).astype(np.int32)
+        c.z_in = int(xhi) if xt in (U8, U4) else 0
+        want = to_bytes(oracle_conv(c, x, w, r), yt)
+        got = gpu_conv(c, x, w, r)
+        assert_bytes_equal(got, want, "adversarial x%d w%d" % (xt, wt))
+
+
+def test_conv_relu_is_passive_clamp():
+    # Conv_Relu == max(Conv, Z_out) byte for byte on the GPU too
+    require_gpu()
+    c = synth.conv_case(3, 2, 9, 9, 32, 64, 3, 1, 1, U8, I8, U8, RELU)
+    x, w, _ = conv_codes(c)
+    relu = gpu_conv(c, x, w, None)
+    c.epi = NONE
+    none = gpu_conv(c, x, w, None)
+    assert np.array_equal(relu, np.maximum(none, np.uint8(c.z_out)))
+
+
+def test_conv3x3_int8_full_size():
+    """ResNet 3x3 conv workload: N=32 56x56 64->64, uint8 in, Conv_Relu to uint8."""
+    require_gpu()
+    c = synth.conv3x3_int8(seed=0)
+    x, w, _ = conv_codes(c)
+    got = gpu_conv(c, x, w, None)
+    images = [0, 1, 17, 31]
+    want = to_bytes(oracle_conv(c, x, w, None, images), c.y_type)
+    assert_bytes_equal(got[images], want, "conv3x3_int8")
+    # discrimination: the case exercises most output codes and rarely saturates
+    q = got[images]
+    assert len(np.unique(q)) >= 64 and (q == 255).mean() < 0.01
+
+
+def test_conv3x3_4bit_full_size():
+    """4-bit workload: N=64 28x28 128->128, uint4 in/out/residual, int4 weights, Conv_Add_Relu."""
+    require_gpu()
+    c = synth.conv3x3_4bit(seed=0)
+    x, w, res = conv_codes(c)
+    got = gpu_conv(c, x, w, res)
+    images = [0, 5, 63]
+    want = to_bytes(oracle_conv(c, x, w, res, images), c.y_type)
+    assert_bytes_equal(got[images], want, "conv3x3_4bit")
+    codes = O.unpack(got[images], O.UINT4)
+    assert len(np.unique(codes)) == 16 and (codes == 15).mean() < 0.01

@@ -1,0 +1,80 @@
+"""GPU parity: quantize, dequantize and max pooling, byte/bit exact against the oracle."""
+import numpy as np
+import pytest
+
+import oracle as O
+from parity_util import assert_bytes_equal, otype, require_gpu, to_bytes
+
+pytestmark = pytest.mark.gpu
+
+
+def _quant_inputs(rng, n):
+    s = np.float32(0.0371)
+    x = np.concatenate([
+        rng.standard_normal(n).astype(np.float32) * 3,
+        (rng.integers(-300, 300, 4096) + 0.5).astype(np.float32) * np.float32(0.25),   # exact ties at S=0.25
+        np.array([np.inf, -np.inf, 1e30, -1e30, 0.0, -0.0, 1e-40, -1e-40], np.float32),
+    ])
+    return x, s
+
+
+@pytest.mark.parametrize("qt", [0, 1, 2, 3])
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_quantize_parity(qt, per_channel):
+    torch = require_gpu()
+    from integer_quantized_nn_amd.layers import quantize
+    rng = np.random.default_rng(100 + qt)
+    x, _ = _quant_inputs(rng, 50000)
+    ch = 6
+    x = x[: (x.size // ch // 2) * ch * 2 - 2 * ch].reshape(-1, ch)   # ragged vs the 16-element chunks
+    x = np.concatenate([x, np.full((1, ch), 0.125, np.float32)])
+    if per_channel:
+        s = np.array([0.25, 0.0371, 0.5, 0.011, 1.0, 0.003], np.float32)
+        lo, hi = O.qrange(otype(qt))
+        z = rng.integers(lo, hi + 1, ch).astype(np.int32) if qt in (1, 3) else np.zeros(ch, np.int32)
+    else:
+        s, z = np.float32(0.25), (7 if qt in (1, 3) else 0)
+    want = to_bytes(O.quantize(x, s, z, otype(qt)), qt)
+    got = quantize(torch.from_numpy(x).cuda(), s, z, qt).cpu().numpy()
+    assert_bytes_equal(got, want, "quantize qt=%d pc=%s" % (qt, per_channel))
+
+
+def test_quantize_weights_per_output_channel():
+    torch = require_gpu()
+    from integer_quantized_nn_amd.layers import quantize
+    rng = np.random.default_rng(7)
+    for qt in (0, 2):
+        w = rng.standard_normal((40, 3, 3, 16)).astype(np.float32) * 0.05
+        s = (np.abs(w).reshape(40, -1).max(1) / (127 if qt == 0 else 7)).astype(np.float32)
+        want = to_bytes(O.quantize(w, s, 0, otype(qt), axis=0), qt)
+        got = quantize(torch.from_numpy(w).cuda(), s, 0, qt, axis=0).cpu().numpy()
+        assert_bytes_equal(got, want, "weights qt=%d" % qt)
+
+
+@pytest.mark.parametrize("qt", [0, 1, 2, 3])
+def test_dequantize_parity(qt):
+    torch = require_gpu()
+    from integer_quantized_nn_amd.layers import dequantize
+    rng = np.random.default_rng(200 + qt)
+    lo, hi = O.qrange(otype(qt))
+    codes = rng.integers(lo, hi + 1, size=(1001, 10)).astype(np.int32)
+    s = rng.uniform(1e-3, 2.0, 10).astype(np.float32)
+    z = rng.integers(lo, hi + 1, 10).astype(np.int32) if qt in (1, 3) else np.zeros(10, np.int32)
+    for scale, zp in ((s, z), (s[0], int(z[0]))):
+        want = O.dequantize(codes, scale, zp)
+        got = dequantize(torch.from_numpy(to_bytes(codes, qt)).cuda(), codes.shape, scale, zp, qt).cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("dt", [0, 1])
+def test_maxpool_parity(dt):
+    torch = require_gpu()
+    from integer_quantized_nn_amd.layers import maxpool2d
+    rng = np.random.default_rng(300 + dt)
+    lo, hi = O.qrange(otype(dt))
+    for (n, h, w, c, k, s, p) in [(2, 17, 13, 32, 3, 2, 1), (1, 112, 112, 64, 3, 2, 1), (3, 5, 6, 16, 2, 2, 0),
+                                  (1, 7, 7, 48, 3, 1, 1)]:
+        x = rng.integers(lo, hi + 1, size=(n, h, w, c)).astype(np.int32)
+        want = to_bytes(O.maxpool2d(x, k, s, p), dt)
+        got = maxpool2d(torch.from_numpy(to_bytes(x, dt)).cuda(), n, h, w, c, k, s, p, dt).cpu().numpy()
+        assert_bytes_equal(got, want, "maxpool %s" % ((n, h, w, c, k, s, p),))

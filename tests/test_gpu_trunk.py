@@ -1,0 +1,81 @@
+"""GPU parity of the ResNet-50 conv trunk (53 fused quantized convs + max pooling).
+
+The oracle runs the same chain layer by layer on the CPU from the same input and
+weight codes: its inputs come only from the oracle's own quantize, never from a
+GPU result.  Batch elements are independent, so at batch 256 the comparison is
+over whole sampled images."""
+import numpy as np
+import pytest
+
+import oracle as O
+from integer_quantized_nn_amd import synth
+from parity_util import assert_bytes_equal, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_trunk(tr, x_codes, w_codes, images):
+    acts = {"input": x_codes[images]}
+    for layer in tr.layers:
+        c = layer.case
+        res = acts[layer.res_src] if layer.res_src is not None else None
+        acts[layer.out] = O.qconv(acts[layer.src], c.z_in, c.s_in, w_codes[layer.name], c.s_w, c.bias, c.s_out,
+                                  c.z_out, O.UINT8, c.epi, c.stride, c.pad, res, c.s_res, c.z_res)
+        if layer.name == "stem":
+            acts["pool"] = O.maxpool2d(acts["stem"], 3, 2, 1)
+    return acts
+
+
+def _codes(tr):
+    x = O.quantize(tr.x, tr.s_in, tr.z_in, O.UINT8)
+    w = {l.name: O.quantize(l.case.w, l.case.s_w, 0, O.INT8, axis=0) for l in tr.layers}
+    return x, w
+
+
+def _run_gpu(tr, x, w):
+    import torch
+    from integer_quantized_nn_amd.resnet50 import QuantResNet50Trunk
+    net = QuantResNet50Trunk(tr, weight_codes={k: O.pack(v, O.INT8) for k, v in w.items()})
+    net.bufs["input"].copy_(torch.from_numpy(O.pack(x, O.UINT8)))
+    net.run_codes()
+    torch.cuda.synchronize()
+    return net
+
+
+def test_trunk_every_layer_small_batch():
+    """Batch 2 at 224x224: every intermediate tensor of both images, byte for byte."""
+    require_gpu()
+    tr = synth.resnet50_trunk(seed=3, batch=2)
+    x, w = _codes(tr)
+    net = _run_gpu(tr, x, w)
+    ref = oracle_trunk(tr, x, w, [0, 1])
+    for name, buf in net.bufs.items():
+        if name == "input":
+            continue
+        assert_bytes_equal(buf.cpu().numpy(), O.pack(ref[name], O.UINT8), name)
+
+
+def test_trunk_full_batch_sampled_images():
+    """Batch 256 (the benchmark configuration): the final output of sampled images,
+    plus the float step (GPU quantize -> trunk -> dequantize) against the oracle."""
+    torch = require_gpu()
+    from integer_quantized_nn_amd.resnet50 import QuantResNet50Trunk
+    tr = synth.resnet50_trunk(seed=0, batch=256)
+    x, w = _codes(tr)
+    images = [0, 255]
+    ref = oracle_trunk(tr, x, w, images)
+    final = tr.layers[-1].out
+    # the full step exactly as the benchmark runs it: float input, GPU-quantized weights
+    net = QuantResNet50Trunk(tr)
+    xd = torch.from_numpy(tr.x).cuda()
+    y = net.step(xd)
+    torch.cuda.synchronize()
+    got_codes = net.bufs[final].cpu().numpy()[images]
+    assert_bytes_equal(got_codes, O.pack(ref[final], O.UINT8), "trunk output codes")
+    s_f, z_f = tr.qparams[final]
+    want_f = O.dequantize(ref[final], s_f, z_f)
+    assert np.array_equal(y.cpu().numpy()[images].view(np.uint32), want_f.view(np.uint32))
+    # discrimination: the outputs span many codes and rarely saturate
+    for name in ("stem", "l1.0.out", "l3.5.out", final):
+        q = ref[name]
+        assert len(np.unique(q)) >= 32 and (q == 255).mean() < 0.02, name
