@@ -62,6 +62,26 @@ def measured_traffic(workload):
     return None
 
 
+def traffic_from_dbs(fetch_db, write_db, workload):
+    """Per-launch HBM traffic of qconv_igemm from two rocprofv3 --pmc databases (FETCH_SIZE,
+    WRITE_SIZE; KiB per dispatch), each scaled by what the same counter reads for the
+    calibration copy (--calib-copy-mib) whose true byte count is known."""
+    import sqlite3
+
+    def per_dispatch(path):
+        cur = sqlite3.connect(path).cursor()
+        return cur.execute("select dispatch_id, kernel_name, value from counters_collection").fetchall()
+
+    out = {}
+    for tag, path in (("fetch", fetch_db), ("write", write_db)):
+        rows = per_dispatch(path)
+        copies = [v for (_, n, v) in rows if "copyBuffer" in n or "copy" in n.lower()]
+        calib_kib = max(copies)
+        q = [v for (_, n, v) in rows if "qconv_igemm" in n]
+        out[tag] = (calib_kib, float(np.mean(q)), len(q))
+    return out
+
+
 # ---------------------------------------------------------------- trunk
 
 
@@ -276,7 +296,26 @@ def main():
                     choices=["resnet50_trunk", "conv3x3_int8", "conv3x3_4bit", "vitl_fc1", "gemm_int8_256"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--traffic-db", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="print the TRAFFIC record of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) made "
+                         "with --calib-copy-mib and exit (no GPU needed)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB before warm-up: a plain copy "
+                         "kernel of known size that scales the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
+    if args.traffic_db:
+        t = traffic_from_dbs(args.traffic_db[0], args.traffic_db[1], args.workload)
+        true_bytes = args.calib_copy_mib << 20
+        f_fetch = true_bytes / (t["fetch"][0] * 1024.0)
+        f_write = true_bytes / (t["write"][0] * 1024.0)
+        per_launch = t["fetch"][1] * 1024.0 * f_fetch + t["write"][1] * 1024.0 * f_write
+        wl = args.workload if args.workload != "resnet50_trunk" else "resnet50_trunk_b%d" % args.batch
+        rec = {"workload": wl, "kernel_source": kernel_source_tag(), "bytes_per_launch": per_launch,
+               "fetch_bytes_per_launch": t["fetch"][1] * 1024.0 * f_fetch,
+               "write_bytes_per_launch": t["write"][1] * 1024.0 * f_write,
+               "fetch_scale": f_fetch, "write_scale": f_write, "launches": t["fetch"][2]}
+        print("TRAFFIC " + json.dumps(rec))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
               file=sys.stderr)
@@ -287,6 +326,15 @@ def main():
         sys.exit(2)
     from integer_quantized_nn_amd import binding
     binding.lib()
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: %d bytes read, %d bytes written" % (n, n))
+        del src, dst
     rec = bench_trunk(args) if args.workload == "resnet50_trunk" else bench_layer(args)
     print(json.dumps(rec), flush=True)
 
