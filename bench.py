@@ -145,9 +145,9 @@ def bench_trunk(args):
 
     def timed_step(evs):
         from integer_quantized_nn_amd import binding as B
-        from integer_quantized_nn_amd.layers import dequantize, maxpool2d, quantize
+        from integer_quantized_nn_amd.layers import dequantize, maxpool2d, quantize_pad
         b = net.bufs
-        quantize(x, net.in_scale, net.in_zp, B.UINT8, out=b["input"])
+        quantize_pad(x, net.in_scale, net.in_zp, B.UINT8, net.stem_pad, 4, out=b["input"])
         for i, layer in enumerate(tr.layers):
             conv = net.convs[layer.name]
             res = b[layer.res_src] if layer.res_src is not None else None

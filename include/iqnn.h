@@ -91,8 +91,9 @@ typedef enum {
  * y_type: INT8, UINT8, INT4, UINT4, or INT32 with IQNN_EPI_RAW_INT32.
  * res_type: type of the residual for ADD / ADD_RELU (8- or 4-bit), else ignored.
  * z_in / z_out / z_res: zero points, within the code range of their type.
- * 4-bit activations need C_in % 16 == 0; 8-bit activations with C_in % 16 != 0
- * take a slower element-gather path (e.g. the 3-channel stem). */
+ * 4-bit activations need C_in % 16 == 0.  8-bit activations with C_in == 4 and no
+ * padding (an input from iqnn_quantize_pad) take a 4-taps-per-load gather; other
+ * C_in % 16 != 0 take a slower element gather. */
 typedef struct {
     int32_t n, h, w, c_in, c_out;
     int32_t kh, kw, stride_h, stride_w, pad_h, pad_w;
@@ -144,6 +145,19 @@ iqnn_status iqnn_dequantize(const void *q_dev, float *x_dev, int64_t outer, int6
                             int64_t inner, const float *scale_dev, const int32_t *zp_dev,
                             int per_channel, int32_t qtype, void *stream);
 
+/* Quantize an fp32 NHWC tensor [n][h][w][c] into codes laid out
+ * [n][h+2*pad][w+2*pad][c_pad] (c_pad >= c): interior elements are quantized as by
+ * iqnn_quantize (per_channel: scale_dev[c], zp_dev[c] along the channel axis), and
+ * every border pixel and every extra channel holds the zero-point code, i.e. the
+ * real value 0.  A convolution with padding p over the unpadded tensor equals the
+ * same convolution with padding 0 over this one (zero padding means real 0; an
+ * extra channel multiplies a zero-valued input).  Used for image inputs: 3 channels
+ * padded to 4 let the convolution load 4 taps x 4 channels per 16 bytes.
+ * qtype: INT8 or UINT8.  Alignment: x_dev, q_dev 4 bytes. */
+iqnn_status iqnn_quantize_pad(const float *x_dev, void *q_dev, int32_t n, int32_t h, int32_t w,
+                              int32_t c, int32_t pad, int32_t c_pad, const float *scale_dev,
+                              const int32_t *zp_dev, int per_channel, int32_t qtype, void *stream);
+
 /* ---------------------------------------------------------------- convolution */
 
 /* Bytes of device memory the prepacked form of this layer needs. 0 if the
@@ -164,8 +178,9 @@ size_t iqnn_qconv_packed_size(const iqnn_conv_desc *desc);
  *   contiguous channels: MegEngine 4-bit article, conv 算子優化, Fig. 8).
  * packed_dev: device buffer of iqnn_qconv_packed_size() bytes, 256-byte aligned.
  * Errors: INVALID_ARG (bad desc, code out of range, non-positive/non-finite scale,
- *   multiplier not a normal float), OVERFLOW (folded bias or accumulator bound
- *   outside int32). */
+ *   a multiplier M[c] or M_res that is not a normal float in [FLT_MIN, 1e20] -- the
+ *   bound keeps every epilogue intermediate finite), OVERFLOW (folded bias or
+ *   accumulator bound outside int32). */
 iqnn_status iqnn_qconv_prepack(const iqnn_conv_desc *desc, const void *w_host,
                                const float *bias_host, float s_in, const float *s_w_host,
                                int per_channel, float s_out, float s_res, void *packed_dev,
@@ -179,9 +194,10 @@ iqnn_status iqnn_qconv_prepack(const iqnn_conv_desc *desc, const void *w_host,
  * (K = KH*KW*C_in), is:
  *   int32 bias[OCP]     folded bias per physical output channel
  *   float mult[OCP]     requant multiplier M[c] (1.0 for RAW_INT32)
- *   float m_res; zero padding to 8*OCP + 256 bytes
+ *   256-byte header:    float m_res at +0; 64 bytes holding the input zero-point
+ *                       code (the row the kernel reads for padding) at +64; zeros
  *   int8  w[OCP][KP]    weight codes; row packed_row(c) holds channel c, where for
- *                       c = 64b + 16g + 4t + r, packed_row(c) = 64b + 16t + 4g + r;
+ *                       c = 32b + 16h + 4j + r, packed_row(c) = 32b + 8j + 4h + r;
  *                       for 4-bit activations the K positions inside every group of
  *                       16 are ordered 0,2,4,6,1,3,5,7,8,10,12,14,9,11,13,15
  *                       (the order the kernel unpacks nibbles in); zero padding.

@@ -9,5 +9,5 @@ from .binding import (  # noqa: F401
     ConvDesc, GemmDesc, IqnnError, iqnn_abi_version, iqnn_dequantize, iqnn_maxpool2d, iqnn_qconv_fwd,
     iqnn_qconv_packed_size, iqnn_qconv_prepack, iqnn_qconv_prepack_host, iqnn_qgemm_fwd, iqnn_qgemm_packed_size,
     iqnn_qgemm_prepack, iqnn_qgemm_prepack_host,
-    iqnn_quantize,
+    iqnn_quantize, iqnn_quantize_pad,
 )

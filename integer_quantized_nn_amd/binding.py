@@ -63,6 +63,7 @@ def lib():
         "iqnn_last_error": (ctypes.c_char_p, []),
         "iqnn_quantize": (I, [P, P, I64, I64, I64, P, P, I, I32, P]),
         "iqnn_dequantize": (I, [P, P, I64, I64, I64, P, P, I, I32, P]),
+        "iqnn_quantize_pad": (I, [P, P, I32, I32, I32, I32, I32, I32, P, P, I, I32, P]),
         "iqnn_qconv_packed_size": (SZ, [CD]),
         "iqnn_qconv_prepack": (I, [CD, P, P, F, P, I, F, F, P, SZ, P]),
         "iqnn_qconv_prepack_host": (I, [CD, P, P, F, P, I, F, F, P, SZ]),
@@ -124,6 +125,11 @@ def iqnn_quantize(x, q, outer, ch, inner, scale, zp, per_channel, qtype, stream=
 def iqnn_dequantize(q, x, outer, ch, inner, scale, zp, per_channel, qtype, stream=None):
     _check(lib().iqnn_dequantize(_dev(q), _dev(x), outer, ch, inner, _dev(scale), _dev(zp), int(per_channel),
                                  qtype, _stream(stream, x)))
+
+
+def iqnn_quantize_pad(x, q, n, h, w, c, pad, c_pad, scale, zp, per_channel, qtype, stream=None):
+    _check(lib().iqnn_quantize_pad(_dev(x), _dev(q), n, h, w, c, pad, c_pad, _dev(scale), _dev(zp), int(per_channel),
+                                   qtype, _stream(stream, x)))
 
 
 def iqnn_qconv_packed_size(desc):

@@ -191,7 +191,43 @@ __global__ __launch_bounds__(256) void maxpool_kernel(const PoolParams p) {
     *reinterpret_cast<uint4*>(p.y + pix * p.c + g * 16) = make_uint4(m[0] ^ bias, m[1] ^ bias, m[2] ^ bias, m[3] ^ bias);
 }
 
+// Quantize into a spatially padded NHWC tensor with c_pad >= c channels: every
+// border pixel and every extra channel holds the zero-point code (the real value 0),
+// which is what a convolution's zero padding means in the quantized domain.  One
+// thread per output pixel.
+__global__ __launch_bounds__(256) void quantize_pad_kernel(const QuantPadParams p) {
+    const int hp = p.h + 2 * p.pad, wp = p.w + 2 * p.pad;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t total = (int64_t)p.n * hp * wp;
+    if (t >= total) return;
+    const int x = (int)(t % wp);
+    const int y = (int)((t / wp) % hp);
+    const int64_t n = t / ((int64_t)wp * hp);
+    const int iy = y - p.pad, ix = x - p.pad;
+    const bool inside = iy >= 0 && iy < p.h && ix >= 0 && ix < p.w;
+    const float* src = p.x + ((n * p.h + iy) * p.w + ix) * p.c;
+    uint8_t* dst = p.q + t * p.c_pad;
+    for (int c = 0; c < p.c_pad; ++c) {
+        const int32_t z = p.per_channel ? p.zp[c < p.c ? c : 0] : p.zp[0];
+        int32_t q = z;
+        if (inside && c < p.c) {
+            const float s = p.per_channel ? p.scale[c] : p.scale[0];
+            q = quant_one(src[c], s, z, p.qmin, p.qmax);
+        }
+        dst[c] = (uint8_t)(q & 0xFF);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_quantize_pad(const QuantPadParams& p, hipStream_t stream) {
+    const int64_t total = (int64_t)p.n * (p.h + 2 * p.pad) * (p.w + 2 * p.pad);
+    if (total == 0) return hipSuccess;
+    const int64_t blocks = (total + 255) / 256;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(quantize_pad_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_quantize(const QuantParams& p, hipStream_t stream) {
     const int64_t chunks = (p.total + 15) / 16;

@@ -7,7 +7,9 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <limits>
 #include <string>
 #include <vector>
@@ -142,7 +144,32 @@ iqnn_status gemm_layer(const iqnn_gemm_desc* d, Layer* L) {
     return check_layer(*L);
 }
 
-int64_t packed_size(const Layer& L) { return pack_geom(L.c_out, L.k).bytes; }
+// Optional tile override for tuning sweeps: IQNN_FORCE_TILE=0..4, read once.
+int forced_tile() {
+    static const int t = [] {
+        const char* e = std::getenv("IQNN_FORCE_TILE");
+        if (!e || !*e) return -1;
+        int v = std::atoi(e);
+        return (v >= 0 && v <= 4) ? v : -1;
+    }();
+    return t;
+}
+
+// The 4-channel gather of the pipelined kernel: 8-bit activations with exactly 4
+// channels and no padding (the input carries its own border, see
+// iqnn_quantize_pad).  The filter row is widened to KWP in {4, 8, 16} taps (zero
+// weights), so a stage of 64 K elements is a whole number of filter rows; the
+// widened window of the last output column must still lie inside the input row.
+int32_t c4_kwp(const Layer& L) { return L.kw <= 4 ? 4 : (L.kw <= 8 ? 8 : 16); }
+bool c4_path(const Layer& L) {
+    if (is_4bit(L.x_type) || L.c != 4 || L.ph != 0 || L.pw != 0 || L.kw > 16) return false;
+    if (L.n * L.h * L.w >= ((int64_t)1 << 31)) return false;   // pixel indices are int32
+    return (L.ow - 1) * (int64_t)L.sw + c4_kwp(L) <= L.w;
+}
+// K of the packed weights and of the kernel's loop.
+int64_t kdim(const Layer& L) { return c4_path(L) ? (int64_t)L.kh * c4_kwp(L) * 4 : L.k; }
+
+int64_t packed_size(const Layer& L) { return pack_geom(L.c_out, kdim(L)).bytes; }
 
 // Staged K position of logical K index k.  4-bit activations are unpacked in
 // 16-element segments as [0,2,4,6, 1,3,5,7, 8,10,12,14, 9,11,13,15] (low nibbles of
@@ -157,7 +184,9 @@ int64_t staged_k(int64_t k, bool act4) {
 // Writes the packed layer (layout in PackGeom) into host memory `dst` of g.bytes.
 iqnn_status prepack_into(const Layer& L, const void* w_host, const float* bias_host, float s_in,
                          const float* s_w_host, int per_channel, float s_out, float s_res, uint8_t* dst) {
-    const PackGeom g = pack_geom(L.c_out, L.k);
+    const PackGeom g = pack_geom(L.c_out, kdim(L));
+    const bool c4 = c4_path(L);
+    const int64_t kwp = c4_kwp(L);
     if (!scale_ok(s_in)) return fail(IQNN_ERR_INVALID_ARG, "input scale must be positive and finite");
     const bool raw = L.epi == E_RAW;
     const bool add = L.epi == E_ADD || L.epi == E_ADD_RELU;
@@ -168,7 +197,8 @@ iqnn_status prepack_into(const Layer& L, const void* w_host, const float* bias_h
     std::memset(dst, 0, (size_t)g.bytes);
     int32_t* bias = reinterpret_cast<int32_t*>(dst);
     float* mult = reinterpret_cast<float*>(dst + (size_t)g.ocp * 4);
-    float* mres = reinterpret_cast<float*>(dst + (size_t)g.ocp * 8);
+    float* mres = reinterpret_cast<float*>(dst + (size_t)g.ocp * 8 + kHdrMres);
+    std::memset(dst + (size_t)g.ocp * 8 + kHdrPad, L.z_in & 0xFF, 64);   // padding row: raw Z_in codes
     int8_t* wp = reinterpret_cast<int8_t*>(dst + g.w_off);
 
     const bool act4 = is_4bit(L.x_type);
@@ -213,18 +243,26 @@ iqnn_status prepack_into(const Layer& L, const void* w_host, const float* bias_h
         bias[oc] = (int32_t)fold;
         if (!raw) {
             const float m = sw_in / s_out;
-            if (!normal_ok(m))
-                return fail(IQNN_ERR_INVALID_ARG, "requant multiplier of channel %lld is not a normal float", (long long)oc);
+            if (!normal_ok(m) || m > 1e20f)
+                return fail(IQNN_ERR_INVALID_ARG, "requant multiplier of channel %lld is not a normal float in [FLT_MIN, 1e20]", (long long)oc);
             mult[oc] = m;
         } else {
             mult[oc] = 1.0f;
         }
         int8_t* dst = wp + (int64_t)packed_row_of_channel((int32_t)oc) * g.kp;
-        for (int64_t k = 0; k < L.k; ++k) dst[staged_k(k, act4)] = (int8_t)row[(size_t)k];
+        for (int64_t k = 0; k < L.k; ++k) {
+            int64_t pos = staged_k(k, act4);
+            if (c4) {   // (kh, kw, ci) -> (kh, kw in a row widened to kwp taps, ci)
+                const int64_t kh = k / (L.kw * 4), kw = (k / 4) % L.kw, ci = k % 4;
+                pos = (kh * kwp + kw) * 4 + ci;
+            }
+            dst[pos] = (int8_t)row[(size_t)k];
+        }
     }
     if (add) {
         const float m = s_res / s_out;
-        if (!normal_ok(m)) return fail(IQNN_ERR_INVALID_ARG, "residual multiplier is not a normal float");
+        if (!normal_ok(m) || m > 1e20f)
+            return fail(IQNN_ERR_INVALID_ARG, "residual multiplier is not a normal float in [FLT_MIN, 1e20]");
         mres[0] = m;
     }
     return ok();
@@ -234,7 +272,7 @@ iqnn_status prepack_host(const Layer& L, const void* w_host, const float* bias_h
                          const float* s_w_host, int per_channel, float s_out, float s_res, void* packed_host,
                          size_t packed_bytes) {
     if (!w_host || !s_w_host || !packed_host) return fail(IQNN_ERR_INVALID_ARG, "null weight, scale or output pointer");
-    const PackGeom g = pack_geom(L.c_out, L.k);
+    const PackGeom g = pack_geom(L.c_out, kdim(L));
     if ((int64_t)packed_bytes < g.bytes)
         return fail(IQNN_ERR_INVALID_ARG, "packed buffer has %zu bytes, needs %lld", packed_bytes, (long long)g.bytes);
     return prepack_into(L, w_host, bias_host, s_in, s_w_host, per_channel, s_out, s_res,
@@ -245,7 +283,7 @@ iqnn_status prepack_dev(const Layer& L, const void* w_host, const float* bias_ho
                         const float* s_w_host, int per_channel, float s_out, float s_res, void* packed_dev,
                         size_t packed_bytes, hipStream_t stream) {
     if (!w_host || !s_w_host || !packed_dev) return fail(IQNN_ERR_INVALID_ARG, "null weight, scale or output pointer");
-    const PackGeom g = pack_geom(L.c_out, L.k);
+    const PackGeom g = pack_geom(L.c_out, kdim(L));
     if ((int64_t)packed_bytes < g.bytes)
         return fail(IQNN_ERR_INVALID_ARG, "packed buffer has %zu bytes, needs %lld", packed_bytes, (long long)g.bytes);
     if (!aligned(packed_dev, 256)) return fail(IQNN_ERR_ALIGNMENT, "packed buffer must be 256-byte aligned");
@@ -265,7 +303,8 @@ iqnn_status forward(const Layer& L, const void* x, const void* packed, const voi
     if (!aligned(x, 16) || !aligned(y, 16) || (add && !aligned(res, 16)))
         return fail(IQNN_ERR_ALIGNMENT, "activation, output and residual pointers must be 16-byte aligned");
     if (!aligned(packed, 256)) return fail(IQNN_ERR_ALIGNMENT, "packed buffer must be 256-byte aligned");
-    const PackGeom g = pack_geom(L.c_out, L.k);
+    const PackGeom g = pack_geom(L.c_out, kdim(L));
+    const bool c4 = c4_path(L);
 
     ConvParams p;
     std::memset(&p, 0, sizeof p);
@@ -273,7 +312,8 @@ iqnn_status forward(const Layer& L, const void* x, const void* packed, const voi
     p.w = reinterpret_cast<const int8_t*>(static_cast<const uint8_t*>(packed) + g.w_off);
     p.bias = static_cast<const int32_t*>(packed);
     p.mult = reinterpret_cast<const float*>(static_cast<const uint8_t*>(packed) + (size_t)g.ocp * 4);
-    p.m_res = reinterpret_cast<const float*>(static_cast<const uint8_t*>(packed) + (size_t)g.ocp * 8);
+    p.m_res = reinterpret_cast<const float*>(static_cast<const uint8_t*>(packed) + (size_t)g.ocp * 8 + kHdrMres);
+    p.pad_row = static_cast<const uint8_t*>(packed) + (size_t)g.ocp * 8 + kHdrPad;
     p.res = add ? static_cast<const uint8_t*>(res) : nullptr;
     p.y = static_cast<uint8_t*>(y);
     p.m = L.m;
@@ -282,8 +322,8 @@ iqnn_status forward(const Layer& L, const void* x, const void* packed, const voi
     p.c = (int32_t)L.c;
     p.oh = (int32_t)(L.oh > 0x7FFFFFFF ? 0x7FFFFFFF : L.oh);
     p.ow = (int32_t)(L.ow > 0x7FFFFFFF ? 0x7FFFFFFF : L.ow);
-    p.kh = L.kh; p.kw = L.kw; p.sh = L.sh; p.sw = L.sw; p.ph = L.ph; p.pw = L.pw;
-    p.k = (int32_t)L.k;
+    p.kh = L.kh; p.kw = c4 ? c4_kwp(L) : L.kw; p.sh = L.sh; p.sw = L.sw; p.ph = L.ph; p.pw = L.pw;
+    p.k = (int32_t)kdim(L);
     p.kp = g.kp;
     p.c_out = (int32_t)L.c_out;
     const uint32_t pad_byte = (L.x_type == T_UINT8) ? ((uint32_t)L.z_in ^ 0x80u) & 0xFF : (uint32_t)L.z_in & 0xFF;
@@ -298,14 +338,24 @@ iqnn_status forward(const Layer& L, const void* x, const void* packed, const voi
     if (L.epi != E_RAW) {
         int32_t lo, hi;
         code_range(L.y_type, &lo, &hi);
-        p.lo = (float)(lo - L.z_out);
-        p.hi = (float)(hi - L.z_out);
+        const int32_t shift = L.y_type == T_INT8 ? 128 : (L.y_type == T_INT4 ? 8 : 0);
+        const bool relu = L.epi == E_RELU || L.epi == E_ADD_RELU;
+        const int32_t low = relu ? std::max(lo, L.z_out) : lo;   // passive ReLU: clamp at Z_out
+        p.out_zf = (float)(L.z_out + shift);
+        p.lo = (float)(low + shift);
+        p.hi = (float)(hi + shift);
+        p.out_xor = L.y_type == T_INT8 ? 0x80808080u : (L.y_type == T_INT4 ? 0x88888888u : 0u);
+    }
+    if (L.epi == E_ADD || L.epi == E_ADD_RELU) {
+        const int32_t rshift = L.res_type == T_INT8 ? 128 : (L.res_type == T_INT4 ? 8 : 0);
+        p.res_zf = (float)(L.z_res + rshift);
+        p.res_xor = L.res_type == T_INT8 ? 0x80808080u : (L.res_type == T_INT4 ? 0x88888888u : 0u);
     }
     p.vec_store = L.c_out % 16 == 0;
-    const int gather = is_4bit(L.x_type) ? GATHER_B4 : (L.c % 16 == 0 ? GATHER_B8 : GATHER_B8_ELEM);
-    const bool is_1x1 = gather != GATHER_B8_ELEM && L.kh == 1 && L.kw == 1 && L.sh == 1 && L.sw == 1 &&
+    const int gather = is_4bit(L.x_type) ? GATHER_B4 : (L.c % 16 == 0 ? GATHER_B8 : (c4 ? GATHER_C4 : GATHER_B8_ELEM));
+    const bool is_1x1 = gather != GATHER_B8_ELEM && gather != GATHER_C4 && L.kh == 1 && L.kw == 1 && L.sh == 1 && L.sw == 1 &&
                         L.ph == 0 && L.pw == 0;
-    hipError_t e = launch_qconv(p, gather, is_1x1, stream);
+    hipError_t e = launch_qconv(p, gather, is_1x1, stream, forced_tile());
     if (e != hipSuccess) return fail(IQNN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }
@@ -364,6 +414,25 @@ iqnn_status iqnn_dequantize(const void* q_dev, float* x_dev, int64_t outer, int6
                     per_channel ? 1 : 0, qtype};
     hipError_t e = launch_dequantize(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(IQNN_ERR_HIP, "dequantize launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+iqnn_status iqnn_quantize_pad(const float* x_dev, void* q_dev, int32_t n, int32_t h, int32_t w, int32_t c,
+                              int32_t pad, int32_t c_pad, const float* scale_dev, const int32_t* zp_dev,
+                              int per_channel, int32_t qtype, void* stream) {
+    int32_t lo, hi;
+    if (qtype != T_INT8 && qtype != T_UINT8) return fail(IQNN_ERR_UNSUPPORTED, "quantize_pad: 8-bit codes only");
+    code_range(qtype, &lo, &hi);
+    if (n < 0 || h <= 0 || w <= 0 || c <= 0 || pad < 0 || c_pad < c)
+        return fail(IQNN_ERR_INVALID_ARG, "quantize_pad: bad sizes (need c_pad >= c, pad >= 0)");
+    if ((int64_t)(h + 2 * pad) * (w + 2 * pad) * c_pad > ((int64_t)1 << 40))
+        return fail(IQNN_ERR_UNSUPPORTED, "quantize_pad: output too large");
+    if (n > 0 && (!x_dev || !q_dev || !scale_dev || !zp_dev)) return fail(IQNN_ERR_INVALID_ARG, "quantize_pad: null pointer");
+    if (!aligned(x_dev, 4) || !aligned(q_dev, 4)) return fail(IQNN_ERR_ALIGNMENT, "quantize_pad: misaligned pointer");
+    QuantPadParams p{x_dev, static_cast<uint8_t*>(q_dev), scale_dev, zp_dev, n, h, w, c, pad, c_pad,
+                     per_channel ? 1 : 0, lo, hi};
+    hipError_t e = launch_quantize_pad(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(IQNN_ERR_HIP, "quantize_pad launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 

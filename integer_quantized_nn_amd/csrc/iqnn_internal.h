@@ -15,13 +15,14 @@ enum : int32_t { E_NONE = 0, E_RELU = 1, E_ADD = 2, E_ADD_RELU = 3, E_RAW = 4 };
 enum : int32_t {
     GATHER_B8 = 0,     // 8-bit codes, C_in % 16 == 0: one 16-byte load per K segment
     GATHER_B4 = 1,     // 4-bit codes, C_in % 16 == 0: one 8-byte load, unpacked to 16 int8
-    GATHER_B8_ELEM = 2 // 8-bit codes, any C_in: element-wise gather (e.g. a 3-channel stem)
+    GATHER_B8_ELEM = 2, // 8-bit codes, any C_in: element-wise gather
+    GATHER_C4 = 3       // 8-bit codes, C_in == 4, no padding: one 16-byte load = 4 taps x 4 channels
 };
 
 // Geometry of the prepacked layer buffer (device).  All offsets in bytes.
 //   [0, 4*ocp)            int32  folded bias per output channel (physical order)
 //   [4*ocp, 8*ocp)        float  requant multiplier M[c]
-//   [8*ocp, 8*ocp+256)    float  M_res, padding
+//   [8*ocp, 8*ocp+256)    header: float M_res at +0, 64 pad-code bytes at +64
 //   [w_off, w_off+ocp*kp) int8   weights, rows in kernel order, K padded to kp
 struct PackGeom {
     int32_t ocp;    // output channels padded to a multiple of kOcPad
@@ -36,16 +37,19 @@ constexpr int kBK = 128;      // K elements staged per pipeline step
 
 PackGeom pack_geom(int64_t c_out, int64_t k);
 
-// Position of physical output channel `oc` in the packed weight rows.  Each wave
-// owns 64 channels as four 16-row MFMA tiles; lane group g of the 16x16 MFMA
-// accumulator holds rows 4g..4g+3 of every tile.  Swapping the tile index and the
-// lane-group index inside each 64-channel block makes the 16 values one lane holds
-// 16 consecutive physical channels.
+// Position of physical output channel `oc` in the packed weight rows.  A 32x32
+// MFMA accumulator gives lane half h the rows 8j + 4h + r (j, r = 0..3) of its
+// 32-row tile.  Storing channel 32b + 16h + 4j + r at row 32b + 8j + 4h + r makes
+// the 16 values a lane holds 16 consecutive physical channels.
 inline int32_t packed_row_of_channel(int32_t oc) {
-    int32_t blk = oc & ~63, w = oc & 63;
-    int32_t g = w >> 4, t = (w >> 2) & 3, r = w & 3;
-    return blk + t * 16 + g * 4 + r;
+    int32_t blk = oc & ~31, w = oc & 31;
+    int32_t h = w >> 4, j = (w >> 2) & 3, r = w & 3;
+    return blk + j * 8 + h * 4 + r;
 }
+
+// Byte offsets inside the packed layer header (after the two per-channel arrays).
+constexpr int kHdrMres = 0;     // float M_res
+constexpr int kHdrPad = 64;     // 64 bytes of the input zero-point code (the padding row)
 
 struct ConvParams {
     const uint8_t* x;
@@ -62,17 +66,30 @@ struct ConvParams {
     int32_t kp;               // padded K = weight row stride (bytes)
     int32_t c_out;
     int32_t n_oc_tiles;
+    int32_t n_px_tiles;       // set by the launcher
+    int32_t group_px;         // pixel tiles per rasterization group (set by the launcher)
     uint32_t pad_word;        // four copies of the staged padding byte
     uint32_t x_xor;           // 0x80808080 for UINT8 activations, else 0
     int32_t x_signed4;        // INT4 activations: sign-extend nibbles
     int32_t y_type, res_type, epi;
     int32_t z_out, z_res;
     const float* m_res;       // residual multiplier S_res/S_out (in the packed buffer)
-    float lo, hi;             // clip bounds minus z_out, as floats
+    const uint8_t* pad_row;   // 64 bytes of the raw input zero-point code (in the packed buffer)
+    // Epilogue constants (host-computed).  Outputs are formed as unsigned codes
+    // shifted by out_shift = 128 (INT8) / 8 (INT4) / 0: out_zf = Z_out + out_shift,
+    // [lo, hi] = [Q_MIN (or max(Q_MIN, Z_out) with ReLU), Q_MAX] + out_shift, and
+    // out_xor undoes the shift on the packed word.  Residual codes are read the same
+    // way: (code ^ res_xor) - res_zf == r - Z_res.
+    float out_zf, lo, hi;
+    uint32_t out_xor;
+    float res_zf;
+    uint32_t res_xor;
     int32_t vec_store;        // C_out % 16 == 0: vector stores
 };
 
-hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_t stream);
+// tile < 0 picks the pipelined kernel's tile configuration from the layer shape;
+// 0..4 force one (the IQNN_FORCE_TILE environment variable, for tuning sweeps).
+hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_t stream, int tile);
 
 struct QuantParams {
     const float* x;
@@ -96,6 +113,17 @@ struct DequantParams {
     int32_t qtype;
 };
 hipError_t launch_dequantize(const DequantParams& p, hipStream_t stream);
+
+struct QuantPadParams {
+    const float* x;           // [n][h][w][c]
+    uint8_t* q;               // [n][h+2*pad][w+2*pad][c_pad]
+    const float* scale;
+    const int32_t* zp;
+    int32_t n, h, w, c, pad, c_pad;
+    int32_t per_channel;
+    int32_t qmin, qmax;
+};
+hipError_t launch_quantize_pad(const QuantPadParams& p, hipStream_t stream);
 
 struct PoolParams {
     const uint8_t* x;

@@ -7,28 +7,38 @@
 //   y[p][oc]   = epilogue(a)                          requant / ReLU / residual add
 // where p runs over output pixels (n, oh, ow) and k over (kh, kw, ci).  The im2col
 // matrix A is never built: each workgroup gathers its tile straight from the NHWC
-// activations while staging it into LDS, as the MegEngine article describes for
-// its global->shared load (conv 算子優化, after Fig. 5).
+// activations on the way into LDS, as the MegEngine article describes for its
+// global->shared load (conv 算子優化, after Fig. 5).
 //
-// gfx950 design
-//   * Contraction on v_mfma_i32_16x16x64_i8 (signed int8 only).  UINT8 activations
-//     are shifted to int8 with XOR 0x80 during staging (q - 128); the host folds
-//     the +128*sum(W) back into the bias.  4-bit activations are unpacked to int8
-//     during staging (UINT4 zero-extended, INT4 sign-extended): CDNA4 has no 4-bit
-//     integer MFMA, so 4-bit data saves HBM bytes, not MFMA cycles.
-//   * The output channel is the MFMA row (A operand = weights) and the pixel the
-//     MFMA column (B operand = activations), so the accumulator a lane holds runs
-//     along channels -- the NHWC-friendly orientation the MegEngine article gets by
-//     transposing its output (conv 算子優化, Fig. 7 and after).  The prepacked
-//     weight rows are permuted (the column-permutation identity of its Fig. 8) so
-//     each lane ends with 16 consecutive channels: one 16-byte store per pixel.
-//   * 256 threads = 4 waves; each wave owns 64 channels x (BN/WN) pixels.  K is
-//     staged 128 elements at a time through double-buffered LDS with rows padded
-//     to 144 bytes, which keeps the 16-byte fragment reads bank-conflict free.
-//   * Workgroup ids are remapped so that consecutive tiles land on the same XCD
-//     (workgroups are dealt round-robin over the 8 XCDs, each with its own L2).
-//   * The epilogue runs in registers in strict binary32 (no contraction), with
+// gfx950 design shared by both kernels below
+//   * Contraction on v_mfma_i32_32x32x32_i8 (signed int8 only; it sustains ~87 % of
+//     the int8 peak on MI355X, more than the 16x16x64 form).  UINT8 activations
+//     enter the MFMA as q - 128 (XOR 0x80); the host folds +128*sum(W) into the
+//     bias.  4-bit activations are unpacked to int8 on chip (UINT4 zero-extended,
+//     INT4 sign-extended): CDNA4 has no 4-bit integer MFMA, so 4-bit data saves HBM
+//     bytes, not MFMA cycles.
+//   * Output channels are the MFMA rows (A operand = weights), pixels the columns
+//     (B operand = activations): the accumulator a lane holds runs along channels,
+//     the NHWC-friendly orientation the MegEngine article gets by transposing its
+//     output (conv 算子優化, Fig. 7 and after).  A 32x32 accumulator gives lane half
+//     h the rows 8j+4h+r; the prepacked weight rows are permuted inside every
+//     32-channel block (the column-permutation identity of the article's Fig. 8) so
+//     those 16 values are 16 consecutive channels: one 16-byte store per pixel.
+//   * 256 threads = 4 waves.  Workgroup ids are remapped so consecutive tiles land
+//     on the same XCD (ids are dealt round-robin over 8 XCDs, each with its own L2).
+//   * The epilogue runs in registers in strict binary32 (no contraction) with
 //     round-half-to-even, then packs and stores.
+//
+// qconv_pipe (8-bit activations, C_in % 64 == 0): a 4-deep ring of LDS stages
+//   filled by global_load_lds_dwordx4 (global -> LDS without registers).  The
+//   uint8 shift is applied to the fragments after they are read from LDS, and
+//   out-of-image taps / rows past the end load a 16-byte row of pad codes kept in
+//   the packed layer, so the DMA needs no per-element work.  LDS rows are 64 bytes
+//   with their four 16-byte slots XOR-swizzled, which keeps both the DMA writes and
+//   the 16-byte fragment reads free of bank conflicts.
+// qconv_igemm (every other case: 4-bit activations, C_in % 64 != 0, the 3-channel
+//   stem): register-staged double buffering, transforms and padding applied while
+//   staging, rows padded to 144 bytes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -40,8 +50,11 @@ namespace iqnn {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
-constexpr int kLdsStride = kBK + 16;   // bytes per staged row
+constexpr int kLdsStride = kBK + 16;   // bytes per staged row (register-staged kernel)
 constexpr int kSegPerRow = kBK / 16;   // 16-element segments per staged row (8)
 constexpr int kRowsPerPass = 256 / kSegPerRow;
 
@@ -54,28 +67,142 @@ __device__ __forceinline__ uint32_t unpack_hi(uint32_t v, int sign) {
     return sign ? (n | ((n & 0x08080808u) * 0x1Eu)) : n;
 }
 
-// One requantized output, strict binary32, one rounding per operation.
-__device__ __forceinline__ int32_t requant_one(int32_t a, float m, int32_t rcode, bool add, bool relu,
-                                               float m_res, const ConvParams& p) {
-    float t = (float)a * m;
-    if (add) {
-        float d = (float)(rcode - p.z_res);
-        float u = d * m_res;
-        t = t + u;
-    }
-    if (relu) t = (t > 0.0f) ? t : 0.0f;
-    float r = __builtin_rintf(t);
-    r = fminf(fmaxf(r, p.lo), p.hi);
-    return (int32_t)r + p.z_out;
+__device__ __forceinline__ int xcd_remap(int bid, int G) {
+    const int xcd = bid & 7, idx = bid >> 3;
+    const int q8 = G >> 3, r8 = G & 7;
+    return (xcd < r8) ? xcd * (q8 + 1) + idx : r8 * (q8 + 1) + (xcd - r8) * q8 + idx;
 }
 
-__device__ __forceinline__ int32_t res_code(const uint32_t* rw, int i, int type) {
-    if (type == T_UINT8) return (int32_t)((rw[i >> 2] >> (8 * (i & 3))) & 0xFF);
-    if (type == T_INT8) return (int32_t)(int8_t)((rw[i >> 2] >> (8 * (i & 3))) & 0xFF);
-    int32_t nib = (int32_t)((rw[i >> 3] >> (4 * (i & 7))) & 0xF);
-    if (type == T_INT4 && nib >= 8) nib -= 16;
-    return nib;
+// Tile of workgroup `bid`.  Logical ids are first made contiguous per XCD, then
+// walked in groups of `group_px` pixel tiles: inside a group, channel tiles are the
+// outer loop and pixel tiles the inner one, so the workgroups that run together on
+// one XCD share a few activation tiles and one weight tile, and that working set
+// stays in the XCD's L2.
+__device__ __forceinline__ void tile_of(int bid, int G, int n_oc, int n_px, int group_px, int& tile_oc,
+                                        int& tile_px) {
+    const int L = xcd_remap(bid, G);
+    const int span = group_px * n_oc;
+    const int pg = L / span;
+    const int rem = L - pg * span;
+    const int first = pg * group_px;
+    const int gsize = min(group_px, n_px - first);
+    tile_oc = rem / gsize;
+    tile_px = first + (rem - tile_oc * gsize);
 }
+
+// Per-lane channel parameters for 16 consecutive channels starting at ocb.
+struct ChanParams {
+    int32_t bias[16];
+    float mult[16];
+};
+
+__device__ __forceinline__ void load_chan(const ConvParams& p, int ocb, ChanParams& c) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        int4 bv = *reinterpret_cast<const int4*>(p.bias + ocb + 4 * j);
+        float4 mv = *reinterpret_cast<const float4*>(p.mult + ocb + 4 * j);
+        c.bias[4 * j] = bv.x; c.bias[4 * j + 1] = bv.y; c.bias[4 * j + 2] = bv.z; c.bias[4 * j + 3] = bv.w;
+        c.mult[4 * j] = mv.x; c.mult[4 * j + 1] = mv.y; c.mult[4 * j + 2] = mv.z; c.mult[4 * j + 3] = mv.w;
+    }
+}
+
+// Residual words of 16 consecutive channels (8-bit: 4 words; 4-bit: 2 words).
+__device__ __forceinline__ void load_res16(const ConvParams& p, int64_t oidx, int ocb, uint32_t rw[4]) {
+    rw[0] = rw[1] = rw[2] = rw[3] = 0;
+    if (p.res_type == T_INT8 || p.res_type == T_UINT8) {
+        if (p.vec_store) {
+            uint4 v = *reinterpret_cast<const uint4*>(p.res + oidx);
+            rw[0] = v.x; rw[1] = v.y; rw[2] = v.z; rw[3] = v.w;
+        } else {
+            for (int j = 0; j < 16 && ocb + j < p.c_out; ++j) rw[j >> 2] |= (uint32_t)p.res[oidx + j] << (8 * (j & 3));
+        }
+    } else {
+        if (p.vec_store) {
+            uint2 v = *reinterpret_cast<const uint2*>(p.res + (oidx >> 1));
+            rw[0] = v.x; rw[1] = v.y;
+        } else {
+            for (int j = 0; j < 8 && ocb + 2 * j < p.c_out; ++j)
+                rw[j >> 2] |= (uint32_t)p.res[(oidx >> 1) + j] << (8 * (j & 3));
+        }
+    }
+}
+
+// Requantizing epilogue of 16 consecutive channels ocb..ocb+15 of output pixel pix,
+// strict binary32 with one rounding per operation:
+//   t = float(acc + bias) * M[c];   t = t + float(r - Z_res) * M_res   (ADD)
+//   y = clip(rne(t) + Z_out, lo, Q_MAX)
+// ReLU is the passive clamp at the real value 0 ("Quantization" blog, 量化激活函数):
+// since rne is monotone and rne(0) = 0, clip(rne(max(t,0)) + Z) == clip(rne(t) + Z)
+// with the lower bound raised to max(Q_MIN, Z_out); the host folds it into `lo`.
+// Signed outputs are produced shifted into the unsigned range (+128 / +8) so one
+// v_cvt_pk_u8_f32 packs each byte, and the shift is undone with one XOR per word.
+// Every intermediate is an exact integer below 2^24 or is clamped away, so this is
+// bit-identical to rounding, adding Z_out as an integer and clipping.
+__device__ __forceinline__ void epi_store16(const ConvParams& p, const v16i& acc, const int32_t* bias,
+                                            const float* mult, uint32_t rw[4], int ocb, int64_t pix, bool add,
+                                            float m_res) {
+    const int64_t oidx = pix * p.c_out + ocb;   // element index of the first channel
+    if (p.epi == E_RAW) {
+        int32_t a[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) a[j] = acc[j] + bias[j];
+        int32_t* yo = reinterpret_cast<int32_t*>(p.y) + oidx;
+        if (p.vec_store) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<int4*>(yo + 4 * j) = make_int4(a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]);
+        } else {
+            for (int j = 0; j < 16 && ocb + j < p.c_out; ++j) yo[j] = a[j];
+        }
+        return;
+    }
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = (float)(acc[j] + bias[j]) * mult[j];
+    if (add) {
+        const bool r8 = p.res_type == T_INT8 || p.res_type == T_UINT8;
+        uint32_t w[4] = {rw[0] ^ p.res_xor, rw[1] ^ p.res_xor, rw[2] ^ p.res_xor, rw[3] ^ p.res_xor};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const uint32_t code = r8 ? (w[j >> 2] >> (8 * (j & 3))) & 0xFFu : (w[j >> 3] >> (4 * (j & 7))) & 0xFu;
+            const float d = (float)code - p.res_zf;   // == float(r - Z_res), exact
+            const float u = d * m_res;
+            v[j] = v[j] + u;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = __builtin_amdgcn_fmed3f(__builtin_rintf(v[j]) + p.out_zf, p.lo, p.hi);
+    if (p.y_type == T_INT8 || p.y_type == T_UINT8) {
+        uint32_t ow[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            uint32_t x = __builtin_amdgcn_cvt_pk_u8_f32(v[4 * d], 0, 0);
+            x = __builtin_amdgcn_cvt_pk_u8_f32(v[4 * d + 1], 1, x);
+            x = __builtin_amdgcn_cvt_pk_u8_f32(v[4 * d + 2], 2, x);
+            x = __builtin_amdgcn_cvt_pk_u8_f32(v[4 * d + 3], 3, x);
+            ow[d] = x ^ p.out_xor;
+        }
+        if (p.vec_store) {
+            *reinterpret_cast<uint4*>(p.y + oidx) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+        } else {
+            for (int j = 0; j < 16 && ocb + j < p.c_out; ++j) p.y[oidx + j] = (uint8_t)(ow[j >> 2] >> (8 * (j & 3)));
+        }
+    } else {
+        uint32_t ow[2] = {0, 0};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) ow[j >> 3] |= ((uint32_t)v[j]) << (4 * (j & 7));
+        ow[0] ^= p.out_xor;
+        ow[1] ^= p.out_xor;
+        if (p.vec_store) {
+            *reinterpret_cast<uint2*>(p.y + (oidx >> 1)) = make_uint2(ow[0], ow[1]);
+        } else {
+            for (int j = 0; j < 8 && ocb + 2 * j < p.c_out; ++j)
+                p.y[(oidx >> 1) + j] = (uint8_t)(ow[j >> 2] >> (8 * (j & 3)));
+        }
+    }
+}
+
+// ============================================================ register-staged kernel
 
 // The second launch bound is the number of workgroups per CU that the LDS
 // footprint allows (160 KB of LDS per CU on gfx950).
@@ -83,12 +210,13 @@ template <int BM, int BN, int WM, int WN, int GATHER, bool IS1X1>
 __global__ __launch_bounds__(256, (2 * 2 * (BM + BN) * kLdsStride <= 160 * 1024 ? 2 : 1))
 void qconv_igemm(const ConvParams p) {
     constexpr int WPX = BN / WN;      // pixels per wave
-    constexpr int TN = WPX / 16;      // MFMA tiles along pixels per wave
+    constexpr int TN = WPX / 32;      // 32x32 MFMA tiles along pixels per wave
+    constexpr int TM = 2;             // 32x32 MFMA tiles along channels per wave (64 channels)
     constexpr int A_SEGS = BM * kSegPerRow / 256;
     constexpr int B_SEGS = BN * kSegPerRow / 256;
     static_assert(BM / WM == 64, "a wave owns 64 output channels");
     static_assert(WM * WN == 4, "four waves");
-    static_assert(A_SEGS >= 1 && B_SEGS >= 1, "tile too small");
+    static_assert(A_SEGS >= 1 && B_SEGS >= 1 && TN >= 1, "tile too small");
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + BN) * kLdsStride];
 
@@ -98,15 +226,8 @@ void qconv_igemm(const ConvParams p) {
     const int wave_oc = wave % WM;
     const int wave_px = wave / WM;
 
-    // XCD-aware remap of the workgroup id: the hardware deals ids round-robin over
-    // 8 XCDs; give each XCD a contiguous range of logical tiles.
-    const int G = gridDim.x;
-    const int bid = blockIdx.x;
-    const int xcd = bid & 7, idx = bid >> 3;
-    const int q8 = G >> 3, r8 = G & 7;
-    const int L = (xcd < r8) ? xcd * (q8 + 1) + idx : r8 * (q8 + 1) + (xcd - r8) * q8 + idx;
-    const int tile_oc = L % p.n_oc_tiles;
-    const int tile_px = L / p.n_oc_tiles;
+    int tile_oc, tile_px;
+    tile_of(blockIdx.x, gridDim.x, p.n_oc_tiles, p.n_px_tiles, p.group_px, tile_oc, tile_px);
     const int oc0 = tile_oc * BM;
     const int64_t px0 = (int64_t)tile_px * BN;
 
@@ -249,15 +370,15 @@ void qconv_igemm(const ConvParams p) {
         }
     };
 
-    v4i acc[4][TN];
+    v16i acc[TM][TN];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < TM; ++t)
 #pragma unroll
-        for (int u = 0; u < TN; ++u) acc[t][u] = v4i{0, 0, 0, 0};
+        for (int u = 0; u < TN; ++u) acc[t][u] = v16i{};
 
     const int nstages = (p.kp + kBK - 1) / kBK;
-    const int frag_row = lane & 15;
-    const int frag_col = (lane >> 4) * 16;
+    const int frag_row = lane & 31;
+    const int frag_col = (lane >> 5) * 16;
     const int a_row0 = wave_oc * 64 + frag_row;
     const int b_row0 = BM + wave_px * WPX + frag_row;
 
@@ -275,127 +396,363 @@ void qconv_igemm(const ConvParams p) {
         }
         const uint8_t* L0 = lds[buf];
 #pragma unroll
-        for (int kk = 0; kk < kBK / 64; ++kk) {
-            if (s * kBK + kk * 64 >= p.kp) break;
-            v4i a[4], b[TN];
+        for (int kk = 0; kk < kBK / 32; ++kk) {
+            if (s * kBK + kk * 32 >= p.kp) break;
+            v4i a[TM], b[TN];
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                a[t] = *reinterpret_cast<const v4i*>(&L0[(a_row0 + t * 16) * kLdsStride + kk * 64 + frag_col]);
+            for (int t = 0; t < TM; ++t)
+                a[t] = *reinterpret_cast<const v4i*>(&L0[(a_row0 + t * 32) * kLdsStride + kk * 32 + frag_col]);
 #pragma unroll
             for (int u = 0; u < TN; ++u)
-                b[u] = *reinterpret_cast<const v4i*>(&L0[(b_row0 + u * 16) * kLdsStride + kk * 64 + frag_col]);
+                b[u] = *reinterpret_cast<const v4i*>(&L0[(b_row0 + u * 32) * kLdsStride + kk * 32 + frag_col]);
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < TM; ++t)
 #pragma unroll
                 for (int u = 0; u < TN; ++u)
-                    acc[t][u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], b[u], acc[t][u], 0, 0, 0);
+                    acc[t][u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[t], b[u], acc[t][u], 0, 0, 0);
         }
         if (more) store_stage(buf ^ 1);
         __syncthreads();
     }
 
     // ---------------------------------------------------------------- epilogue
-    // Lane group g holds MFMA rows 4g..4g+3 of each of the 4 channel tiles; with the
-    // packed row permutation these are physical channels ocb + 4t + r.
-    const int g = lane >> 4;
-    const int ocb = oc0 + wave_oc * 64 + g * 16;
-    if (ocb >= p.c_out) return;
     const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;
-    const bool relu = p.epi == E_RELU || p.epi == E_ADD_RELU;
     const float m_res = add ? *p.m_res : 0.0f;
-
-    int32_t bias[16];
-    float mult[16];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        int4 bv = *reinterpret_cast<const int4*>(p.bias + ocb + 4 * j);
-        float4 mv = *reinterpret_cast<const float4*>(p.mult + ocb + 4 * j);
-        bias[4 * j] = bv.x; bias[4 * j + 1] = bv.y; bias[4 * j + 2] = bv.z; bias[4 * j + 3] = bv.w;
-        mult[4 * j] = mv.x; mult[4 * j + 1] = mv.y; mult[4 * j + 2] = mv.z; mult[4 * j + 3] = mv.w;
-    }
-
+    for (int t = 0; t < TM; ++t) {
+        const int ocb = oc0 + wave_oc * 64 + t * 32 + (lane >> 5) * 16;
+        if (ocb >= p.c_out) continue;
+        ChanParams cp;
+        load_chan(p, ocb, cp);
 #pragma unroll
-    for (int u = 0; u < TN; ++u) {
-        const int64_t pix = px0 + wave_px * WPX + u * 16 + frag_row;
-        if (pix >= p.m) continue;
-        int32_t a[16];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) a[4 * t + r] = acc[t][u][r] + bias[4 * t + r];
-
-        const int64_t oidx = pix * p.c_out + ocb;   // element index of the first channel
-        if (p.epi == E_RAW) {
-            int32_t* yo = reinterpret_cast<int32_t*>(p.y) + oidx;
-            if (p.vec_store) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<int4*>(yo + 4 * j) = make_int4(a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]);
-            } else {
-                for (int j = 0; j < 16 && ocb + j < p.c_out; ++j) yo[j] = a[j];
-            }
-            continue;
-        }
-
-        uint32_t rw[4] = {0, 0, 0, 0};
-        if (add) {
-            if (p.res_type == T_INT8 || p.res_type == T_UINT8) {
-                if (p.vec_store) {
-                    uint4 v = *reinterpret_cast<const uint4*>(p.res + oidx);
-                    rw[0] = v.x; rw[1] = v.y; rw[2] = v.z; rw[3] = v.w;
-                } else {
-                    for (int j = 0; j < 16 && ocb + j < p.c_out; ++j)
-                        rw[j >> 2] |= (uint32_t)p.res[oidx + j] << (8 * (j & 3));
-                }
-            } else {
-                if (p.vec_store) {
-                    uint2 v = *reinterpret_cast<const uint2*>(p.res + (oidx >> 1));
-                    rw[0] = v.x; rw[1] = v.y;
-                } else {
-                    for (int j = 0; j < 8 && ocb + 2 * j < p.c_out; ++j)
-                        rw[j >> 2] |= (uint32_t)p.res[(oidx >> 1) + j] << (8 * (j & 3));
-                }
-            }
-        }
-
-        int32_t q[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-            q[j] = requant_one(a[j], mult[j], add ? res_code(rw, j, p.res_type) : 0, add, relu, m_res, p);
-
-        if (p.y_type == T_INT8 || p.y_type == T_UINT8) {
-            uint32_t ow[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                ow[j] = (uint32_t)(q[4 * j] & 0xFF) | ((uint32_t)(q[4 * j + 1] & 0xFF) << 8) |
-                        ((uint32_t)(q[4 * j + 2] & 0xFF) << 16) | ((uint32_t)(q[4 * j + 3] & 0xFF) << 24);
-            if (p.vec_store) {
-                *reinterpret_cast<uint4*>(p.y + oidx) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
-            } else {
-                for (int j = 0; j < 16 && ocb + j < p.c_out; ++j) p.y[oidx + j] = (uint8_t)(q[j] & 0xFF);
-            }
-        } else {
-            uint32_t ow[2] = {0, 0};
-#pragma unroll
-            for (int j = 0; j < 16; ++j) ow[j >> 3] |= (uint32_t)(q[j] & 0xF) << (4 * (j & 7));
-            if (p.vec_store) {
-                *reinterpret_cast<uint2*>(p.y + (oidx >> 1)) = make_uint2(ow[0], ow[1]);
-            } else {
-                for (int j = 0; j < 8 && ocb + 2 * j < p.c_out; ++j)
-                    p.y[(oidx >> 1) + j] = (uint8_t)((ow[j >> 2] >> (8 * (j & 3))) & 0xFF);
-            }
+        for (int u = 0; u < TN; ++u) {
+            const int64_t pix = px0 + wave_px * WPX + u * 32 + frag_row;
+            if (pix >= p.m) continue;
+            uint32_t rw[4] = {0, 0, 0, 0};
+            if (add) load_res16(p, pix * p.c_out + ocb, ocb, rw);
+            epi_store16(p, acc[t][u], cp.bias, cp.mult, rw, ocb, pix, add, m_res);
         }
     }
 }
 
+// ============================================================ pipelined kernel
+
+constexpr int kPipeBK = 64;     // K bytes per stage
+
+// XOR swizzle of the four 16-byte slots of a 64-byte LDS row.  Over any 16
+// consecutive rows (and any 8) the fragment reads of one slot hit distinct banks.
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+// s_waitcnt for vmcnt <= n only (expcnt and lgkmcnt left at their maximum).
+#define IQNN_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// One tile configuration of the pipelined kernel: block BM channels x BN pixels,
+// WM x (4/WM) waves, a ring of NST LDS stages.
+template <int BM_, int BN_, int WM_, int NST_>
+struct PipeCfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = 4 / WM_, NST = NST_;
+    static constexpr int WOC = BM / WM;     // channels per wave
+    static constexpr int WPX = BN / WN;     // pixels per wave
+    static constexpr int TM = WOC / 32, TN = WPX / 32;
+    static constexpr int STAGE = (BM + BN) * kPipeBK;
+    static constexpr int OCC = NST * STAGE <= 80 * 1024 ? 2 : 1;
+};
+
+// RES: 8-bit residual with C_out % 16 == 0, fetched into registers before the main
+// loop so its latency hides behind the contraction.
+// C4: the 4-channel gather (4-byte DMA per tap; see iqnn_api.cpp c4_path).
+template <class C, bool IS1X1, bool RES, bool C4>
+__global__ __launch_bounds__(256, C::OCC) void qconv_pipe(const ConvParams p) {
+    constexpr int BM = C::BM, BN = C::BN, WM = C::WM, NST = C::NST;
+    constexpr int TM = C::TM, TN = C::TN, STAGE = C::STAGE;
+    constexpr int A_INST = BM / 64;   // DMA instructions (16 rows each) per wave per stage
+    constexpr int B_INST = BN / 64;
+    constexpr int LOADS = A_INST + (C4 ? BN / 16 : B_INST);
+    static_assert(TM >= 1 && TN >= 1 && A_INST >= 1 && B_INST >= 1, "tile too small");
+    static_assert(NST == 3 || NST == 4, "ring depth");
+
+    // The ring is separate LDS arrays addressed with compile-time slot numbers, so the
+    // compiler can tell the DMA into one slot from the fragment reads of another and
+    // does not serialise them with a full vmcnt wait.
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds2[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds3[NST == 4 ? STAGE : 16];
+    __shared__ __attribute__((aligned(16))) int32_t cbias[BM];
+    __shared__ __attribute__((aligned(16))) float cmult[BM];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wave_oc = wave % WM;
+    const int wave_px = wave / WM;
+
+    int tile_oc, tile_px;
+    tile_of(blockIdx.x, gridDim.x, p.n_oc_tiles, p.n_px_tiles, p.group_px, tile_oc, tile_px);
+    const int oc0 = tile_oc * BM;
+    const int64_t px0 = (int64_t)tile_px * BN;
+
+    // channel parameters of this block (the packed arrays are padded past oc0 + BM)
+    int32_t my_bias = 0;
+    float my_mult = 0.0f;
+    if (tid < BM) {
+        my_bias = p.bias[oc0 + tid];
+        my_mult = p.mult[oc0 + tid];
+    }
+
+    // DMA lane assignment: instruction j of this wave fills 16 LDS rows; lane -> row
+    // (lane / 4), slot (lane % 4), which holds global K segment slot ^ swz(row).
+    const int drow = lane >> 2;
+    const int dslot = lane & 3;
+    const uint8_t* padrow = p.pad_row;
+
+    const int8_t* wsrc[A_INST];
+#pragma unroll
+    for (int j = 0; j < A_INST; ++j) {
+        const int row = wave * (BM / 4) + 16 * j + drow;
+        wsrc[j] = p.w + (int64_t)(oc0 + row) * p.kp + (dslot ^ swz(row)) * 16;
+    }
+    int64_t rbase[B_INST];
+    int32_t rih[B_INST], riw[B_INST];
+    int32_t bseg[B_INST];
+#pragma unroll
+    for (int j = 0; j < B_INST; ++j) {
+        const int row = wave * (BN / 4) + 16 * j + drow;
+        bseg[j] = (dslot ^ swz(row)) * 16;
+        const int64_t pix = px0 + row;
+        if (pix < p.m) {
+            if (IS1X1) {
+                rbase[j] = pix * p.c;
+                rih[j] = 0;
+                riw[j] = 0;
+            } else {
+                const int64_t ohw = (int64_t)p.oh * p.ow;
+                const int64_t n = pix / ohw;
+                const int32_t rem = (int32_t)(pix - n * ohw);
+                const int32_t oy = rem / p.ow, ox = rem - oy * p.ow;
+                rbase[j] = n * p.h * p.w_in * (int64_t)p.c;
+                rih[j] = oy * p.sh - p.ph;
+                riw[j] = ox * p.sw - p.pw;
+            }
+        } else {
+            rbase[j] = -1;
+            rih[j] = -(1 << 29);
+            riw[j] = -(1 << 29);
+        }
+    }
+
+    // 4-channel gather: each 4-byte DMA instruction fills 4 rows; lane -> row
+    // (lane / 16), 4-byte position (lane % 16) = tap j of slot s, holding K segment
+    // s ^ swz(row) of that row.
+    // With the filter row widened to KWP in {4, 8, 16} taps, a 64-element stage is 16
+    // taps = 16 / KWP whole filter rows, so a lane's tap column is the same in every
+    // stage and its filter row advances by 16 / KWP per stage.
+    constexpr int C4_INST = C4 ? BN / 16 : 1;
+    int32_t coff[C4_INST];    // input pixel index of this lane's tap at stage 0 (-1: row past the end)
+    int32_t cky[C4_INST];     // its filter row at stage 0
+    if constexpr (C4) {
+#pragma unroll
+        for (int j = 0; j < C4_INST; ++j) {
+            const int row = wave * (BN / 4) + 4 * j + (lane >> 4);
+            const int slot = (lane >> 2) & 3, jj = lane & 3;
+            const int tap0 = (slot ^ swz(row)) * 4 + jj;       // tap index inside the stage
+            const int ky0 = tap0 / p.kw, kx0 = tap0 - ky0 * p.kw;
+            const int64_t pix = px0 + row;
+            coff[j] = -1;
+            cky[j] = ky0;
+            if (pix < p.m) {
+                const int64_t ohw = (int64_t)p.oh * p.ow;
+                const int32_t n = (int32_t)(pix / ohw);
+                const int32_t rem = (int32_t)(pix - (int64_t)n * ohw);
+                const int32_t oy = rem / p.ow, ox = rem - oy * p.ow;
+                coff[j] = (n * p.h + oy * p.sh + ky0) * p.w_in + ox * p.sw + kx0;
+            }
+        }
+    }
+
+    const int nst = p.kp / kPipeBK;   // K % 64 == 0 on this path
+
+    // Issue the DMA of stage s into ring slot `dst`.  With C % 64 == 0 a 64-element K
+    // chunk lies inside one filter tap, so the tap is wave-uniform.
+    auto issue = [&](int s, uint8_t* dst) {
+        const int k0 = s * kPipeBK;
+#pragma unroll
+        for (int j = 0; j < A_INST; ++j) {
+            uint8_t* d = dst + (wave * (BM / 4) + 16 * j) * kPipeBK;
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(wsrc[j] + k0), (lds_ptr_t)d, 16, 0, 0);
+        }
+        if constexpr (C4) {
+#pragma unroll
+            for (int j = 0; j < C4_INST; ++j) {
+                uint8_t* d = dst + (BM + wave * (BN / 4) + 4 * j) * kPipeBK;
+                const int32_t rows = s * (16 / p.kw);   // filter rows advanced since stage 0
+                const uint8_t* src = padrow;
+                if (coff[j] >= 0 && cky[j] + rows < p.kh)
+                    src = p.x + (int64_t)(coff[j] + rows * p.w_in) * 4;
+                __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)d, 4, 0, 0);
+            }
+            return;
+        }
+        int32_t ci0 = k0, ky = 0, kx = 0;
+        if (!IS1X1) {
+            const int32_t tap = k0 / p.c;
+            ci0 = k0 - tap * p.c;
+            ky = tap / p.kw;
+            kx = tap - ky * p.kw;
+        }
+#pragma unroll
+        for (int j = 0; j < B_INST; ++j) {
+            uint8_t* d = dst + (BM + wave * (BN / 4) + 16 * j) * kPipeBK;
+            const uint8_t* src;
+            if (IS1X1) {
+                src = rbase[j] >= 0 ? p.x + rbase[j] + k0 + bseg[j] : padrow;
+            } else {
+                const int32_t iy = rih[j] + ky, ix = riw[j] + kx;
+                const bool ok = (uint32_t)iy < (uint32_t)p.h && (uint32_t)ix < (uint32_t)p.w_in;
+                src = ok ? p.x + rbase[j] + ((int64_t)iy * p.w_in + ix) * p.c + ci0 + bseg[j] : padrow;
+            }
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)d, 16, 0, 0);
+        }
+    };
+
+    constexpr int D = NST - 1;   // prefetch distance in stages
+    issue(0, lds0);
+    if (nst > 1) issue(1, lds1);
+    if (D > 2 && nst > 2) issue(2, lds2);
+
+    // residual fragments for the epilogue, fetched now
+    const int frow = lane & 31;
+    uint4 rres[TM][TN];
+    if (RES) {
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+#pragma unroll
+            for (int u = 0; u < TN; ++u) {
+                const int ocb = oc0 + wave_oc * C::WOC + t * 32 + (lane >> 5) * 16;
+                const int64_t pix = px0 + wave_px * C::WPX + u * 32 + frow;
+                rres[t][u] = make_uint4(0, 0, 0, 0);
+                if (ocb < p.c_out && pix < p.m)
+                    rres[t][u] = *reinterpret_cast<const uint4*>(p.res + pix * p.c_out + ocb);
+            }
+    }
+    if (tid < BM) {
+        cbias[tid] = my_bias;
+        cmult[tid] = my_mult;
+    }
+
+    v16i acc[TM][TN];
+#pragma unroll
+    for (int t = 0; t < TM; ++t)
+#pragma unroll
+        for (int u = 0; u < TN; ++u) acc[t][u] = v16i{};
+
+    // fragment offsets inside a stage: row lane%32 of each tile, K slot per k-step
+    const int fsw = swz(frow);
+    const int foff0 = frow * kPipeBK + (((lane >> 5) + 0) ^ fsw) * 16;
+    const int foff1 = frow * kPipeBK + (((lane >> 5) + 2) ^ fsw) * 16;
+    const uint32_t bxor = p.x_xor;
+
+    // One pipeline step: wait for stage s (this wave's DMA, then everyone's), refill
+    // the slot freed by stage s-1 with stage s+D, compute stage s from `cur`.
+    auto step = [&](int s, const uint8_t* cur, uint8_t* refill) {
+        const int ahead = nst - 1 - s;
+        if (D - 1 >= 2 && ahead >= 2) IQNN_WAIT_VM(2 * LOADS);
+        else if (ahead >= 1) IQNN_WAIT_VM(LOADS);
+        else IQNN_WAIT_VM(0);
+        // Plain s_barrier, not __syncthreads(): its workgroup fence would wait for every
+        // DMA in flight (vmcnt(0)) and collapse the ring.  Each wave has waited for its
+        // own share of stage s above; the barrier makes that true for all waves, and
+        // guarantees every wave is done reading the slot refilled next.
+        __builtin_amdgcn_s_barrier();
+        if (s + D < nst) issue(s + D, refill);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int fo = kk ? foff1 : foff0;
+            v4i a[TM], b[TN];
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+                a[t] = *reinterpret_cast<const v4i*>(cur + (wave_oc * C::WOC + 32 * t) * kPipeBK + fo);
+#pragma unroll
+            for (int u = 0; u < TN; ++u) {
+                v4i v = *reinterpret_cast<const v4i*>(cur + (BM + wave_px * C::WPX + 32 * u) * kPipeBK + fo);
+                v[0] ^= bxor; v[1] ^= bxor; v[2] ^= bxor; v[3] ^= bxor;
+                b[u] = v;
+            }
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+#pragma unroll
+                for (int u = 0; u < TN; ++u)
+                    acc[t][u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[t], b[u], acc[t][u], 0, 0, 0);
+        }
+    };
+
+    if constexpr (NST == 4) {
+        for (int s = 0; s < nst; s += 4) {
+            step(s, lds0, lds3);
+            if (s + 1 < nst) step(s + 1, lds1, lds0);
+            if (s + 2 < nst) step(s + 2, lds2, lds1);
+            if (s + 3 < nst) step(s + 3, lds3, lds2);
+        }
+    } else {
+        for (int s = 0; s < nst; s += 3) {
+            step(s, lds0, lds2);
+            if (s + 1 < nst) step(s + 1, lds1, lds0);
+            if (s + 2 < nst) step(s + 2, lds2, lds1);
+        }
+    }
+
+    // ---------------------------------------------------------------- epilogue
+    const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;
+    const float m_res = add ? *p.m_res : 0.0f;
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+        const int ocl = wave_oc * C::WOC + t * 32 + (lane >> 5) * 16;   // channel inside the block
+        const int ocb = oc0 + ocl;
+        if (ocb >= p.c_out) continue;
+        ChanParams cp;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int4 bv = *reinterpret_cast<const int4*>(&cbias[ocl + 4 * j]);
+            float4 mv = *reinterpret_cast<const float4*>(&cmult[ocl + 4 * j]);
+            cp.bias[4 * j] = bv.x; cp.bias[4 * j + 1] = bv.y; cp.bias[4 * j + 2] = bv.z; cp.bias[4 * j + 3] = bv.w;
+            cp.mult[4 * j] = mv.x; cp.mult[4 * j + 1] = mv.y; cp.mult[4 * j + 2] = mv.z; cp.mult[4 * j + 3] = mv.w;
+        }
+#pragma unroll
+        for (int u = 0; u < TN; ++u) {
+            const int64_t pix = px0 + wave_px * C::WPX + u * 32 + frow;
+            if (pix >= p.m) continue;
+            uint32_t rw[4] = {0, 0, 0, 0};
+            if (RES) {
+                rw[0] = rres[t][u].x; rw[1] = rres[t][u].y; rw[2] = rres[t][u].z; rw[3] = rres[t][u].w;
+            } else if (add) {
+                load_res16(p, pix * p.c_out + ocb, ocb, rw);
+            }
+            epi_store16(p, acc[t][u], cp.bias, cp.mult, rw, ocb, pix, add, m_res);
+        }
+    }
+}
+
+// Pixel tiles per rasterization group: about 1.5 MB of activation tiles (the
+// gathered tile bytes are BN * K), and at most an eighth of all pixel tiles so every
+// XCD gets its own groups.
+int group_px_for(int64_t n_px, int64_t tile_bytes) {
+    int64_t g = (int64_t)(1536 * 1024) / (tile_bytes > 0 ? tile_bytes : 1);
+    const int64_t eighth = (n_px + 7) / 8;
+    if (g > eighth) g = eighth;
+    if (g < 1) g = 1;
+    return (int)g;
+}
+
 template <int BM, int BN, int WM, int WN>
-hipError_t launch_shape(const ConvParams& p, int gather, bool is_1x1, hipStream_t stream) {
+hipError_t launch_staged(const ConvParams& p, int gather, bool is_1x1, hipStream_t stream) {
     ConvParams q = p;
     q.n_oc_tiles = (p.c_out + BM - 1) / BM;
     const int64_t n_px = (p.m + BN - 1) / BN;
     const int64_t grid = n_px * q.n_oc_tiles;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+    q.n_px_tiles = (int32_t)n_px;
+    q.group_px = group_px_for(n_px, (int64_t)BN * p.k);
     dim3 g((unsigned)grid), b(256);
     if (gather == GATHER_B8 && is_1x1)
         hipLaunchKernelGGL((qconv_igemm<BM, BN, WM, WN, GATHER_B8, true>), g, b, 0, stream, q);
@@ -410,11 +767,79 @@ hipError_t launch_shape(const ConvParams& p, int gather, bool is_1x1, hipStream_
     return hipGetLastError();
 }
 
+template <class C>
+hipError_t launch_pipe(const ConvParams& p, bool is_1x1, bool res_prefetch, bool c4, hipStream_t stream) {
+    ConvParams q = p;
+    q.n_oc_tiles = (p.c_out + C::BM - 1) / C::BM;
+    const int64_t n_px = (p.m + C::BN - 1) / C::BN;
+    const int64_t grid = n_px * q.n_oc_tiles;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+    q.n_px_tiles = (int32_t)n_px;
+    q.group_px = group_px_for(n_px, (int64_t)C::BN * p.k);
+    dim3 g((unsigned)grid), b(256);
+    if constexpr (C::BM <= 128 && C::BN <= 256 && C::NST == 4) {   // the 4-channel gather's shapes
+        if (c4 && res_prefetch) {
+            hipLaunchKernelGGL((qconv_pipe<C, false, true, true>), g, b, 0, stream, q);
+            return hipGetLastError();
+        }
+        if (c4) {
+            hipLaunchKernelGGL((qconv_pipe<C, false, false, true>), g, b, 0, stream, q);
+            return hipGetLastError();
+        }
+    } else if (c4) {
+        return hipErrorInvalidValue;
+    }
+    if (is_1x1 && res_prefetch)
+        hipLaunchKernelGGL((qconv_pipe<C, true, true, false>), g, b, 0, stream, q);
+    else if (is_1x1)
+        hipLaunchKernelGGL((qconv_pipe<C, true, false, false>), g, b, 0, stream, q);
+    else if (res_prefetch)
+        hipLaunchKernelGGL((qconv_pipe<C, false, true, false>), g, b, 0, stream, q);
+    else
+        hipLaunchKernelGGL((qconv_pipe<C, false, false, false>), g, b, 0, stream, q);
+    return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_t stream) {
-    if (p.c_out <= 64) return launch_shape<64, 256, 1, 4>(p, gather, is_1x1, stream);
-    return launch_shape<128, 128, 2, 2>(p, gather, is_1x1, stream);
+bool pipe_eligible(int gather, int32_t c, int64_t k) {
+    return (gather == GATHER_B8 && c % 64 == 0 && k % kPipeBK == 0) || gather == GATHER_C4;
+}
+
+// Tile configurations of the pipelined kernel (block channels x pixels, waves along
+// channels, ring depth).
+using P64x256 = PipeCfg<64, 256, 1, 4>;
+using P128x128 = PipeCfg<128, 128, 2, 4>;
+using P128x256 = PipeCfg<128, 256, 2, 3>;
+using P256x128 = PipeCfg<256, 128, 2, 3>;
+using P256x256 = PipeCfg<256, 256, 2, 4>;
+
+int pipe_tile_choice(int64_t m, int32_t c_out, int64_t k, bool res) {
+    (void)m;
+    (void)res;
+    if (c_out <= 64) return 0;
+    if (k <= 256 || c_out <= 128) return 1;
+    return 3;
+}
+
+hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_t stream, int tile) {
+    if (pipe_eligible(gather, p.c, p.k)) {
+        const bool c4 = gather == GATHER_C4;
+        const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;
+        const bool res_prefetch = add && p.vec_store && (p.res_type == T_INT8 || p.res_type == T_UINT8);
+        if (tile < 0) tile = pipe_tile_choice(p.m, p.c_out, p.k, res_prefetch);
+        if (c4) tile = p.c_out <= 64 ? 0 : 1;   // the 4-channel gather is built for these two
+        switch (tile) {
+        case 0: return launch_pipe<P64x256>(p, is_1x1, res_prefetch, c4, stream);
+        case 1: return launch_pipe<P128x128>(p, is_1x1, res_prefetch, c4, stream);
+        case 2: return launch_pipe<P128x256>(p, is_1x1, res_prefetch, c4, stream);
+        case 3: return launch_pipe<P256x128>(p, is_1x1, res_prefetch, c4, stream);
+        default: return launch_pipe<P256x256>(p, is_1x1, res_prefetch, c4, stream);
+        }
+    }
+    if (p.c_out <= 64) return launch_staged<64, 256, 1, 4>(p, gather, is_1x1, stream);
+    return launch_staged<128, 128, 2, 2>(p, gather, is_1x1, stream);
 }
 
 }  // namespace iqnn

@@ -48,6 +48,19 @@ def quantize(x, scale, zp, qtype, axis=-1, out=None, stream=None):
     return out
 
 
+def quantize_pad(x, scale, zp, qtype, pad, c_pad, out=None, stream=None):
+    """Codes of NHWC float x with a border of `pad` pixels and channels padded to c_pad,
+    all padding holding the zero-point code."""
+    n, h, w, c = (int(v) for v in x.shape)
+    s = scale if torch.is_tensor(scale) else _scalar_or_vec(scale, torch.float32, x.device)
+    z = zp if torch.is_tensor(zp) else _scalar_or_vec(zp, torch.int32, x.device)
+    per_channel = s.numel() > 1 or z.numel() > 1
+    if out is None:
+        out = torch.empty((n, h + 2 * pad, w + 2 * pad, c_pad), dtype=torch.uint8, device=x.device)
+    B.iqnn_quantize_pad(x, out, n, h, w, c, pad, c_pad, s, z, per_channel, qtype, stream)
+    return out
+
+
 def dequantize(q, shape, scale, zp, qtype, axis=-1, out=None, stream=None):
     shape = tuple(shape)
     axis = axis % len(shape)

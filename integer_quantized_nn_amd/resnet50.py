@@ -13,10 +13,18 @@ import numpy as np
 import torch
 
 from . import binding as B
-from .layers import QConv, dequantize, empty_codes, maxpool2d, quantize
+from .layers import QConv, dequantize, empty_codes, maxpool2d, quantize, quantize_pad
+
+STEM_PAD_CHANNELS = 4
 
 
 class QuantResNet50Trunk:
+    """The trunk's 3-channel image enters through iqnn_quantize_pad: the stem's zero
+    padding (3 pixels) and a 4th channel are written as the input zero-point code, so
+    the stem runs as a padding-free 4-channel conv whose loads take 4 taps x 4
+    channels at a time.  A zero weight on the extra channel and the real-0 border make
+    it the same convolution as the 3-channel padded one."""
+
     def __init__(self, trunk, device="cuda", weight_codes=None, stream=None):
         """trunk: synth.Trunk.  weight_codes: optional {layer name: OHWI int8 bytes};
         by default the float weights are quantized per output channel on the GPU."""
@@ -24,7 +32,10 @@ class QuantResNet50Trunk:
         self.device = device
         n = trunk.batch
         self.convs = {}
-        self.shapes = {"input": (n,) + trunk.x.shape[1:]}
+        stem = trunk.layers[0]
+        self.stem_pad = stem.case.pad
+        hin, win, cin = trunk.x.shape[1:]
+        self.shapes = {"input": (n, hin + 2 * self.stem_pad, win + 2 * self.stem_pad, STEM_PAD_CHANNELS)}
         for layer in trunk.layers:
             c = layer.case
             co, kh, kw, ci = c.w.shape
@@ -34,7 +45,11 @@ class QuantResNet50Trunk:
                 w_dev = torch.from_numpy(c.w).to(device)
                 w_bytes = quantize(w_dev, c.s_w, 0, B.INT8, axis=0, stream=stream).cpu().numpy()
             h, w = layer.in_hw
-            conv = QConv(n, h, w, ci, co, kh, c.stride, c.pad, B.UINT8, B.INT8, B.UINT8, c.epi, c.z_in, c.z_out,
+            pad = c.pad
+            if layer is stem:   # padded 4-channel input, zero weights on the extra channel
+                w_bytes = np.pad(w_bytes.reshape(co, kh, kw, ci), ((0, 0), (0, 0), (0, 0), (0, STEM_PAD_CHANNELS - ci)))
+                h, w, ci, pad = h + 2 * pad, w + 2 * pad, STEM_PAD_CHANNELS, 0
+            conv = QConv(n, h, w, ci, co, kh, c.stride, pad, B.UINT8, B.INT8, B.UINT8, c.epi, c.z_in, c.z_out,
                          w_bytes, c.bias, c.s_in, c.s_w, c.s_out, res_type=B.UINT8, z_res=c.z_res,
                          s_res=c.s_res, device=device, stream=stream)
             self.convs[layer.name] = conv
@@ -65,29 +80,34 @@ class QuantResNet50Trunk:
 
     def step(self, x_f32, stream=None):
         """One full forward: quantize -> trunk -> dequantize.  Returns fp32 NHWC output."""
-        quantize(x_f32, self.in_scale, self.in_zp, B.UINT8, out=self.bufs["input"], stream=stream)
+        quantize_pad(x_f32, self.in_scale, self.in_zp, B.UINT8, self.stem_pad, STEM_PAD_CHANNELS,
+                     out=self.bufs["input"], stream=stream)
         self.run_codes(stream)
         dequantize(self.bufs[self.final], self.shapes[self.final], self.final_scale, self.final_zp, B.UINT8,
                    out=self.out_f32, stream=stream)
         return self.out_f32
 
     def launches(self):
-        """(kernel family, algorithmic ops, algorithmic bytes) of every launch in one step."""
+        """(kernel family, algorithmic ops, algorithmic bytes) of every launch in one step.
+        Ops and bytes are those of the unpadded layer (the stem's 3 channels, K = 147)."""
         out = []
-        n_in = int(np.prod(self.shapes["input"]))
+        n = self.trunk.batch
+        n_in = int(np.prod(self.trunk.x.shape))
         out.append(("quantize", 0, n_in * 4 + n_in))
         for layer in self.trunk.layers:
-            conv = self.convs[layer.name]
-            d = conv.desc
-            oh, ow = d.out_hw()
-            ops = 2 * d.n * oh * ow * d.c_out * d.kh * d.kw * d.c_in
-            by = d.n * d.h * d.w * d.c_in + d.c_out * d.kh * d.kw * d.c_in + d.n * oh * ow * d.c_out
+            c = layer.case
+            co, kh, kw, ci = c.w.shape
+            h, w = layer.in_hw
+            oh = (h + 2 * c.pad - kh) // c.stride + 1
+            ow = (w + 2 * c.pad - kw) // c.stride + 1
+            ops = 2 * n * oh * ow * co * kh * kw * ci
+            by = n * h * w * ci + co * kh * kw * ci + n * oh * ow * co
             if layer.res_src is not None:
-                by += d.n * oh * ow * d.c_out
+                by += n * oh * ow * co
             out.append(("qconv:" + layer.name, ops, by))
             if layer.name == "stem":
-                n, h, w, c = self.shapes["stem"]
-                out.append(("maxpool", 0, n * h * w * c + int(np.prod(self.shapes["pool"]))))
+                _, sh, sw, sc = self.shapes["stem"]
+                out.append(("maxpool", 0, n * sh * sw * sc + int(np.prod(self.shapes["pool"]))))
         n_out = int(np.prod(self.shapes[self.final]))
         out.append(("dequantize", 0, n_out + 4 * n_out))
         return out

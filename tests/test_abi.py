@@ -100,12 +100,13 @@ def _unpack_layout(buf, c_out, k, act4):
     bias = buf[:4 * ocp].view(np.int32)
     mult = buf[4 * ocp:8 * ocp].view(np.float32)
     mres = buf[8 * ocp:8 * ocp + 4].view(np.float32)[0]
+    pad = buf[8 * ocp + 64:8 * ocp + 128]
     w = buf[8 * ocp + 256:8 * ocp + 256 + ocp * kp].view(np.int8).reshape(ocp, kp)
     rows = []
     for c in range(c_out):
-        b, r64 = divmod(c, 64)
-        g, t, r = r64 // 16, (r64 // 4) % 4, r64 % 4
-        rows.append(64 * b + 16 * t + 4 * g + r)
+        b, r32 = divmod(c, 32)
+        h, j, r = r32 // 16, (r32 // 4) % 4, r32 % 4
+        rows.append(32 * b + 8 * j + 4 * h + r)
     w = w[rows][:, :k]
     if act4:
         order = [0, 2, 4, 6, 1, 3, 5, 7, 8, 10, 12, 14, 9, 11, 13, 15]
@@ -114,7 +115,7 @@ def _unpack_layout(buf, c_out, k, act4):
             for p, e in enumerate(order):
                 logical[:, s0 + e] = w[:, s0 + p]
         w = logical
-    return bias[:c_out], mult[:c_out], mres, w
+    return bias[:c_out], mult[:c_out], mres, w, pad
 
 
 @pytest.mark.parametrize("x_type,w_type,c_in,c_out,epi", [
@@ -139,7 +140,9 @@ def test_host_prepack_matches_oracle_qparams(lib, x_type, w_type, c_in, c_out, e
                   z_out=1, res_type=B.UINT4, z_res=2)
     buf = _host_pack(d, w, w_type, bias, s_in, s_w, s_out, s_res)
     act4 = x_type in (B.UINT4, B.INT4)
-    fold, mult, mres, wl = _unpack_layout(buf, c_out, 9 * c_in, act4)
+    fold, mult, mres, wl, pad = _unpack_layout(buf, c_out, 9 * c_in, act4)
+    # the padding row holds the raw input zero-point code
+    assert np.all(pad == (z_in & 0xFF))
     # weights: exactly the codes, back in OHWI order after undoing the documented permutations
     assert np.array_equal(wl.astype(np.int32), w.reshape(c_out, -1))
     # multipliers: the oracle's requant_multiplier / residual_multiplier

@@ -47,6 +47,28 @@ def test_conv_small_shapes(case):
     assert_bytes_equal(got, want, str(case))
 
 
+@pytest.mark.parametrize("hw,k,stride,co", [((23, 23), 7, 2, 64), ((20, 17), 7, 2, 128), ((12, 12), 3, 1, 64),
+                                             ((9, 14), 5, 2, 96)])
+def test_conv_four_channel_padded_input(hw, k, stride, co):
+    """The 4-channel gather (image stems): a 3-channel image quantized into a border
+    of Z_in codes plus a 4th Z_in channel, convolved without padding, equals the
+    oracle's padded 3-channel convolution."""
+    torch = require_gpu()
+    from integer_quantized_nn_amd.layers import QConv
+    h, w = hw
+    pad = k // 2
+    c = synth.conv_case(hash((hw, k, stride, co)) % 2 ** 31, 2, h, w, 3, co, k, stride, pad, U8, I8, U8, RELU)
+    x, wc, _ = conv_codes(c)
+    want = to_bytes(oracle_conv(c, x, wc, None), U8)
+    xp = np.pad(x, ((0, 0), (pad, pad), (pad, pad), (0, 1)), constant_values=c.z_in)
+    wp = np.pad(wc, ((0, 0), (0, 0), (0, 0), (0, 1)))
+    conv = QConv(2, h + 2 * pad, w + 2 * pad, 4, co, k, stride, 0, U8, I8, U8, RELU, c.z_in, c.z_out,
+                 to_bytes(wp, I8), c.bias, c.s_in, c.s_w, c.s_out)
+    y = conv(torch.from_numpy(to_bytes(xp, U8)).cuda())
+    torch.cuda.synchronize()
+    assert_bytes_equal(y.cpu().numpy(), want, "c4 %s" % ((hw, k, stride, co),))
+
+
 def test_conv_adversarial_codes_and_padding():
     # every code of each type, including -128 / 255 / -8 / 15, on tiny images where
     # most taps read padding

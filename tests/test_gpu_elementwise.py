@@ -78,3 +78,28 @@ def test_maxpool_parity(dt):
         want = to_bytes(O.maxpool2d(x, k, s, p), dt)
         got = maxpool2d(torch.from_numpy(to_bytes(x, dt)).cuda(), n, h, w, c, k, s, p, dt).cpu().numpy()
         assert_bytes_equal(got, want, "maxpool %s" % ((n, h, w, c, k, s, p),))
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_quantize_pad_parity(per_channel):
+    # padded layout == oracle quantize of the interior, zero-point code everywhere else
+    torch = require_gpu()
+    from integer_quantized_nn_amd.layers import quantize_pad
+    rng = np.random.default_rng(400 + per_channel)
+    x = (rng.standard_normal((3, 11, 9, 3)) * 2).astype(np.float32)
+    if per_channel:
+        s, z = np.array([0.02, 0.03, 0.05], np.float32), np.array([100, 7, 255], np.int32)
+    else:
+        s, z = np.float32(0.021), 119
+    for pad, cp in ((3, 4), (0, 3), (1, 8)):
+        q = O.quantize(x, s, z, O.UINT8)
+        zc = np.broadcast_to(np.atleast_1d(z), (3,)) if per_channel else np.full(3, z)
+        want = np.empty((3, 11 + 2 * pad, 9 + 2 * pad, cp), np.int32)
+        want[...] = zc[0] if not per_channel else 0
+        if per_channel:
+            # border pixels take each channel's zero point, extra channels the first one's
+            want[..., :3] = zc
+            want[..., 3:] = zc[0]
+        want[:, pad:pad + 11, pad:pad + 9, :3] = q
+        got = quantize_pad(torch.from_numpy(x).cuda(), s, z, 1, pad, cp).cpu().numpy()
+        assert_bytes_equal(got, O.pack(want, O.UINT8), "quantize_pad pad=%d cp=%d" % (pad, cp))

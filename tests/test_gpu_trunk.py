@@ -36,7 +36,11 @@ def _run_gpu(tr, x, w):
     import torch
     from integer_quantized_nn_amd.resnet50 import QuantResNet50Trunk
     net = QuantResNet50Trunk(tr, weight_codes={k: O.pack(v, O.INT8) for k, v in w.items()})
-    net.bufs["input"].copy_(torch.from_numpy(O.pack(x, O.UINT8)))
+    # the trunk's input buffer is the image with the stem's border and a 4th channel,
+    # all holding the input zero-point code
+    p = net.stem_pad
+    xp = np.pad(x, ((0, 0), (p, p), (p, p), (0, 1)), constant_values=tr.z_in)
+    net.bufs["input"].copy_(torch.from_numpy(O.pack(xp, O.UINT8)))
     net.run_codes()
     torch.cuda.synchronize()
     return net
