@@ -445,6 +445,8 @@ __device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) &
 
 // s_waitcnt for vmcnt <= n only (expcnt and lgkmcnt left at their maximum).
 #define IQNN_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+// s_waitcnt for vmcnt <= n and lgkmcnt == 0.
+#define IQNN_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4))
 
 // One tile configuration of the pipelined kernel: block BM channels x BN pixels,
 // WM x (4/WM) waves, a ring of NST LDS stages.
@@ -652,52 +654,92 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_pipe(const ConvParams p) {
     const int foff1 = frow * kPipeBK + (((lane >> 5) + 2) ^ fsw) * 16;
     const uint32_t bxor = p.x_xor;
 
-    // One pipeline step: wait for stage s (this wave's DMA, then everyone's), refill
-    // the slot freed by stage s-1 with stage s+D, compute stage s from `cur`.
-    auto step = [&](int s, const uint8_t* cur, uint8_t* refill) {
-        const int ahead = nst - 1 - s;
-        if (D - 1 >= 2 && ahead >= 2) IQNN_WAIT_VM(2 * LOADS);
-        else if (ahead >= 1) IQNN_WAIT_VM(LOADS);
-        else IQNN_WAIT_VM(0);
-        // Plain s_barrier, not __syncthreads(): its workgroup fence would wait for every
-        // DMA in flight (vmcnt(0)) and collapse the ring.  Each wave has waited for its
-        // own share of stage s above; the barrier makes that true for all waves, and
-        // guarantees every wave is done reading the slot refilled next.
-        __builtin_amdgcn_s_barrier();
-        if (s + D < nst) issue(s + D, refill);
+    // Software pipeline per stage (two k-steps of 32):
+    //   1. k-step-0 MFMAs, with the k-step-1 fragment reads slotted one by one between
+    //      them (pinned by sched_group_barrier), so LDS latency hides behind the matrix pipe;
+    //   2. k-step-1 MFMAs, issued before the next stage's barrier so the wait at the
+    //      barrier overlaps matrix work;
+    //   3. the next stage's barrier and refill DMA, then its k-step-0 fragment reads.
+    v4i fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+    auto read_frags = [&](const uint8_t* cur, int fo, v4i (&fa)[TM], v4i (&fb)[TN]) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int fo = kk ? foff1 : foff0;
-            v4i a[TM], b[TN];
+        for (int t = 0; t < TM; ++t)
+            fa[t] = *reinterpret_cast<const v4i*>(cur + (wave_oc * C::WOC + 32 * t) * kPipeBK + fo);
 #pragma unroll
-            for (int t = 0; t < TM; ++t)
-                a[t] = *reinterpret_cast<const v4i*>(cur + (wave_oc * C::WOC + 32 * t) * kPipeBK + fo);
+        for (int u = 0; u < TN; ++u)
+            fb[u] = *reinterpret_cast<const v4i*>(cur + (BM + wave_px * C::WPX + 32 * u) * kPipeBK + fo);
+    };
+    auto shift_b = [&](v4i (&fb)[TN]) {
 #pragma unroll
-            for (int u = 0; u < TN; ++u) {
-                v4i v = *reinterpret_cast<const v4i*>(cur + (BM + wave_px * C::WPX + 32 * u) * kPipeBK + fo);
-                v[0] ^= bxor; v[1] ^= bxor; v[2] ^= bxor; v[3] ^= bxor;
-                b[u] = v;
-            }
-#pragma unroll
-            for (int t = 0; t < TM; ++t)
-#pragma unroll
-                for (int u = 0; u < TN; ++u)
-                    acc[t][u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[t], b[u], acc[t][u], 0, 0, 0);
+        for (int u = 0; u < TN; ++u) {
+            fb[u][0] ^= bxor; fb[u][1] ^= bxor; fb[u][2] ^= bxor; fb[u][3] ^= bxor;
         }
     };
+    // MFMAs number i in [lo, hi) of the TM x TN fragment grid, row-major
+    auto mfmas = [&](v4i (&fa)[TM], v4i (&fb)[TN], int lo, int hi) {
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+#pragma unroll
+            for (int u = 0; u < TN; ++u)
+                if (t * TN + u >= lo && t * TN + u < hi)
+                    acc[t][u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[t], fb[u], acc[t][u], 0, 0, 0);
+    };
+    // Stage s is ready once this wave's DMA for it has landed (vmcnt) and every wave
+    // has passed the barrier.  lgkmcnt(0) first: this wave's reads of the slot about to
+    // be refilled must be complete before anyone passes.  Plain s_barrier, not
+    // __syncthreads(): its fence would wait for every DMA in flight and collapse the
+    // ring.  After the barrier the slot freed by stage s-1 is refilled with stage s+D.
+    auto sync_stage = [&](int s, uint8_t* refill) {
+        const int ahead = nst - 1 - s;
+        if (D - 1 >= 2 && ahead >= 2) IQNN_WAIT_VM_LGKM0(2 * LOADS);
+        else if (ahead >= 1) IQNN_WAIT_VM_LGKM0(LOADS);
+        else IQNN_WAIT_VM_LGKM0(0);
+        __builtin_amdgcn_s_barrier();
+        if (s + D < nst) issue(s + D, refill);
+    };
+    constexpr int NMF = TM * TN, NRD = TM + TN, HALF = NMF / 2;
+    auto stage = [&](int s, const uint8_t* cur, const uint8_t* next, uint8_t* next_refill) {
+        shift_b(fb0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(fa0, fb0, 0, NMF);
+        read_frags(cur, foff1, fa1, fb1);
+        // interleave: MFMA, read, MFMA, read, ... then the remaining MFMAs
+#pragma unroll
+        for (int i = 0; i < (NMF < NRD ? NMF : NRD); ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        }
+        if (NMF > NRD) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NRD, 0);
+        if (NRD > NMF) __builtin_amdgcn_sched_group_barrier(0x100, NRD - NMF, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        shift_b(fb1);
+        mfmas(fa1, fb1, 0, HALF);
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 1 < nst) sync_stage(s + 1, next_refill);
+        // the next stage's k-step-0 reads go out first and land behind the other half of
+        // the k-step-1 MFMAs.  Unconditional, so the wait-count pass keeps them ordered;
+        // after the last stage they re-read valid LDS and the values are unused.
+        read_frags(next, foff0, fa0, fb0);
+        mfmas(fa1, fb1, HALF, NMF);
+        __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NMF - HALF, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
 
+    sync_stage(0, NST == 4 ? lds3 : lds2);
+    read_frags(lds0, foff0, fa0, fb0);
     if constexpr (NST == 4) {
         for (int s = 0; s < nst; s += 4) {
-            step(s, lds0, lds3);
-            if (s + 1 < nst) step(s + 1, lds1, lds0);
-            if (s + 2 < nst) step(s + 2, lds2, lds1);
-            if (s + 3 < nst) step(s + 3, lds3, lds2);
+            stage(s, lds0, lds1, lds0);
+            if (s + 1 < nst) stage(s + 1, lds1, lds2, lds1);
+            if (s + 2 < nst) stage(s + 2, lds2, lds3, lds2);
+            if (s + 3 < nst) stage(s + 3, lds3, lds0, lds3);
         }
     } else {
         for (int s = 0; s < nst; s += 3) {
-            step(s, lds0, lds2);
-            if (s + 1 < nst) step(s + 1, lds1, lds0);
-            if (s + 2 < nst) step(s + 2, lds2, lds1);
+            stage(s, lds0, lds1, lds0);
+            if (s + 1 < nst) stage(s + 1, lds1, lds2, lds1);
+            if (s + 2 < nst) stage(s + 2, lds2, lds0, lds2);
         }
     }
 
