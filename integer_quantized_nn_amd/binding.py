@@ -61,6 +61,7 @@ def lib():
         "iqnn_abi_version": (I, []),
         "iqnn_status_str": (ctypes.c_char_p, [I]),
         "iqnn_last_error": (ctypes.c_char_p, []),
+        "iqnn_set_conv_tile": (I, [I32]),
         "iqnn_quantize": (I, [P, P, I64, I64, I64, P, P, I, I32, P]),
         "iqnn_dequantize": (I, [P, P, I64, I64, I64, P, P, I, I32, P]),
         "iqnn_quantize_pad": (I, [P, P, I32, I32, I32, I32, I32, I32, P, P, I, I32, P]),
@@ -115,6 +116,10 @@ def _stream(stream, like=None):
 
 def iqnn_abi_version():
     return lib().iqnn_abi_version()
+
+
+def iqnn_set_conv_tile(tile):
+    _check(lib().iqnn_set_conv_tile(int(tile)))
 
 
 def iqnn_quantize(x, q, outer, ch, inner, scale, zp, per_channel, qtype, stream=None):

@@ -144,16 +144,18 @@ iqnn_status gemm_layer(const iqnn_gemm_desc* d, Layer* L) {
     return check_layer(*L);
 }
 
-// Optional tile override for tuning sweeps: IQNN_FORCE_TILE=0..4, read once.
-int forced_tile() {
-    static const int t = [] {
+// Tile override for tuning sweeps (iqnn_set_conv_tile); starts from IQNN_FORCE_TILE.
+constexpr int kMaxTile = 13;
+int& tile_override() {
+    static int t = [] {
         const char* e = std::getenv("IQNN_FORCE_TILE");
         if (!e || !*e) return -1;
         int v = std::atoi(e);
-        return (v >= 0 && v <= 4) ? v : -1;
+        return (v >= 0 && v <= kMaxTile) ? v : -1;
     }();
     return t;
 }
+int forced_tile() { return tile_override(); }
 
 // The 4-channel gather of the pipelined kernel: 8-bit activations with exactly 4
 // channels and no padding (the input carries its own border, see
@@ -379,6 +381,12 @@ const char* iqnn_status_str(iqnn_status s) {
 }
 
 const char* iqnn_last_error(void) { return g_err.c_str(); }
+
+iqnn_status iqnn_set_conv_tile(int32_t tile) {
+    if (tile < -1 || tile > kMaxTile) return fail(IQNN_ERR_INVALID_ARG, "tile %d outside -1..%d", tile, kMaxTile);
+    tile_override() = tile;
+    return ok();
+}
 
 iqnn_status iqnn_quantize(const float* x_dev, void* q_dev, int64_t outer, int64_t ch, int64_t inner,
                           const float* scale_dev, const int32_t* zp_dev, int per_channel, int32_t qtype,

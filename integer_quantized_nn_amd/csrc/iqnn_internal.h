@@ -68,6 +68,8 @@ struct ConvParams {
     int32_t n_oc_tiles;
     int32_t n_px_tiles;       // set by the launcher
     int32_t group_px;         // pixel tiles per rasterization group (set by the launcher)
+    int32_t gx;               // streaming kernel: workgroups per XCD (set by the launcher)
+    int32_t px_chunk;         // streaming kernel: pixel tiles per XCD share (set by the launcher)
     uint32_t pad_word;        // four copies of the staged padding byte
     uint32_t x_xor;           // 0x80808080 for UINT8 activations, else 0
     int32_t x_signed4;        // INT4 activations: sign-extend nibbles

@@ -42,6 +42,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "iqnn_internal.h"
 
 #pragma clang fp contract(off)
@@ -457,7 +459,10 @@ struct PipeCfg {
     static constexpr int WPX = BN / WN;     // pixels per wave
     static constexpr int TM = WOC / 32, TN = WPX / 32;
     static constexpr int STAGE = (BM + BN) * kPipeBK;
-    static constexpr int OCC = NST * STAGE <= 80 * 1024 ? 2 : 1;
+    // blocks per CU that the 160 KB of LDS allows (capped at 3: 168 VGPRs per lane)
+    static constexpr int LDS_FIT = 160 * 1024 / (NST * STAGE);
+    static constexpr int OCC = LDS_FIT >= 3 ? 3 : (LDS_FIT >= 2 ? 2 : 1);
+    static_assert(STAGE >= 8 * BM, "epilogue tables live in ring slot 0");
 };
 
 // RES: 8-bit residual with C_out % 16 == 0, fetched into registers before the main
@@ -480,8 +485,10 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_pipe(const ConvParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t lds2[STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t lds3[NST == 4 ? STAGE : 16];
-    __shared__ __attribute__((aligned(16))) int32_t cbias[BM];
-    __shared__ __attribute__((aligned(16))) float cmult[BM];
+    // the epilogue's per-channel bias and multiplier tables reuse ring slot 0 once the
+    // contraction is done, so the whole LDS budget of a block is the ring
+    int32_t* const cbias = reinterpret_cast<int32_t*>(lds0);
+    float* const cmult = reinterpret_cast<float*>(lds0 + 4 * BM);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -637,11 +644,6 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_pipe(const ConvParams p) {
                     rres[t][u] = *reinterpret_cast<const uint4*>(p.res + pix * p.c_out + ocb);
             }
     }
-    if (tid < BM) {
-        cbias[tid] = my_bias;
-        cmult[tid] = my_mult;
-    }
-
     v16i acc[TM][TN];
 #pragma unroll
     for (int t = 0; t < TM; ++t)
@@ -744,6 +746,12 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_pipe(const ConvParams p) {
     }
 
     // ---------------------------------------------------------------- epilogue
+    __syncthreads();   // every wave is done with the ring
+    if (tid < BM) {
+        cbias[tid] = my_bias;
+        cmult[tid] = my_mult;
+    }
+    __syncthreads();
     const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;
     const float m_res = add ? *p.m_res : 0.0f;
 #pragma unroll
@@ -843,6 +851,410 @@ hipError_t launch_pipe(const ConvParams& p, bool is_1x1, bool res_prefetch, bool
     return hipGetLastError();
 }
 
+// ============================================================ streaming kernel
+//
+// qconv_stream: persistent workgroups that consume one continuous stream of LDS
+// stages.  A workgroup keeps one channel tile for its whole life and walks a strided
+// run of pixel tiles inside its XCD's contiguous share of the pixel range, so the
+// channel tables are loaded once and the workgroups of an XCD that hold the other
+// channel tiles read the same activation tiles at about the same time (one HBM read,
+// the rest L2 hits).  The stream of a tile is its nst K-stages, then (Conv_Add_Relu
+// with an 8-bit residual) one R-stage that brings the residual tile into LDS.  Stages
+// are filled by LDS DMA NST-1 stages ahead, across tile boundaries, so the next
+// tile's data is in flight while the epilogue of the current one runs and the ring
+// never drains.
+//
+// The DMA is issued from inline assembly, invisible to the compiler's wait-count
+// pass, so the ring can be one array addressed by a run-time slot without the
+// compiler serialising every fragment read behind the DMA in flight.  Every wait on
+// the ring is explicit: each issue is exactly K_LOADS DMA instructions per wave
+// (R-stages are padded, the stream end re-issues its last stage into a free slot),
+// so "stage g has landed" is always vmcnt <= (NST-2)*K_LOADS.  Loads return in
+// order, so stores in flight can only make that wait stricter, never unsafe.
+
+// LDS address (offset in the workgroup's LDS) of a __shared__ location
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(lds_ptr_t)(p);
+}
+
+// One global -> LDS DMA of 16 (4) bytes per lane: lane i writes LDS bytes
+// [m0 + 16 i, +16) ([m0 + 4 i, +4)).  m0 takes one wait state before the load reads it.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(src)
+                 : "memory", "m0");
+}
+
+template <int BM_, int BN_, int WM_, int NST_>
+struct StreamCfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = 4 / WM_, NST = NST_;
+    static constexpr int WOC = BM / WM, WPX = BN / WN;
+    static constexpr int TM = WOC / 32, TN = WPX / 32;
+    static constexpr int STAGE = (BM + BN) * kPipeBK;
+    static constexpr int LDS = NST * STAGE + 8 * BM;
+    static constexpr int OCC = 160 * 1024 / LDS >= 2 ? 2 : 1;   // 160 KB of LDS per CU
+};
+
+template <class C, bool IS1X1, bool RES, bool C4>
+__global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) {
+    constexpr int BM = C::BM, BN = C::BN, WM = C::WM, NST = C::NST;
+    constexpr int TM = C::TM, TN = C::TN, STAGE = C::STAGE;
+    constexpr int A_INST = BM / 64;                   // weight rows: 16 per instruction per wave
+    constexpr int B_INST = C4 ? BN / 16 : BN / 64;    // activation rows: 16 (4 for C4) per instruction
+    constexpr int K_LOADS = A_INST + B_INST;          // DMA instructions per wave per stage
+    constexpr int R_INST = RES ? BM * BN / 4096 : 0;  // residual: 1 KB per instruction per wave
+    constexpr int D = NST - 1;                        // stages issued ahead
+    static_assert(TM >= 1 && TN >= 1 && A_INST >= 1 && BN % 64 == 0, "tile shape");
+    static_assert(NST >= 3, "ring depth");
+    static_assert(D * K_LOADS <= 60, "DMA in flight must fit the 6-bit vmcnt");
+    static_assert(R_INST <= K_LOADS, "a residual tile fits one stage");
+    static_assert(!(RES && C4), "the 4-channel gather has no residual stage");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[NST * STAGE];
+    __shared__ __attribute__((aligned(16))) int32_t cbias[BM];
+    __shared__ __attribute__((aligned(16))) float cmult[BM];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_oc = wave % WM;
+    const int wave_px = wave / WM;
+
+    // ------------------------------------------------------------ schedule
+    const int xcd = blockIdx.x & 7, widx = blockIdx.x >> 3;
+    const int n_oc = p.n_oc_tiles;
+    const int oc_t = widx % n_oc;
+    const int member = widx / n_oc, members = p.gx / n_oc;
+    const int chunk0 = xcd * p.px_chunk;
+    const int chunk_len = min(p.px_chunk, p.n_px_tiles - chunk0);
+    const int J = chunk_len > member ? (chunk_len - member + members - 1) / members : 0;
+    if (J <= 0) return;
+    const int oc0 = oc_t * BM;
+    auto tile_px0 = [&](int j) -> int64_t { return (int64_t)(chunk0 + member + j * members) * BN; };
+
+    if (tid < BM) {
+        cbias[tid] = p.bias[oc0 + tid];
+        cmult[tid] = p.mult[oc0 + tid];
+    }
+    __syncthreads();
+
+    const int nst = p.kp / kPipeBK;
+    constexpr int EXTRA = RES ? 1 : 0;
+    const int spt = nst + EXTRA;   // stages per tile
+    const uint32_t ring0 = lds_addr(ring);
+
+    // ------------------------------------------------------------ issue side
+    // DMA lane assignment of a K-stage: instruction j of this wave fills 16 LDS rows;
+    // lane -> row lane/4, slot lane%4, which holds K segment slot ^ swz(row).
+    const int drow = lane >> 2;
+    const int dslot = lane & 3;
+    const uint8_t* padrow = p.pad_row;
+    const int8_t* wsrc[A_INST];
+#pragma unroll
+    for (int j = 0; j < A_INST; ++j) {
+        const int row = wave * (BM / 4) + 16 * j + drow;
+        wsrc[j] = p.w + (int64_t)(oc0 + row) * p.kp + (dslot ^ swz(row)) * 16;
+    }
+    int32_t bseg[C4 ? 1 : B_INST];
+    if constexpr (!C4) {
+#pragma unroll
+        for (int j = 0; j < B_INST; ++j) bseg[j] = (dslot ^ swz(wave * (BN / 4) + 16 * j + drow)) * 16;
+    }
+    // per-tile geometry of the tile being issued
+    int64_t rbase[C4 ? 1 : B_INST];
+    int32_t rih[C4 ? 1 : B_INST], riw[C4 ? 1 : B_INST];
+    constexpr int C4N = C4 ? B_INST : 1;
+    int32_t coff[C4N], cky[C4N];
+    const uint8_t* rsrc[RES ? R_INST : 1];
+    auto set_issue_tile = [&](int j) {
+        const int64_t px0 = tile_px0(j);
+        if constexpr (C4) {
+            // each 4-byte instruction fills 4 rows; lane -> row lane/16, 4-byte position
+            // lane%16 = tap jj of slot s, holding K segment s ^ swz(row)
+#pragma unroll
+            for (int i = 0; i < B_INST; ++i) {
+                const int row = wave * (BN / 4) + 4 * i + (lane >> 4);
+                const int slot = (lane >> 2) & 3, jj = lane & 3;
+                const int tap0 = (slot ^ swz(row)) * 4 + jj;
+                const int ky0 = tap0 / p.kw, kx0 = tap0 - ky0 * p.kw;
+                const int64_t pix = px0 + row;
+                coff[i] = -1;
+                cky[i] = ky0;
+                if (pix < p.m) {
+                    const int64_t ohw = (int64_t)p.oh * p.ow;
+                    const int32_t n = (int32_t)(pix / ohw);
+                    const int32_t rem = (int32_t)(pix - (int64_t)n * ohw);
+                    const int32_t oy = rem / p.ow, ox = rem - oy * p.ow;
+                    coff[i] = (n * p.h + oy * p.sh + ky0) * p.w_in + ox * p.sw + kx0;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < B_INST; ++i) {
+                const int64_t pix = px0 + wave * (BN / 4) + 16 * i + drow;
+                if (pix < p.m) {
+                    if (IS1X1) {
+                        rbase[i] = pix * p.c;
+                        rih[i] = 0;
+                        riw[i] = 0;
+                    } else {
+                        const int64_t ohw = (int64_t)p.oh * p.ow;
+                        const int64_t n = pix / ohw;
+                        const int32_t rem = (int32_t)(pix - n * ohw);
+                        const int32_t oy = rem / p.ow, ox = rem - oy * p.ow;
+                        rbase[i] = n * p.h * p.w_in * (int64_t)p.c;
+                        rih[i] = oy * p.sh - p.ph;
+                        riw[i] = ox * p.sw - p.pw;
+                    }
+                } else {
+                    rbase[i] = -1;
+                    rih[i] = -(1 << 29);
+                    riw[i] = -(1 << 29);
+                }
+            }
+        }
+        if constexpr (RES) {
+            // residual rows [px][BM] bytes: instruction i of this wave covers 1024/BM rows,
+            // BM/16 lanes per row
+            constexpr int LPR = BM / 16;
+#pragma unroll
+            for (int i = 0; i < R_INST; ++i) {
+                const int row = (wave * R_INST + i) * (1024 / BM) + lane / LPR;
+                const int ch = oc0 + (lane % LPR) * 16;
+                const int64_t pix = px0 + row;
+                rsrc[i] = (pix < p.m && ch < p.c_out) ? p.res + pix * p.c_out + ch : p.res;
+            }
+        }
+    };
+    int is_j = 0, is_s = 0;            // next stage to issue (local tile, stage in tile)
+    int k_ci = 0, k_kx = 0, k_ky = 0;  // its K position: channel offset, filter column, row
+    uint32_t is_off = 0;               // its ring slot
+    set_issue_tile(0);
+    auto issue = [&]() {
+        const uint32_t dst = ring0 + is_off;
+        if (RES && is_s == nst) {
+#pragma unroll
+            for (int i = 0; i < R_INST; ++i) dma16(rsrc[i], dst + (wave * R_INST + i) * 1024);
+#pragma unroll
+            for (int i = R_INST; i < K_LOADS; ++i)   // padding: same count as a K-stage
+                dma16(p.res, dst + 4 * R_INST * 1024 + (wave * (K_LOADS - R_INST) + i - R_INST) * 1024);
+        } else {
+            const int k0 = is_s * kPipeBK;
+#pragma unroll
+            for (int j = 0; j < A_INST; ++j) dma16(wsrc[j] + k0, dst + (wave * (BM / 4) + 16 * j) * kPipeBK);
+            if constexpr (C4) {
+                const int32_t rows = is_s * (16 / p.kw);   // filter rows advanced since stage 0
+#pragma unroll
+                for (int i = 0; i < B_INST; ++i) {
+                    const uint8_t* src = padrow;
+                    if (coff[i] >= 0 && cky[i] + rows < p.kh) src = p.x + (int64_t)(coff[i] + rows * p.w_in) * 4;
+                    dma4(src, dst + (BM + wave * (BN / 4) + 4 * i) * kPipeBK);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < B_INST; ++i) {
+                    const uint8_t* src;
+                    if (IS1X1) {
+                        src = rbase[i] >= 0 ? p.x + rbase[i] + k0 + bseg[i] : padrow;
+                    } else {
+                        const int32_t iy = rih[i] + k_ky, ix = riw[i] + k_kx;
+                        const bool ok = (uint32_t)iy < (uint32_t)p.h && (uint32_t)ix < (uint32_t)p.w_in;
+                        src = ok ? p.x + rbase[i] + ((int64_t)iy * p.w_in + ix) * p.c + k_ci + bseg[i] : padrow;
+                    }
+                    dma16(src, dst + (BM + wave * (BN / 4) + 16 * i) * kPipeBK);
+                }
+            }
+        }
+        is_off = is_off + STAGE == NST * STAGE ? 0 : is_off + STAGE;
+        // advance the cursor; past the end it stays on the last stage
+        if (is_s + 1 < spt) {
+            ++is_s;
+            if (!IS1X1 && !C4 && is_s < nst) {
+                k_ci += kPipeBK;
+                if (k_ci == p.c) {
+                    k_ci = 0;
+                    if (++k_kx == p.kw) { k_kx = 0; ++k_ky; }
+                }
+            }
+        } else if (is_j + 1 < J) {
+            ++is_j;
+            is_s = 0;
+            k_ci = k_kx = k_ky = 0;
+            set_issue_tile(is_j);
+        }
+    };
+
+    // ------------------------------------------------------------ compute side
+    const int frow = lane & 31;
+    const int fsw = swz(frow);
+    const int foff0 = frow * kPipeBK + (((lane >> 5) + 0) ^ fsw) * 16;
+    const int foff1 = frow * kPipeBK + (((lane >> 5) + 2) ^ fsw) * 16;
+    const uint32_t bxor = p.x_xor;
+    v16i acc[TM][TN];
+#pragma unroll
+    for (int t = 0; t < TM; ++t)
+#pragma unroll
+        for (int u = 0; u < TN; ++u) acc[t][u] = v16i{};
+
+    v4i fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+    auto read_frags = [&](const uint8_t* cur, int fo, v4i (&fa)[TM], v4i (&fb)[TN]) {
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+            fa[t] = *reinterpret_cast<const v4i*>(cur + (wave_oc * C::WOC + 32 * t) * kPipeBK + fo);
+#pragma unroll
+        for (int u = 0; u < TN; ++u)
+            fb[u] = *reinterpret_cast<const v4i*>(cur + (BM + wave_px * C::WPX + 32 * u) * kPipeBK + fo);
+    };
+    auto shift_b = [&](v4i (&fb)[TN]) {
+#pragma unroll
+        for (int u = 0; u < TN; ++u) {
+            fb[u][0] ^= bxor; fb[u][1] ^= bxor; fb[u][2] ^= bxor; fb[u][3] ^= bxor;
+        }
+    };
+    auto mfmas = [&](v4i (&fa)[TM], v4i (&fb)[TN], int lo, int hi) {
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+#pragma unroll
+            for (int u = 0; u < TN; ++u)
+                if (t * TN + u >= lo && t * TN + u < hi)
+                    acc[t][u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[t], fb[u], acc[t][u], 0, 0, 0);
+    };
+    // The next stage is ready once this wave's DMA for it has landed and every wave has
+    // passed the barrier; lgkmcnt(0) first, so the slot refilled right after the
+    // barrier (the one consumed last) has no reads left in flight.
+    auto sync = [&]() {
+        IQNN_WAIT_VM_LGKM0((D - 1) * K_LOADS);
+        __builtin_amdgcn_s_barrier();
+        issue();
+    };
+
+    for (int i = 0; i < D; ++i) issue();
+    uint32_t cur_off = 0;
+    auto advance = [&]() { cur_off = cur_off + STAGE == NST * STAGE ? 0 : cur_off + STAGE; };
+    sync();
+    read_frags(ring + cur_off, foff0, fa0, fb0);
+
+    constexpr int NMF = TM * TN, NRD = TM + TN, HALF = NMF / 2;
+    // residual epilogues run only with the residual stage (the host routes the rest to
+    // qconv_pipe), so no global load of the epilogue is ever pending in the loop
+    constexpr bool add = RES;
+    const float m_res = RES ? *p.m_res : 0.0f;
+    for (int j = 0; j < J; ++j) {
+        const bool last_tile = j + 1 == J;
+        for (int s = 0; s < nst; ++s) {
+            const uint8_t* cur = ring + cur_off;
+            shift_b(fb0);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(fa0, fb0, 0, NMF);
+            read_frags(cur, foff1, fa1, fb1);
+#pragma unroll
+            for (int i = 0; i < (NMF < NRD ? NMF : NRD); ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+            }
+            if (NMF > NRD) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NRD, 0);
+            if (NRD > NMF) __builtin_amdgcn_sched_group_barrier(0x100, NRD - NMF, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            shift_b(fb1);
+            mfmas(fa1, fb1, 0, HALF);
+            __builtin_amdgcn_sched_barrier(0);
+            advance();
+            if (!(last_tile && s + 1 == nst && !RES)) sync();
+            if (s + 1 < nst) read_frags(ring + cur_off, foff0, fa0, fb0);
+            mfmas(fa1, fb1, HALF, NMF);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // -------------------------------------------------------- epilogue of tile j
+        const int64_t px0 = tile_px0(j);
+        const uint8_t* rtile = ring + cur_off;   // the R-stage, synced above
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            const int ocl = wave_oc * C::WOC + t * 32 + (lane >> 5) * 16;   // channel inside the block
+            const int ocb = oc0 + ocl;
+            if (ocb >= p.c_out) continue;
+            ChanParams cp;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                int4 bv = *reinterpret_cast<const int4*>(&cbias[ocl + 4 * q]);
+                float4 mv = *reinterpret_cast<const float4*>(&cmult[ocl + 4 * q]);
+                cp.bias[4 * q] = bv.x; cp.bias[4 * q + 1] = bv.y; cp.bias[4 * q + 2] = bv.z; cp.bias[4 * q + 3] = bv.w;
+                cp.mult[4 * q] = mv.x; cp.mult[4 * q + 1] = mv.y; cp.mult[4 * q + 2] = mv.z; cp.mult[4 * q + 3] = mv.w;
+            }
+#pragma unroll
+            for (int u = 0; u < TN; ++u) {
+                const int pl = wave_px * C::WPX + u * 32 + frow;   // pixel inside the block
+                const int64_t pix = px0 + pl;
+                if (pix >= p.m) continue;
+                uint32_t rw[4] = {0, 0, 0, 0};
+                if (RES) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(rtile + pl * BM + ocl);
+                    rw[0] = v.x; rw[1] = v.y; rw[2] = v.z; rw[3] = v.w;
+                }
+                epi_store16(p, acc[t][u], cp.bias, cp.mult, rw, ocb, pix, add, m_res);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+#pragma unroll
+            for (int u = 0; u < TN; ++u) acc[t][u] = v16i{};
+        if (RES) {
+            advance();
+            if (!last_tile) sync();
+        }
+        if (!last_tile) read_frags(ring + cur_off, foff0, fa0, fb0);
+    }
+    // no DMA may still be writing this workgroup's LDS when it ends
+    IQNN_WAIT_VM(0);
+}
+
+template <class C>
+hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bool c4, hipStream_t stream) {
+    ConvParams q = p;
+    q.n_oc_tiles = (p.c_out + C::BM - 1) / C::BM;
+    const int64_t n_px = (p.m + C::BN - 1) / C::BN;
+    if (n_px <= 0) return hipSuccess;
+    if (n_px > 0x3FFFFFFF) return hipErrorInvalidValue;
+    q.n_px_tiles = (int32_t)n_px;
+    q.px_chunk = (int32_t)((n_px + 7) / 8);
+    // workgroups per XCD: a multiple of the channel tiles, about OCC per CU (32 CUs per
+    // XCD), no more than there are tiles in one XCD's share
+    const int n_oc = q.n_oc_tiles;
+    int per = n_oc * std::max(1, C::OCC * 32 / n_oc);
+    per = std::min<int64_t>(per, (int64_t)q.px_chunk * n_oc);
+    q.gx = per;
+    dim3 g((unsigned)(8 * per)), b(256);
+    if constexpr ((C::NST - 1) * (C::BM / 64 + C::BN / 16) <= 60) {
+        if (c4) {
+            hipLaunchKernelGGL((qconv_stream<C, false, false, true>), g, b, 0, stream, q);
+            return hipGetLastError();
+        }
+    } else if (c4) {
+        return hipErrorInvalidValue;
+    }
+    // the residual rides in the stream when a tile of it fits one stage
+    constexpr bool kResStage = C::BM * C::BN / 4096 <= C::BM / 64 + C::BN / 64;
+    const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;
+    if (add && !(kResStage && res_prefetch)) return hipErrorInvalidValue;
+    if constexpr (kResStage) {
+        if (res_prefetch) {
+            if (is_1x1)
+                hipLaunchKernelGGL((qconv_stream<C, true, true, false>), g, b, 0, stream, q);
+            else
+                hipLaunchKernelGGL((qconv_stream<C, false, true, false>), g, b, 0, stream, q);
+            return hipGetLastError();
+        }
+    }
+    if (is_1x1)
+        hipLaunchKernelGGL((qconv_stream<C, true, false, false>), g, b, 0, stream, q);
+    else
+        hipLaunchKernelGGL((qconv_stream<C, false, false, false>), g, b, 0, stream, q);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 bool pipe_eligible(int gather, int32_t c, int64_t k) {
@@ -856,13 +1268,24 @@ using P128x128 = PipeCfg<128, 128, 2, 4>;
 using P128x256 = PipeCfg<128, 256, 2, 3>;
 using P256x128 = PipeCfg<256, 128, 2, 3>;
 using P256x256 = PipeCfg<256, 256, 2, 4>;
+using P128x128s3 = PipeCfg<128, 128, 2, 3>;
+using P64x128 = PipeCfg<64, 128, 1, 4>;
+using S64x128d12 = StreamCfg<64, 128, 1, 12>;
+using S64x128d6 = StreamCfg<64, 128, 1, 6>;
+using S128x128d8 = StreamCfg<128, 128, 2, 8>;
+using S128x128d4 = StreamCfg<128, 128, 2, 4>;
+using S64x256d7 = StreamCfg<64, 256, 1, 7>;
+using S256x128d6 = StreamCfg<256, 128, 2, 6>;
+using S128x256d6 = StreamCfg<128, 256, 2, 6>;
 
+// Automatic tile: the streaming kernel with 64x128 / 128x128 blocks (two per CU) for
+// the memory-bound and mid-size layers; wide, deep contractions (c_out >= 1024,
+// K >= 1024, no residual) keep the 128x256 ring kernel, whose larger block reuses
+// each fragment more.
 int pipe_tile_choice(int64_t m, int32_t c_out, int64_t k, bool res) {
     (void)m;
-    (void)res;
-    if (c_out <= 64) return 0;
-    if (k <= 256 || c_out <= 128) return 1;
-    return 3;
+    if (c_out >= 1024 && k >= 1024 && !res) return 2;
+    return c_out <= 64 ? 8 : 10;
 }
 
 hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_t stream, int tile) {
@@ -871,13 +1294,25 @@ hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_
         const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;
         const bool res_prefetch = add && p.vec_store && (p.res_type == T_INT8 || p.res_type == T_UINT8);
         if (tile < 0) tile = pipe_tile_choice(p.m, p.c_out, p.k, res_prefetch);
-        if (c4) tile = p.c_out <= 64 ? 0 : 1;   // the 4-channel gather is built for these two
+        // the streaming kernel takes a residual only as a stage of its stream
+        if (tile >= 7 && add && !(res_prefetch && tile != 12 && tile != 13)) tile = p.c_out <= 64 ? 0 : 1;
+        if (c4 && tile >= 7 && tile != 8 && tile != 10 && tile != 12) tile = p.c_out <= 64 ? 8 : 10;
+        if (c4 && tile < 7 && tile != 0 && tile != 1 && tile != 6) tile = p.c_out <= 64 ? 0 : 1;   // the 4-channel gather's shapes
         switch (tile) {
         case 0: return launch_pipe<P64x256>(p, is_1x1, res_prefetch, c4, stream);
         case 1: return launch_pipe<P128x128>(p, is_1x1, res_prefetch, c4, stream);
         case 2: return launch_pipe<P128x256>(p, is_1x1, res_prefetch, c4, stream);
         case 3: return launch_pipe<P256x128>(p, is_1x1, res_prefetch, c4, stream);
-        default: return launch_pipe<P256x256>(p, is_1x1, res_prefetch, c4, stream);
+        case 4: return launch_pipe<P256x256>(p, is_1x1, res_prefetch, c4, stream);
+        case 5: return launch_pipe<P128x128s3>(p, is_1x1, res_prefetch, c4, stream);
+        case 6: return launch_pipe<P64x128>(p, is_1x1, res_prefetch, c4, stream);
+        case 7: return launch_stream<S64x128d12>(p, is_1x1, res_prefetch, c4, stream);
+        case 8: return launch_stream<S64x128d6>(p, is_1x1, res_prefetch, c4, stream);
+        case 9: return launch_stream<S128x128d8>(p, is_1x1, res_prefetch, c4, stream);
+        case 10: return launch_stream<S128x128d4>(p, is_1x1, res_prefetch, c4, stream);
+        case 11: return launch_stream<S64x256d7>(p, is_1x1, res_prefetch, c4, stream);
+        case 12: return launch_stream<S256x128d6>(p, is_1x1, res_prefetch, c4, stream);
+        default: return launch_stream<S128x256d6>(p, is_1x1, res_prefetch, c4, stream);
         }
     }
     if (p.c_out <= 64) return launch_staged<64, 256, 1, 4>(p, gather, is_1x1, stream);

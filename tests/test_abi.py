@@ -38,6 +38,16 @@ def test_version_and_status_strings(lib):
     assert lib.iqnn_status_str(4) == b"IQNN_ERR_OVERFLOW"
 
 
+def test_conv_tile_override_range(lib):
+    for t in (0, 13, -1):
+        B.iqnn_set_conv_tile(t)
+    for bad in (-2, 14):
+        with pytest.raises(B.IqnnError) as ei:
+            B.iqnn_set_conv_tile(bad)
+        assert ei.value.status == 1 and "tile" in str(ei.value)
+    B.iqnn_set_conv_tile(-1)
+
+
 def conv_desc(**kw):
     d = B.ConvDesc()
     base = dict(n=1, h=8, w=8, c_in=16, c_out=32, kh=3, kw=3, stride_h=1, stride_w=1, pad_h=1, pad_w=1,

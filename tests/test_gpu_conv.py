@@ -69,6 +69,51 @@ def test_conv_four_channel_padded_input(hw, k, stride, co):
     assert_bytes_equal(y.cpu().numpy(), want, "c4 %s" % ((hw, k, stride, co),))
 
 
+# 8-bit layers with C_in % 64 == 0 (the pipelined kernel): ring depths that do not
+# divide the stage count, one-stage contractions, ragged pixel tails and channel
+# counts that are not multiples of any block
+PIPE = [
+    # n, h, w, c_in, c_out, k, stride, pad, epi
+    (2, 13, 11, 64, 64, 1, 1, 0, RELU),          # one stage
+    (2, 13, 11, 64, 256, 1, 1, 0, ADD_RELU),     # residual prefetch
+    (1, 17, 9, 320, 96, 1, 1, 0, ADD_RELU),      # 5 stages
+    (2, 9, 10, 64, 64, 3, 1, 1, RELU),           # 9 stages, padding taps
+    (1, 15, 15, 128, 320, 3, 2, 1, NONE),        # stride 2, 18 stages
+    (3, 7, 7, 512, 128, 1, 2, 0, NONE),          # strided 1x1 downsample
+]
+
+
+@pytest.mark.parametrize("tile", range(14))
+def test_conv_every_tile(tile):
+    """Each block tile of the pipelined kernel (forced through iqnn_set_conv_tile)
+    gives the oracle's bytes on the same layers, and so does the 4-channel gather on
+    the tiles it is built for."""
+    torch = require_gpu()
+    from integer_quantized_nn_amd import binding as B
+    from integer_quantized_nn_amd.layers import QConv
+    B.iqnn_set_conv_tile(tile)
+    try:
+        for i, (n, h, w, ci, co, k, s, p, epi) in enumerate(PIPE):
+            c = synth.conv_case(1000 + 17 * i, n, h, w, ci, co, k, s, p, U8, I8, U8, epi, res_type=U8)
+            x, wc, res = conv_codes(c)
+            want = to_bytes(oracle_conv(c, x, wc, res), U8)
+            assert_bytes_equal(gpu_conv(c, x, wc, res), want, "tile %d %s" % (tile, PIPE[i]))
+        if tile in (0, 1, 6, 8, 10, 12):
+            h, w, k, st, co = 21, 19, 7, 2, 64 if tile != 1 else 128
+            c = synth.conv_case(77 + tile, 2, h, w, 3, co, k, st, 3, U8, I8, U8, RELU)
+            x, wc, _ = conv_codes(c)
+            want = to_bytes(oracle_conv(c, x, wc, None), U8)
+            xp = np.pad(x, ((0, 0), (3, 3), (3, 3), (0, 1)), constant_values=c.z_in)
+            wp = np.pad(wc, ((0, 0), (0, 0), (0, 0), (0, 1)))
+            conv = QConv(2, h + 6, w + 6, 4, co, k, st, 0, U8, I8, U8, RELU, c.z_in, c.z_out,
+                         to_bytes(wp, I8), c.bias, c.s_in, c.s_w, c.s_out)
+            y = conv(torch.from_numpy(to_bytes(xp, U8)).cuda())
+            torch.cuda.synchronize()
+            assert_bytes_equal(y.cpu().numpy(), want, "tile %d four-channel gather" % tile)
+    finally:
+        B.iqnn_set_conv_tile(-1)
+
+
 def test_conv_adversarial_codes_and_padding():
     # every code of each type, including -128 / 255 / -8 / 15, on tiny images where
     # most taps read padding
