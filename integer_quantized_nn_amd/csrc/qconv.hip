@@ -140,14 +140,20 @@ __device__ __forceinline__ void load_res16(const ConvParams& p, int64_t oidx, in
 // v_cvt_pk_u8_f32 packs each byte, and the shift is undone with one XOR per word.
 // Every intermediate is an exact integer below 2^24 or is clamped away, so this is
 // bit-identical to rounding, adding Z_out as an integer and clipping.
+//
+// BIAS: add bias[] here (otherwise the accumulator started from the folded bias).
+// ADDK: 0 = residual add decided by `add` and p.res_type at run time, 1 = always an
+// 8-bit residual, 2 = never a residual.
+template <bool BIAS = true, int ADDK = 0>
 __device__ __forceinline__ void epi_store16(const ConvParams& p, const v16i& acc, const int32_t* bias,
-                                            const float* mult, uint32_t rw[4], int ocb, int64_t pix, bool add,
+                                            const float* mult, uint32_t rw[4], int ocb, int64_t pix, bool add_rt,
                                             float m_res) {
+    const bool add = ADDK == 1 ? true : (ADDK == 2 ? false : add_rt);
     const int64_t oidx = pix * p.c_out + ocb;   // element index of the first channel
     if (p.epi == E_RAW) {
         int32_t a[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) a[j] = acc[j] + bias[j];
+        for (int j = 0; j < 16; ++j) a[j] = acc[j] + (BIAS ? bias[j] : 0);
         int32_t* yo = reinterpret_cast<int32_t*>(p.y) + oidx;
         if (p.vec_store) {
 #pragma unroll
@@ -160,9 +166,9 @@ __device__ __forceinline__ void epi_store16(const ConvParams& p, const v16i& acc
     }
     float v[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = (float)(acc[j] + bias[j]) * mult[j];
+    for (int j = 0; j < 16; ++j) v[j] = (float)(acc[j] + (BIAS ? bias[j] : 0)) * mult[j];
     if (add) {
-        const bool r8 = p.res_type == T_INT8 || p.res_type == T_UINT8;
+        const bool r8 = ADDK == 1 || p.res_type == T_INT8 || p.res_type == T_UINT8;
         uint32_t w[4] = {rw[0] ^ p.res_xor, rw[1] ^ p.res_xor, rw[2] ^ p.res_xor, rw[3] ^ p.res_xor};
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -441,9 +447,16 @@ void qconv_igemm(const ConvParams p) {
 
 constexpr int kPipeBK = 64;     // K bytes per stage
 
-// XOR swizzle of the four 16-byte slots of a 64-byte LDS row.  Over any 16
-// consecutive rows (and any 8) the fragment reads of one slot hit distinct banks.
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// XOR swizzle of the four 16-byte slots of a 64-byte LDS row.  A fragment read is one
+// ds_read_b128 of 32 consecutive rows x 2 slots; with the slot XORed by bits 2..3 of
+// the row it runs conflict-free on gfx950 (measured: 4 LDS cycles per read, against
+// 8 for the row>>1 family of swizzles and 16 unswizzled).
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+
+// Swizzle of the 16-byte chunks of a residual row of `lpr` chunks (lpr = 4: 64-byte
+// rows, lpr = 8: 128-byte rows), chosen the same way: conflict-free reads of one
+// chunk over 32 consecutive rows.
+__device__ __forceinline__ int rswz(int row, int lpr) { return lpr == 8 ? (row >> 1) & 7 : (row >> 2) & 3; }
 
 // s_waitcnt for vmcnt <= n only (expcnt and lgkmcnt left at their maximum).
 #define IQNN_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
@@ -879,23 +892,31 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // One global -> LDS DMA of 16 (4) bytes per lane: lane i writes LDS bytes
 // [m0 + 16 i, +16) ([m0 + 4 i, +4)).  m0 takes one wait state before the load reads it.
+// The LDS address is wave-uniform; readfirstlane pins it to an SGPR even when the
+// compiler has parked it in a VGPR under register pressure.
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src)
+    const uint32_t m = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m), "v"(src)
                  : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(src)
+    const uint32_t m = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(m), "v"(src)
                  : "memory", "m0");
 }
 
-template <int BM_, int BN_, int WM_, int NST_>
+// OCC_: workgroups per CU to compile for (0: as many as the LDS allows, at most 2);
+// 3 caps the kernel at 168 VGPRs.
+template <int BM_, int BN_, int WM_, int NST_, int OCC_ = 0>
 struct StreamCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = 4 / WM_, NST = NST_;
     static constexpr int WOC = BM / WM, WPX = BN / WN;
     static constexpr int TM = WOC / 32, TN = WPX / 32;
     static constexpr int STAGE = (BM + BN) * kPipeBK;
     static constexpr int LDS = NST * STAGE + 8 * BM;
-    static constexpr int OCC = 160 * 1024 / LDS >= 2 ? 2 : 1;   // 160 KB of LDS per CU
+    static constexpr int LDS_FIT = 160 * 1024 / LDS;   // 160 KB of LDS per CU
+    static constexpr int OCC = OCC_ > 0 ? OCC_ : (LDS_FIT >= 2 ? 2 : 1);
+    static_assert(OCC <= LDS_FIT, "LDS for the requested occupancy");
 };
 
 template <class C, bool IS1X1, bool RES, bool C4>
@@ -912,6 +933,7 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
     static_assert(D * K_LOADS <= 60, "DMA in flight must fit the 6-bit vmcnt");
     static_assert(R_INST <= K_LOADS, "a residual tile fits one stage");
     static_assert(!(RES && C4), "the 4-channel gather has no residual stage");
+    static_assert(!RES || BM == 64 || BM == 128, "residual rows of 4 or 8 chunks");
 
     __shared__ __attribute__((aligned(1024))) uint8_t ring[NST * STAGE];
     __shared__ __attribute__((aligned(16))) int32_t cbias[BM];
@@ -958,17 +980,21 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
         const int row = wave * (BM / 4) + 16 * j + drow;
         wsrc[j] = p.w + (int64_t)(oc0 + row) * p.kp + (dslot ^ swz(row)) * 16;
     }
-    int32_t bseg[C4 ? 1 : B_INST];
-    if constexpr (!C4) {
-#pragma unroll
-        for (int j = 0; j < B_INST; ++j) bseg[j] = (dslot ^ swz(wave * (BN / 4) + 16 * j + drow)) * 16;
-    }
-    // per-tile geometry of the tile being issued
-    int64_t rbase[C4 ? 1 : B_INST];
-    int32_t rih[C4 ? 1 : B_INST], riw[C4 ? 1 : B_INST];
+    // Per-tile state of the tile being issued.  Activation rows (B) are pixels:
+    //   1x1:    prow = the pixel's row + its 16-byte segment; rows past the end point at
+    //           the last pixel instead (a pixel's accumulator column depends only on its
+    //           own row, and the epilogue never stores those columns), so a stage's
+    //           address is prow + k0 with no test.
+    //   KHxKW:  prow = the row of filter tap (0, 0), possibly outside the image, and
+    //           tmask = the taps that fall inside it; a stage reads prow + tapoff when
+    //           its tap is in tmask, else the row of pad codes.
+    constexpr int NB = C4 ? 1 : B_INST;
+    const uint8_t* prow[NB];
+    uint64_t tmask[NB];
     constexpr int C4N = C4 ? B_INST : 1;
     int32_t coff[C4N], cky[C4N];
     const uint8_t* rsrc[RES ? R_INST : 1];
+    const uint32_t ohw = (uint32_t)(p.oh * p.ow);   // < 2^31, checked by the host
     auto set_issue_tile = [&](int j) {
         const int64_t px0 = tile_px0(j);
         if constexpr (C4) {
@@ -984,35 +1010,38 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
                 coff[i] = -1;
                 cky[i] = ky0;
                 if (pix < p.m) {
-                    const int64_t ohw = (int64_t)p.oh * p.ow;
-                    const int32_t n = (int32_t)(pix / ohw);
-                    const int32_t rem = (int32_t)(pix - (int64_t)n * ohw);
-                    const int32_t oy = rem / p.ow, ox = rem - oy * p.ow;
-                    coff[i] = (n * p.h + oy * p.sh + ky0) * p.w_in + ox * p.sw + kx0;
+                    const uint32_t pu = (uint32_t)pix;
+                    const uint32_t n = pu / ohw, rem = pu - n * ohw;
+                    const uint32_t oy = rem / (uint32_t)p.ow, ox = rem - oy * (uint32_t)p.ow;
+                    coff[i] = ((int32_t)n * p.h + (int32_t)oy * p.sh + ky0) * p.w_in + (int32_t)ox * p.sw + kx0;
                 }
             }
         } else {
 #pragma unroll
             for (int i = 0; i < B_INST; ++i) {
                 const int64_t pix = px0 + wave * (BN / 4) + 16 * i + drow;
-                if (pix < p.m) {
-                    if (IS1X1) {
-                        rbase[i] = pix * p.c;
-                        rih[i] = 0;
-                        riw[i] = 0;
-                    } else {
-                        const int64_t ohw = (int64_t)p.oh * p.ow;
-                        const int64_t n = pix / ohw;
-                        const int32_t rem = (int32_t)(pix - n * ohw);
-                        const int32_t oy = rem / p.ow, ox = rem - oy * p.ow;
-                        rbase[i] = n * p.h * p.w_in * (int64_t)p.c;
-                        rih[i] = oy * p.sh - p.ph;
-                        riw[i] = ox * p.sw - p.pw;
+                const int32_t seg = (dslot ^ swz(wave * (BN / 4) + 16 * i + drow)) * 16;
+                if (IS1X1) {
+                    prow[i] = p.x + (pix < p.m ? pix : p.m - 1) * p.c + seg;
+                    tmask[i] = 0;
+                } else if (pix < p.m) {
+                    const uint32_t pu = (uint32_t)pix;
+                    const uint32_t n = pu / ohw, rem = pu - n * ohw;
+                    const uint32_t oy = rem / (uint32_t)p.ow, ox = rem - oy * (uint32_t)p.ow;
+                    const int32_t iy0 = (int32_t)oy * p.sh - p.ph, ix0 = (int32_t)ox * p.sw - p.pw;
+                    prow[i] = p.x + ((int64_t)((int32_t)n * p.h + iy0) * p.w_in + ix0) * p.c + seg;
+                    // taps inside the image: kx in [xlo, xhi), ky in [ylo, yhi)
+                    const int32_t xlo = max(0, -ix0), xhi = min(p.kw, p.w_in - ix0);
+                    const int32_t ylo = max(0, -iy0), yhi = min(p.kh, p.h - iy0);
+                    uint64_t m = 0;
+                    if (xlo < xhi) {
+                        const uint64_t xm = ((uint64_t)1 << xhi) - ((uint64_t)1 << xlo);
+                        for (int ky = ylo; ky < yhi; ++ky) m |= xm << (ky * p.kw);
                     }
+                    tmask[i] = m;
                 } else {
-                    rbase[i] = -1;
-                    rih[i] = -(1 << 29);
-                    riw[i] = -(1 << 29);
+                    prow[i] = padrow;
+                    tmask[i] = 0;
                 }
             }
         }
@@ -1023,15 +1052,20 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
 #pragma unroll
             for (int i = 0; i < R_INST; ++i) {
                 const int row = (wave * R_INST + i) * (1024 / BM) + lane / LPR;
-                const int ch = oc0 + (lane % LPR) * 16;
+                const int ch = oc0 + ((lane % LPR) ^ rswz(row, LPR)) * 16;
                 const int64_t pix = px0 + row;
                 rsrc[i] = (pix < p.m && ch < p.c_out) ? p.res + pix * p.c_out + ch : p.res;
             }
         }
     };
-    int is_j = 0, is_s = 0;            // next stage to issue (local tile, stage in tile)
-    int k_ci = 0, k_kx = 0, k_ky = 0;  // its K position: channel offset, filter column, row
-    uint32_t is_off = 0;               // its ring slot
+    // the next stage to issue: local tile, stage in tile, ring slot, and its K position
+    // (byte offset of the tap row plus channel offset from prow, tap index, channel
+    // offset inside the tap, filter column)
+    int is_j = 0, is_s = 0;
+    uint32_t is_off = 0;
+    int64_t tapoff = 0;
+    int tap = 0, k_ci = 0, k_kx = 0;
+    const int64_t row_jump = (int64_t)(p.w_in - p.kw) * p.c;   // end of a filter row -> start of the next
     set_issue_tile(0);
     auto issue = [&]() {
         const uint32_t dst = ring0 + is_off;
@@ -1053,17 +1087,13 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
                     if (coff[i] >= 0 && cky[i] + rows < p.kh) src = p.x + (int64_t)(coff[i] + rows * p.w_in) * 4;
                     dma4(src, dst + (BM + wave * (BN / 4) + 4 * i) * kPipeBK);
                 }
+            } else if constexpr (IS1X1) {
+#pragma unroll
+                for (int i = 0; i < B_INST; ++i) dma16(prow[i] + k0, dst + (BM + wave * (BN / 4) + 16 * i) * kPipeBK);
             } else {
 #pragma unroll
                 for (int i = 0; i < B_INST; ++i) {
-                    const uint8_t* src;
-                    if (IS1X1) {
-                        src = rbase[i] >= 0 ? p.x + rbase[i] + k0 + bseg[i] : padrow;
-                    } else {
-                        const int32_t iy = rih[i] + k_ky, ix = riw[i] + k_kx;
-                        const bool ok = (uint32_t)iy < (uint32_t)p.h && (uint32_t)ix < (uint32_t)p.w_in;
-                        src = ok ? p.x + rbase[i] + ((int64_t)iy * p.w_in + ix) * p.c + k_ci + bseg[i] : padrow;
-                    }
+                    const uint8_t* src = ((tmask[i] >> tap) & 1) ? prow[i] + tapoff : padrow;
                     dma16(src, dst + (BM + wave * (BN / 4) + 16 * i) * kPipeBK);
                 }
             }
@@ -1073,16 +1103,22 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
         if (is_s + 1 < spt) {
             ++is_s;
             if (!IS1X1 && !C4 && is_s < nst) {
+                tapoff += kPipeBK;
                 k_ci += kPipeBK;
                 if (k_ci == p.c) {
                     k_ci = 0;
-                    if (++k_kx == p.kw) { k_kx = 0; ++k_ky; }
+                    ++tap;
+                    if (++k_kx == p.kw) {
+                        k_kx = 0;
+                        tapoff += row_jump;
+                    }
                 }
             }
         } else if (is_j + 1 < J) {
             ++is_j;
             is_s = 0;
-            k_ci = k_kx = k_ky = 0;
+            tapoff = 0;
+            tap = k_ci = k_kx = 0;
             set_issue_tile(is_j);
         }
     };
@@ -1093,11 +1129,24 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
     const int foff0 = frow * kPipeBK + (((lane >> 5) + 0) ^ fsw) * 16;
     const int foff1 = frow * kPipeBK + (((lane >> 5) + 2) ^ fsw) * 16;
     const uint32_t bxor = p.x_xor;
+    // accumulators start from the folded bias of their channels: lane half h of channel
+    // block t holds channels ocl(t) .. ocl(t)+15 of the block
     v16i acc[TM][TN];
+    auto init_acc = [&]() {
 #pragma unroll
-    for (int t = 0; t < TM; ++t)
+        for (int t = 0; t < TM; ++t) {
+            const int ocl = wave_oc * C::WOC + t * 32 + (lane >> 5) * 16;
+            v16i b;
 #pragma unroll
-        for (int u = 0; u < TN; ++u) acc[t][u] = v16i{};
+            for (int q = 0; q < 4; ++q) {
+                const int4 bv = *reinterpret_cast<const int4*>(&cbias[ocl + 4 * q]);
+                b[4 * q] = bv.x; b[4 * q + 1] = bv.y; b[4 * q + 2] = bv.z; b[4 * q + 3] = bv.w;
+            }
+#pragma unroll
+            for (int u = 0; u < TN; ++u) acc[t][u] = b;
+        }
+    };
+    init_acc();
 
     v4i fa0[TM], fb0[TN], fa1[TM], fb1[TN];
     auto read_frags = [&](const uint8_t* cur, int fo, v4i (&fa)[TM], v4i (&fb)[TN]) {
@@ -1176,13 +1225,11 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
             const int ocl = wave_oc * C::WOC + t * 32 + (lane >> 5) * 16;   // channel inside the block
             const int ocb = oc0 + ocl;
             if (ocb >= p.c_out) continue;
-            ChanParams cp;
+            float mult[16];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                int4 bv = *reinterpret_cast<const int4*>(&cbias[ocl + 4 * q]);
-                float4 mv = *reinterpret_cast<const float4*>(&cmult[ocl + 4 * q]);
-                cp.bias[4 * q] = bv.x; cp.bias[4 * q + 1] = bv.y; cp.bias[4 * q + 2] = bv.z; cp.bias[4 * q + 3] = bv.w;
-                cp.mult[4 * q] = mv.x; cp.mult[4 * q + 1] = mv.y; cp.mult[4 * q + 2] = mv.z; cp.mult[4 * q + 3] = mv.w;
+                const float4 mv = *reinterpret_cast<const float4*>(&cmult[ocl + 4 * q]);
+                mult[4 * q] = mv.x; mult[4 * q + 1] = mv.y; mult[4 * q + 2] = mv.z; mult[4 * q + 3] = mv.w;
             }
 #pragma unroll
             for (int u = 0; u < TN; ++u) {
@@ -1191,16 +1238,13 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
                 if (pix >= p.m) continue;
                 uint32_t rw[4] = {0, 0, 0, 0};
                 if (RES) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(rtile + pl * BM + ocl);
+                    const uint4 v = *reinterpret_cast<const uint4*>(rtile + pl * BM + (((ocl >> 4) ^ rswz(pl, BM / 16)) << 4));
                     rw[0] = v.x; rw[1] = v.y; rw[2] = v.z; rw[3] = v.w;
                 }
-                epi_store16(p, acc[t][u], cp.bias, cp.mult, rw, ocb, pix, add, m_res);
+                epi_store16<false, RES ? 1 : 2>(p, acc[t][u], nullptr, mult, rw, ocb, pix, add, m_res);
             }
         }
-#pragma unroll
-        for (int t = 0; t < TM; ++t)
-#pragma unroll
-            for (int u = 0; u < TN; ++u) acc[t][u] = v16i{};
+        init_acc();
         if (RES) {
             advance();
             if (!last_tile) sync();
@@ -1217,7 +1261,7 @@ hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bo
     q.n_oc_tiles = (p.c_out + C::BM - 1) / C::BM;
     const int64_t n_px = (p.m + C::BN - 1) / C::BN;
     if (n_px <= 0) return hipSuccess;
-    if (n_px > 0x3FFFFFFF) return hipErrorInvalidValue;
+    if (p.m >= ((int64_t)1 << 31) || (!is_1x1 && !c4 && p.kh * p.kw > 64)) return hipErrorInvalidValue;
     q.n_px_tiles = (int32_t)n_px;
     q.px_chunk = (int32_t)((n_px + 7) / 8);
     // workgroups per XCD: a multiple of the channel tiles, about OCC per CU (32 CUs per
@@ -1227,7 +1271,7 @@ hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bo
     per = std::min<int64_t>(per, (int64_t)q.px_chunk * n_oc);
     q.gx = per;
     dim3 g((unsigned)(8 * per)), b(256);
-    if constexpr ((C::NST - 1) * (C::BM / 64 + C::BN / 16) <= 60) {
+    if constexpr ((C::NST - 1) * (C::BM / 64 + C::BN / 16) <= 60 && C::OCC < 3) {
         if (c4) {
             hipLaunchKernelGGL((qconv_stream<C, false, false, true>), g, b, 0, stream, q);
             return hipGetLastError();
@@ -1236,7 +1280,7 @@ hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bo
         return hipErrorInvalidValue;
     }
     // the residual rides in the stream when a tile of it fits one stage
-    constexpr bool kResStage = C::BM * C::BN / 4096 <= C::BM / 64 + C::BN / 64;
+    constexpr bool kResStage = C::BM * C::BN / 4096 <= C::BM / 64 + C::BN / 64 && C::OCC < 3;
     const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;
     if (add && !(kResStage && res_prefetch)) return hipErrorInvalidValue;
     if constexpr (kResStage) {
@@ -1277,14 +1321,17 @@ using S128x128d4 = StreamCfg<128, 128, 2, 4>;
 using S64x256d7 = StreamCfg<64, 256, 1, 7>;
 using S256x128d6 = StreamCfg<256, 128, 2, 6>;
 using S128x256d6 = StreamCfg<128, 256, 2, 6>;
+using S128x128d3o3 = StreamCfg<128, 128, 2, 3, 3>;
+using S128x256d3 = StreamCfg<128, 256, 2, 3>;
+using S256x128d3 = StreamCfg<256, 128, 2, 3>;
 
-// Automatic tile: the streaming kernel with 64x128 / 128x128 blocks (two per CU) for
-// the memory-bound and mid-size layers; wide, deep contractions (c_out >= 1024,
-// K >= 1024, no residual) keep the 128x256 ring kernel, whose larger block reuses
-// each fragment more.
+// Automatic tile, all on the streaming kernel at two blocks per CU: 256x128 blocks
+// (each wave 128 channels x 64 pixels: 0.75 KB of fragment reads per MFMA) for the
+// wide, deep contractions (C_out >= 256, K >= 1024, no residual); 128x128 blocks
+// for the rest, 64x128 when C_out <= 64.
 int pipe_tile_choice(int64_t m, int32_t c_out, int64_t k, bool res) {
     (void)m;
-    if (c_out >= 1024 && k >= 1024 && !res) return 2;
+    if (c_out >= 256 && k >= 1024 && !res) return 16;
     return c_out <= 64 ? 8 : 10;
 }
 
@@ -1294,8 +1341,12 @@ hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_
         const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;
         const bool res_prefetch = add && p.vec_store && (p.res_type == T_INT8 || p.res_type == T_UINT8);
         if (tile < 0) tile = pipe_tile_choice(p.m, p.c_out, p.k, res_prefetch);
-        // the streaming kernel takes a residual only as a stage of its stream
-        if (tile >= 7 && add && !(res_prefetch && tile != 12 && tile != 13)) tile = p.c_out <= 64 ? 0 : 1;
+        // the streaming kernel takes a residual only as a stage of its stream, decodes
+        // pixel indices in 32 bits and keeps a 64-bit mask of in-image filter taps
+        const bool stream_ok = p.m < ((int64_t)1 << 31) && (is_1x1 || c4 || p.kh * p.kw <= 64);
+        if (tile == 14 && (add || c4)) tile = 10;   // compiled without those variants
+        if (tile >= 7 && (!stream_ok || (add && !(res_prefetch && tile != 12 && tile != 13 && tile < 15))))
+            tile = p.c_out <= 64 ? 0 : 1;
         if (c4 && tile >= 7 && tile != 8 && tile != 10 && tile != 12) tile = p.c_out <= 64 ? 8 : 10;
         if (c4 && tile < 7 && tile != 0 && tile != 1 && tile != 6) tile = p.c_out <= 64 ? 0 : 1;   // the 4-channel gather's shapes
         switch (tile) {
@@ -1312,7 +1363,10 @@ hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_
         case 10: return launch_stream<S128x128d4>(p, is_1x1, res_prefetch, c4, stream);
         case 11: return launch_stream<S64x256d7>(p, is_1x1, res_prefetch, c4, stream);
         case 12: return launch_stream<S256x128d6>(p, is_1x1, res_prefetch, c4, stream);
-        default: return launch_stream<S128x256d6>(p, is_1x1, res_prefetch, c4, stream);
+        case 13: return launch_stream<S128x256d6>(p, is_1x1, res_prefetch, c4, stream);
+        case 14: return launch_stream<S128x128d3o3>(p, is_1x1, res_prefetch, c4, stream);
+        case 15: return launch_stream<S128x256d3>(p, is_1x1, res_prefetch, c4, stream);
+        default: return launch_stream<S256x128d3>(p, is_1x1, res_prefetch, c4, stream);
         }
     }
     if (p.c_out <= 64) return launch_staged<64, 256, 1, 4>(p, gather, is_1x1, stream);
