@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "int8/int4 quantized conv+GEMM TOPS and % of int8 MFMA peak, bit-exact"
 PEAK_INT8_OPS = 5.0e15      # MI355X dense int8 MFMA, ops/s
 PEAK_HBM = 8.0e12           # MI355X HBM3E, bytes/s
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qconv_igemm_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qconv_resnet50_trunk_b256_traffic.md")
 
 
 def log(*a):
@@ -63,7 +63,7 @@ def measured_traffic(workload):
 
 
 def traffic_from_dbs(fetch_db, write_db, workload):
-    """Per-launch HBM traffic of qconv_igemm from two rocprofv3 --pmc databases (FETCH_SIZE,
+    """Per-launch HBM traffic of the conv kernels from two rocprofv3 --pmc databases (FETCH_SIZE,
     WRITE_SIZE; KiB per dispatch), each scaled by what the same counter reads for the
     calibration copy (--calib-copy-mib) whose true byte count is known."""
     import sqlite3
@@ -77,7 +77,7 @@ def traffic_from_dbs(fetch_db, write_db, workload):
         rows = per_dispatch(path)
         copies = [v for (_, n, v) in rows if "copyBuffer" in n or "copy" in n.lower()]
         calib_kib = max(copies)
-        q = [v for (_, n, v) in rows if "qconv_igemm" in n]
+        q = [v for (_, n, v) in rows if "qconv_" in n]
         out[tag] = (calib_kib, float(np.mean(q)), len(q))
     return out
 
@@ -182,7 +182,7 @@ def bench_trunk(args):
     roof["frac"] = roof["achieved"] / roof["peak"]
     tr_bytes = measured_traffic("resnet50_trunk_b%d" % args.batch)
     roof["traffic"] = tr_bytes
-    roof["kernel"] = "qconv_igemm (all instantiations; %d launches per step)" % n_conv
+    roof["kernel"] = "qconv (qconv_stream / qconv_pipe / qconv_igemm; %d launches per step)" % n_conv
     roof["algorithmic_bytes_per_launch"] = bytes_per_launch
     roof["algorithmic_ops_per_launch"] = ops_per_launch
     roof["avg_launch_us"] = avg_dur * 1e6
