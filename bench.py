@@ -159,13 +159,27 @@ def bench_trunk(args):
                 maxpool2d(b["stem"], n, h, w, c, 3, 2, 1, B.UINT8, out=b["pool"])
         dequantize(b[net.final], net.shapes[net.final], net.final_scale, net.final_zp, B.UINT8, out=net.out_f32)
 
+    # eager steps with per-conv events: the launch durations for the roofline
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for s in range(args.steps):
         timed_step(ev[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step_eager = wall * 1e3 / args.steps
+    ms_per_step = ms_per_step_eager
+    if not args.no_graph:
+        # the step as one HIP graph launch (the same kernels, without per-launch host gaps)
+        graph = net.capture(x)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for s in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+        ms_per_step = wall * 1e3 / args.steps
 
     dur = np.array([[a.elapsed_time(b) * 1e-3 for (a, b) in row] for row in ev])   # seconds [steps][conv]
     conv_ops = np.array([l[1] for l in conv_launches], np.float64)
@@ -204,7 +218,9 @@ def bench_trunk(args):
                    "step": "quantize fp32 input, 53 fused convs + max pooling, dequantize output"},
         "pct_int8_mfma_peak": value * 1e12 / PEAK_INT8_OPS,
         "roofline": roof,
-        "conv_time_share": float(dur.sum() / wall),
+        "conv_time_share": float(dur.sum() / args.steps / (ms_per_step * 1e-3)),
+        "launch": "one HIP graph per step" if not args.no_graph else "eager launches",
+        "ms_per_step_eager": ms_per_step_eager,
         "per_layer_us_tops": per_layer,
     }
     if not args.no_cpu_baseline:
@@ -295,6 +311,8 @@ def main():
     ap.add_argument("--workload", default="resnet50_trunk",
                     choices=["resnet50_trunk", "conv3x3_int8", "conv3x3_4bit", "vitl_fc1", "gemm_int8_256"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="trunk: time eager launches instead of one captured HIP graph per step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--traffic-db", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="print the TRAFFIC record of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) made "

@@ -890,19 +890,68 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(lds_ptr_t)(p);
 }
 
-// One global -> LDS DMA of 16 (4) bytes per lane: lane i writes LDS bytes
-// [m0 + 16 i, +16) ([m0 + 4 i, +4)).  m0 takes one wait state before the load reads it.
-// The LDS address is wave-uniform; readfirstlane pins it to an SGPR even when the
-// compiler has parked it in a VGPR under register pressure.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+// Runs of global -> LDS DMA issued from one m0 value.  Each instruction moves 16 (4)
+// bytes per lane: lane i of instruction j writes LDS bytes [lds + j*STEP + 16 i, +16)
+// ([lds + j*STEP + 4 i, +4)), STEP = 1024 (256).  The instruction's immediate offset
+// shifts both the LDS and the global address (measured on gfx950), so each source
+// pointer is passed lowered by j*STEP and m0 is written once per run.  m0 and its
+// loads sit in one asm statement so nothing can use m0 in between; m0 takes one wait
+// state before the first load reads it.  The LDS address is wave-uniform;
+// readfirstlane pins it to an SGPR even when the compiler has parked it in a VGPR.
+template <int N>
+__device__ __forceinline__ void dma16_run(uint32_t lds, const void* const* src) {
+    static_assert(N >= 1 && N <= 4, "16-byte runs of 1..4 KB");
     const uint32_t m = __builtin_amdgcn_readfirstlane(lds);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m), "v"(src)
-                 : "memory", "m0");
+    const char* q0 = static_cast<const char*>(src[0]);
+    if constexpr (N == 1) {
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m), "v"(q0)
+                     : "memory", "m0");
+    } else if constexpr (N == 2) {
+        const char* q1 = static_cast<const char*>(src[1]) - 1024;
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+                     "global_load_lds_dwordx4 %2, off offset:1024" ::"s"(m), "v"(q0), "v"(q1)
+                     : "memory", "m0");
+    } else if constexpr (N == 3) {
+        const char* q1 = static_cast<const char*>(src[1]) - 1024;
+        const char* q2 = static_cast<const char*>(src[2]) - 2048;
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+                     "global_load_lds_dwordx4 %2, off offset:1024\n\tglobal_load_lds_dwordx4 %3, off offset:2048"
+                     ::"s"(m), "v"(q0), "v"(q1), "v"(q2) : "memory", "m0");
+    } else {
+        const char* q1 = static_cast<const char*>(src[1]) - 1024;
+        const char* q2 = static_cast<const char*>(src[2]) - 2048;
+        const char* q3 = static_cast<const char*>(src[3]) - 3072;
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+                     "global_load_lds_dwordx4 %2, off offset:1024\n\tglobal_load_lds_dwordx4 %3, off offset:2048\n\t"
+                     "global_load_lds_dwordx4 %4, off offset:3072"
+                     ::"s"(m), "v"(q0), "v"(q1), "v"(q2), "v"(q3) : "memory", "m0");
+    }
 }
-__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
-    const uint32_t m = __builtin_amdgcn_readfirstlane(lds);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(m), "v"(src)
-                 : "memory", "m0");
+// 16-byte DMA of N KB-instructions to consecutive KB of LDS, in runs of at most 4.
+template <int N>
+__device__ __forceinline__ void dma16_seq(uint32_t lds, const void* const* src) {
+    if constexpr (N > 0) {
+        constexpr int R = N < 4 ? N : 4;
+        dma16_run<R>(lds, src);
+        dma16_seq<N - R>(lds + R * 1024, src + R);
+    }
+}
+// 4-byte DMA of N 256-byte instructions to consecutive LDS, in runs of 4.
+template <int N>
+__device__ __forceinline__ void dma4_seq(uint32_t lds, const void* const* src) {
+    if constexpr (N > 0) {
+        static_assert(N % 4 == 0, "4-byte runs of 4");
+        const uint32_t m = __builtin_amdgcn_readfirstlane(lds);
+        const char* q0 = static_cast<const char*>(src[0]);
+        const char* q1 = static_cast<const char*>(src[1]) - 256;
+        const char* q2 = static_cast<const char*>(src[2]) - 512;
+        const char* q3 = static_cast<const char*>(src[3]) - 768;
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\t"
+                     "global_load_lds_dword %2, off offset:256\n\tglobal_load_lds_dword %3, off offset:512\n\t"
+                     "global_load_lds_dword %4, off offset:768"
+                     ::"s"(m), "v"(q0), "v"(q1), "v"(q2), "v"(q3) : "memory", "m0");
+        dma4_seq<N - 4>(lds + 1024, src + 4);
+    }
 }
 
 // OCC_: workgroups per CU to compile for (0: as many as the LDS allows, at most 2);
@@ -1070,32 +1119,42 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
     auto issue = [&]() {
         const uint32_t dst = ring0 + is_off;
         if (RES && is_s == nst) {
+            if constexpr (RES) {
+                const void* rs[R_INST];
 #pragma unroll
-            for (int i = 0; i < R_INST; ++i) dma16(rsrc[i], dst + (wave * R_INST + i) * 1024);
+                for (int i = 0; i < R_INST; ++i) rs[i] = rsrc[i];
+                dma16_seq<R_INST>(dst + wave * R_INST * 1024, rs);
+                constexpr int NPAD = K_LOADS - R_INST;   // padding: same count as a K-stage
+                if constexpr (NPAD > 0) {
+                    const void* ps[NPAD];
 #pragma unroll
-            for (int i = R_INST; i < K_LOADS; ++i)   // padding: same count as a K-stage
-                dma16(p.res, dst + 4 * R_INST * 1024 + (wave * (K_LOADS - R_INST) + i - R_INST) * 1024);
+                    for (int i = 0; i < NPAD; ++i) ps[i] = p.res;
+                    dma16_seq<NPAD>(dst + 4 * R_INST * 1024 + wave * NPAD * 1024, ps);
+                }
+            }
         } else {
             const int k0 = is_s * kPipeBK;
+            const void* as[A_INST];
 #pragma unroll
-            for (int j = 0; j < A_INST; ++j) dma16(wsrc[j] + k0, dst + (wave * (BM / 4) + 16 * j) * kPipeBK);
+            for (int j = 0; j < A_INST; ++j) as[j] = wsrc[j] + k0;
+            dma16_seq<A_INST>(dst + wave * (BM / 4) * kPipeBK, as);
+            const void* bs[B_INST];
             if constexpr (C4) {
                 const int32_t rows = is_s * (16 / p.kw);   // filter rows advanced since stage 0
 #pragma unroll
                 for (int i = 0; i < B_INST; ++i) {
                     const uint8_t* src = padrow;
                     if (coff[i] >= 0 && cky[i] + rows < p.kh) src = p.x + (int64_t)(coff[i] + rows * p.w_in) * 4;
-                    dma4(src, dst + (BM + wave * (BN / 4) + 4 * i) * kPipeBK);
+                    bs[i] = src;
                 }
-            } else if constexpr (IS1X1) {
-#pragma unroll
-                for (int i = 0; i < B_INST; ++i) dma16(prow[i] + k0, dst + (BM + wave * (BN / 4) + 16 * i) * kPipeBK);
+                dma4_seq<B_INST>(dst + (BM + wave * (BN / 4)) * kPipeBK, bs);
             } else {
 #pragma unroll
                 for (int i = 0; i < B_INST; ++i) {
-                    const uint8_t* src = ((tmask[i] >> tap) & 1) ? prow[i] + tapoff : padrow;
-                    dma16(src, dst + (BM + wave * (BN / 4) + 16 * i) * kPipeBK);
+                    if constexpr (IS1X1) bs[i] = prow[i] + k0;
+                    else bs[i] = ((tmask[i] >> tap) & 1) ? prow[i] + tapoff : padrow;
                 }
+                dma16_seq<B_INST>(dst + (BM + wave * (BN / 4)) * kPipeBK, bs);
             }
         }
         is_off = is_off + STAGE == NST * STAGE ? 0 : is_off + STAGE;
@@ -1324,6 +1383,7 @@ using S128x256d6 = StreamCfg<128, 256, 2, 6>;
 using S128x128d3o3 = StreamCfg<128, 128, 2, 3, 3>;
 using S128x256d3 = StreamCfg<128, 256, 2, 3>;
 using S256x128d3 = StreamCfg<256, 128, 2, 3>;
+using S256x256d4 = StreamCfg<256, 256, 2, 4>;
 
 // Automatic tile, all on the streaming kernel at two blocks per CU: 256x128 blocks
 // (each wave 128 channels x 64 pixels: 0.75 KB of fragment reads per MFMA) for the
@@ -1366,7 +1426,8 @@ hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_
         case 13: return launch_stream<S128x256d6>(p, is_1x1, res_prefetch, c4, stream);
         case 14: return launch_stream<S128x128d3o3>(p, is_1x1, res_prefetch, c4, stream);
         case 15: return launch_stream<S128x256d3>(p, is_1x1, res_prefetch, c4, stream);
-        default: return launch_stream<S256x128d3>(p, is_1x1, res_prefetch, c4, stream);
+        case 16: return launch_stream<S256x128d3>(p, is_1x1, res_prefetch, c4, stream);
+        default: return launch_stream<S256x256d4>(p, is_1x1, res_prefetch, c4, stream);
         }
     }
     if (p.c_out <= 64) return launch_staged<64, 256, 1, 4>(p, gather, is_1x1, stream);

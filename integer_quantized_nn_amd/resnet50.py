@@ -87,6 +87,23 @@ class QuantResNet50Trunk:
                    out=self.out_f32, stream=stream)
         return self.out_f32
 
+    def capture(self, x_f32):
+        """Record one step on x_f32 (a fixed device buffer) into a HIP graph, so a
+        step is one graph launch instead of 56 kernel launches.  Replay with
+        graph.replay(); the result lands in self.out_f32 as with step().  Every
+        launch of the step is a plain kernel on the capture stream (no memsets, no
+        host synchronisation, no allocation)."""
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):   # warm the capture stream once, eagerly
+            self.step(x_f32)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            self.step(x_f32)
+        return g
+
     def launches(self):
         """(kernel family, algorithmic ops, algorithmic bytes) of every launch in one step.
         Ops and bytes are those of the unpadded layer (the stem's 3 channels, K = 147)."""

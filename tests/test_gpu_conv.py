@@ -83,7 +83,7 @@ PIPE = [
 ]
 
 
-@pytest.mark.parametrize("tile", range(17))
+@pytest.mark.parametrize("tile", range(18))
 def test_conv_every_tile(tile):
     """Each block tile of the pipelined kernel (forced through iqnn_set_conv_tile)
     gives the oracle's bytes on the same layers, and so does the 4-channel gather on

@@ -83,3 +83,26 @@ def test_trunk_full_batch_sampled_images():
     for name in ("stem", "l1.0.out", "l3.5.out", final):
         q = ref[name]
         assert len(np.unique(q)) >= 32 and (q == 255).mean() < 0.02, name
+
+
+def test_trunk_graph_replay_matches_eager():
+    """The step captured in a HIP graph and replayed three times, with other eager
+    work and synchronisations in between, gives the eager step's bytes each time."""
+    torch = require_gpu()
+    from integer_quantized_nn_amd.resnet50 import QuantResNet50Trunk
+    tr = synth.resnet50_trunk(seed=5, batch=2)
+    net = QuantResNet50Trunk(tr)
+    x = torch.from_numpy(tr.x).cuda()
+    want = net.step(x).clone()
+    want_codes = net.bufs[tr.layers[-1].out].clone()
+    g = net.capture(x)
+    for i in range(3):
+        net.out_f32.fill_(-1.0)
+        net.bufs[tr.layers[-1].out].fill_(0)
+        junk = torch.randn(1 << 16, device="cuda").sum()   # unrelated eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(net.bufs[tr.layers[-1].out], want_codes), "replay %d codes" % i
+        assert torch.equal(net.out_f32.view(torch.int32), want.view(torch.int32)), "replay %d floats" % i
+        del junk
