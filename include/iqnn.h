@@ -167,7 +167,8 @@ iqnn_status iqnn_dequantize(const void *q_dev, float *x_dev, int64_t outer, int6
  * same convolution with padding 0 over this one (zero padding means real 0; an
  * extra channel multiplies a zero-valued input).  Used for image inputs: 3 channels
  * padded to 4 let the convolution load 4 taps x 4 channels per 16 bytes.
- * qtype: INT8 or UINT8.  Alignment: x_dev, q_dev 4 bytes. */
+ * qtype: INT8 or UINT8.  Alignment: x_dev, q_dev 4 bytes.  Size: n*(h+2pad)*(w+2pad)
+ * below 2^31 (IQNN_ERR_UNSUPPORTED otherwise). */
 iqnn_status iqnn_quantize_pad(const float *x_dev, void *q_dev, int32_t n, int32_t h, int32_t w,
                               int32_t c, int32_t pad, int32_t c_pad, const float *scale_dev,
                               const int32_t *zp_dev, int per_channel, int32_t qtype, void *stream);
@@ -261,7 +262,8 @@ iqnn_status iqnn_qgemm_fwd(const iqnn_gemm_desc *desc, const void *a_dev,
 /* Max pooling k x k, stride s, padding p over NHWC codes of dtype INT8 or UINT8;
  * taps outside the image are skipped (requires 2p <= k-1).  Passive: the output
  * keeps the input's scale and zero point ("Quantization" blog, 量化激活函数).
- * Alignment: x, y 16 bytes; C % 16 == 0. */
+ * Alignment: x, y 16 bytes; C % 16 == 0; N*OH*OW*C/16 below 2^31
+ * (IQNN_ERR_UNSUPPORTED otherwise). */
 iqnn_status iqnn_maxpool2d(const void *x_dev, void *y_dev, int32_t n, int32_t h, int32_t w,
                            int32_t c, int32_t k, int32_t stride, int32_t pad, int32_t dtype,
                            void *stream);

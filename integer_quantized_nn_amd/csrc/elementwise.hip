@@ -103,12 +103,15 @@ __device__ __forceinline__ int32_t code_at(const uint32_t* w, int j, int32_t qty
     return nib;
 }
 
+// One thread per 16 elements; QT and PC (per-channel parameters) fixed per
+// instantiation.
+template <int QT, bool PC>
 __global__ __launch_bounds__(256) void dequantize_kernel(const DequantParams p) {
     const int64_t chunk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t e0 = chunk * 16;
     if (e0 >= p.total) return;
     const int n = (int)((p.total - e0) < 16 ? (p.total - e0) : 16);
-    const bool four = p.qtype == T_INT4 || p.qtype == T_UINT4;
+    constexpr bool four = QT == T_INT4 || QT == T_UINT4;
     uint32_t w[4] = {0, 0, 0, 0};
     if (n == 16) {
         if (four) {
@@ -124,11 +127,11 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const DequantParams p) 
         for (int j = 0; j < nb; ++j) w[j >> 2] |= (uint32_t)src[j] << (8 * (j & 3));
     }
     float out[16];
-    if (p.per_channel) {
+    if (PC) {
         ChanCursor cur(e0, p.ch, p.inner);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            float centred = (float)(code_at(w, j, p.qtype) - p.zp[cur.c]);
+            float centred = (float)(code_at(w, j, QT) - p.zp[cur.c]);
             out[j] = centred * p.scale[cur.c];
             cur.next(p.ch, p.inner);
         }
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const DequantParams p) 
         const int32_t z = p.zp[0];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            float centred = (float)(code_at(w, j, p.qtype) - z);
+            float centred = (float)(code_at(w, j, QT) - z);
             out[j] = centred * s;
         }
     }
@@ -150,71 +153,81 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const DequantParams p) 
     }
 }
 
-// Byte-wise max of packed bytes via 16-bit lanes: even and odd bytes separately.
-__device__ __forceinline__ uint32_t max_u8x4(uint32_t a, uint32_t b) {
-    uint32_t ae = a & 0x00FF00FFu, ao = (a >> 8) & 0x00FF00FFu;
-    uint32_t be = b & 0x00FF00FFu, bo = (b >> 8) & 0x00FF00FFu;
-    uint32_t me = (ae & 0xFFFFu) > (be & 0xFFFFu) ? (ae & 0xFFFFu) : (be & 0xFFFFu);
-    me |= ((ae >> 16) > (be >> 16) ? (ae >> 16) : (be >> 16)) << 16;
-    uint32_t mo = (ao & 0xFFFFu) > (bo & 0xFFFFu) ? (ao & 0xFFFFu) : (bo & 0xFFFFu);
-    mo |= ((ao >> 16) > (bo >> 16) ? (ao >> 16) : (bo >> 16)) << 16;
-    return me | (mo << 8);
-}
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
+// Max pooling over 16-channel groups: thread -> (output pixel, group).  The running
+// maximum of each 32-bit word is kept as its even and odd bytes in two pairs of
+// 16-bit lanes, so one packed 16-bit max (v_pk_max_u16) covers two bytes.  Signed
+// codes are biased by 0x80 so that the unsigned order is the signed order.
+// Indices are 32-bit (the host checks N*OH*OW*C/16 < 2^31).
 __global__ __launch_bounds__(256) void maxpool_kernel(const PoolParams p) {
-    // thread -> (output pixel, 16-channel group); signed codes are biased by 0x80
-    // so that an unsigned byte max orders them correctly.
-    const int cg = p.c / 16;
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t total = (int64_t)p.n * p.oh * p.ow * cg;
+    const uint32_t cg = (uint32_t)p.c / 16;
+    const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+    const uint32_t total = (uint32_t)p.n * p.oh * p.ow * cg;
     if (t >= total) return;
-    const int g = (int)(t % cg);
-    const int64_t pix = t / cg;
-    const int ox = (int)(pix % p.ow);
-    const int oy = (int)((pix / p.ow) % p.oh);
-    const int64_t n = pix / ((int64_t)p.ow * p.oh);
+    const uint32_t pix = t / cg, g = t - pix * cg;
+    const uint32_t ohw = (uint32_t)p.oh * p.ow;
+    const uint32_t n = pix / ohw, rem = pix - n * ohw;
+    const uint32_t oy = rem / (uint32_t)p.ow, ox = rem - oy * (uint32_t)p.ow;
     const uint32_t bias = p.is_signed ? 0x80808080u : 0u;
-    uint32_t m[4] = {0, 0, 0, 0};
+    u16x2 me[4], mo[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) { me[d] = u16x2{0, 0}; mo[d] = u16x2{0, 0}; }
+    const uint8_t* img = p.x + (int64_t)n * p.h * p.w * p.c + g * 16;
     for (int ky = 0; ky < p.k; ++ky) {
-        const int iy = oy * p.s - p.p + ky;
+        const int iy = (int)oy * p.s - p.p + ky;
         if (iy < 0 || iy >= p.h) continue;
         for (int kx = 0; kx < p.k; ++kx) {
-            const int ix = ox * p.s - p.p + kx;
+            const int ix = (int)ox * p.s - p.p + kx;
             if (ix < 0 || ix >= p.w) continue;
-            uint4 v = *reinterpret_cast<const uint4*>(p.x + ((n * p.h + iy) * p.w + ix) * p.c + g * 16);
-            m[0] = max_u8x4(m[0], v.x ^ bias);
-            m[1] = max_u8x4(m[1], v.y ^ bias);
-            m[2] = max_u8x4(m[2], v.z ^ bias);
-            m[3] = max_u8x4(m[3], v.w ^ bias);
+            const uint4 v = *reinterpret_cast<const uint4*>(img + ((int64_t)iy * p.w + ix) * p.c);
+            const uint32_t vw[4] = {v.x ^ bias, v.y ^ bias, v.z ^ bias, v.w ^ bias};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                me[d] = __builtin_elementwise_max(me[d], __builtin_bit_cast(u16x2, vw[d] & 0x00FF00FFu));
+                mo[d] = __builtin_elementwise_max(mo[d], __builtin_bit_cast(u16x2, (vw[d] >> 8) & 0x00FF00FFu));
+            }
         }
     }
-    *reinterpret_cast<uint4*>(p.y + pix * p.c + g * 16) = make_uint4(m[0] ^ bias, m[1] ^ bias, m[2] ^ bias, m[3] ^ bias);
+    uint32_t r[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+        r[d] = (__builtin_bit_cast(uint32_t, me[d]) | (__builtin_bit_cast(uint32_t, mo[d]) << 8)) ^ bias;
+    *reinterpret_cast<uint4*>(p.y + (int64_t)pix * p.c + g * 16) = make_uint4(r[0], r[1], r[2], r[3]);
 }
 
 // Quantize into a spatially padded NHWC tensor with c_pad >= c channels: every
 // border pixel and every extra channel holds the zero-point code (the real value 0),
-// which is what a convolution's zero padding means in the quantized domain.  One
-// thread per output pixel.
+// which is what a convolution's zero padding means in the quantized domain.
+// One thread per padded pixel; with c_pad == 4 the pixel is one 32-bit store.
+// Indices are 32-bit (the host checks N*(H+2p)*(W+2p) < 2^31).
 __global__ __launch_bounds__(256) void quantize_pad_kernel(const QuantPadParams p) {
-    const int hp = p.h + 2 * p.pad, wp = p.w + 2 * p.pad;
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t total = (int64_t)p.n * hp * wp;
-    if (t >= total) return;
-    const int x = (int)(t % wp);
-    const int y = (int)((t / wp) % hp);
-    const int64_t n = t / ((int64_t)wp * hp);
-    const int iy = y - p.pad, ix = x - p.pad;
+    const uint32_t hp = (uint32_t)(p.h + 2 * p.pad), wp = (uint32_t)(p.w + 2 * p.pad);
+    const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= (uint32_t)p.n * hp * wp) return;
+    const uint32_t row = t / wp, x = t - row * wp;
+    const uint32_t n = row / hp, y = row - n * hp;
+    const int iy = (int)y - p.pad, ix = (int)x - p.pad;
     const bool inside = iy >= 0 && iy < p.h && ix >= 0 && ix < p.w;
-    const float* src = p.x + ((n * p.h + iy) * p.w + ix) * p.c;
-    uint8_t* dst = p.q + t * p.c_pad;
-    for (int c = 0; c < p.c_pad; ++c) {
-        const int32_t z = p.per_channel ? p.zp[c < p.c ? c : 0] : p.zp[0];
-        int32_t q = z;
-        if (inside && c < p.c) {
-            const float s = p.per_channel ? p.scale[c] : p.scale[0];
-            q = quant_one(src[c], s, z, p.qmin, p.qmax);
+    const float* src = p.x + (((int64_t)n * p.h + iy) * p.w + ix) * p.c;
+    uint8_t* dst = p.q + (int64_t)t * p.c_pad;
+    if (p.c_pad == 4) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int32_t z = p.per_channel ? p.zp[c < p.c ? c : 0] : p.zp[0];
+            int32_t q = z;
+            if (inside && c < p.c) q = quant_one(src[c], p.per_channel ? p.scale[c] : p.scale[0], z, p.qmin, p.qmax);
+            word |= (uint32_t)(q & 0xFF) << (8 * c);
         }
-        dst[c] = (uint8_t)(q & 0xFF);
+        *reinterpret_cast<uint32_t*>(dst) = word;
+    } else {
+        for (int c = 0; c < p.c_pad; ++c) {
+            const int32_t z = p.per_channel ? p.zp[c < p.c ? c : 0] : p.zp[0];
+            int32_t q = z;
+            if (inside && c < p.c) q = quant_one(src[c], p.per_channel ? p.scale[c] : p.scale[0], z, p.qmin, p.qmax);
+            dst[c] = (uint8_t)(q & 0xFF);
+        }
     }
 }
 
@@ -223,8 +236,8 @@ __global__ __launch_bounds__(256) void quantize_pad_kernel(const QuantPadParams 
 hipError_t launch_quantize_pad(const QuantPadParams& p, hipStream_t stream) {
     const int64_t total = (int64_t)p.n * (p.h + 2 * p.pad) * (p.w + 2 * p.pad);
     if (total == 0) return hipSuccess;
+    if (total >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     const int64_t blocks = (total + 255) / 256;
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     hipLaunchKernelGGL(quantize_pad_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
@@ -243,15 +256,26 @@ hipError_t launch_dequantize(const DequantParams& p, hipStream_t stream) {
     if (chunks == 0) return hipSuccess;
     const int64_t blocks = (chunks + 255) / 256;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(dequantize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
-    return hipGetLastError();
+    const dim3 g((unsigned)blocks), b(256);
+#define IQNN_DEQ(QT)                                                                          \
+    if (p.qtype == QT) {                                                                      \
+        if (p.per_channel) hipLaunchKernelGGL((dequantize_kernel<QT, true>), g, b, 0, stream, p); \
+        else hipLaunchKernelGGL((dequantize_kernel<QT, false>), g, b, 0, stream, p);        \
+        return hipGetLastError();                                                             \
+    }
+    IQNN_DEQ(T_INT8)
+    IQNN_DEQ(T_UINT8)
+    IQNN_DEQ(T_INT4)
+    IQNN_DEQ(T_UINT4)
+#undef IQNN_DEQ
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_maxpool(const PoolParams& p, hipStream_t stream) {
     const int64_t total = (int64_t)p.n * p.oh * p.ow * (p.c / 16);
     if (total == 0) return hipSuccess;
+    if (total >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     const int64_t blocks = (total + 255) / 256;
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     hipLaunchKernelGGL(maxpool_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
 }

@@ -433,8 +433,9 @@ iqnn_status iqnn_quantize_pad(const float* x_dev, void* q_dev, int32_t n, int32_
     code_range(qtype, &lo, &hi);
     if (n < 0 || h <= 0 || w <= 0 || c <= 0 || pad < 0 || c_pad < c)
         return fail(IQNN_ERR_INVALID_ARG, "quantize_pad: bad sizes (need c_pad >= c, pad >= 0)");
-    if ((int64_t)(h + 2 * pad) * (w + 2 * pad) * c_pad > ((int64_t)1 << 40))
-        return fail(IQNN_ERR_UNSUPPORTED, "quantize_pad: output too large");
+    if ((int64_t)n * (h + 2 * pad) * (w + 2 * pad) >= ((int64_t)1 << 31) ||
+        (int64_t)(h + 2 * pad) * (w + 2 * pad) * c_pad > ((int64_t)1 << 40))
+        return fail(IQNN_ERR_UNSUPPORTED, "quantize_pad: N*(H+2pad)*(W+2pad) must be below 2^31");
     if (n > 0 && (!x_dev || !q_dev || !scale_dev || !zp_dev)) return fail(IQNN_ERR_INVALID_ARG, "quantize_pad: null pointer");
     if (!aligned(x_dev, 4) || !aligned(q_dev, 4)) return fail(IQNN_ERR_ALIGNMENT, "quantize_pad: misaligned pointer");
     QuantPadParams p{x_dev, static_cast<uint8_t*>(q_dev), scale_dev, zp_dev, n, h, w, c, pad, c_pad,
@@ -520,6 +521,11 @@ iqnn_status iqnn_maxpool2d(const void* x_dev, void* y_dev, int32_t n, int32_t h,
     if (2 * pad > k - 1) return fail(IQNN_ERR_INVALID_ARG, "maxpool: padding must satisfy 2*pad <= k-1");
     if (c % 16 != 0) return fail(IQNN_ERR_UNSUPPORTED, "maxpool: C %% 16 != 0");
     if (h + 2 * pad < k || w + 2 * pad < k) return fail(IQNN_ERR_INVALID_ARG, "maxpool: window larger than input");
+    {
+        const int64_t ohp = (h + 2 * pad - k) / stride + 1, owp = (w + 2 * pad - k) / stride + 1;
+        if ((int64_t)n * ohp * owp * (c / 16) >= ((int64_t)1 << 31))
+            return fail(IQNN_ERR_UNSUPPORTED, "maxpool: N*OH*OW*C/16 must be below 2^31");
+    }
     if (!x_dev || !y_dev) return fail(IQNN_ERR_INVALID_ARG, "maxpool: null pointer");
     if (!aligned(x_dev, 16) || !aligned(y_dev, 16)) return fail(IQNN_ERR_ALIGNMENT, "maxpool: misaligned pointer");
     PoolParams p{static_cast<const uint8_t*>(x_dev), static_cast<uint8_t*>(y_dev), n, h, w, c, k, stride, pad,
