@@ -1358,6 +1358,148 @@ hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bo
     return hipGetLastError();
 }
 
+// ============================================================ stem kernel
+//
+// qconv_stem: the image stem (4-channel input laid out by iqnn_quantize_pad, filter
+// rows widened to 8 taps, stride 2, C_out <= 64) as a direct convolution.  A tile is
+// 128 consecutive output pixels of one image; the input rows they need (at most
+// max_rows) are one contiguous byte range, copied into LDS with 16-byte DMA while
+// the previous tile computes (two buffers).  Each wave holds the A fragments of all
+// 64 channels and every filter row in registers for its whole life, and builds the
+// B fragment of filter row ky straight from the slab: pixel (oy, ox), taps
+// 4h..4h+3 of row ky are 16 consecutive bytes at slab row 2(oy-oy0)+ky, column 2ox+4h.
+// One 32-byte k-step per filter row: K = 7 x 8 x 4 = 224, no per-tap gather.
+constexpr int kStemBN = 128;
+constexpr int kStemBuf = 12288;   // LDS bytes per slab buffer (12 DMA instructions of 1 KB)
+constexpr int kStemKH = 8;        // filter rows held in registers
+
+__global__ __launch_bounds__(256, 3) void qconv_stem(const ConvParams p, int32_t n_tiles, int64_t in_bytes) {
+    __shared__ __attribute__((aligned(1024))) uint8_t slab[2][kStemBuf];
+    __shared__ __attribute__((aligned(16))) int32_t cbias[64];
+    __shared__ __attribute__((aligned(16))) float cmult[64];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if ((int)blockIdx.x >= n_tiles) return;
+    if (tid < 64) {
+        cbias[tid] = p.bias[tid];
+        cmult[tid] = p.mult[tid];
+    }
+    // A fragments: packed rows 32t + lane%32, K bytes 32 ky + 16 (lane/32)
+    v4i wa[2][kStemKH];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ky = 0; ky < kStemKH; ++ky)
+            wa[t][ky] = ky < p.kh ? *reinterpret_cast<const v4i*>(p.w + (int64_t)(32 * t + (lane & 31)) * p.kp +
+                                                                  32 * ky + 16 * (lane >> 5))
+                                  : v4i{0, 0, 0, 0};
+    __syncthreads();
+
+    const uint32_t ohw = (uint32_t)(p.oh * p.ow);
+    const int64_t row_bytes = (int64_t)p.w_in * 4;
+    auto slab_start = [&](int tile, int64_t& start, uint32_t& oy0) {
+        const uint32_t P0 = (uint32_t)tile * kStemBN;
+        const uint32_t n = P0 / ohw, pix0 = P0 - n * ohw;
+        oy0 = pix0 / (uint32_t)p.ow;
+        start = ((int64_t)n * p.h + 2 * (int64_t)oy0) * row_bytes;   // 8-byte aligned (W even)
+    };
+    auto issue = [&](int tile, int buf) {
+        int64_t start;
+        uint32_t oy0;
+        slab_start(tile, start, oy0);
+        const int64_t base = start & ~(int64_t)15;
+        for (int j = wave; j < kStemBuf / 1024; j += 4) {
+            const int64_t off = base + j * 1024 + lane * 16;
+            const void* src = off + 16 <= in_bytes ? (const void*)(p.x + off) : (const void*)p.x;
+            dma16_run<1>(lds_addr(&slab[buf][0]) + j * 1024, &src);
+        }
+    };
+
+    v16i acc[2];
+    const int frow = lane & 31;
+    const uint32_t bxor = p.x_xor;
+    int buf = 0;
+    issue(blockIdx.x, 0);
+    for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+        // this tile's slab has landed (and every wave is done with the other buffer)
+        IQNN_WAIT_VM_LGKM0(0);
+        __builtin_amdgcn_s_barrier();
+        const int next = tile + (int)gridDim.x;
+        if (next < n_tiles) issue(next, buf ^ 1);
+
+        int64_t start;
+        uint32_t oy0;
+        slab_start(tile, start, oy0);
+        const uint32_t shift = (uint32_t)(start & 15);
+        const uint32_t P0 = (uint32_t)tile * kStemBN;
+        const uint32_t pl = wave * 32 + frow;               // pixel inside the tile
+        const uint32_t pix = (P0 % ohw) + pl;
+        const uint32_t oy = pix / (uint32_t)p.ow, ox = pix - oy * (uint32_t)p.ow;
+        const uint32_t b0 = shift + (uint32_t)((2 * (oy - oy0)) * row_bytes) + ox * 8 + 16 * (lane >> 5);
+        const uint2* sv = reinterpret_cast<const uint2*>(&slab[buf][0]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int ocl = t * 32 + (lane >> 5) * 16;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int4 bv = *reinterpret_cast<const int4*>(&cbias[ocl + 4 * q]);
+                acc[t][4 * q] = bv.x; acc[t][4 * q + 1] = bv.y; acc[t][4 * q + 2] = bv.z; acc[t][4 * q + 3] = bv.w;
+            }
+        }
+#pragma unroll
+        for (int ky = 0; ky < kStemKH; ++ky) {
+            if (ky < p.kh) {
+                const uint32_t a = (b0 + ky * (uint32_t)row_bytes) >> 3;   // 8-byte units
+                const uint2 lo = sv[a], hi = sv[a + 1];
+                v4i fb = {(int)(lo.x ^ bxor), (int)(lo.y ^ bxor), (int)(hi.x ^ bxor), (int)(hi.y ^ bxor)};
+                acc[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wa[0][ky], fb, acc[0], 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wa[1][ky], fb, acc[1], 0, 0, 0);
+            }
+        }
+        const int64_t opix = (int64_t)P0 + pl;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int ocb = t * 32 + (lane >> 5) * 16;
+            if (ocb >= p.c_out) continue;
+            float mult[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 mv = *reinterpret_cast<const float4*>(&cmult[ocb + 4 * q]);
+                mult[4 * q] = mv.x; mult[4 * q + 1] = mv.y; mult[4 * q + 2] = mv.z; mult[4 * q + 3] = mv.w;
+            }
+            uint32_t rw[4] = {0, 0, 0, 0};
+            epi_store16<false, 2>(p, acc[t], nullptr, mult, rw, ocb, opix, false, 0.0f);
+        }
+        buf ^= 1;
+    }
+    // no DMA may still be writing this workgroup's LDS when it ends
+    IQNN_WAIT_VM(0);
+}
+
+// The stem kernel's conditions (see qconv_stem): 4-channel gather with 8-tap rows,
+// stride 2, at most kStemKH filter rows, C_out <= 64 in 16-channel groups, whole
+// 128-pixel tiles per image, an even input width (8-byte aligned slab reads), a
+// slab that fits one buffer, no residual.
+bool stem_ok(const ConvParams& p) {
+    if (p.kw != 8 || p.sh != 2 || p.sw != 2 || p.kh > kStemKH || p.c_out > 64 || !p.vec_store) return false;
+    if (p.epi == E_ADD || p.epi == E_ADD_RELU) return false;
+    const int64_t ohw = (int64_t)p.oh * p.ow;
+    if (ohw % kStemBN != 0 || p.w_in % 2 != 0 || p.m >= ((int64_t)1 << 31)) return false;
+    const int64_t out_rows = (kStemBN - 1 + p.ow - 1) / p.ow + 1;   // output rows one tile can touch
+    const int64_t max_rows = 2 * (out_rows - 1) + p.kh;
+    return max_rows * p.w_in * 4 + 16 <= kStemBuf;
+}
+
+hipError_t launch_stem(const ConvParams& p, hipStream_t stream) {
+    const int64_t n_tiles = p.m / kStemBN;
+    if (n_tiles <= 0) return hipSuccess;
+    const int64_t in_bytes = p.m / ((int64_t)p.oh * p.ow) * p.h * (int64_t)p.w_in * 4;
+    const int64_t grid = std::min<int64_t>(n_tiles, 256 * 3);
+    hipLaunchKernelGGL(qconv_stem, dim3((unsigned)grid), dim3(256), 0, stream, p, (int32_t)n_tiles, in_bytes);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 bool pipe_eligible(int gather, int32_t c, int64_t k) {
@@ -1396,6 +1538,7 @@ int pipe_tile_choice(int64_t m, int32_t c_out, int64_t k, bool res) {
 }
 
 hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_t stream, int tile) {
+    if (gather == GATHER_C4 && tile < 0 && stem_ok(p)) return launch_stem(p, stream);
     if (pipe_eligible(gather, p.c, p.k)) {
         const bool c4 = gather == GATHER_C4;
         const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;

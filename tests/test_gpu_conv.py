@@ -48,7 +48,9 @@ def test_conv_small_shapes(case):
 
 
 @pytest.mark.parametrize("hw,k,stride,co", [((23, 23), 7, 2, 64), ((20, 17), 7, 2, 128), ((12, 12), 3, 1, 64),
-                                             ((9, 14), 5, 2, 96)])
+                                             ((9, 14), 5, 2, 96),
+                                             # direct stem kernel: even padded width, whole 128-pixel tiles
+                                             ((32, 32), 7, 2, 64), ((32, 32), 7, 2, 32), ((64, 48), 7, 2, 64)])
 def test_conv_four_channel_padded_input(hw, k, stride, co):
     """The 4-channel gather (image stems): a 3-channel image quantized into a border
     of Z_in codes plus a 4th Z_in channel, convolved without padding, equals the
