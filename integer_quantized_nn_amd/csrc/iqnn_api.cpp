@@ -177,10 +177,27 @@ int64_t packed_size(const Layer& L) { return pack_geom(L.c_out, kdim(L)).bytes; 
 // 16-element segments as [0,2,4,6, 1,3,5,7, 8,10,12,14, 9,11,13,15] (low nibbles of
 // four bytes, then their high nibbles); the weights are stored in the same order
 // so both MFMA operands see one consistent K permutation.
-int64_t staged_k(int64_t k, bool act4) {
+// stream4: the streaming kernel's 4-bit order, where a lane's one 16-byte read per
+// 64-element stage carries its half of both 32-element k-steps: inside every group of
+// 64 the 16-element blocks (1, 2) trade places, so channel block 2h + kk is K block
+// 2kk + h.
+int64_t staged_k(int64_t k, bool act4, bool stream4 = false) {
     if (!act4) return k;
     static const int pos_of_elem[16] = {0, 4, 1, 5, 2, 6, 3, 7, 8, 12, 9, 13, 10, 14, 11, 15};
-    return (k & ~(int64_t)15) | pos_of_elem[k & 15];
+    int64_t blk = (k >> 4) & 3;
+    if (stream4 && (blk == 1 || blk == 2)) blk ^= 3;
+    return (k & ~(int64_t)63) | (blk << 4) | pos_of_elem[k & 15];
+}
+
+// 4-bit activations take the streaming kernel when every 64-channel group lies inside
+// one filter tap and the residual, if any, is 4-bit in whole 16-byte chunks.  The
+// packed layout depends on this choice, so prepack and forward both ask here.
+bool b4_stream(const Layer& L) {
+    if (!is_4bit(L.x_type) || L.c % 64 != 0 || L.kh * L.kw > 64) return false;
+    if (L.m >= ((int64_t)1 << 31)) return false;
+    const bool add = L.epi == E_ADD || L.epi == E_ADD_RELU;
+    if (add && (!is_4bit(L.res_type) || L.c_out % 32 != 0)) return false;
+    return true;
 }
 
 // Writes the packed layer (layout in PackGeom) into host memory `dst` of g.bytes.
@@ -188,6 +205,7 @@ iqnn_status prepack_into(const Layer& L, const void* w_host, const float* bias_h
                          const float* s_w_host, int per_channel, float s_out, float s_res, uint8_t* dst) {
     const PackGeom g = pack_geom(L.c_out, kdim(L));
     const bool c4 = c4_path(L);
+    const bool b4s = b4_stream(L);
     const int64_t kwp = c4_kwp(L);
     if (!scale_ok(s_in)) return fail(IQNN_ERR_INVALID_ARG, "input scale must be positive and finite");
     const bool raw = L.epi == E_RAW;
@@ -200,7 +218,9 @@ iqnn_status prepack_into(const Layer& L, const void* w_host, const float* bias_h
     int32_t* bias = reinterpret_cast<int32_t*>(dst);
     float* mult = reinterpret_cast<float*>(dst + (size_t)g.ocp * 4);
     float* mres = reinterpret_cast<float*>(dst + (size_t)g.ocp * 8 + kHdrMres);
-    std::memset(dst + (size_t)g.ocp * 8 + kHdrPad, L.z_in & 0xFF, 64);   // padding row: raw Z_in codes
+    // padding row: raw Z_in codes (two per byte for 4-bit activations)
+    const int pad_code = is_4bit(L.x_type) ? ((L.z_in & 0xF) | ((L.z_in & 0xF) << 4)) : (L.z_in & 0xFF);
+    std::memset(dst + (size_t)g.ocp * 8 + kHdrPad, pad_code, 64);
     int8_t* wp = reinterpret_cast<int8_t*>(dst + g.w_off);
 
     const bool act4 = is_4bit(L.x_type);
@@ -253,7 +273,7 @@ iqnn_status prepack_into(const Layer& L, const void* w_host, const float* bias_h
         }
         int8_t* dst = wp + (int64_t)packed_row_of_channel((int32_t)oc) * g.kp;
         for (int64_t k = 0; k < L.k; ++k) {
-            int64_t pos = staged_k(k, act4);
+            int64_t pos = staged_k(k, act4, b4s);
             if (c4) {   // (kh, kw, ci) -> (kh, kw in a row widened to kwp taps, ci)
                 const int64_t kh = k / (L.kw * 4), kw = (k / 4) % L.kw, ci = k % 4;
                 pos = (kh * kwp + kw) * 4 + ci;
@@ -354,7 +374,8 @@ iqnn_status forward(const Layer& L, const void* x, const void* packed, const voi
         p.res_xor = L.res_type == T_INT8 ? 0x80808080u : (L.res_type == T_INT4 ? 0x88888888u : 0u);
     }
     p.vec_store = L.c_out % 16 == 0;
-    const int gather = is_4bit(L.x_type) ? GATHER_B4 : (L.c % 16 == 0 ? GATHER_B8 : (c4 ? GATHER_C4 : GATHER_B8_ELEM));
+    const int gather = is_4bit(L.x_type) ? (b4_stream(L) ? GATHER_B4S : GATHER_B4)
+                                          : (L.c % 16 == 0 ? GATHER_B8 : (c4 ? GATHER_C4 : GATHER_B8_ELEM));
     const bool is_1x1 = gather != GATHER_B8_ELEM && gather != GATHER_C4 && L.kh == 1 && L.kw == 1 && L.sh == 1 && L.sw == 1 &&
                         L.ph == 0 && L.pw == 0;
     hipError_t e = launch_qconv(p, gather, is_1x1, stream, forced_tile());

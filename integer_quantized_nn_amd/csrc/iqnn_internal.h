@@ -16,7 +16,8 @@ enum : int32_t {
     GATHER_B8 = 0,     // 8-bit codes, C_in % 16 == 0: one 16-byte load per K segment
     GATHER_B4 = 1,     // 4-bit codes, C_in % 16 == 0: one 8-byte load, unpacked to 16 int8
     GATHER_B8_ELEM = 2, // 8-bit codes, any C_in: element-wise gather
-    GATHER_C4 = 3       // 8-bit codes, C_in == 4, no padding: one 16-byte load = 4 taps x 4 channels
+    GATHER_C4 = 3,      // 8-bit codes, C_in == 4, no padding: one 16-byte load = 4 taps x 4 channels
+    GATHER_B4S = 4      // 4-bit codes, C_in % 64 == 0: packed rows streamed to LDS, unpacked per fragment
 };
 
 // Geometry of the prepacked layer buffer (device).  All offsets in bytes.

@@ -143,12 +143,12 @@ __device__ __forceinline__ void load_res16(const ConvParams& p, int64_t oidx, in
 //
 // BIAS: add bias[] here (otherwise the accumulator started from the folded bias).
 // ADDK: 0 = residual add decided by `add` and p.res_type at run time, 1 = always an
-// 8-bit residual, 2 = never a residual.
+// 8-bit residual, 2 = never a residual, 3 = always a 4-bit residual.
 template <bool BIAS = true, int ADDK = 0>
 __device__ __forceinline__ void epi_store16(const ConvParams& p, const v16i& acc, const int32_t* bias,
                                             const float* mult, uint32_t rw[4], int ocb, int64_t pix, bool add_rt,
                                             float m_res) {
-    const bool add = ADDK == 1 ? true : (ADDK == 2 ? false : add_rt);
+    const bool add = (ADDK == 1 || ADDK == 3) ? true : (ADDK == 2 ? false : add_rt);
     const int64_t oidx = pix * p.c_out + ocb;   // element index of the first channel
     if (p.epi == E_RAW) {
         int32_t a[16];
@@ -168,7 +168,7 @@ __device__ __forceinline__ void epi_store16(const ConvParams& p, const v16i& acc
 #pragma unroll
     for (int j = 0; j < 16; ++j) v[j] = (float)(acc[j] + (BIAS ? bias[j] : 0)) * mult[j];
     if (add) {
-        const bool r8 = ADDK == 1 || p.res_type == T_INT8 || p.res_type == T_UINT8;
+        const bool r8 = ADDK == 1 || (ADDK != 3 && (p.res_type == T_INT8 || p.res_type == T_UINT8));
         uint32_t w[4] = {rw[0] ^ p.res_xor, rw[1] ^ p.res_xor, rw[2] ^ p.res_xor, rw[3] ^ p.res_xor};
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -453,10 +453,17 @@ constexpr int kPipeBK = 64;     // K bytes per stage
 // 8 for the row>>1 family of swizzles and 16 unswizzled).
 __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
-// Swizzle of the 16-byte chunks of a residual row of `lpr` chunks (lpr = 4: 64-byte
-// rows, lpr = 8: 128-byte rows), chosen the same way: conflict-free reads of one
-// chunk over 32 consecutive rows.
-__device__ __forceinline__ int rswz(int row, int lpr) { return lpr == 8 ? (row >> 1) & 7 : (row >> 2) & 3; }
+// Swizzle of the 16-byte chunks of a residual row of `lpr` chunks (lpr = 2, 4, 8:
+// 32-, 64-, 128-byte rows), chosen the same way: conflict-free reads of one chunk
+// over 32 consecutive rows.
+__device__ __forceinline__ int rswz(int row, int lpr) {
+    return lpr == 8 ? (row >> 1) & 7 : (lpr == 4 ? (row >> 2) & 3 : (row >> 3) & 1);
+}
+
+// 4-bit activation rows in LDS are 32 bytes (64 codes) per stage; their two 16-byte
+// halves are swapped on rows with bit 3 set (measured conflict-free for the
+// 32-row x 2-half ds_read_b128).
+__device__ __forceinline__ int swz4(int row) { return (row >> 3) & 1; }
 
 // s_waitcnt for vmcnt <= n only (expcnt and lgkmcnt left at their maximum).
 #define IQNN_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
@@ -968,21 +975,27 @@ struct StreamCfg {
     static_assert(OCC <= LDS_FIT, "LDS for the requested occupancy");
 };
 
-template <class C, bool IS1X1, bool RES, bool C4>
+template <class C, bool IS1X1, bool RES, bool C4, bool B4 = false>
 __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) {
     constexpr int BM = C::BM, BN = C::BN, WM = C::WM, NST = C::NST;
-    constexpr int TM = C::TM, TN = C::TN, STAGE = C::STAGE;
+    constexpr int TM = C::TM, TN = C::TN;
+    constexpr int BROW = B4 ? 32 : kPipeBK;           // bytes of an activation row per stage
+    constexpr int STAGE = BM * kPipeBK + BN * BROW;   // bytes of one ring slot
     constexpr int A_INST = BM / 64;                   // weight rows: 16 per instruction per wave
-    constexpr int B_INST = C4 ? BN / 16 : BN / 64;    // activation rows: 16 (4 for C4) per instruction
+    // activation rows per instruction: 16 (8-bit), 32 (4-bit), 4 (4-channel gather)
+    constexpr int B_INST = C4 ? BN / 16 : (B4 ? BN / 128 : BN / 64);
     constexpr int K_LOADS = A_INST + B_INST;          // DMA instructions per wave per stage
-    constexpr int R_INST = RES ? BM * BN / 4096 : 0;  // residual: 1 KB per instruction per wave
+    constexpr int RROW = B4 ? BM / 2 : BM;            // bytes of a residual row
+    constexpr int R_INST = RES ? BN * RROW / 4096 : 0;   // residual: 1 KB per instruction per wave
     constexpr int D = NST - 1;                        // stages issued ahead
-    static_assert(TM >= 1 && TN >= 1 && A_INST >= 1 && BN % 64 == 0, "tile shape");
+    static_assert(TM >= 1 && TN >= 1 && A_INST >= 1 && B_INST >= 1 && BN % 64 == 0, "tile shape");
+    static_assert(C4 || K_LOADS * 4096 == STAGE, "a stage is K_LOADS KB-instructions per wave");
+    static_assert(!(B4 && C4), "one gather mode");
     static_assert(NST >= 3, "ring depth");
     static_assert(D * K_LOADS <= 60, "DMA in flight must fit the 6-bit vmcnt");
     static_assert(R_INST <= K_LOADS, "a residual tile fits one stage");
     static_assert(!(RES && C4), "the 4-channel gather has no residual stage");
-    static_assert(!RES || BM == 64 || BM == 128, "residual rows of 4 or 8 chunks");
+    static_assert(!RES || RROW == 32 || RROW == 64 || RROW == 128, "residual rows of 2, 4 or 8 chunks");
 
     __shared__ __attribute__((aligned(1024))) uint8_t ring[NST * STAGE];
     __shared__ __attribute__((aligned(16))) int32_t cbias[BM];
@@ -1068,17 +1081,21 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
         } else {
 #pragma unroll
             for (int i = 0; i < B_INST; ++i) {
-                const int64_t pix = px0 + wave * (BN / 4) + 16 * i + drow;
-                const int32_t seg = (dslot ^ swz(wave * (BN / 4) + 16 * i + drow)) * 16;
+                // 8-bit: 16 rows of 64 bytes per instruction, lane -> row lane/4, slot lane%4;
+                // 4-bit: 32 rows of 32 bytes, lane -> row lane/2, half lane%2
+                const int row = B4 ? wave * (BN / 4) + 32 * i + (lane >> 1) : wave * (BN / 4) + 16 * i + drow;
+                const int64_t pix = px0 + row;
+                const int32_t seg = B4 ? ((lane & 1) ^ swz4(row)) * 16 : (dslot ^ swz(row)) * 16;
+                constexpr int SH = B4 ? 1 : 0;   // element offset -> byte offset
                 if (IS1X1) {
-                    prow[i] = p.x + (pix < p.m ? pix : p.m - 1) * p.c + seg;
+                    prow[i] = p.x + (((pix < p.m ? pix : p.m - 1) * p.c) >> SH) + seg;
                     tmask[i] = 0;
                 } else if (pix < p.m) {
                     const uint32_t pu = (uint32_t)pix;
                     const uint32_t n = pu / ohw, rem = pu - n * ohw;
                     const uint32_t oy = rem / (uint32_t)p.ow, ox = rem - oy * (uint32_t)p.ow;
                     const int32_t iy0 = (int32_t)oy * p.sh - p.ph, ix0 = (int32_t)ox * p.sw - p.pw;
-                    prow[i] = p.x + ((int64_t)((int32_t)n * p.h + iy0) * p.w_in + ix0) * p.c + seg;
+                    prow[i] = p.x + ((((int64_t)((int32_t)n * p.h + iy0) * p.w_in + ix0) * p.c) >> SH) + seg;
                     // taps inside the image: kx in [xlo, xhi), ky in [ylo, yhi)
                     const int32_t xlo = max(0, -ix0), xhi = min(p.kw, p.w_in - ix0);
                     const int32_t ylo = max(0, -iy0), yhi = min(p.kh, p.h - iy0);
@@ -1097,13 +1114,15 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
         if constexpr (RES) {
             // residual rows [px][BM] bytes: instruction i of this wave covers 1024/BM rows,
             // BM/16 lanes per row
-            constexpr int LPR = BM / 16;
+            constexpr int LPR = RROW / 16;
+            constexpr int CPC = B4 ? 32 : 16;   // channels per 16-byte chunk
+            constexpr int SH = B4 ? 1 : 0;
 #pragma unroll
             for (int i = 0; i < R_INST; ++i) {
-                const int row = (wave * R_INST + i) * (1024 / BM) + lane / LPR;
-                const int ch = oc0 + ((lane % LPR) ^ rswz(row, LPR)) * 16;
+                const int row = (wave * R_INST + i) * (1024 / RROW) + lane / LPR;
+                const int ch = oc0 + ((lane % LPR) ^ rswz(row, LPR)) * CPC;
                 const int64_t pix = px0 + row;
-                rsrc[i] = (pix < p.m && ch < p.c_out) ? p.res + pix * p.c_out + ch : p.res;
+                rsrc[i] = (pix < p.m && ch < p.c_out) ? p.res + ((pix * p.c_out + ch) >> SH) : p.res;
             }
         }
     };
@@ -1149,12 +1168,13 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
                 }
                 dma4_seq<B_INST>(dst + (BM + wave * (BN / 4)) * kPipeBK, bs);
             } else {
+                constexpr int SH = B4 ? 1 : 0;
 #pragma unroll
                 for (int i = 0; i < B_INST; ++i) {
-                    if constexpr (IS1X1) bs[i] = prow[i] + k0;
-                    else bs[i] = ((tmask[i] >> tap) & 1) ? prow[i] + tapoff : padrow;
+                    if constexpr (IS1X1) bs[i] = prow[i] + (k0 >> SH);
+                    else bs[i] = ((tmask[i] >> tap) & 1) ? prow[i] + (tapoff >> SH) : padrow;
                 }
-                dma16_seq<B_INST>(dst + (BM + wave * (BN / 4)) * kPipeBK, bs);
+                dma16_seq<B_INST>(dst + BM * kPipeBK + wave * (BN / 4) * BROW, bs);
             }
         }
         is_off = is_off + STAGE == NST * STAGE ? 0 : is_off + STAGE;
@@ -1208,18 +1228,39 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
     init_acc();
 
     v4i fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+    // 4-bit: a lane's 16 bytes of a pixel row hold its half of both k-steps (8 bytes
+    // each), read once per stage at k-step 0 and unpacked per k-step
+    uint4 b4raw[B4 ? TN : 1];
+    const int b4off = (((lane >> 5) ^ swz4(frow)) * 16) + frow * 32;
+    const int x_signed4 = p.x_signed4;
     auto read_frags = [&](const uint8_t* cur, int fo, v4i (&fa)[TM], v4i (&fb)[TN]) {
 #pragma unroll
         for (int t = 0; t < TM; ++t)
             fa[t] = *reinterpret_cast<const v4i*>(cur + (wave_oc * C::WOC + 32 * t) * kPipeBK + fo);
+        if constexpr (B4) {
+            if (fo == foff0) {
 #pragma unroll
-        for (int u = 0; u < TN; ++u)
-            fb[u] = *reinterpret_cast<const v4i*>(cur + (BM + wave_px * C::WPX + 32 * u) * kPipeBK + fo);
+                for (int u = 0; u < TN; ++u)
+                    b4raw[u] = *reinterpret_cast<const uint4*>(cur + BM * kPipeBK + (wave_px * C::WPX + 32 * u) * 32 + b4off);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < TN; ++u)
+                fb[u] = *reinterpret_cast<const v4i*>(cur + (BM + wave_px * C::WPX + 32 * u) * kPipeBK + fo);
+        }
     };
-    auto shift_b = [&](v4i (&fb)[TN]) {
+    // make the B fragments of k-step kk MFMA-ready: the uint8 shift (XOR 0x80), or the
+    // 4-bit unpack (UINT4 zero-, INT4 sign-extended) of this k-step's 8 bytes
+    auto shift_b = [&](v4i (&fb)[TN], int kk) {
 #pragma unroll
         for (int u = 0; u < TN; ++u) {
-            fb[u][0] ^= bxor; fb[u][1] ^= bxor; fb[u][2] ^= bxor; fb[u][3] ^= bxor;
+            if constexpr (B4) {
+                const uint32_t w0 = kk == 0 ? b4raw[u].x : b4raw[u].z, w1 = kk == 0 ? b4raw[u].y : b4raw[u].w;
+                fb[u][0] = (int)unpack_lo(w0, x_signed4); fb[u][1] = (int)unpack_hi(w0, x_signed4);
+                fb[u][2] = (int)unpack_lo(w1, x_signed4); fb[u][3] = (int)unpack_hi(w1, x_signed4);
+            } else {
+                fb[u][0] ^= bxor; fb[u][1] ^= bxor; fb[u][2] ^= bxor; fb[u][3] ^= bxor;
+            }
         }
     };
     auto mfmas = [&](v4i (&fa)[TM], v4i (&fb)[TN], int lo, int hi) {
@@ -1254,7 +1295,7 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
         const bool last_tile = j + 1 == J;
         for (int s = 0; s < nst; ++s) {
             const uint8_t* cur = ring + cur_off;
-            shift_b(fb0);
+            shift_b(fb0, 0);
             __builtin_amdgcn_sched_barrier(0);
             mfmas(fa0, fb0, 0, NMF);
             read_frags(cur, foff1, fa1, fb1);
@@ -1266,7 +1307,7 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
             if (NMF > NRD) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NRD, 0);
             if (NRD > NMF) __builtin_amdgcn_sched_group_barrier(0x100, NRD - NMF, 0);
             __builtin_amdgcn_sched_barrier(0);
-            shift_b(fb1);
+            shift_b(fb1, 1);
             mfmas(fa1, fb1, 0, HALF);
             __builtin_amdgcn_sched_barrier(0);
             advance();
@@ -1296,11 +1337,15 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
                 const int64_t pix = px0 + pl;
                 if (pix >= p.m) continue;
                 uint32_t rw[4] = {0, 0, 0, 0};
-                if (RES) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(rtile + pl * BM + (((ocl >> 4) ^ rswz(pl, BM / 16)) << 4));
+                if (RES && !B4) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(rtile + pl * RROW + (((ocl >> 4) ^ rswz(pl, RROW / 16)) << 4));
                     rw[0] = v.x; rw[1] = v.y; rw[2] = v.z; rw[3] = v.w;
+                } else if (RES) {   // 16 channels = 8 bytes: half (ocl/16)%2 of chunk ocl/32
+                    const uint2 v = *reinterpret_cast<const uint2*>(
+                        rtile + pl * RROW + (((ocl >> 5) ^ rswz(pl, RROW / 16)) << 4) + ((ocl >> 4) & 1) * 8);
+                    rw[0] = v.x; rw[1] = v.y;
                 }
-                epi_store16<false, RES ? 1 : 2>(p, acc[t][u], nullptr, mult, rw, ocb, pix, add, m_res);
+                epi_store16<false, RES ? (B4 ? 3 : 1) : 2>(p, acc[t][u], nullptr, mult, rw, ocb, pix, add, m_res);
             }
         }
         init_acc();
@@ -1315,7 +1360,8 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
 }
 
 template <class C>
-hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bool c4, hipStream_t stream) {
+hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bool c4, hipStream_t stream,
+                         bool b4 = false) {
     ConvParams q = p;
     q.n_oc_tiles = (p.c_out + C::BM - 1) / C::BM;
     const int64_t n_px = (p.m + C::BN - 1) / C::BN;
@@ -1330,6 +1376,17 @@ hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bo
     per = std::min<int64_t>(per, (int64_t)q.px_chunk * n_oc);
     q.gx = per;
     dim3 g((unsigned)(8 * per)), b(256);
+    if (b4) {   // 4-bit activations: the 64x128 and 128x128 configurations only
+        if constexpr (C::OCC < 3 && C::BN == 128 && ((C::BM == 64 && C::NST == 6) || (C::BM == 128 && C::NST == 4))) {
+            const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;
+            if (is_1x1 && add) hipLaunchKernelGGL((qconv_stream<C, true, true, false, true>), g, b, 0, stream, q);
+            else if (is_1x1) hipLaunchKernelGGL((qconv_stream<C, true, false, false, true>), g, b, 0, stream, q);
+            else if (add) hipLaunchKernelGGL((qconv_stream<C, false, true, false, true>), g, b, 0, stream, q);
+            else hipLaunchKernelGGL((qconv_stream<C, false, false, false, true>), g, b, 0, stream, q);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
     if constexpr ((C::NST - 1) * (C::BM / 64 + C::BN / 16) <= 60 && C::OCC < 3) {
         if (c4) {
             hipLaunchKernelGGL((qconv_stream<C, false, false, true>), g, b, 0, stream, q);
@@ -1539,6 +1596,10 @@ int pipe_tile_choice(int64_t m, int32_t c_out, int64_t k, bool res) {
 
 hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_t stream, int tile) {
     if (gather == GATHER_C4 && tile < 0 && stem_ok(p)) return launch_stem(p, stream);
+    if (gather == GATHER_B4S) {   // its packed layout is the streaming kernel's: no other tile
+        if (p.c_out <= 64) return launch_stream<S64x128d6>(p, is_1x1, true, false, stream, true);
+        return launch_stream<S128x128d4>(p, is_1x1, true, false, stream, true);
+    }
     if (pipe_eligible(gather, p.c, p.k)) {
         const bool c4 = gather == GATHER_C4;
         const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;

@@ -104,7 +104,7 @@ def _host_pack(d, w_codes, wt, bias, s_in, s_w, s_out, s_res=1.0):
     return buf
 
 
-def _unpack_layout(buf, c_out, k, act4):
+def _unpack_layout(buf, c_out, k, act4, stream4=False):
     ocp = (c_out + 255) // 256 * 256
     kp = (k + 63) // 64 * 64
     bias = buf[:4 * ocp].view(np.int32)
@@ -119,11 +119,15 @@ def _unpack_layout(buf, c_out, k, act4):
         rows.append(32 * b + 8 * j + 4 * h + r)
     w = w[rows][:, :k]
     if act4:
+        # nibble unpack order inside every 16 K positions; with the streaming kernel's
+        # 4-bit layout (C_in % 64 == 0) also blocks 1 and 2 of every 64 trade places
         order = [0, 2, 4, 6, 1, 3, 5, 7, 8, 10, 12, 14, 9, 11, 13, 15]
         logical = np.empty_like(w)
         for s0 in range(0, k, 16):
+            blk = (s0 // 16) % 4
+            src0 = s0 - 16 * blk + 16 * ({1: 2, 2: 1}.get(blk, blk) if stream4 else blk)
             for p, e in enumerate(order):
-                logical[:, s0 + e] = w[:, s0 + p]
+                logical[:, s0 + e] = w[:, src0 + p]
         w = logical
     return bias[:c_out], mult[:c_out], mres, w, pad
 
@@ -133,6 +137,7 @@ def _unpack_layout(buf, c_out, k, act4):
     (B.INT8, B.INT8, 32, 64, B.EPI_NONE),
     (B.UINT4, B.INT4, 32, 48, B.EPI_ADD_RELU),
     (B.INT4, B.INT4, 16, 16, B.EPI_ADD),
+    (B.UINT4, B.INT4, 64, 64, B.EPI_ADD_RELU),
     (B.UINT8, B.INT8, 3, 64, B.EPI_RELU),
 ])
 def test_host_prepack_matches_oracle_qparams(lib, x_type, w_type, c_in, c_out, epi):
@@ -150,9 +155,9 @@ def test_host_prepack_matches_oracle_qparams(lib, x_type, w_type, c_in, c_out, e
                   z_out=1, res_type=B.UINT4, z_res=2)
     buf = _host_pack(d, w, w_type, bias, s_in, s_w, s_out, s_res)
     act4 = x_type in (B.UINT4, B.INT4)
-    fold, mult, mres, wl, pad = _unpack_layout(buf, c_out, 9 * c_in, act4)
-    # the padding row holds the raw input zero-point code
-    assert np.all(pad == (z_in & 0xFF))
+    fold, mult, mres, wl, pad = _unpack_layout(buf, c_out, 9 * c_in, act4, stream4=act4 and c_in % 64 == 0)
+    # the padding row holds the raw input zero-point code (two per byte for 4-bit codes)
+    assert np.all(pad == ((z_in & 0xF) * 0x11 if act4 else z_in & 0xFF))
     # weights: exactly the codes, back in OHWI order after undoing the documented permutations
     assert np.array_equal(wl.astype(np.int32), w.reshape(c_out, -1))
     # multipliers: the oracle's requant_multiplier / residual_multiplier

@@ -116,6 +116,30 @@ def test_conv_every_tile(tile):
         B.iqnn_set_conv_tile(-1)
 
 
+# 4-bit activations with C_in % 64 == 0 (the streaming kernel's 4-bit path): both
+# block heights (C_out <= 64 -> 64-channel blocks, 32-byte residual rows; else 128),
+# UINT4 and INT4 codes, 4-bit residuals, stride 2, ragged pixel tails
+B4S = [
+    # n, h, w, c_in, c_out, k, stride, pad, x_type, y_type, epi, res_type
+    (2, 9, 11, 64, 64, 3, 1, 1, U4, U4, ADD_RELU, U4),
+    (1, 13, 7, 128, 128, 3, 1, 1, U4, U4, ADD_RELU, U4),
+    (2, 8, 9, 64, 96, 1, 1, 0, I4, I4, ADD, I4),
+    (1, 15, 15, 128, 64, 3, 2, 1, I4, U8, RELU, U4),
+    (3, 7, 7, 192, 32, 1, 1, 0, U4, I8, NONE, U4),
+    (1, 6, 5, 64, 256, 3, 1, 1, U4, U4, RELU, U4),
+]
+
+
+@pytest.mark.parametrize("case", B4S, ids=lambda c: "n%dh%dw%dci%dco%dk%ds%dp%d_x%dy%de%d" % c[:11])
+def test_conv_4bit_streaming(case):
+    require_gpu()
+    n, h, w, ci, co, k, s, p, xt, yt, epi, rt = case
+    c = synth.conv_case(hash(case) % 2 ** 31, n, h, w, ci, co, k, s, p, xt, I4, yt, epi, res_type=rt)
+    x, wc, res = conv_codes(c)
+    want = to_bytes(oracle_conv(c, x, wc, res), yt)
+    assert_bytes_equal(gpu_conv(c, x, wc, res), want, str(case))
+
+
 def test_conv_adversarial_codes_and_padding():
     # every code of each type, including -128 / 255 / -8 / 15, on tiny images where
     # most taps read padding
