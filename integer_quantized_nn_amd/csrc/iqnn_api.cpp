@@ -360,13 +360,13 @@ iqnn_status forward(const Layer& L, const void* x, const void* packed, const voi
     if (L.epi != E_RAW) {
         int32_t lo, hi;
         code_range(L.y_type, &lo, &hi);
-        const int32_t shift = L.y_type == T_INT8 ? 128 : (L.y_type == T_INT4 ? 8 : 0);
         const bool relu = L.epi == E_RELU || L.epi == E_ADD_RELU;
         const int32_t low = relu ? std::max(lo, L.z_out) : lo;   // passive ReLU: clamp at Z_out
-        p.out_zf = (float)(L.z_out + shift);
-        p.lo = (float)(low + shift);
-        p.hi = (float)(hi + shift);
-        p.out_xor = L.y_type == T_INT8 ? 0x80808080u : (L.y_type == T_INT4 ? 0x88888888u : 0u);
+        const int32_t fix = L.z_out & 1;                         // odd part (two's complement)
+        p.t_lo = (float)(low - L.z_out);
+        p.t_hi = (float)(hi - L.z_out);
+        p.out_magic = 12582912.0f + (float)(L.z_out - fix);      // 1.5 * 2^23 + even part of Z_out
+        p.out_fix = (uint32_t)fix;
     }
     if (L.epi == E_ADD || L.epi == E_ADD_RELU) {
         const int32_t rshift = L.res_type == T_INT8 ? 128 : (L.res_type == T_INT4 ? 8 : 0);

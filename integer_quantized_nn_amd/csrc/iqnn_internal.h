@@ -78,13 +78,15 @@ struct ConvParams {
     int32_t z_out, z_res;
     const float* m_res;       // residual multiplier S_res/S_out (in the packed buffer)
     const uint8_t* pad_row;   // 64 bytes of the raw input zero-point code (in the packed buffer)
-    // Epilogue constants (host-computed).  Outputs are formed as unsigned codes
-    // shifted by out_shift = 128 (INT8) / 8 (INT4) / 0: out_zf = Z_out + out_shift,
-    // [lo, hi] = [Q_MIN (or max(Q_MIN, Z_out) with ReLU), Q_MAX] + out_shift, and
-    // out_xor undoes the shift on the packed word.  Residual codes are read the same
-    // way: (code ^ res_xor) - res_zf == r - Z_res.
-    float out_zf, lo, hi;
-    uint32_t out_xor;
+    // Epilogue constants (host-computed).  The requantized value is clipped to
+    // [t_lo, t_hi] = [Q_MIN (or max(Q_MIN, Z_out) with ReLU), Q_MAX] - Z_out, then
+    // out_magic = 1.5 * 2^23 + (Z_out minus its odd part) is added, which rounds to
+    // nearest even; out_fix (the odd part of Z_out, 0 or 1) is added to the float's
+    // bits, leaving the output code in the low byte.  Residual codes are read as
+    // unsigned codes shifted by 128 (INT8) / 8 (INT4) / 0: (code ^ res_xor) - res_zf
+    // == r - Z_res.
+    float t_lo, t_hi, out_magic;
+    uint32_t out_fix;
     float res_zf;
     uint32_t res_xor;
     int32_t vec_store;        // C_out % 16 == 0: vector stores
