@@ -135,15 +135,16 @@ __device__ __forceinline__ void load_res16(const ConvParams& p, int64_t oidx, in
 //   y = clip(rne(t) + Z_out, lo, Q_MAX)
 // ReLU is the passive clamp at the real value 0 ("Quantization" blog, 量化激活函数):
 // since rne is monotone and rne(0) = 0, clip(rne(max(t,0)) + Z) == clip(rne(t) + Z)
-// with the lower bound raised to max(Q_MIN, Z_out); the host folds it into `lo`.
-// Signed outputs are produced shifted into the unsigned range (+128 / +8) so one
-// v_cvt_pk_u8_f32 packs each byte, and the shift is undone with one XOR per word.
-// Every intermediate is an exact integer below 2^24 or is clamped away, so this is
-// bit-identical to rounding, adding Z_out as an integer and clipping.
+// with the lower bound raised to max(Q_MIN, Z_out).  The clip moves before the
+// rounding, into the offset domain [lo - Z_out, hi - Z_out] (integer bounds, so
+// rne(clip(t)) == clip(rne(t))).  Rounding and the zero point are one addition:
+// C = 1.5 * 2^23 + Z_even, with Z_even the even part of Z_out, puts t + C in
+// [2^23, 2^24) where binary32 steps by exactly 1, so the add rounds t to nearest
+// even and the low mantissa bits hold rne(t) + Z_even (an even C keeps the tie
+// parity of rne(t)).  Adding the odd part of Z_out (0 or 1) as an integer leaves the
+// code in the low byte, two's complement for signed types; bytes are packed with
+// v_perm_b32, nibbles with shifts.
 //
-// BIAS: add bias[] here (otherwise the accumulator started from the folded bias).
-// ADDK: 0 = residual add decided by `add` and p.res_type at run time, 1 = always an
-// 8-bit residual, 2 = never a residual, 3 = always a 4-bit residual.
 template <bool BIAS = true, int ADDK = 0>
 __device__ __forceinline__ void epi_store16(const ConvParams& p, const v16i& acc, const int32_t* bias,
                                             const float* mult, uint32_t rw[4], int ocb, int64_t pix, bool add_rt,
@@ -178,17 +179,21 @@ __device__ __forceinline__ void epi_store16(const ConvParams& p, const v16i& acc
             v[j] = v[j] + u;
         }
     }
+    uint32_t b[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = __builtin_amdgcn_fmed3f(__builtin_rintf(v[j]) + p.out_zf, p.lo, p.hi);
+    for (int j = 0; j < 16; ++j)
+        b[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_fmed3f(v[j], p.t_lo, p.t_hi) + p.out_magic);
+    if (p.out_fix) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) b[j] += 1u;
+    }
     if (p.y_type == T_INT8 || p.y_type == T_UINT8) {
         uint32_t ow[4];
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            uint32_t x = __builtin_amdgcn_cvt_pk_u8_f32(v[4 * d], 0, 0);
-            x = __builtin_amdgcn_cvt_pk_u8_f32(v[4 * d + 1], 1, x);
-            x = __builtin_amdgcn_cvt_pk_u8_f32(v[4 * d + 2], 2, x);
-            x = __builtin_amdgcn_cvt_pk_u8_f32(v[4 * d + 3], 3, x);
-            ow[d] = x ^ p.out_xor;
+            const uint32_t lo2 = __builtin_amdgcn_perm(b[4 * d + 1], b[4 * d], 0x0C0C0400u);
+            const uint32_t hi2 = __builtin_amdgcn_perm(b[4 * d + 3], b[4 * d + 2], 0x0C0C0400u);
+            ow[d] = lo2 | (hi2 << 16);
         }
         if (p.vec_store) {
             *reinterpret_cast<uint4*>(p.y + oidx) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
@@ -198,9 +203,7 @@ __device__ __forceinline__ void epi_store16(const ConvParams& p, const v16i& acc
     } else {
         uint32_t ow[2] = {0, 0};
 #pragma unroll
-        for (int j = 0; j < 16; ++j) ow[j >> 3] |= ((uint32_t)v[j]) << (4 * (j & 7));
-        ow[0] ^= p.out_xor;
-        ow[1] ^= p.out_xor;
+        for (int j = 0; j < 16; ++j) ow[j >> 3] |= (b[j] & 0xFu) << (4 * (j & 7));
         if (p.vec_store) {
             *reinterpret_cast<uint2*>(p.y + (oidx >> 1)) = make_uint2(ow[0], ow[1]);
         } else {
@@ -1576,7 +1579,7 @@ using S64x128d12 = StreamCfg<64, 128, 1, 12>;
 using S64x128d6 = StreamCfg<64, 128, 1, 6>;
 using S128x128d8 = StreamCfg<128, 128, 2, 8>;
 using S128x128d4 = StreamCfg<128, 128, 2, 4>;
-using S64x256d7 = StreamCfg<64, 256, 1, 7>;
+using S64x256d3 = StreamCfg<64, 256, 1, 3>;
 using S256x128d6 = StreamCfg<256, 128, 2, 6>;
 using S128x256d6 = StreamCfg<128, 256, 2, 6>;
 using S128x128d3o3 = StreamCfg<128, 128, 2, 3, 3>;
@@ -1587,11 +1590,14 @@ using S256x256d4 = StreamCfg<256, 256, 2, 4>;
 // Automatic tile, all on the streaming kernel at two blocks per CU: 256x128 blocks
 // (each wave 128 channels x 64 pixels: 0.75 KB of fragment reads per MFMA) for the
 // wide, deep contractions (C_out >= 256, K >= 1024, no residual); 128x128 blocks
-// for the rest, 64x128 when C_out <= 64.
+// for the rest.  C_out <= 64: 64x256 blocks (each wave 64 x 64: 1 KB of fragment
+// reads per MFMA, 20 KB stages at ring depth 3) for one-stage and 3x3-deep
+// contractions, 64x128 blocks (deeper ring) between those.
 int pipe_tile_choice(int64_t m, int32_t c_out, int64_t k, bool res) {
     (void)m;
     if (c_out >= 256 && k >= 1024 && !res) return 16;
-    return c_out <= 64 ? 8 : 10;
+    if (c_out <= 64) return (k == kPipeBK || k >= 576) ? 11 : 8;
+    return 10;
 }
 
 hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_t stream, int tile) {
@@ -1625,7 +1631,7 @@ hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_
         case 8: return launch_stream<S64x128d6>(p, is_1x1, res_prefetch, c4, stream);
         case 9: return launch_stream<S128x128d8>(p, is_1x1, res_prefetch, c4, stream);
         case 10: return launch_stream<S128x128d4>(p, is_1x1, res_prefetch, c4, stream);
-        case 11: return launch_stream<S64x256d7>(p, is_1x1, res_prefetch, c4, stream);
+        case 11: return launch_stream<S64x256d3>(p, is_1x1, res_prefetch, c4, stream);
         case 12: return launch_stream<S256x128d6>(p, is_1x1, res_prefetch, c4, stream);
         case 13: return launch_stream<S128x256d6>(p, is_1x1, res_prefetch, c4, stream);
         case 14: return launch_stream<S128x128d3o3>(p, is_1x1, res_prefetch, c4, stream);
