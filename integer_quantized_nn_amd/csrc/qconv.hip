@@ -1592,10 +1592,13 @@ using S256x256d4 = StreamCfg<256, 256, 2, 4>;
 // wide, deep contractions (C_out >= 256, K >= 1024, no residual); 128x128 blocks
 // for the rest.  C_out <= 64: 64x256 blocks (each wave 64 x 64: 1 KB of fragment
 // reads per MFMA, 20 KB stages at ring depth 3) for one-stage and 3x3-deep
-// contractions, 64x128 blocks (deeper ring) between those.
+// contractions, 64x128 blocks (deeper ring) between those.  Without a residual and
+// with C_out >= 128, the very deep contractions (K >= 4096) and the one-stage ones
+// run 128x128 blocks three to a CU, and C_out >= 512 takes the 256x128 blocks at any K.
 int pipe_tile_choice(int64_t m, int32_t c_out, int64_t k, bool res) {
     (void)m;
-    if (c_out >= 256 && k >= 1024 && !res) return 16;
+    if (!res && c_out >= 128 && (k >= 4096 || k == kPipeBK)) return 14;
+    if (!res && c_out >= 256 && (k >= 1024 || c_out >= 512)) return 16;
     if (c_out <= 64) return (k == kPipeBK || k >= 576) ? 11 : 8;
     return 10;
 }
