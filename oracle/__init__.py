@@ -256,16 +256,18 @@ def im2col(x, z_in, kh, kw, stride=1, pad=0):
 
 
 def qconv(x, z_in, s_in, w, s_w, bias, s_out, z_out, out_qtype, epi, stride=1, pad=0,
-          res=None, s_res=1.0, z_res=0):
+          res=None, s_res=1.0, z_res=0, z_w=0):
     """Quantized conv with fused epilogue: codes in, codes out (int32 acc for EPI_RAW).
 
-    x: NHWC input codes; w: OHWI weight codes (symmetric, Z_w = 0); s_w: scalar or [co];
-    bias: float32 [co] or None; res: NHWC residual codes for ADD / ADD_RELU.
+    x: NHWC input codes; w: OHWI weight codes with per-tensor zero point z_w (0:
+    symmetric); s_w: scalar or [co]; bias: float32 [co] or None; res: NHWC residual
+    codes for ADD / ADD_RELU.  The accumulator is the plain definition
+    sum (x - Z_in)(w - Z_w) (MegEngine 4-bit article, 緩解精度下降).
     """
     co = w.shape[0]
     s_w_c = np.broadcast_to(np.atleast_1d(np.asarray(s_w, np.float32)), (co,))
     bias_q = quantize_bias(bias, s_in, s_w_c) if bias is not None else None
-    acc = conv2d_acc(x, z_in, w, 0, stride, pad, bias_q)
+    acc = conv2d_acc(x, z_in, w, z_w, stride, pad, bias_q)
     if epi == EPI_RAW:
         return requant(acc, np.ones(co, np.float32), EPI_RAW, 0, INT32)
     mult = requant_multiplier(s_in, s_w_c, s_out)
@@ -273,12 +275,12 @@ def qconv(x, z_in, s_in, w, s_w, bias, s_out, z_out, out_qtype, epi, stride=1, p
     return requant(acc, mult, epi, z_out, out_qtype, res, z_res, m_res)
 
 
-def qgemm(a, z_a, s_a, b, s_b, bias, s_out, z_out, out_qtype, epi, res=None, s_res=1.0, z_res=0):
-    """Quantized GEMM C = A B^T (B stored [n][k]) with fused epilogue."""
+def qgemm(a, z_a, s_a, b, s_b, bias, s_out, z_out, out_qtype, epi, res=None, s_res=1.0, z_res=0, z_b=0):
+    """Quantized GEMM C = A B^T (B stored [n][k], zero point z_b) with fused epilogue."""
     n = b.shape[0]
     s_b_c = np.broadcast_to(np.atleast_1d(np.asarray(s_b, np.float32)), (n,))
     bias_q = quantize_bias(bias, s_a, s_b_c) if bias is not None else None
-    acc = gemm_acc(a, z_a, b, 0, bias_q)
+    acc = gemm_acc(a, z_a, b, z_b, bias_q)
     if epi == EPI_RAW:
         return requant(acc, np.ones(n, np.float32), EPI_RAW, 0, INT32)
     mult = requant_multiplier(s_a, s_b_c, s_out)

@@ -68,6 +68,56 @@ def test_conv_acc_with_weight_zero_point_matches_torch():
     assert np.array_equal(got, _torch_conv_acc(x, 40, wt - 8, 1, 1))
 
 
+@pytest.mark.parametrize("case", CONV_CASES[1:5])
+def test_asymmetric_weights_match_torch_conv2d(case):
+    # MegEngine 4-bit article, section 緩解精度下降: weights in UINT4 (or UINT8) carry a
+    # zero point Z_W; the accumulator is sum (Q(I) - Z_I)(Q(W) - Z_W).  torch conv2d in
+    # float64 on the centred operands is exact for these integer sums.
+    n, h, w, ci, co, kh, kw, stride, pad = case
+    rng = np.random.default_rng(hash(("zw",) + case) % 2 ** 32)
+    for (wlo, whi, zw) in [(0, 255, 131), (0, 255, 0), (0, 15, 7), (-128, 127, -9), (-8, 7, 3)]:
+        x = _rand_codes(rng, (n, h, w, ci), 0, 255)
+        wt = _rand_codes(rng, (co, kh, kw, ci), wlo, whi)
+        bq = _rand_codes(rng, (co,), -5000, 5000)
+        got = O.conv2d_acc(x, 21, wt, zw, stride, pad, bq)
+        assert np.array_equal(got, _torch_conv_acc(x, 21, wt - zw, stride, pad, bq))
+
+
+def test_weight_zero_point_term_is_a_per_pixel_window_sum():
+    # MegEngine 4-bit article, section 緩解精度下降: a nonzero Z_W adds the red term
+    # -Z_W * sum Q(I), which depends on the input and so varies per output pixel:
+    # acc(Z_W) == acc(0) - Z_W * (window sums of Q(I) - Z_I), the window sums taken by an
+    # all-ones kernel (torch conv2d, float64, exact).
+    rng = np.random.default_rng(12)
+    x = _rand_codes(rng, (2, 7, 6, 5), 0, 255)
+    wt = _rand_codes(rng, (3, 3, 3, 5), 0, 255)
+    for zw, z_in, stride, pad in [(117, 30, 1, 1), (200, 0, 2, 1), (1, 255, 1, 2)]:
+        a0 = O.conv2d_acc(x, z_in, wt, 0, stride, pad)
+        az = O.conv2d_acc(x, z_in, wt, zw, stride, pad)
+        ones = np.ones((1, 3, 3, 5), np.int32)
+        win = _torch_conv_acc(x, z_in, ones, stride, pad)[..., 0]
+        assert np.array_equal(az, a0 - zw * win[..., None])
+
+
+def test_weights_equal_to_their_zero_point_give_the_bias():
+    rng = np.random.default_rng(13)
+    x = _rand_codes(rng, (1, 6, 6, 4), 0, 255)
+    bq = _rand_codes(rng, (3,), -1000, 1000)
+    for zw in (0, 9, 200):
+        wt = np.full((3, 3, 3, 4), zw, np.int32)
+        acc = O.conv2d_acc(x, 77, wt, zw, 2, 1, bq)
+        assert np.array_equal(acc, np.broadcast_to(bq.astype(np.int64), acc.shape))
+
+
+def test_gemm_with_weight_zero_point_matches_numpy():
+    rng = np.random.default_rng(14)
+    a = _rand_codes(rng, (29, 128), 0, 255)
+    b = _rand_codes(rng, (13, 128), 0, 255)
+    bq = _rand_codes(rng, (13,), -1000, 1000)
+    want = (a.astype(np.int64) - 111) @ (b.astype(np.int64) - 140).T + bq
+    assert np.array_equal(O.gemm_acc(a, 111, b, 140, bq), want)
+
+
 def test_identity_1x1_gives_centred_input():
     rng = np.random.default_rng(12)
     x = _rand_codes(rng, (2, 5, 6, 4), 0, 255)
