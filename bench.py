@@ -241,13 +241,19 @@ def bench_layer(args):
     from integer_quantized_nn_amd.layers import QConv, QGemm, quantize
 
     wl = args.workload
-    if wl in ("conv3x3_int8", "conv3x3_4bit"):
-        c = synth.conv3x3_int8() if wl == "conv3x3_int8" else synth.conv3x3_4bit()
+    if wl in ("conv3x3_int8", "conv3x3_4bit", "conv3x3_uint8w"):
+        c = synth.conv3x3_4bit() if wl == "conv3x3_4bit" else synth.conv3x3_int8()
         n, h, w, ci = c.x.shape
         co = c.c_out
-        wq = quantize(torch.from_numpy(c.w).cuda(), c.s_w, 0, c.w_type, axis=0).cpu().numpy()
-        layer = QConv(n, h, w, ci, co, 3, c.stride, c.pad, c.x_type, c.w_type, c.y_type, c.epi, c.z_in, c.z_out,
-                      wq, c.bias, c.s_in, c.s_w, c.s_out, res_type=c.res_type, z_res=c.z_res, s_res=c.s_res)
+        w_type, s_w, z_w = c.w_type, c.s_w, 0
+        if wl == "conv3x3_uint8w":   # asymmetric weights: per-tensor min-max UINT8 codes
+            w_type = synth.UINT8
+            s_w, z_w = synth.minmax_qparams(c.w.min(), c.w.max(), w_type)
+            wq = quantize(torch.from_numpy(c.w).cuda(), s_w, z_w, w_type).cpu().numpy()
+        else:
+            wq = quantize(torch.from_numpy(c.w).cuda(), c.s_w, 0, c.w_type, axis=0).cpu().numpy()
+        layer = QConv(n, h, w, ci, co, 3, c.stride, c.pad, c.x_type, w_type, c.y_type, c.epi, c.z_in, c.z_out,
+                      wq, c.bias, c.s_in, s_w, c.s_out, res_type=c.res_type, z_res=c.z_res, s_res=c.s_res, z_w=z_w)
         xd = quantize(torch.from_numpy(c.x).cuda(), c.s_in, c.z_in, c.x_type)
         rd = quantize(torch.from_numpy(c.res).cuda(), c.s_res, c.z_res, c.res_type) if c.res is not None else None
         ops = c.ops(n, h, w)
@@ -328,7 +334,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--batch", type=int, default=256)
     ap.add_argument("--workload", default="resnet50_trunk",
-                    choices=["resnet50_trunk", "conv3x3_int8", "conv3x3_4bit", "vitl_fc1", "gemm_int8_256"])
+                    choices=["resnet50_trunk", "conv3x3_int8", "conv3x3_4bit", "conv3x3_uint8w", "vitl_fc1",
+                             "gemm_int8_256"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="trunk: time eager launches instead of one captured HIP graph per step")

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define IQNN_ABI_VERSION 1
+#define IQNN_ABI_VERSION 2
 
 typedef enum {
     IQNN_OK = 0,
@@ -87,29 +87,40 @@ typedef enum {
 
 /* Convolution descriptor.  Dilation 1, groups 1.  Output size
  * OH = (H + 2*pad_h - KH)/stride_h + 1, OW likewise.
- * x_type: INT8, UINT8, INT4 or UINT4.  w_type: INT8 or INT4 (symmetric).
+ * x_type: INT8, UINT8, INT4 or UINT4.  w_type: INT8, UINT8, INT4 or UINT4 with
+ * the per-tensor weight zero point z_w (INT8 / INT4 with z_w = 0 are symmetric).
  * y_type: INT8, UINT8, INT4, UINT4, or INT32 with IQNN_EPI_RAW_INT32.
  * res_type: type of the residual for ADD / ADD_RELU (8- or 4-bit), else ignored.
- * z_in / z_out / z_res: zero points, within the code range of their type.
+ * z_in / z_out / z_res / z_w: zero points, within the code range of their type.
  * 4-bit activations need C_in % 16 == 0.  8-bit activations with C_in == 4 and no
  * padding (an input from iqnn_quantize_pad) take a 4-taps-per-load gather; other
- * C_in % 16 != 0 take a slower element gather. */
+ * C_in % 16 != 0 take a slower element gather.
+ * Asymmetric weights (MegEngine 4-bit article, 緩解精度下降: a nonzero Z_W adds
+ * the term Z_W * sum_k Q(I) of each output pixel, which depends on the input and
+ * cannot be folded into the bias).  The kernels hold weights as w - s_w with
+ * s_w = 128 for UINT8 and 0 otherwise; when z_w != s_w the per-pixel term is
+ * accumulated next to the contraction, which the streaming path does for 8-bit
+ * activations with C_in % 64 == 0, KH*KW <= 64 and N*OH*OW < 2^31.  Other layers
+ * with z_w != s_w return IQNN_ERR_UNSUPPORTED (descriptor checks of every call). */
 typedef struct {
     int32_t n, h, w, c_in, c_out;
     int32_t kh, kw, stride_h, stride_w, pad_h, pad_w;
     int32_t x_type, w_type, y_type, res_type;
     int32_t epilogue;
     int32_t z_in, z_out, z_res;
+    int32_t z_w;
 } iqnn_conv_desc;
 
 /* GEMM descriptor: C[M][N] = epilogue(A[M][K] * B[N][K]^T).  a_type is the
- * activation type (8- or 4-bit, zero point z_a), b_type the weight type (INT8 or
- * INT4), c_type / res_type / epilogue / z_out / z_res as for convolution. */
+ * activation type (8- or 4-bit, zero point z_a), b_type the weight type with zero
+ * point z_b (as w_type / z_w of a convolution; the per-pixel term needs K % 64 ==
+ * 0), c_type / res_type / epilogue / z_out / z_res as for convolution. */
 typedef struct {
     int64_t m, n, k;
     int32_t a_type, b_type, c_type, res_type;
     int32_t epilogue;
     int32_t z_a, z_out, z_res;
+    int32_t z_b;
 } iqnn_gemm_desc;
 
 /* ---------------------------------------------------------------- misc */
@@ -187,8 +198,8 @@ size_t iqnn_qconv_packed_size(const iqnn_conv_desc *desc);
  *   s_res: residual scale (ADD / ADD_RELU; ignored otherwise).
  * Computes, once: bias_q[c] = rne(B[c] / (S_in*S_w[c])) (MegEngine 4-bit article,
  *   緩解精度下降: terms known before inference go into the bias), the folded int32
- *   bias bias_q[c] - Z_in*sum(W[c]) (plus the kernel-private shift term for uint8
- *   activations), M[c] = (S_in*S_w[c])/S_out and M_res = S_res/S_out in binary32
+ *   bias (bias_q[c] plus the Z_in and Z_in*Z_W terms, in the kernel's shifted
+ *   operands; see iqnn_qconv_prepack_host), M[c] = (S_in*S_w[c])/S_out and M_res = S_res/S_out in binary32
  *   ("Quantization" blog, 量化乘法: the combined scale is precomputed), and the
  *   weights reordered for the kernel (output channels permuted so each lane stores
  *   contiguous channels: MegEngine 4-bit article, conv 算子優化, Fig. 8).
@@ -217,8 +228,12 @@ iqnn_status iqnn_qconv_prepack(const iqnn_conv_desc *desc, const void *w_host,
  *                       for 4-bit activations the K positions inside every group of
  *                       16 are ordered 0,2,4,6,1,3,5,7,8,10,12,14,9,11,13,15
  *                       (the order the kernel unpacks nibbles in); zero padding.
- * The folded bias is rne(B[c]/(S_in*S_w[c])) - (Z_in - s)*sum_k W[c][k] with s = 128
- * for UINT8 activations (the kernel stages them as q - 128) and 0 otherwise. */
+ * The kernel contracts a = q_I - s (s = 128 for UINT8 activations, else 0) with the
+ * stored weights b = q_W - s_w (s_w = 128 for UINT8 weights, else 0), so
+ *   sum_k (q_I - Z_in)(q_W - Z_w) = sum a*b + (s - Z_in) sum_k b + K (s - Z_in)(s_w - Z_w)
+ *                                   + (s_w - Z_w) sum_k a,
+ * and the folded bias is rne(B[c]/(S_in*S_w[c])) + (s - Z_in)*sum_k b[c][k]
+ * + K*(s - Z_in)*(s_w - Z_w); the last term, per output pixel, is the kernel's. */
 iqnn_status iqnn_qconv_prepack_host(const iqnn_conv_desc *desc, const void *w_host,
                                     const float *bias_host, float s_in, const float *s_w_host,
                                     int per_channel, float s_out, float s_res, void *packed_host,

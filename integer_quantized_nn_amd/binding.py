@@ -29,7 +29,7 @@ class IqnnError(RuntimeError):
 class ConvDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n", "h", "w", "c_in", "c_out", "kh", "kw", "stride_h", "stride_w", "pad_h", "pad_w",
-        "x_type", "w_type", "y_type", "res_type", "epilogue", "z_in", "z_out", "z_res")]
+        "x_type", "w_type", "y_type", "res_type", "epilogue", "z_in", "z_out", "z_res", "z_w")]
 
     def out_hw(self):
         return ((self.h + 2 * self.pad_h - self.kh) // self.stride_h + 1,
@@ -39,7 +39,7 @@ class ConvDesc(ctypes.Structure):
 class GemmDesc(ctypes.Structure):
     _fields_ = [("m", ctypes.c_int64), ("n", ctypes.c_int64), ("k", ctypes.c_int64)] + \
                [(n, ctypes.c_int32) for n in ("a_type", "b_type", "c_type", "res_type", "epilogue",
-                                              "z_a", "z_out", "z_res")]
+                                              "z_a", "z_out", "z_res", "z_b")]
 
 
 _lib = None

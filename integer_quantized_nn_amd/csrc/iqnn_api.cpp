@@ -76,9 +76,15 @@ bool normal_ok(float s) { return std::isfinite(s) && s >= std::numeric_limits<fl
 struct Layer {
     int64_t n, h, w, c, c_out, oh, ow, m, k;
     int32_t kh, kw, sh, sw, ph, pw;
-    int32_t x_type, w_type, y_type, res_type, epi, z_in, z_out, z_res;
+    int32_t x_type, w_type, y_type, res_type, epi, z_in, z_out, z_res, z_w;
     bool gemm;
 };
+
+// Weights are held as q_W - s_w (s_w = 128 for UINT8, else 0) so every type fits
+// int8; zw_red = s_w - Z_w is the coefficient of the per-pixel sum of the kernel's
+// activation operands (MegEngine 4-bit article, 緩解精度下降: the red term).
+int32_t weight_shift(const Layer& L) { return L.w_type == T_UINT8 ? 128 : 0; }
+int32_t zw_red(const Layer& L) { return weight_shift(L) - L.z_w; }
 
 iqnn_status check_layer(const Layer& L) {
     if (L.n <= 0 || L.h <= 0 || L.w <= 0 || L.c <= 0 || L.c_out <= 0)
@@ -91,8 +97,19 @@ iqnn_status check_layer(const Layer& L) {
     if (L.c_out > (1 << 24) || L.k > (1 << 24))
         return fail(IQNN_ERR_UNSUPPORTED, "C_out or K above 2^24");
     if (!is_code_type(L.x_type)) return fail(IQNN_ERR_INVALID_ARG, "activation type %d is not a code type", L.x_type);
-    if (L.w_type != T_INT8 && L.w_type != T_INT4)
-        return fail(IQNN_ERR_INVALID_ARG, "weight type must be INT8 or INT4 (symmetric)");
+    if (!is_code_type(L.w_type)) return fail(IQNN_ERR_INVALID_ARG, "weight type %d is not a code type", L.w_type);
+    if (!in_range(L.w_type, L.z_w)) return fail(IQNN_ERR_INVALID_ARG, "z_w %d outside the weight code range", L.z_w);
+    if (zw_red(L) != 0) {
+        // the per-pixel term rides on the streaming kernel's 8-bit gather
+        const bool add = L.epi == E_ADD || L.epi == E_ADD_RELU;
+        const bool streamable = !is_4bit(L.x_type) && L.c % 64 == 0 && L.m < ((int64_t)1 << 31) &&
+                                (int64_t)L.kh * L.kw <= 64 &&
+                                (!add || (!is_4bit(L.res_type) && L.c_out % 16 == 0));
+        if (!streamable)
+            return fail(IQNN_ERR_UNSUPPORTED,
+                        "weight zero point %d (w_type %d) needs 8-bit activations, C_in %% 64 == 0, KH*KW <= 64, "
+                        "N*OH*OW < 2^31 and an 8-bit residual with C_out %% 16 == 0", L.z_w, L.w_type);
+    }
     if (L.epi < E_NONE || L.epi > E_RAW) return fail(IQNN_ERR_INVALID_ARG, "unknown epilogue %d", L.epi);
     if ((L.epi == E_RAW) != (L.y_type == T_INT32))
         return fail(IQNN_ERR_INVALID_ARG, "INT32 output goes with the RAW_INT32 epilogue and only with it");
@@ -110,8 +127,8 @@ iqnn_status check_layer(const Layer& L) {
         return fail(IQNN_ERR_UNSUPPORTED, "4-bit activations need C_in %% 16 == 0 (C_in=%lld)", (long long)L.c);
     if ((is_4bit(L.y_type) || (add && is_4bit(L.res_type))) && L.c_out % 2 != 0)
         return fail(IQNN_ERR_INVALID_ARG, "4-bit outputs / residuals need an even C_out");
-    if (L.w_type == T_INT4 && L.c % 2 != 0)
-        return fail(IQNN_ERR_INVALID_ARG, "INT4 weights need an even C_in (nibble pairs)");
+    if (is_4bit(L.w_type) && L.c % 2 != 0)
+        return fail(IQNN_ERR_INVALID_ARG, "4-bit weights need an even C_in (nibble pairs)");
     if (!is_4bit(L.x_type) && L.c % 16 != 0 && L.w > 0x7FFFFFFF)
         return fail(IQNN_ERR_UNSUPPORTED, "element-gather path limited to 2^31 columns");
     if (L.m > ((int64_t)1 << 40)) return fail(IQNN_ERR_UNSUPPORTED, "too many output pixels");
@@ -124,7 +141,7 @@ iqnn_status conv_layer(const iqnn_conv_desc* d, Layer* L) {
     L->n = d->n; L->h = d->h; L->w = d->w; L->c = d->c_in; L->c_out = d->c_out;
     L->kh = d->kh; L->kw = d->kw; L->sh = d->stride_h; L->sw = d->stride_w; L->ph = d->pad_h; L->pw = d->pad_w;
     L->x_type = d->x_type; L->w_type = d->w_type; L->y_type = d->y_type; L->res_type = d->res_type;
-    L->epi = d->epilogue; L->z_in = d->z_in; L->z_out = d->z_out; L->z_res = d->z_res;
+    L->epi = d->epilogue; L->z_in = d->z_in; L->z_out = d->z_out; L->z_res = d->z_res; L->z_w = d->z_w;
     L->oh = L->sh > 0 ? (L->h + 2 * (int64_t)L->ph - L->kh) / L->sh + 1 : 0;
     L->ow = L->sw > 0 ? (L->w + 2 * (int64_t)L->pw - L->kw) / L->sw + 1 : 0;
     L->m = L->n * L->oh * L->ow;
@@ -138,7 +155,7 @@ iqnn_status gemm_layer(const iqnn_gemm_desc* d, Layer* L) {
     L->n = 1; L->h = 1; L->w = d->m; L->c = d->k; L->c_out = d->n;
     L->kh = L->kw = L->sh = L->sw = 1; L->ph = L->pw = 0;
     L->x_type = d->a_type; L->w_type = d->b_type; L->y_type = d->c_type; L->res_type = d->res_type;
-    L->epi = d->epilogue; L->z_in = d->z_a; L->z_out = d->z_out; L->z_res = d->z_res;
+    L->epi = d->epilogue; L->z_in = d->z_a; L->z_out = d->z_out; L->z_res = d->z_res; L->z_w = d->z_b;
     L->oh = 1; L->ow = d->m; L->m = d->m; L->k = d->k;
     if (d->m <= 0 || d->n <= 0 || d->k <= 0) return fail(IQNN_ERR_INVALID_ARG, "GEMM sizes must be positive");
     return check_layer(*L);
@@ -236,10 +253,12 @@ iqnn_status prepack_into(const Layer& L, const void* w_host, const float* bias_h
             int32_t v;
             if (L.w_type == T_INT8) {
                 v = (int8_t)wb[e];
+            } else if (L.w_type == T_UINT8) {
+                v = (int32_t)wb[e] - 128;   // held as q_W - 128
             } else {
                 uint8_t byte = wb[e >> 1];
                 v = (e & 1) ? (byte >> 4) : (byte & 0xF);
-                if (v >= 8) v -= 16;
+                if (L.w_type == T_INT4 && v >= 8) v -= 16;
             }
             row[(size_t)k] = v;
             sum += v;
@@ -257,10 +276,11 @@ iqnn_status prepack_into(const Layer& L, const void* w_host, const float* bias_h
                 return fail(IQNN_ERR_OVERFLOW, "quantized bias of channel %lld leaves int32", (long long)oc);
             bias_q = (int64_t)rb;
         }
-        const int64_t fold = bias_q + (shift - L.z_in) * sum;
+        const int64_t red = zw_red(L);   // nonzero only on the 8-bit streaming path (checked)
+        const int64_t fold = bias_q + (shift - L.z_in) * sum + L.k * (shift - L.z_in) * red;
         if (fold < INT32_MIN || fold > INT32_MAX)
             return fail(IQNN_ERR_OVERFLOW, "folded bias of channel %lld leaves int32", (long long)oc);
-        if (mx * abs_sum + (fold < 0 ? -fold : fold) > INT32_MAX)
+        if (mx * abs_sum + (fold < 0 ? -fold : fold) + (red < 0 ? -red : red) * mx * L.k > INT32_MAX)
             return fail(IQNN_ERR_OVERFLOW, "accumulator of channel %lld may leave int32", (long long)oc);
         bias[oc] = (int32_t)fold;
         if (!raw) {
@@ -357,6 +377,7 @@ iqnn_status forward(const Layer& L, const void* x, const void* packed, const voi
     p.epi = L.epi;
     p.z_out = L.z_out;
     p.z_res = L.z_res;
+    p.zw_red = zw_red(L);
     if (L.epi != E_RAW) {
         int32_t lo, hi;
         code_range(L.y_type, &lo, &hi);

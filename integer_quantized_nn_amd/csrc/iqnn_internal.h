@@ -76,6 +76,7 @@ struct ConvParams {
     int32_t x_signed4;        // INT4 activations: sign-extend nibbles
     int32_t y_type, res_type, epi;
     int32_t z_out, z_res;
+    int32_t zw_red;           // s_w - Z_w: coefficient of the per-pixel activation sum (0: none)
     const float* m_res;       // residual multiplier S_res/S_out (in the packed buffer)
     const uint8_t* pad_row;   // 64 bytes of the raw input zero-point code (in the packed buffer)
     // Epilogue constants (host-computed).  The requantized value is clipped to

@@ -978,7 +978,11 @@ struct StreamCfg {
     static_assert(OCC <= LDS_FIT, "LDS for the requested occupancy");
 };
 
-template <class C, bool IS1X1, bool RES, bool C4, bool B4 = false>
+// ZW: asymmetric weights.  The per-pixel sum of the activation operands is kept next
+// to the contraction (one v_dot4 with ones per 16 bytes of a B fragment; lanes l and
+// l+32 hold the two K halves of pixel l%32) and zw_red times it is added to every
+// channel of the pixel before the epilogue.
+template <class C, bool IS1X1, bool RES, bool C4, bool B4 = false, bool ZW = false>
 __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) {
     constexpr int BM = C::BM, BN = C::BN, WM = C::WM, NST = C::NST;
     constexpr int TM = C::TM, TN = C::TN;
@@ -998,6 +1002,7 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
     static_assert(D * K_LOADS <= 60, "DMA in flight must fit the 6-bit vmcnt");
     static_assert(R_INST <= K_LOADS, "a residual tile fits one stage");
     static_assert(!(RES && C4), "the 4-channel gather has no residual stage");
+    static_assert(!(ZW && (B4 || C4)), "the per-pixel weight zero-point term needs the 8-bit gather");
     static_assert(!RES || RROW == 32 || RROW == 64 || RROW == 128, "residual rows of 2, 4 or 8 chunks");
 
     __shared__ __attribute__((aligned(1024))) uint8_t ring[NST * STAGE];
@@ -1214,7 +1219,12 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
     // accumulators start from the folded bias of their channels: lane half h of channel
     // block t holds channels ocl(t) .. ocl(t)+15 of the block
     v16i acc[TM][TN];
+    int32_t ssum[ZW ? TN : 1];
     auto init_acc = [&]() {
+        if constexpr (ZW) {
+#pragma unroll
+            for (int u = 0; u < TN; ++u) ssum[u] = 0;
+        }
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
             const int ocl = wave_oc * C::WOC + t * 32 + (lane >> 5) * 16;
@@ -1263,6 +1273,10 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
                 fb[u][2] = (int)unpack_lo(w1, x_signed4); fb[u][3] = (int)unpack_hi(w1, x_signed4);
             } else {
                 fb[u][0] ^= bxor; fb[u][1] ^= bxor; fb[u][2] ^= bxor; fb[u][3] ^= bxor;
+                if constexpr (ZW) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ssum[u] = __builtin_amdgcn_sdot4(fb[u][i], 0x01010101, ssum[u], false);
+                }
             }
         }
     };
@@ -1323,6 +1337,16 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
         // -------------------------------------------------------- epilogue of tile j
         const int64_t px0 = tile_px0(j);
         const uint8_t* rtile = ring + cur_off;   // the R-stage, synced above
+        if constexpr (ZW) {
+#pragma unroll
+            for (int u = 0; u < TN; ++u) {
+                const int32_t red = p.zw_red * (ssum[u] + __shfl_xor(ssum[u], 32));
+#pragma unroll
+                for (int t = 0; t < TM; ++t)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) acc[t][u][q] += red;
+            }
+        }
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
             const int ocl = wave_oc * C::WOC + t * 32 + (lane >> 5) * 16;   // channel inside the block
@@ -1364,7 +1388,7 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
 
 template <class C>
 hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bool c4, hipStream_t stream,
-                         bool b4 = false) {
+                         bool b4 = false, bool zw = false) {
     ConvParams q = p;
     q.n_oc_tiles = (p.c_out + C::BM - 1) / C::BM;
     const int64_t n_px = (p.m + C::BN - 1) / C::BN;
@@ -1386,6 +1410,19 @@ hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bo
             else if (is_1x1) hipLaunchKernelGGL((qconv_stream<C, true, false, false, true>), g, b, 0, stream, q);
             else if (add) hipLaunchKernelGGL((qconv_stream<C, false, true, false, true>), g, b, 0, stream, q);
             else hipLaunchKernelGGL((qconv_stream<C, false, false, false, true>), g, b, 0, stream, q);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
+    if (zw) {   // asymmetric weights: the 64x256 and 128x128 configurations only
+        if constexpr (C::OCC < 3 && ((C::BN == 256 && C::BM == 64 && C::NST == 3) ||
+                                     (C::BN == 128 && C::BM == 128 && C::NST == 4))) {
+            const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;
+            if (c4 || (add && !res_prefetch)) return hipErrorInvalidValue;
+            if (is_1x1 && add) hipLaunchKernelGGL((qconv_stream<C, true, true, false, false, true>), g, b, 0, stream, q);
+            else if (is_1x1) hipLaunchKernelGGL((qconv_stream<C, true, false, false, false, true>), g, b, 0, stream, q);
+            else if (add) hipLaunchKernelGGL((qconv_stream<C, false, true, false, false, true>), g, b, 0, stream, q);
+            else hipLaunchKernelGGL((qconv_stream<C, false, false, false, false, true>), g, b, 0, stream, q);
             return hipGetLastError();
         }
         return hipErrorInvalidValue;
@@ -1608,6 +1645,14 @@ hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_
     if (gather == GATHER_B4S) {   // its packed layout is the streaming kernel's: no other tile
         if (p.c_out <= 64) return launch_stream<S64x128d6>(p, is_1x1, true, false, stream, true);
         return launch_stream<S128x128d4>(p, is_1x1, true, false, stream, true);
+    }
+    if (p.zw_red != 0) {   // asymmetric weights ride on the streaming kernel only
+        const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;
+        const bool res_prefetch = add && p.vec_store && (p.res_type == T_INT8 || p.res_type == T_UINT8);
+        if (gather != GATHER_B8 || !pipe_eligible(gather, p.c, p.k) || (add && !res_prefetch))
+            return hipErrorInvalidValue;
+        if (p.c_out <= 64) return launch_stream<S64x256d3>(p, is_1x1, res_prefetch, false, stream, false, true);
+        return launch_stream<S128x128d4>(p, is_1x1, res_prefetch, false, stream, false, true);
     }
     if (pipe_eligible(gather, p.c, p.k)) {
         const bool c4 = gather == GATHER_C4;

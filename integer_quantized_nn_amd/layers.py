@@ -94,13 +94,13 @@ class QConv:
 
     def __init__(self, n, h, w, c_in, c_out, k, stride, pad, x_type, w_type, y_type, epi, z_in, z_out,
                  w_bytes, bias, s_in, s_w, s_out, res_type=B.UINT8, z_res=0, s_res=1.0, kw=None,
-                 device="cuda", stream=None):
+                 device="cuda", stream=None, z_w=0):
         kw = k if kw is None else kw
         d = B.ConvDesc()
         d.n, d.h, d.w, d.c_in, d.c_out = n, h, w, c_in, c_out
         d.kh, d.kw, d.stride_h, d.stride_w, d.pad_h, d.pad_w = k, kw, stride, stride, pad, pad
         d.x_type, d.w_type, d.y_type, d.res_type, d.epilogue = x_type, w_type, y_type, res_type, epi
-        d.z_in, d.z_out, d.z_res = z_in, z_out, z_res
+        d.z_in, d.z_out, d.z_res, d.z_w = z_in, z_out, z_res, z_w
         self.desc = d
         self.out_shape = (n,) + d.out_hw() + (c_out,)
         s_w = np.atleast_1d(np.asarray(s_w, np.float32))
@@ -119,11 +119,11 @@ class QGemm:
     """One prepacked quantized GEMM: C[M][N] = epilogue(A[M][K] B[N][K]^T)."""
 
     def __init__(self, m, n, k, a_type, b_type, c_type, epi, z_a, z_out, b_bytes, bias, s_a, s_b, s_out,
-                 res_type=B.UINT8, z_res=0, s_res=1.0, device="cuda", stream=None):
+                 res_type=B.UINT8, z_res=0, s_res=1.0, device="cuda", stream=None, z_b=0):
         d = B.GemmDesc()
         d.m, d.n, d.k = m, n, k
         d.a_type, d.b_type, d.c_type, d.res_type, d.epilogue = a_type, b_type, c_type, res_type, epi
-        d.z_a, d.z_out, d.z_res = z_a, z_out, z_res
+        d.z_a, d.z_out, d.z_res, d.z_b = z_a, z_out, z_res, z_b
         self.desc = d
         self.out_shape = (m, n)
         s_b = np.atleast_1d(np.asarray(s_b, np.float32))

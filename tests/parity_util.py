@@ -72,24 +72,28 @@ def conv_codes(case):
     return x, w, res
 
 
-def oracle_conv(case, x, w, res, images=None):
-    """Oracle output codes (int32) for the given images (default: all)."""
+def oracle_conv(case, x, w, res, images=None, z_w=0, s_w=None):
+    """Oracle output codes (int32) for the given images (default: all).  z_w / s_w:
+    weight zero point and scale when the weight codes are not case.w_type symmetric."""
     if images is not None:
         x = x[images]
         res = res[images] if res is not None else None
-    return O.qconv(x, case.z_in, case.s_in, w, case.s_w, case.bias, case.s_out, case.z_out,
-                   otype(case.y_type), oepi(case.epi), case.stride, case.pad, res, case.s_res, case.z_res)
+    return O.qconv(x, case.z_in, case.s_in, w, case.s_w if s_w is None else s_w, case.bias, case.s_out,
+                   case.z_out, otype(case.y_type), oepi(case.epi), case.stride, case.pad, res, case.s_res,
+                   case.z_res, z_w=z_w)
 
 
-def gpu_conv(case, x, w, res, stream=None):
+def gpu_conv(case, x, w, res, stream=None, w_type=None, z_w=0, s_w=None):
     """libiqnn output bytes (numpy) for the whole batch."""
     import torch
     from integer_quantized_nn_amd.layers import QConv
     n, h, wd, ci = x.shape
     co, kh, kw, _ = w.shape
-    conv = QConv(n, h, wd, ci, co, kh, case.stride, case.pad, case.x_type, case.w_type, case.y_type, case.epi,
-                 case.z_in, case.z_out, to_bytes(w, case.w_type), case.bias, case.s_in, case.s_w, case.s_out,
-                 res_type=case.res_type, z_res=case.z_res, s_res=case.s_res, kw=kw, stream=stream)
+    wt = case.w_type if w_type is None else w_type
+    conv = QConv(n, h, wd, ci, co, kh, case.stride, case.pad, case.x_type, wt, case.y_type, case.epi,
+                 case.z_in, case.z_out, to_bytes(w, wt), case.bias, case.s_in, case.s_w if s_w is None else s_w,
+                 case.s_out, res_type=case.res_type, z_res=case.z_res, s_res=case.s_res, kw=kw, stream=stream,
+                 z_w=z_w)
     xd = torch.from_numpy(to_bytes(x, case.x_type)).cuda()
     rd = torch.from_numpy(to_bytes(res, case.res_type)).cuda() if res is not None else None
     y = conv(xd, res=rd, stream=stream)

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert B.iqnn_abi_version() == 1
+    assert B.iqnn_abi_version() == 2
     assert lib.iqnn_status_str(0) == b"IQNN_OK"
     assert lib.iqnn_status_str(4) == b"IQNN_ERR_OVERFLOW"
 
@@ -52,7 +52,7 @@ def conv_desc(**kw):
     d = B.ConvDesc()
     base = dict(n=1, h=8, w=8, c_in=16, c_out=32, kh=3, kw=3, stride_h=1, stride_w=1, pad_h=1, pad_w=1,
                 x_type=B.UINT8, w_type=B.INT8, y_type=B.UINT8, res_type=B.UINT8, epilogue=B.EPI_RELU,
-                z_in=3, z_out=5, z_res=0)
+                z_in=3, z_out=5, z_res=0, z_w=0)
     base.update(kw)
     for k, v in base.items():
         setattr(d, k, v)
@@ -61,7 +61,12 @@ def conv_desc(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(n=0), 1), (dict(c_out=0), 1), (dict(kh=11, pad_h=0), 1), (dict(x_type=7), 1),
-    (dict(w_type=B.UINT8), 1), (dict(y_type=B.INT32), 1), (dict(epilogue=B.EPI_RAW_INT32), 1),
+    (dict(w_type=9), 1), (dict(w_type=B.UINT8, z_w=256), 1), (dict(w_type=B.INT4, z_w=8), 1),
+    # a weight zero point other than the kernel's weight shift needs the streaming path
+    (dict(w_type=B.UINT8), 2), (dict(w_type=B.INT8, z_w=5), 2),
+    (dict(x_type=B.UINT4, c_in=64, w_type=B.UINT4, z_w=3), 2),
+    (dict(c_in=64, w_type=B.UINT8, z_w=7, epilogue=B.EPI_ADD, res_type=B.UINT4), 2),
+    (dict(y_type=B.INT32), 1), (dict(epilogue=B.EPI_RAW_INT32), 1),
     (dict(z_in=300), 1), (dict(z_out=-1), 1), (dict(x_type=B.UINT4, c_in=8, z_in=3), 2),
     (dict(epilogue=B.EPI_ADD, res_type=9), 1), (dict(y_type=B.UINT4, c_out=33, z_out=1), 1),
     (dict(stride_h=0), 1), (dict(pad_w=-1), 1),
@@ -172,6 +177,44 @@ def test_host_prepack_matches_oracle_qparams(lib, x_type, w_type, c_in, c_out, e
     for q in (xlo, z_in, xhi):
         lhs = (q - z_in) * w.reshape(c_out, -1).astype(np.int64).sum(1) + bq
         rhs = (q - shift) * w.reshape(c_out, -1).astype(np.int64).sum(1) + fold.astype(np.int64)
+        assert np.array_equal(lhs, rhs)
+
+
+@pytest.mark.parametrize("x_type,w_type,z_w,c_in,epi", [
+    (B.UINT8, B.UINT8, 131, 64, B.EPI_RELU),
+    (B.INT8, B.UINT8, 0, 128, B.EPI_NONE),
+    (B.UINT8, B.INT8, -7, 64, B.EPI_ADD_RELU),
+    (B.UINT8, B.UINT4, 6, 64, B.EPI_RELU),
+    (B.UINT8, B.UINT8, 128, 16, B.EPI_RELU),   # z_w == the weight shift: no per-pixel term, any path
+])
+def test_host_prepack_asymmetric_weights(lib, x_type, w_type, z_w, c_in, epi):
+    # MegEngine 4-bit article, section 緩解精度下降: with Z_W != 0 only the Z_I and Z_I*Z_W
+    # terms are known before inference; the Z_W * sum Q(I) term stays per pixel.
+    rng = np.random.default_rng(c_in + 7 * z_w % 1000)
+    c_out = 48
+    lo, hi = O.qrange(otype(w_type))
+    w = rng.integers(lo, hi + 1, size=(c_out, 3, 3, c_in)).astype(np.int32)
+    xlo, xhi = O.qrange(otype(x_type))
+    z_in = int(rng.integers(xlo, xhi + 1)) if x_type == B.UINT8 else -5
+    s_in, s_out, s_res = np.float32(0.02), np.float32(0.09), np.float32(0.04)
+    s_w = rng.uniform(0.001, 0.01, c_out).astype(np.float32)
+    bias = rng.normal(0, 0.3, c_out).astype(np.float32)
+    d = conv_desc(x_type=x_type, w_type=w_type, z_w=z_w, c_in=c_in, c_out=c_out, epilogue=epi, z_in=z_in,
+                  y_type=B.UINT8, z_out=2, res_type=B.UINT8, z_res=9)
+    buf = _host_pack(d, w, w_type, bias, s_in, s_w, s_out, s_res)
+    fold, mult, _, wl, _ = _unpack_layout(buf, c_out, 9 * c_in, False)
+    s_w_shift = 128 if w_type == B.UINT8 else 0
+    assert np.array_equal(wl.astype(np.int32), w.reshape(c_out, -1) - s_w_shift)
+    assert np.array_equal(mult, O.requant_multiplier(s_in, s_w, s_out))
+    # every tap reads q: sum_k (q - Z_in)(w - Z_w) + bias_q
+    #   == sum_k (q - s)(w - s_w) + fold + (s_w - Z_w) * K * (q - s)
+    s = 128 if x_type == B.UINT8 else 0
+    k = 9 * c_in
+    bq = O.quantize_bias(bias, s_in, s_w).astype(np.int64)
+    wf = w.reshape(c_out, -1).astype(np.int64)
+    for q in (xlo, z_in, xhi):
+        lhs = (q - z_in) * (wf - z_w).sum(1) + bq
+        rhs = (q - s) * (wf - s_w_shift).sum(1) + fold.astype(np.int64) + (s_w_shift - z_w) * k * (q - s)
         assert np.array_equal(lhs, rhs)
 
 
