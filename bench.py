@@ -144,20 +144,7 @@ def bench_trunk(args):
           for _ in range(args.steps)]
 
     def timed_step(evs):
-        from integer_quantized_nn_amd import binding as B
-        from integer_quantized_nn_amd.layers import dequantize, maxpool2d, quantize_pad
-        b = net.bufs
-        quantize_pad(x, net.in_scale, net.in_zp, B.UINT8, net.stem_pad, 4, out=b["input"])
-        for i, layer in enumerate(tr.layers):
-            conv = net.convs[layer.name]
-            res = b[layer.res_src] if layer.res_src is not None else None
-            evs[i][0].record(stream)
-            conv(b[layer.src], res=res, out=b[layer.out])
-            evs[i][1].record(stream)
-            if layer.name == "stem":
-                n, h, w, c = net.shapes["stem"]
-                maxpool2d(b["stem"], n, h, w, c, 3, 2, 1, B.UINT8, out=b["pool"])
-        dequantize(b[net.final], net.shapes[net.final], net.final_scale, net.final_zp, B.UINT8, out=net.out_f32)
+        net.step(x, events=evs)
 
     # eager steps with per-conv events: the launch durations for the roofline
     torch.cuda.synchronize()
@@ -215,7 +202,8 @@ def bench_trunk(args):
         "config": {"workload": "resnet50_trunk_b%d" % args.batch, "batch": args.batch, "image_hw": 224,
                    "convs": n_conv, "ops_per_step": step_ops,
                    "activations": "uint8 asymmetric per-tensor", "weights": "int8 per-channel symmetric",
-                   "step": "quantize fp32 input, 53 fused convs + max pooling, dequantize output"},
+                   "step": "quantize fp32 input, 53 fused convs + max pooling (fused with the stem), "
+                           "dequantize output"},
         "pct_int8_mfma_peak": value * 1e12 / PEAK_INT8_OPS,
         "roofline": roof,
         "conv_time_share": float(dur.sum() / args.steps / (ms_per_step * 1e-3)),

@@ -249,6 +249,21 @@ iqnn_status iqnn_qconv_fwd(const iqnn_conv_desc *desc, const void *x_dev,
                            const void *packed_dev, const void *res_dev, void *y_dev,
                            void *stream);
 
+/* Quantized conv followed by max pooling of its output codes, fused: the conv's
+ * output is never written, only y_dev = maxpool(conv(x)) [N][PH][PW][C_out] with
+ * PH = (OH + 2*pool_pad - pool_k)/pool_stride + 1, PW likewise.  Max pooling is
+ * passive on codes ("Quantization" blog, 量化激活函数; the stem -> pooling step of
+ * the ResNet-50 graph in the MegEngine 4-bit article, 算子融合優化, Fig. 3), so the
+ * bytes equal iqnn_qconv_fwd followed by iqnn_maxpool2d.  Supported: the image stem
+ * shape class -- 8-bit activations with C_in == 4 and no padding (an input from
+ * iqnn_quantize_pad), stride 2, KH <= 8, KW <= 8, C_out == 64 with 8-bit codes,
+ * Conv or Conv_Relu, symmetric weights (or z_w equal to the weight shift), OH even,
+ * OW % 16 == 0, OW <= 128, pool 3x3 stride 2 padding 1; IQNN_ERR_UNSUPPORTED
+ * otherwise (validated before any launch).  Alignment: x, y 16 bytes; packed 256. */
+iqnn_status iqnn_qconv_maxpool_fwd(const iqnn_conv_desc *desc, const void *x_dev,
+                                   const void *packed_dev, void *y_dev, int32_t pool_k,
+                                   int32_t pool_stride, int32_t pool_pad, void *stream);
+
 /* ---------------------------------------------------------------------- GEMM */
 
 size_t iqnn_qgemm_packed_size(const iqnn_gemm_desc *desc);

@@ -69,6 +69,7 @@ def lib():
         "iqnn_qconv_prepack": (I, [CD, P, P, F, P, I, F, F, P, SZ, P]),
         "iqnn_qconv_prepack_host": (I, [CD, P, P, F, P, I, F, F, P, SZ]),
         "iqnn_qconv_fwd": (I, [CD, P, P, P, P, P]),
+        "iqnn_qconv_maxpool_fwd": (I, [CD, P, P, P, I32, I32, I32, P]),
         "iqnn_qgemm_packed_size": (SZ, [GD]),
         "iqnn_qgemm_prepack": (I, [GD, P, P, F, P, I, F, F, P, SZ, P]),
         "iqnn_qgemm_prepack_host": (I, [GD, P, P, F, P, I, F, F, P, SZ]),
@@ -166,6 +167,11 @@ def iqnn_qconv_prepack_host(desc, w_host, bias_host, s_in, s_w_host, per_channel
 
 def iqnn_qconv_fwd(desc, x, packed, res, y, stream=None):
     _check(lib().iqnn_qconv_fwd(ctypes.byref(desc), _dev(x), _dev(packed), _dev(res), _dev(y), _stream(stream, y)))
+
+
+def iqnn_qconv_maxpool_fwd(desc, x, packed, y, pool_k, pool_stride, pool_pad, stream=None):
+    _check(lib().iqnn_qconv_maxpool_fwd(ctypes.byref(desc), _dev(x), _dev(packed), _dev(y), pool_k, pool_stride,
+                                        pool_pad, _stream(stream, y)))
 
 
 def iqnn_qgemm_packed_size(desc):

@@ -338,17 +338,11 @@ iqnn_status prepack_dev(const Layer& L, const void* w_host, const float* bias_ho
     return ok();
 }
 
-iqnn_status forward(const Layer& L, const void* x, const void* packed, const void* res, void* y, hipStream_t stream) {
+// Kernel parameters of a validated layer and its pointers.
+void conv_params(const Layer& L, const void* x, const void* packed, const void* res, void* y, ConvParams& p) {
     const bool add = L.epi == E_ADD || L.epi == E_ADD_RELU;
-    if (!x || !packed || !y) return fail(IQNN_ERR_INVALID_ARG, "null input, packed or output pointer");
-    if (add && !res) return fail(IQNN_ERR_INVALID_ARG, "ADD / ADD_RELU epilogue needs a residual");
-    if (!aligned(x, 16) || !aligned(y, 16) || (add && !aligned(res, 16)))
-        return fail(IQNN_ERR_ALIGNMENT, "activation, output and residual pointers must be 16-byte aligned");
-    if (!aligned(packed, 256)) return fail(IQNN_ERR_ALIGNMENT, "packed buffer must be 256-byte aligned");
     const PackGeom g = pack_geom(L.c_out, kdim(L));
     const bool c4 = c4_path(L);
-
-    ConvParams p;
     std::memset(&p, 0, sizeof p);
     p.x = static_cast<const uint8_t*>(x);
     p.w = reinterpret_cast<const int8_t*>(static_cast<const uint8_t*>(packed) + g.w_off);
@@ -395,11 +389,48 @@ iqnn_status forward(const Layer& L, const void* x, const void* packed, const voi
         p.res_xor = L.res_type == T_INT8 ? 0x80808080u : (L.res_type == T_INT4 ? 0x88888888u : 0u);
     }
     p.vec_store = L.c_out % 16 == 0;
+}
+
+iqnn_status forward(const Layer& L, const void* x, const void* packed, const void* res, void* y, hipStream_t stream) {
+    const bool add = L.epi == E_ADD || L.epi == E_ADD_RELU;
+    if (!x || !packed || !y) return fail(IQNN_ERR_INVALID_ARG, "null input, packed or output pointer");
+    if (add && !res) return fail(IQNN_ERR_INVALID_ARG, "ADD / ADD_RELU epilogue needs a residual");
+    if (!aligned(x, 16) || !aligned(y, 16) || (add && !aligned(res, 16)))
+        return fail(IQNN_ERR_ALIGNMENT, "activation, output and residual pointers must be 16-byte aligned");
+    if (!aligned(packed, 256)) return fail(IQNN_ERR_ALIGNMENT, "packed buffer must be 256-byte aligned");
+    const bool c4 = c4_path(L);
+    ConvParams p;
+    conv_params(L, x, packed, res, y, p);
     const int gather = is_4bit(L.x_type) ? (b4_stream(L) ? GATHER_B4S : GATHER_B4)
                                           : (L.c % 16 == 0 ? GATHER_B8 : (c4 ? GATHER_C4 : GATHER_B8_ELEM));
     const bool is_1x1 = gather != GATHER_B8_ELEM && gather != GATHER_C4 && L.kh == 1 && L.kw == 1 && L.sh == 1 && L.sw == 1 &&
                         L.ph == 0 && L.pw == 0;
     hipError_t e = launch_qconv(p, gather, is_1x1, stream, forced_tile());
+    if (e != hipSuccess) return fail(IQNN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+// Convolution followed by max pooling of its codes, fused (the image stem's shape
+// class; see iqnn_qconv_maxpool_fwd).
+iqnn_status forward_pool(const Layer& L, const void* x, const void* packed, void* y_pool, int32_t pool_k,
+                         int32_t pool_stride, int32_t pool_pad, hipStream_t stream) {
+    if (!x || !packed || !y_pool) return fail(IQNN_ERR_INVALID_ARG, "null input, packed or output pointer");
+    if (!aligned(x, 16) || !aligned(y_pool, 16))
+        return fail(IQNN_ERR_ALIGNMENT, "activation and output pointers must be 16-byte aligned");
+    if (!aligned(packed, 256)) return fail(IQNN_ERR_ALIGNMENT, "packed buffer must be 256-byte aligned");
+    if (pool_k != 3 || pool_stride != 2 || pool_pad != 1)
+        return fail(IQNN_ERR_UNSUPPORTED, "fused pooling is 3x3, stride 2, padding 1 only");
+    if (L.epi != E_NONE && L.epi != E_RELU)
+        return fail(IQNN_ERR_UNSUPPORTED, "fused pooling takes Conv / Conv_Relu epilogues");
+    if (!c4_path(L) || zw_red(L) != 0)
+        return fail(IQNN_ERR_UNSUPPORTED, "fused pooling needs the 4-channel padding-free stem input");
+    ConvParams p;
+    conv_params(L, x, packed, nullptr, nullptr, p);
+    if (!stem_pool_ok(p))
+        return fail(IQNN_ERR_UNSUPPORTED,
+                    "fused pooling needs a stride-2 stem with KH <= 8, 64 8-bit output channels, even OH, "
+                    "OW %% 16 == 0 and OW <= 128");
+    hipError_t e = launch_stem_pool(p, static_cast<uint8_t*>(y_pool), stream);
     if (e != hipSuccess) return fail(IQNN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }
@@ -519,6 +550,16 @@ iqnn_status iqnn_qconv_fwd(const iqnn_conv_desc* desc, const void* x_dev, const 
     iqnn_status s = conv_layer(desc, &L);
     if (s != IQNN_OK) return s;
     return forward(L, x_dev, packed_dev, res_dev, y_dev, static_cast<hipStream_t>(stream));
+}
+
+iqnn_status iqnn_qconv_maxpool_fwd(const iqnn_conv_desc* desc, const void* x_dev, const void* packed_dev,
+                                   void* y_dev, int32_t pool_k, int32_t pool_stride, int32_t pool_pad,
+                                   void* stream) {
+    Layer L;
+    iqnn_status s = conv_layer(desc, &L);
+    if (s != IQNN_OK) return s;
+    return forward_pool(L, x_dev, packed_dev, y_dev, pool_k, pool_stride, pool_pad,
+                        static_cast<hipStream_t>(stream));
 }
 
 size_t iqnn_qgemm_packed_size(const iqnn_gemm_desc* desc) {

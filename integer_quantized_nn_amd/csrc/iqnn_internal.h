@@ -97,6 +97,11 @@ struct ConvParams {
 // 0..4 force one (the IQNN_FORCE_TILE environment variable, for tuning sweeps).
 hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_t stream, int tile);
 
+// The image stem (4-channel padding-free input, stride 2) fused with 3x3 / stride 2 /
+// pad 1 max pooling of its codes into yp [N][OH/2][OW/2][64].
+bool stem_pool_ok(const ConvParams& p);
+hipError_t launch_stem_pool(const ConvParams& p, uint8_t* yp, hipStream_t stream);
+
 struct QuantParams {
     const float* x;
     uint8_t* q;

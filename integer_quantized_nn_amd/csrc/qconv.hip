@@ -129,6 +129,30 @@ __device__ __forceinline__ void load_res16(const ConvParams& p, int64_t oidx, in
     }
 }
 
+// The clip / round / zero-point tail of the epilogue below: b[j] holds output code j
+// in its low byte.
+__device__ __forceinline__ void round_codes16(const ConvParams& p, const float v[16], uint32_t b[16]) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        b[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_fmed3f(v[j], p.t_lo, p.t_hi) + p.out_magic);
+    if (p.out_fix) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) b[j] += 1u;
+    }
+}
+
+// The low bytes of b[0..15] as 16 consecutive bytes.
+__device__ __forceinline__ uint4 pack_bytes16(const uint32_t b[16]) {
+    uint32_t ow[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t lo2 = __builtin_amdgcn_perm(b[4 * d + 1], b[4 * d], 0x0C0C0400u);
+        const uint32_t hi2 = __builtin_amdgcn_perm(b[4 * d + 3], b[4 * d + 2], 0x0C0C0400u);
+        ow[d] = lo2 | (hi2 << 16);
+    }
+    return make_uint4(ow[0], ow[1], ow[2], ow[3]);
+}
+
 // Requantizing epilogue of 16 consecutive channels ocb..ocb+15 of output pixel pix,
 // strict binary32 with one rounding per operation:
 //   t = float(acc + bias) * M[c];   t = t + float(r - Z_res) * M_res   (ADD)
@@ -145,6 +169,9 @@ __device__ __forceinline__ void load_res16(const ConvParams& p, int64_t oidx, in
 // code in the low byte, two's complement for signed types; bytes are packed with
 // v_perm_b32, nibbles with shifts.
 //
+// BIAS: add bias[] here (otherwise the accumulator started from the folded bias).
+// ADDK: 0 = residual add decided by `add` and p.res_type at run time, 1 = always an
+// 8-bit residual, 2 = never a residual, 3 = always a 4-bit residual.
 template <bool BIAS = true, int ADDK = 0>
 __device__ __forceinline__ void epi_store16(const ConvParams& p, const v16i& acc, const int32_t* bias,
                                             const float* mult, uint32_t rw[4], int ocb, int64_t pix, bool add_rt,
@@ -180,23 +207,12 @@ __device__ __forceinline__ void epi_store16(const ConvParams& p, const v16i& acc
         }
     }
     uint32_t b[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-        b[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_fmed3f(v[j], p.t_lo, p.t_hi) + p.out_magic);
-    if (p.out_fix) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) b[j] += 1u;
-    }
+    round_codes16(p, v, b);
     if (p.y_type == T_INT8 || p.y_type == T_UINT8) {
-        uint32_t ow[4];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const uint32_t lo2 = __builtin_amdgcn_perm(b[4 * d + 1], b[4 * d], 0x0C0C0400u);
-            const uint32_t hi2 = __builtin_amdgcn_perm(b[4 * d + 3], b[4 * d + 2], 0x0C0C0400u);
-            ow[d] = lo2 | (hi2 << 16);
-        }
+        const uint4 pk = pack_bytes16(b);
+        const uint32_t ow[4] = {pk.x, pk.y, pk.z, pk.w};
         if (p.vec_store) {
-            *reinterpret_cast<uint4*>(p.y + oidx) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+            *reinterpret_cast<uint4*>(p.y + oidx) = pk;
         } else {
             for (int j = 0; j < 16 && ocb + j < p.c_out; ++j) p.y[oidx + j] = (uint8_t)(ow[j >> 2] >> (8 * (j & 3)));
         }
@@ -1597,7 +1613,232 @@ hipError_t launch_stem(const ConvParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ============================================================ stem + max pooling
+//
+// qconv_stem_pool: the stem convolution of qconv_stem followed by max pooling 3x3,
+// stride 2, padding 1 over its output codes, without writing the convolution's output
+// to memory.  Max pooling is passive on codes ("Quantization" blog, 量化激活函数), so
+// pooling the codes computed here -- the same contraction and the same epilogue
+// arithmetic as qconv_stem -- gives the bytes of pooling the stored stem output.
+// A workgroup owns pooled rows [r0, r1) of one image and NW = 2*OW/32 waves.  For
+// pooled row r it computes stem rows 2r and 2r+1 (wave w: pixels 32w..32w+31 of the
+// row pair, one MFMA block) into a ring of three LDS row slots (row sr in slot
+// sr % 3), where row 2r-1 is still held from row r-1 (at the start of a band it is
+// computed first), then pools row r out of LDS: thread t takes pooled pixel t/8,
+// channels 8(t%8)..8(t%8)+7.  The input rows of a row pair (one contiguous byte range)
+// are copied into LDS with 16-byte DMA kSpAhead pairs ahead, through a ring of
+// kSpAhead+1 slab buffers; every wave issues exactly kSpCpw(NW) DMA instructions per
+// slab (chunks past the end repeat the last chunk: the same bytes to the same place),
+// so "slab r landed" is vmcnt <= (kSpAhead-1)*kSpCpw while later slabs are in flight.
+constexpr int kSpBuf = 9216;       // LDS bytes per slab buffer
+constexpr int kSpAhead = 3;        // row pairs in flight
+constexpr int kSpSlabs = kSpAhead + 1;
+constexpr int kSpMaxOW = 128;      // stem output width limit (8 waves)
+constexpr int kSpCpw(int nw) { return (kSpBuf / 1024 + nw - 1) / nw; }
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+struct StemPoolArgs {
+    uint8_t* yp;                   // pooled output [N][PH][PW][64]
+    int32_t ph, pw;                // pooled height, width
+    int32_t band, n_bands;         // pooled rows per workgroup, workgroups per image
+    uint32_t bias;                 // 0x80808080 for signed codes (unsigned order == signed order)
+    int64_t in_bytes;              // size of the input tensor
+};
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 2) void qconv_stem_pool(const ConvParams p, const StemPoolArgs a) {
+    constexpr int CPW = kSpCpw(NW);
+    static_assert((kSpAhead - 1) * CPW <= 60, "DMA in flight must fit the 6-bit vmcnt");
+    __shared__ __attribute__((aligned(1024))) uint8_t slab[kSpSlabs][kSpBuf];
+    __shared__ __attribute__((aligned(16))) uint8_t rows[3][kSpMaxOW * 64];
+    __shared__ __attribute__((aligned(16))) int32_t cbias[64];
+    __shared__ __attribute__((aligned(16))) float cmult[64];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = (int)blockIdx.x / a.n_bands;
+    const int r0 = ((int)blockIdx.x - n * a.n_bands) * a.band;
+    const int r1 = min(a.ph, r0 + a.band);
+    if (r0 >= r1) return;
+    if (tid < 64) {
+        cbias[tid] = p.bias[tid];
+        cmult[tid] = p.mult[tid];
+    }
+    v4i wa[2][kStemKH];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ky = 0; ky < kStemKH; ++ky)
+            wa[t][ky] = ky < p.kh ? *reinterpret_cast<const v4i*>(p.w + (int64_t)(32 * t + (lane & 31)) * p.kp +
+                                                                  32 * ky + 16 * (lane >> 5))
+                                  : v4i{0, 0, 0, 0};
+    __syncthreads();
+
+    const int ow = p.ow, oh = p.oh;
+    const int64_t row_bytes = (int64_t)p.w_in * 4;
+    // copy input rows [2*sr0, 2*sr0 + nrows) of image n into slab buffer `buf`
+    auto issue = [&](int sr0, int nrows, int buf) {
+        const int64_t start = ((int64_t)n * p.h + 2 * (int64_t)sr0) * row_bytes;
+        const int64_t base = start & ~(int64_t)15;
+        const int chunks = (int)((start - base + nrows * row_bytes + 1023) >> 10);   // <= kSpBuf / 1024
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const int j = min(wave + i * NW, chunks - 1);
+            const int64_t off = base + j * 1024 + lane * 16;
+            const void* src = off + 16 <= a.in_bytes ? (const void*)(p.x + off) : (const void*)p.x;
+            dma16_run<1>(lds_addr(&slab[buf][0]) + j * 1024, &src);
+        }
+    };
+    // stem pixels (this lane's column of the wave's block) of the rows starting at sr0,
+    // from slab buffer `buf`, into the row slots; pixel indices >= limit are not stored
+    const int frow = lane & 31;
+    const uint32_t bxor = p.x_xor;
+    auto compute = [&](int sr0, int buf, int limit) {
+        if (wave * 32 >= limit) return;
+        const int idx = wave * 32 + frow;
+        const int dr = idx >= ow ? 1 : 0;
+        const int ox = idx - dr * ow;
+        const int64_t start = ((int64_t)n * p.h + 2 * (int64_t)sr0) * row_bytes;
+        const uint32_t b0 = (uint32_t)(start & 15) + (uint32_t)(2 * dr * row_bytes) + ox * 8 + 16 * (lane >> 5);
+        const uint2* sv = reinterpret_cast<const uint2*>(&slab[buf][0]);
+        v16i acc[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int ocl = t * 32 + (lane >> 5) * 16;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int4 bv = *reinterpret_cast<const int4*>(&cbias[ocl + 4 * q]);
+                acc[t][4 * q] = bv.x; acc[t][4 * q + 1] = bv.y; acc[t][4 * q + 2] = bv.z; acc[t][4 * q + 3] = bv.w;
+            }
+        }
+#pragma unroll
+        for (int ky = 0; ky < kStemKH; ++ky) {
+            if (ky < p.kh) {
+                const uint32_t ad = (b0 + ky * (uint32_t)row_bytes) >> 3;   // 8-byte units
+                const uint2 lo = sv[ad], hi = sv[ad + 1];
+                v4i fb = {(int)(lo.x ^ bxor), (int)(lo.y ^ bxor), (int)(hi.x ^ bxor), (int)(hi.y ^ bxor)};
+                acc[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wa[0][ky], fb, acc[0], 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wa[1][ky], fb, acc[1], 0, 0, 0);
+            }
+        }
+        if (idx >= limit) return;
+        uint8_t* dst = &rows[(sr0 + dr) % 3][ox * 64];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int ocb = t * 32 + (lane >> 5) * 16;
+            float v[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 mv = *reinterpret_cast<const float4*>(&cmult[ocb + 4 * q]);
+                v[4 * q] = (float)acc[t][4 * q] * mv.x;
+                v[4 * q + 1] = (float)acc[t][4 * q + 1] * mv.y;
+                v[4 * q + 2] = (float)acc[t][4 * q + 2] * mv.z;
+                v[4 * q + 3] = (float)acc[t][4 * q + 3] * mv.w;
+            }
+            uint32_t b[16];
+            round_codes16(p, v, b);
+            *reinterpret_cast<uint4*>(dst + ocb) = pack_bytes16(b);
+        }
+    };
+
+    const int kr = p.kh + 2;   // input rows of a stem row pair
+    if (r0 > 0) {   // stem row 2*r0 - 1, the band's first pooled row's upper tap row
+        issue(2 * r0 - 1, p.kh, 0);
+        IQNN_WAIT_VM_LGKM0(0);
+        __builtin_amdgcn_s_barrier();
+        compute(2 * r0 - 1, 0, ow);
+        __syncthreads();   // slab 0 is free again
+    }
+    for (int i = 0; i < kSpAhead && r0 + i < r1; ++i) issue(2 * (r0 + i), kr, (r0 + i) % kSpSlabs);
+    const int pc = tid >> 3, g8 = (tid & 7) * 8;   // pooled column, channel offset
+    for (int r = r0; r < r1; ++r) {
+        // this pair's slab has landed (the later ones may be in flight), every wave is
+        // done with the slab refilled below and with the row slots this pair overwrites
+        if (r + kSpAhead - 1 < r1) {
+            IQNN_WAIT_VM_LGKM0((kSpAhead - 1) * CPW);
+        } else {
+            IQNN_WAIT_VM_LGKM0(0);
+        }
+        __builtin_amdgcn_s_barrier();
+        if (r + kSpAhead < r1) issue(2 * (r + kSpAhead), kr, (r + kSpAhead) % kSpSlabs);
+        compute(2 * r, r % kSpSlabs, 2 * ow);
+        __syncthreads();
+        // max pooling of row r: rows 2r-1..2r+1, columns 2c-1..2c+1 inside the image
+        if (pc < a.pw) {
+            u16x2 me[2], mo[2];
+#pragma unroll
+            for (int d = 0; d < 2; ++d) { me[d] = u16x2{0, 0}; mo[d] = u16x2{0, 0}; }
+#pragma unroll
+            for (int dy = -1; dy <= 1; ++dy) {
+                const int sr = 2 * r + dy;
+                if (sr < 0 || sr >= oh) continue;
+                const uint8_t* rowp = &rows[sr % 3][0];
+#pragma unroll
+                for (int dx = -1; dx <= 1; ++dx) {
+                    const int sx = 2 * pc + dx;
+                    if (sx < 0 || sx >= ow) continue;
+                    const uint2 v = *reinterpret_cast<const uint2*>(rowp + sx * 64 + g8);
+                    const uint32_t vw[2] = {v.x ^ a.bias, v.y ^ a.bias};
+#pragma unroll
+                    for (int d = 0; d < 2; ++d) {
+                        me[d] = __builtin_elementwise_max(me[d], __builtin_bit_cast(u16x2, vw[d] & 0x00FF00FFu));
+                        mo[d] = __builtin_elementwise_max(mo[d], __builtin_bit_cast(u16x2, (vw[d] >> 8) & 0x00FF00FFu));
+                    }
+                }
+            }
+            uint32_t o[2];
+#pragma unroll
+            for (int d = 0; d < 2; ++d)
+                o[d] = (__builtin_bit_cast(uint32_t, me[d]) | (__builtin_bit_cast(uint32_t, mo[d]) << 8)) ^ a.bias;
+            *reinterpret_cast<uint2*>(a.yp + (((int64_t)n * a.ph + r) * a.pw + pc) * 64 + g8) = make_uint2(o[0], o[1]);
+        }
+    }
+    // no DMA may still be writing this workgroup's LDS when it ends
+    IQNN_WAIT_VM(0);
+}
+
 }  // namespace
+
+// The fused stem + pooling kernel's conditions: the stem kernel's (stem_ok), exactly
+// 64 output channels of 8-bit codes without residual, an even output height and a
+// width that is a multiple of 16 (a row pair is whole 32-pixel blocks) up to
+// kSpMaxOW, and the input rows of a stem row pair within one slab buffer.
+bool stem_pool_ok(const ConvParams& p) {
+    if (!stem_ok(p) || p.c_out != 64 || p.epi == E_RAW) return false;
+    if (p.y_type != T_UINT8 && p.y_type != T_INT8) return false;
+    if (p.oh % 2 != 0 || p.ow % 16 != 0 || p.ow > kSpMaxOW) return false;
+    return (int64_t)(p.kh + 2) * p.w_in * 4 + 16 <= kSpBuf;
+}
+
+hipError_t launch_stem_pool(const ConvParams& p, uint8_t* yp, hipStream_t stream) {
+    if (!stem_pool_ok(p)) return hipErrorInvalidValue;
+    const int64_t n_img = p.m / ((int64_t)p.oh * p.ow);
+    if (n_img <= 0) return hipSuccess;
+    StemPoolArgs a;
+    a.yp = yp;
+    a.ph = p.oh / 2;
+    a.pw = p.ow / 2;
+    a.n_bands = 2;   // two workgroups per image: about two per CU at batch 256
+    a.band = (a.ph + a.n_bands - 1) / a.n_bands;
+    a.bias = p.y_type == T_INT8 ? 0x80808080u : 0u;
+    a.in_bytes = n_img * p.h * (int64_t)p.w_in * 4;
+    const int64_t grid = n_img * a.n_bands;
+    if (grid >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    const dim3 g((unsigned)grid), b((unsigned)(4 * p.ow));
+    switch (p.ow / 16) {   // waves: 2*OW/32
+    case 1: hipLaunchKernelGGL(qconv_stem_pool<1>, g, b, 0, stream, p, a); break;
+    case 2: hipLaunchKernelGGL(qconv_stem_pool<2>, g, b, 0, stream, p, a); break;
+    case 3: hipLaunchKernelGGL(qconv_stem_pool<3>, g, b, 0, stream, p, a); break;
+    case 4: hipLaunchKernelGGL(qconv_stem_pool<4>, g, b, 0, stream, p, a); break;
+    case 5: hipLaunchKernelGGL(qconv_stem_pool<5>, g, b, 0, stream, p, a); break;
+    case 6: hipLaunchKernelGGL(qconv_stem_pool<6>, g, b, 0, stream, p, a); break;
+    case 7: hipLaunchKernelGGL(qconv_stem_pool<7>, g, b, 0, stream, p, a); break;
+    case 8: hipLaunchKernelGGL(qconv_stem_pool<8>, g, b, 0, stream, p, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 bool pipe_eligible(int gather, int32_t c, int64_t k) {
     return (gather == GATHER_B8 && c % 64 == 0 && k % kPipeBK == 0) || gather == GATHER_C4;

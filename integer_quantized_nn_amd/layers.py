@@ -114,6 +114,17 @@ class QConv:
         B.iqnn_qconv_fwd(self.desc, x, self.packed, res, out, stream)
         return out
 
+    def pool_shape(self, k=3, stride=2, pad=1):
+        n, oh, ow, c = self.out_shape
+        return (n, (oh + 2 * pad - k) // stride + 1, (ow + 2 * pad - k) // stride + 1, c)
+
+    def conv_maxpool(self, x, k=3, stride=2, pad=1, out=None, stream=None):
+        """maxpool(conv(x)) in one fused launch (iqnn_qconv_maxpool_fwd)."""
+        if out is None:
+            out = empty_codes(self.pool_shape(k, stride, pad), self.y_type, x.device)
+        B.iqnn_qconv_maxpool_fwd(self.desc, x, self.packed, out, k, stride, pad, stream)
+        return out
+
 
 class QGemm:
     """One prepacked quantized GEMM: C[M][N] = epilogue(A[M][K] B[N][K]^T)."""

@@ -25,10 +25,13 @@ class QuantResNet50Trunk:
     channels at a time.  A zero weight on the extra channel and the real-0 border make
     it the same convolution as the 3-channel padded one."""
 
-    def __init__(self, trunk, device="cuda", weight_codes=None, stream=None):
+    def __init__(self, trunk, device="cuda", weight_codes=None, stream=None, fuse_stem_pool=True):
         """trunk: synth.Trunk.  weight_codes: optional {layer name: OHWI int8 bytes};
-        by default the float weights are quantized per output channel on the GPU."""
+        by default the float weights are quantized per output channel on the GPU.
+        fuse_stem_pool: run the stem and the max pooling as one launch
+        (iqnn_qconv_maxpool_fwd), never writing the stem's output."""
         self.trunk = trunk
+        self.fuse_stem_pool = fuse_stem_pool
         self.device = device
         n = trunk.batch
         self.convs = {}
@@ -57,7 +60,8 @@ class QuantResNet50Trunk:
             if layer.name == "stem":
                 oh, ow = conv.out_shape[1:3]
                 self.shapes["pool"] = (n, (oh + 2 - 3) // 2 + 1, (ow + 2 - 3) // 2 + 1, co)
-        self.bufs = {name: empty_codes(shape, B.UINT8, device) for name, shape in self.shapes.items()}
+        self.bufs = {name: empty_codes(shape, B.UINT8, device) for name, shape in self.shapes.items()
+                     if not (fuse_stem_pool and name == "stem")}
         self.final = trunk.layers[-1].out
         s_f, z_f = trunk.qparams[self.final]
         self.final_scale = torch.tensor([s_f], dtype=torch.float32, device=device)
@@ -66,23 +70,32 @@ class QuantResNet50Trunk:
         self.in_zp = torch.tensor([trunk.z_in], dtype=torch.int32, device=device)
         self.out_f32 = torch.empty(self.shapes[self.final], dtype=torch.float32, device=device)
 
-    def run_codes(self, stream=None):
-        """53 convs + max pooling on the codes already in bufs['input']."""
+    def run_codes(self, stream=None, events=None):
+        """53 convs + max pooling on the codes already in bufs['input'].  events: optional
+        list of (start, end) torch events per conv, recorded around its launch (the stem's
+        launch includes the pooling when fused)."""
         b = self.bufs
-        for layer in self.trunk.layers:
+        for i, layer in enumerate(self.trunk.layers):
             conv = self.convs[layer.name]
             res = b[layer.res_src] if layer.res_src is not None else None
-            conv(b[layer.src], res=res, out=b[layer.out], stream=stream)
-            if layer.name == "stem":
+            if events is not None:
+                events[i][0].record()
+            if layer.name == "stem" and self.fuse_stem_pool:
+                conv.conv_maxpool(b[layer.src], 3, 2, 1, out=b["pool"], stream=stream)
+            else:
+                conv(b[layer.src], res=res, out=b[layer.out], stream=stream)
+            if events is not None:
+                events[i][1].record()
+            if layer.name == "stem" and not self.fuse_stem_pool:
                 n, h, w, c = self.shapes["stem"]
                 maxpool2d(b["stem"], n, h, w, c, 3, 2, 1, B.UINT8, out=b["pool"], stream=stream)
         return b[self.final]
 
-    def step(self, x_f32, stream=None):
+    def step(self, x_f32, stream=None, events=None):
         """One full forward: quantize -> trunk -> dequantize.  Returns fp32 NHWC output."""
         quantize_pad(x_f32, self.in_scale, self.in_zp, B.UINT8, self.stem_pad, STEM_PAD_CHANNELS,
                      out=self.bufs["input"], stream=stream)
-        self.run_codes(stream)
+        self.run_codes(stream, events)
         dequantize(self.bufs[self.final], self.shapes[self.final], self.final_scale, self.final_zp, B.UINT8,
                    out=self.out_f32, stream=stream)
         return self.out_f32
@@ -118,11 +131,14 @@ class QuantResNet50Trunk:
             oh = (h + 2 * c.pad - kh) // c.stride + 1
             ow = (w + 2 * c.pad - kw) // c.stride + 1
             ops = 2 * n * oh * ow * co * kh * kw * ci
-            by = n * h * w * ci + co * kh * kw * ci + n * oh * ow * co
+            out_elems = n * oh * ow * co
+            if layer.name == "stem" and self.fuse_stem_pool:
+                out_elems = int(np.prod(self.shapes["pool"]))   # only the pooled codes are written
+            by = n * h * w * ci + co * kh * kw * ci + out_elems
             if layer.res_src is not None:
                 by += n * oh * ow * co
             out.append(("qconv:" + layer.name, ops, by))
-            if layer.name == "stem":
+            if layer.name == "stem" and not self.fuse_stem_pool:
                 _, sh, sw, sc = self.shapes["stem"]
                 out.append(("maxpool", 0, n * sh * sw * sc + int(np.prod(self.shapes["pool"]))))
         n_out = int(np.prod(self.shapes[self.final]))

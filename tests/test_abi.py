@@ -91,6 +91,22 @@ def test_forward_argument_errors_before_launch(lib):
     assert "null" in lib.iqnn_last_error().decode()
 
 
+def test_fused_conv_pool_rejects_other_shapes_before_launch(lib):
+    P = ctypes.c_void_p
+    stem = conv_desc(n=2, h=38, w=38, c_in=4, c_out=64, kh=7, kw=7, stride_h=2, stride_w=2, pad_h=0, pad_w=0)
+    d = conv_desc()   # a 3x3 16-channel layer: not the stem shape class
+    assert lib.iqnn_qconv_maxpool_fwd(ctypes.byref(d), P(4096), P(4096), P(4096), 3, 2, 1, None) == 2
+    assert "stem" in lib.iqnn_last_error().decode()
+    assert lib.iqnn_qconv_maxpool_fwd(ctypes.byref(stem), P(4096), P(4096), P(4096), 2, 2, 0, None) == 2
+    d = conv_desc(n=2, h=38, w=38, c_in=4, c_out=32, kh=7, kw=7, stride_h=2, stride_w=2, pad_h=0, pad_w=0)
+    assert lib.iqnn_qconv_maxpool_fwd(ctypes.byref(d), P(4096), P(4096), P(4096), 3, 2, 1, None) == 2
+    d = conv_desc(n=2, h=38, w=38, c_in=4, c_out=64, kh=7, kw=7, stride_h=2, stride_w=2, pad_h=0, pad_w=0,
+                  epilogue=B.EPI_ADD_RELU)
+    assert lib.iqnn_qconv_maxpool_fwd(ctypes.byref(d), P(4096), P(4096), P(4096), 3, 2, 1, None) == 2
+    assert lib.iqnn_qconv_maxpool_fwd(ctypes.byref(stem), P(4100), P(4096), P(4096), 3, 2, 1, None) == 3
+    assert lib.iqnn_qconv_maxpool_fwd(ctypes.byref(stem), P(4096), P(4096), None, 3, 2, 1, None) == 1
+
+
 def test_quantize_and_pool_argument_errors(lib):
     P = ctypes.c_void_p
     assert lib.iqnn_quantize(P(4096), P(4096), 1, 3, 1, P(4096), P(4096), 0, 9, None) == 1

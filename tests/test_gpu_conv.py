@@ -71,6 +71,28 @@ def test_conv_four_channel_padded_input(hw, k, stride, co):
     assert_bytes_equal(y.cpu().numpy(), want, "c4 %s" % ((hw, k, stride, co),))
 
 
+@pytest.mark.parametrize("n,hw,y_type,epi", [(2, (32, 32), U8, RELU), (3, (48, 64), I8, NONE), (1, (16, 224), U8, NONE),
+                                          (2, (224, 224), U8, RELU), (1, (40, 64), I8, RELU)])
+def test_stem_fused_max_pooling(n, hw, y_type, epi):
+    """iqnn_qconv_maxpool_fwd (the stem conv and 3x3/2 pad 1 max pooling in one launch)
+    equals the oracle's conv followed by the oracle's max pooling, byte for byte."""
+    torch = require_gpu()
+    from integer_quantized_nn_amd.layers import QConv
+    h, w = hw
+    c = synth.conv_case(hash((n, hw, y_type, epi)) % 2 ** 31, n, h, w, 3, 64, 7, 2, 3, U8, I8, y_type, epi)
+    x, wc, _ = conv_codes(c)
+    conv_ref = oracle_conv(c, x, wc, None)
+    want = to_bytes(O.maxpool2d(conv_ref, 3, 2, 1), y_type)
+    xp = np.pad(x, ((0, 0), (3, 3), (3, 3), (0, 1)), constant_values=c.z_in)
+    wp = np.pad(wc, ((0, 0), (0, 0), (0, 0), (0, 1)))
+    conv = QConv(n, h + 6, w + 6, 4, 64, 7, 2, 0, U8, I8, y_type, epi, c.z_in, c.z_out,
+                 to_bytes(wp, I8), c.bias, c.s_in, c.s_w, c.s_out)
+    y = conv.conv_maxpool(torch.from_numpy(to_bytes(xp, U8)).cuda())
+    torch.cuda.synchronize()
+    assert y.shape == want.shape
+    assert_bytes_equal(y.cpu().numpy(), want, "stem+pool %s" % ((n, hw, y_type, epi),))
+
+
 # 8-bit layers with C_in % 64 == 0 (the pipelined kernel): ring depths that do not
 # divide the stage count, one-stage contractions, ragged pixel tails and channel
 # counts that are not multiples of any block
