@@ -381,7 +381,10 @@ void conv_params(const Layer& L, const void* x, const void* packed, const void* 
         p.t_lo = (float)(low - L.z_out);
         p.t_hi = (float)(hi - L.z_out);
         p.out_magic = 12582912.0f + (float)(L.z_out - fix);      // 1.5 * 2^23 + even part of Z_out
-        p.out_fix = (uint32_t)fix;
+        // bytes hold code - fix; with no code 0 in [low, hi] none is 0xFF before the fix
+        const bool packed_fix = fix && (L.y_type == T_UINT8 || L.y_type == T_INT8) && (low > 0 || hi < 0);
+        p.out_fix = packed_fix ? 0u : (uint32_t)fix;
+        p.out_fix4 = packed_fix ? 0x01010101u : 0u;
     }
     if (L.epi == E_ADD || L.epi == E_ADD_RELU) {
         const int32_t rshift = L.res_type == T_INT8 ? 128 : (L.res_type == T_INT4 ? 8 : 0);

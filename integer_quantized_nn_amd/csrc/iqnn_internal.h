@@ -86,8 +86,11 @@ struct ConvParams {
     // bits, leaving the output code in the low byte.  Residual codes are read as
     // unsigned codes shifted by 128 (INT8) / 8 (INT4) / 0: (code ^ res_xor) - res_zf
     // == r - Z_res.
+    // For 8-bit outputs whose code range excludes 0 (ReLU with Z_out >= 1, say) the
+    // bytes before the fix never hold 0xFF, so the fix is added once per packed word:
+    // out_fix4 = 0x01010101 and out_fix = 0.
     float t_lo, t_hi, out_magic;
-    uint32_t out_fix;
+    uint32_t out_fix, out_fix4;
     float res_zf;
     uint32_t res_xor;
     int32_t vec_store;        // C_out % 16 == 0: vector stores

@@ -141,14 +141,15 @@ __device__ __forceinline__ void round_codes16(const ConvParams& p, const float v
     }
 }
 
-// The low bytes of b[0..15] as 16 consecutive bytes.
-__device__ __forceinline__ uint4 pack_bytes16(const uint32_t b[16]) {
+// The low bytes of b[0..15] as 16 consecutive bytes, plus the packed odd part of Z_out
+// (p.out_fix4 = 0x01010101 when the host found that no byte can carry, see ConvParams).
+__device__ __forceinline__ uint4 pack_bytes16(const ConvParams& p, const uint32_t b[16]) {
     uint32_t ow[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
         const uint32_t lo2 = __builtin_amdgcn_perm(b[4 * d + 1], b[4 * d], 0x0C0C0400u);
         const uint32_t hi2 = __builtin_amdgcn_perm(b[4 * d + 3], b[4 * d + 2], 0x0C0C0400u);
-        ow[d] = lo2 | (hi2 << 16);
+        ow[d] = (lo2 | (hi2 << 16)) + p.out_fix4;
     }
     return make_uint4(ow[0], ow[1], ow[2], ow[3]);
 }
@@ -209,7 +210,7 @@ __device__ __forceinline__ void epi_store16(const ConvParams& p, const v16i& acc
     uint32_t b[16];
     round_codes16(p, v, b);
     if (p.y_type == T_INT8 || p.y_type == T_UINT8) {
-        const uint4 pk = pack_bytes16(b);
+        const uint4 pk = pack_bytes16(p, b);
         const uint32_t ow[4] = {pk.x, pk.y, pk.z, pk.w};
         if (p.vec_store) {
             *reinterpret_cast<uint4*>(p.y + oidx) = pk;
@@ -1738,7 +1739,7 @@ __global__ __launch_bounds__(64 * NW, 2) void qconv_stem_pool(const ConvParams p
             }
             uint32_t b[16];
             round_codes16(p, v, b);
-            *reinterpret_cast<uint4*>(dst + ocb) = pack_bytes16(b);
+            *reinterpret_cast<uint4*>(dst + ocb) = pack_bytes16(p, b);
         }
     };
 
