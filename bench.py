@@ -272,11 +272,11 @@ def bench_layer(args):
         run()
     host_per_step = (time.perf_counter() - t0) / max(args.warmup, 1)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     stream = torch.cuda.current_stream()
     # A launch here can take less GPU time than the host needs to issue it, so the
-    # queue is first held by a spin kernel until every timed step is enqueued:
-    # the events then bracket device time only, not host launch gaps.
+    # queue is first held by a spin kernel until every timed step is enqueued; the
+    # steps then run back to back and one pair of HIP events on the launch stream
+    # brackets them (an event between launches would add its own few microseconds).
     spin0, spin1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     spin0.record(stream)
     torch.cuda._sleep(1 << 20)
@@ -284,19 +284,19 @@ def bench_layer(args):
     torch.cuda.synchronize()
     s_per_cycle = spin0.elapsed_time(spin1) * 1e-3 / (1 << 20)
     hold = 2.0 * args.steps * host_per_step + 2e-3
+    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     spin0.record(stream)
     torch.cuda._sleep(int(hold / s_per_cycle))
     t0 = time.perf_counter()
-    for a, b in evs:
-        a.record(stream)
+    t_begin.record(stream)
+    for _ in range(args.steps):
         run()
-        b.record(stream)
+    t_end.record(stream)
     enqueued = time.perf_counter() - t0
     torch.cuda.synchronize()
-    dur = np.array([a.elapsed_time(b) * 1e-3 for a, b in evs])
-    avg = dur.mean()
-    span = evs[0][0].elapsed_time(evs[-1][1]) * 1e-3
-    if spin0.elapsed_time(evs[0][0]) * 1e-3 < enqueued:
+    span = t_begin.elapsed_time(t_end) * 1e-3
+    avg = span / args.steps   # one launch per step: its duration plus the launch-to-launch gap
+    if spin0.elapsed_time(t_begin) * 1e-3 < enqueued:
         print("warning: the spin kernel ended before every timed step was enqueued", file=sys.stderr)
     ai = ops / nbytes
     if ai < PEAK_INT8_OPS / PEAK_HBM:
