@@ -8,7 +8,9 @@ iqo.c (direct loops, strict binary32, no fused multiply-add); see that file
 for the page passage each step follows.
 
 Codes are numpy int32 arrays holding one logical code per element (4-bit codes
-unpacked); pack()/unpack() convert to and from the byte layout.
+unpacked); pack()/unpack() convert to and from the byte layout.  The integer-only
+requantization (get_mn, requant_int) is written here directly in numpy int64 /
+Python integers.
 
 Parity pins: every function here is pinned by tests/test_oracle_*.py against
 worked values printed on the pages, closed forms, library routines
@@ -229,6 +231,52 @@ def requant(acc, mult, epi, z_out, out_qtype, res=None, z_res=0, m_res=0.0):
     _check(_load().iqo_requant(_ptr(acc), acc.size // ch, ch, _ptr(mult), epi, _ptr(r), int(z_res),
                                float(np.float32(m_res)), int(z_out), out_qtype, _ptr(out)), "requant")
     return out
+
+
+# ---------------------------------------------------------------------------
+# Integer-only requantization: the multiplier M[c] as an integer mantissa and a
+# power-of-two shift, for targets without floating point ("Quantization" blog,
+# 量化模式: integer quantization replaces float arithmetic by a power-of-two
+# scale; FQ-ViT article, section 2 / LayerNorm code: get_MN).
+
+
+def get_mn(x, bit=8):
+    """(M, N) with x ~ M * 2^-N: N = clamp(bit - 1 - floor(log2 x), 0, 31),
+    M = clamp(floor(x * 2^N), 0, 2^bit - 1) (FQ-ViT's get_MN).  floor(log2 x) is the
+    exact binary exponent of the binary32 value x (frexp), not a rounded log."""
+    import math
+    x = float(np.float32(x))
+    assert x > 0.0
+    mant, e = math.frexp(x)           # x = mant * 2^e, mant in [0.5, 1)
+    n = min(max(bit - 1 - (e - 1), 0), 31)
+    m = min(max(math.floor(math.ldexp(x, n)), 0), (1 << bit) - 1)
+    return int(m), int(n)
+
+
+def requant_int(acc, m, n, epi, z_out, out_qtype):
+    """y = clip(rne(acc * M[c] / 2^N[c]) + Z_out) with ReLU as the clamp at Z_out
+    (passive); acc [..., ch] int64, m / n [ch].  rne = round half to even (the blog's
+    round_fn).  Epilogues NONE and RELU only."""
+    assert epi in (EPI_NONE, EPI_RELU)
+    acc = np.asarray(acc, np.int64)
+    ch = acc.shape[-1]
+    m = np.broadcast_to(np.asarray(m, np.int64), (ch,))
+    n = np.broadcast_to(np.asarray(n, np.int64), (ch,))
+    t = acc * m                                   # |t| < 2^62 for |acc| < 2^31, M < 2^31
+    q = t.copy()
+    for c in range(ch):
+        if n[c] == 0:
+            continue
+        tc = t[..., c]
+        q0 = tc >> n[c]                           # floor (arithmetic shift)
+        rem = tc - (q0 << n[c])                   # in [0, 2^N)
+        half = np.int64(1) << (n[c] - 1)
+        up = (rem > half) | ((rem == half) & ((q0 & 1) == 1))
+        q[..., c] = q0 + up.astype(np.int64)
+    lo, hi = qrange(out_qtype)
+    if epi == EPI_RELU:
+        q = np.maximum(q, 0)
+    return np.clip(q + z_out, lo, hi).astype(np.int32)
 
 
 def maxpool2d(x, k, stride, pad):
