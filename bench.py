@@ -229,7 +229,7 @@ def bench_layer(args):
     from integer_quantized_nn_amd.layers import QConv, QGemm, quantize
 
     wl = args.workload
-    if wl in ("conv3x3_int8", "conv3x3_4bit", "conv3x3_uint8w"):
+    if wl in ("conv3x3_int8", "conv3x3_4bit", "conv3x3_uint8w", "conv3x3_intrq"):
         c = synth.conv3x3_4bit() if wl == "conv3x3_4bit" else synth.conv3x3_int8()
         n, h, w, ci = c.x.shape
         co = c.c_out
@@ -240,7 +240,8 @@ def bench_layer(args):
             wq = quantize(torch.from_numpy(c.w).cuda(), s_w, z_w, w_type).cpu().numpy()
         else:
             wq = quantize(torch.from_numpy(c.w).cuda(), c.s_w, 0, c.w_type, axis=0).cpu().numpy()
-        layer = QConv(n, h, w, ci, co, 3, c.stride, c.pad, c.x_type, w_type, c.y_type, c.epi, c.z_in, c.z_out,
+        epi = c.epi | (16 if wl == "conv3x3_intrq" else 0)   # integer-only requantization flag
+        layer = QConv(n, h, w, ci, co, 3, c.stride, c.pad, c.x_type, w_type, c.y_type, epi, c.z_in, c.z_out,
                       wq, c.bias, c.s_in, s_w, c.s_out, res_type=c.res_type, z_res=c.z_res, s_res=c.s_res, z_w=z_w)
         xd = quantize(torch.from_numpy(c.x).cuda(), c.s_in, c.z_in, c.x_type)
         rd = quantize(torch.from_numpy(c.res).cuda(), c.s_res, c.z_res, c.res_type) if c.res is not None else None
@@ -322,8 +323,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--batch", type=int, default=256)
     ap.add_argument("--workload", default="resnet50_trunk",
-                    choices=["resnet50_trunk", "conv3x3_int8", "conv3x3_4bit", "conv3x3_uint8w", "vitl_fc1",
-                             "gemm_int8_256"])
+                    choices=["resnet50_trunk", "conv3x3_int8", "conv3x3_4bit", "conv3x3_uint8w", "conv3x3_intrq",
+                             "vitl_fc1", "gemm_int8_256"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="trunk: time eager launches instead of one captured HIP graph per step")

@@ -82,7 +82,16 @@ typedef enum {
     IQNN_EPI_RELU = 1,
     IQNN_EPI_ADD = 2,
     IQNN_EPI_ADD_RELU = 3,
-    IQNN_EPI_RAW_INT32 = 4
+    IQNN_EPI_RAW_INT32 = 4,
+    /* Flag, OR'ed into NONE or RELU: integer-only requantization for targets without
+     * floating point ("Quantization" blog, 量化模式: integer (power of two)
+     * quantization; FQ-ViT article, LayerNorm code: get_MN).  Prepack writes each
+     * M[c] as M_c * 2^-N_c with N_c = clamp(7 - floor(log2 M[c]), 0, 31) and
+     * M_c = clamp(floor(M[c] * 2^N_c), 0, 255) (floor(log2) = the binary exponent);
+     * the kernel computes y = clip(rne((acc + bias) * M_c / 2^N_c) + Z_out) in
+     * integers (rne: half to even; RELU clamps at Z_out).  Not with ADD, ADD_RELU or
+     * RAW_INT32, nor with iqnn_qconv_maxpool_fwd (IQNN_ERR_UNSUPPORTED). */
+    IQNN_EPI_INT_REQUANT = 16
 } iqnn_epilogue;
 
 /* Convolution descriptor.  Dilation 1, groups 1.  Output size

@@ -77,8 +77,22 @@ struct Layer {
     int64_t n, h, w, c, c_out, oh, ow, m, k;
     int32_t kh, kw, sh, sw, ph, pw;
     int32_t x_type, w_type, y_type, res_type, epi, z_in, z_out, z_res, z_w;
+    bool int_rq;   // integer-only requantization (IQNN_EPI_INT_REQUANT)
     bool gemm;
 };
+
+// (M, N) of a positive binary32 multiplier x ~ M * 2^-N, M of kIntRqBits bits:
+// N = clamp(bits - 1 - floor(log2 x), 0, 31), M = clamp(floor(x * 2^N), 0, 2^bits - 1),
+// with floor(log2 x) the exact binary exponent (FQ-ViT article, LayerNorm code: get_MN).
+constexpr int kIntRqBits = 8;
+void int_multiplier(float x, int32_t* m, int32_t* n) {
+    int e = 0;
+    std::frexp((double)x, &e);   // x = f * 2^e, f in [0.5, 1): floor(log2 x) = e - 1
+    const int32_t nn = std::min(std::max(kIntRqBits - 1 - (e - 1), 0), 31);
+    const double scaled = std::floor(std::ldexp((double)x, nn));
+    *n = nn;
+    *m = (int32_t)std::min(std::max(scaled, 0.0), (double)((1 << kIntRqBits) - 1));
+}
 
 // Weights are held as q_W - s_w (s_w = 128 for UINT8, else 0) so every type fits
 // int8; zw_red = s_w - Z_w is the coefficient of the per-pixel sum of the kernel's
@@ -111,6 +125,10 @@ iqnn_status check_layer(const Layer& L) {
                         "N*OH*OW < 2^31 and an 8-bit residual with C_out %% 16 == 0", L.z_w, L.w_type);
     }
     if (L.epi < E_NONE || L.epi > E_RAW) return fail(IQNN_ERR_INVALID_ARG, "unknown epilogue %d", L.epi);
+    if (L.int_rq && L.epi != E_NONE && L.epi != E_RELU)
+        return fail(IQNN_ERR_UNSUPPORTED, "integer-only requantization goes with NONE or RELU only");
+    if (L.int_rq && zw_red(L) != 0)
+        return fail(IQNN_ERR_UNSUPPORTED, "integer-only requantization takes weights without the Z_W term");
     if ((L.epi == E_RAW) != (L.y_type == T_INT32))
         return fail(IQNN_ERR_INVALID_ARG, "INT32 output goes with the RAW_INT32 epilogue and only with it");
     if (L.epi != E_RAW && !is_code_type(L.y_type))
@@ -141,7 +159,8 @@ iqnn_status conv_layer(const iqnn_conv_desc* d, Layer* L) {
     L->n = d->n; L->h = d->h; L->w = d->w; L->c = d->c_in; L->c_out = d->c_out;
     L->kh = d->kh; L->kw = d->kw; L->sh = d->stride_h; L->sw = d->stride_w; L->ph = d->pad_h; L->pw = d->pad_w;
     L->x_type = d->x_type; L->w_type = d->w_type; L->y_type = d->y_type; L->res_type = d->res_type;
-    L->epi = d->epilogue; L->z_in = d->z_in; L->z_out = d->z_out; L->z_res = d->z_res; L->z_w = d->z_w;
+    L->epi = d->epilogue & ~IQNN_EPI_INT_REQUANT; L->int_rq = (d->epilogue & IQNN_EPI_INT_REQUANT) != 0;
+    L->z_in = d->z_in; L->z_out = d->z_out; L->z_res = d->z_res; L->z_w = d->z_w;
     L->oh = L->sh > 0 ? (L->h + 2 * (int64_t)L->ph - L->kh) / L->sh + 1 : 0;
     L->ow = L->sw > 0 ? (L->w + 2 * (int64_t)L->pw - L->kw) / L->sw + 1 : 0;
     L->m = L->n * L->oh * L->ow;
@@ -155,7 +174,8 @@ iqnn_status gemm_layer(const iqnn_gemm_desc* d, Layer* L) {
     L->n = 1; L->h = 1; L->w = d->m; L->c = d->k; L->c_out = d->n;
     L->kh = L->kw = L->sh = L->sw = 1; L->ph = L->pw = 0;
     L->x_type = d->a_type; L->w_type = d->b_type; L->y_type = d->c_type; L->res_type = d->res_type;
-    L->epi = d->epilogue; L->z_in = d->z_a; L->z_out = d->z_out; L->z_res = d->z_res; L->z_w = d->z_b;
+    L->epi = d->epilogue & ~IQNN_EPI_INT_REQUANT; L->int_rq = (d->epilogue & IQNN_EPI_INT_REQUANT) != 0;
+    L->z_in = d->z_a; L->z_out = d->z_out; L->z_res = d->z_res; L->z_w = d->z_b;
     L->oh = 1; L->ow = d->m; L->m = d->m; L->k = d->k;
     if (d->m <= 0 || d->n <= 0 || d->k <= 0) return fail(IQNN_ERR_INVALID_ARG, "GEMM sizes must be positive");
     return check_layer(*L);
@@ -181,6 +201,7 @@ int forced_tile() { return tile_override(); }
 // widened window of the last output column must still lie inside the input row.
 int32_t c4_kwp(const Layer& L) { return L.kw <= 4 ? 4 : (L.kw <= 8 ? 8 : 16); }
 bool c4_path(const Layer& L) {
+    if (L.int_rq) return false;   // integer requantization runs on the register-staged kernel
     if (is_4bit(L.x_type) || L.c != 4 || L.ph != 0 || L.pw != 0 || L.kw > 16) return false;
     if (L.n * L.h * L.w >= ((int64_t)1 << 31)) return false;   // pixel indices are int32
     return (L.ow - 1) * (int64_t)L.sw + c4_kwp(L) <= L.w;
@@ -210,6 +231,7 @@ int64_t staged_k(int64_t k, bool act4, bool stream4 = false) {
 // one filter tap and the residual, if any, is 4-bit in whole 16-byte chunks.  The
 // packed layout depends on this choice, so prepack and forward both ask here.
 bool b4_stream(const Layer& L) {
+    if (L.int_rq) return false;   // integer requantization runs on the register-staged kernel
     if (!is_4bit(L.x_type) || L.c % 64 != 0 || L.kh * L.kw > 64) return false;
     if (L.m >= ((int64_t)1 << 31)) return false;
     const bool add = L.epi == E_ADD || L.epi == E_ADD_RELU;
@@ -287,7 +309,14 @@ iqnn_status prepack_into(const Layer& L, const void* w_host, const float* bias_h
             const float m = sw_in / s_out;
             if (!normal_ok(m) || m > 1e20f)
                 return fail(IQNN_ERR_INVALID_ARG, "requant multiplier of channel %lld is not a normal float in [FLT_MIN, 1e20]", (long long)oc);
-            mult[oc] = m;
+            if (L.int_rq) {   // the slot holds N << 16 | M instead of the float
+                int32_t mi, ni;
+                int_multiplier(m, &mi, &ni);
+                const uint32_t packed = ((uint32_t)ni << 16) | (uint32_t)mi;
+                std::memcpy(&mult[oc], &packed, 4);
+            } else {
+                mult[oc] = m;
+            }
         } else {
             mult[oc] = 1.0f;
         }
@@ -377,9 +406,12 @@ void conv_params(const Layer& L, const void* x, const void* packed, const void* 
         code_range(L.y_type, &lo, &hi);
         const bool relu = L.epi == E_RELU || L.epi == E_ADD_RELU;
         const int32_t low = relu ? std::max(lo, L.z_out) : lo;   // passive ReLU: clamp at Z_out
-        const int32_t fix = L.z_out & 1;                         // odd part (two's complement)
+        const int32_t fix = L.int_rq ? 0 : (L.z_out & 1);        // odd part (two's complement)
         p.t_lo = (float)(low - L.z_out);
         p.t_hi = (float)(hi - L.z_out);
+        p.q_lo = low - L.z_out;
+        p.q_hi = hi - L.z_out;
+        p.int_rq = L.int_rq ? 1 : 0;
         p.out_magic = 12582912.0f + (float)(L.z_out - fix);      // 1.5 * 2^23 + even part of Z_out
         // bytes hold code - fix; with no code 0 in [low, hi] none is 0xFF before the fix
         const bool packed_fix = fix && (L.y_type == T_UINT8 || L.y_type == T_INT8) && (low > 0 || hi < 0);
@@ -427,6 +459,7 @@ iqnn_status forward_pool(const Layer& L, const void* x, const void* packed, void
         return fail(IQNN_ERR_UNSUPPORTED, "fused pooling takes Conv / Conv_Relu epilogues");
     if (!c4_path(L) || zw_red(L) != 0)
         return fail(IQNN_ERR_UNSUPPORTED, "fused pooling needs the 4-channel padding-free stem input");
+    if (L.int_rq) return fail(IQNN_ERR_UNSUPPORTED, "fused pooling takes the binary32 requantization only");
     ConvParams p;
     conv_params(L, x, packed, nullptr, nullptr, p);
     if (!stem_pool_ok(p))

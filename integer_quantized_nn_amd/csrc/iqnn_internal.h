@@ -91,6 +91,9 @@ struct ConvParams {
     // out_fix4 = 0x01010101 and out_fix = 0.
     float t_lo, t_hi, out_magic;
     uint32_t out_fix, out_fix4;
+    // Integer-only requantization: mult[c] holds N << 16 | M (see int_multiplier);
+    // the rounded value is clipped to [q_lo, q_hi] = [t_lo, t_hi] as integers.
+    int32_t int_rq, q_lo, q_hi;
     float res_zf;
     uint32_t res_xor;
     int32_t vec_store;        // C_out % 16 == 0: vector stores

@@ -173,7 +173,9 @@ __device__ __forceinline__ uint4 pack_bytes16(const ConvParams& p, const uint32_
 // BIAS: add bias[] here (otherwise the accumulator started from the folded bias).
 // ADDK: 0 = residual add decided by `add` and p.res_type at run time, 1 = always an
 // 8-bit residual, 2 = never a residual, 3 = always a 4-bit residual.
-template <bool BIAS = true, int ADDK = 0>
+// INTRQ: integer-only requantization (mult[] holds N << 16 | M); compiled into the
+// register-staged kernel only, so the other kernels' register budgets never see it.
+template <bool BIAS = true, int ADDK = 0, bool INTRQ = false>
 __device__ __forceinline__ void epi_store16(const ConvParams& p, const v16i& acc, const int32_t* bias,
                                             const float* mult, uint32_t rw[4], int ocb, int64_t pix, bool add_rt,
                                             float m_res) {
@@ -193,22 +195,39 @@ __device__ __forceinline__ void epi_store16(const ConvParams& p, const v16i& acc
         }
         return;
     }
-    float v[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = (float)(acc[j] + (BIAS ? bias[j] : 0)) * mult[j];
-    if (add) {
-        const bool r8 = ADDK == 1 || (ADDK != 3 && (p.res_type == T_INT8 || p.res_type == T_UINT8));
-        uint32_t w[4] = {rw[0] ^ p.res_xor, rw[1] ^ p.res_xor, rw[2] ^ p.res_xor, rw[3] ^ p.res_xor};
+    uint32_t b[16];
+    if constexpr (INTRQ) {
+        // integer-only requantization: mult[j] holds N << 16 | M; rne(a * M / 2^N) as
+        // floor((t + 2^(N-1) - 1 + lsb) / 2^N) with lsb the low bit of floor(t / 2^N)
+        // (half to even), clipped in the offset domain, plus Z_out
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const uint32_t code = r8 ? (w[j >> 2] >> (8 * (j & 3))) & 0xFFu : (w[j >> 3] >> (4 * (j & 7))) & 0xFu;
-            const float d = (float)code - p.res_zf;   // == float(r - Z_res), exact
-            const float u = d * m_res;
-            v[j] = v[j] + u;
+            const uint32_t mn = __builtin_bit_cast(uint32_t, mult[j]);
+            const int64_t t = (int64_t)(acc[j] + (BIAS ? bias[j] : 0)) * (int64_t)(mn & 0xFFFFu);
+            const int n = (int)(mn >> 16);
+            int64_t q = t;
+            if (n > 0) q = (t + (((int64_t)1 << (n - 1)) - 1) + ((t >> n) & 1)) >> n;
+            q = q < p.q_lo ? p.q_lo : (q > p.q_hi ? p.q_hi : q);
+            b[j] = (uint32_t)((int32_t)q + p.z_out);
         }
+    } else {
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = (float)(acc[j] + (BIAS ? bias[j] : 0)) * mult[j];
+        if (add) {
+            const bool r8 = ADDK == 1 || (ADDK != 3 && (p.res_type == T_INT8 || p.res_type == T_UINT8));
+            uint32_t w[4] = {rw[0] ^ p.res_xor, rw[1] ^ p.res_xor, rw[2] ^ p.res_xor, rw[3] ^ p.res_xor};
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const uint32_t code =
+                    r8 ? (w[j >> 2] >> (8 * (j & 3))) & 0xFFu : (w[j >> 3] >> (4 * (j & 7))) & 0xFu;
+                const float d = (float)code - p.res_zf;   // == float(r - Z_res), exact
+                const float u = d * m_res;
+                v[j] = v[j] + u;
+            }
+        }
+        round_codes16(p, v, b);
     }
-    uint32_t b[16];
-    round_codes16(p, v, b);
     if (p.y_type == T_INT8 || p.y_type == T_UINT8) {
         const uint4 pk = pack_bytes16(p, b);
         const uint32_t ow[4] = {pk.x, pk.y, pk.z, pk.w};
@@ -234,7 +253,7 @@ __device__ __forceinline__ void epi_store16(const ConvParams& p, const v16i& acc
 
 // The second launch bound is the number of workgroups per CU that the LDS
 // footprint allows (160 KB of LDS per CU on gfx950).
-template <int BM, int BN, int WM, int WN, int GATHER, bool IS1X1>
+template <int BM, int BN, int WM, int WN, int GATHER, bool IS1X1, bool INTRQ = false>
 __global__ __launch_bounds__(256, (2 * 2 * (BM + BN) * kLdsStride <= 160 * 1024 ? 2 : 1))
 void qconv_igemm(const ConvParams p) {
     constexpr int WPX = BN / WN;      // pixels per wave
@@ -458,7 +477,7 @@ void qconv_igemm(const ConvParams p) {
             if (pix >= p.m) continue;
             uint32_t rw[4] = {0, 0, 0, 0};
             if (add) load_res16(p, pix * p.c_out + ocb, ocb, rw);
-            epi_store16(p, acc[t][u], cp.bias, cp.mult, rw, ocb, pix, add, m_res);
+            epi_store16<true, 0, INTRQ>(p, acc[t][u], cp.bias, cp.mult, rw, ocb, pix, add, m_res);
         }
     }
 }
@@ -844,6 +863,21 @@ hipError_t launch_staged(const ConvParams& p, int gather, bool is_1x1, hipStream
     q.n_px_tiles = (int32_t)n_px;
     q.group_px = group_px_for(n_px, (int64_t)BN * p.k);
     dim3 g((unsigned)grid), b(256);
+    if (p.int_rq) {   // integer-only requantization: its own instantiations
+        if (gather == GATHER_B8 && is_1x1)
+            hipLaunchKernelGGL((qconv_igemm<BM, BN, WM, WN, GATHER_B8, true, true>), g, b, 0, stream, q);
+        else if (gather == GATHER_B8)
+            hipLaunchKernelGGL((qconv_igemm<BM, BN, WM, WN, GATHER_B8, false, true>), g, b, 0, stream, q);
+        else if (gather == GATHER_B4 && is_1x1)
+            hipLaunchKernelGGL((qconv_igemm<BM, BN, WM, WN, GATHER_B4, true, true>), g, b, 0, stream, q);
+        else if (gather == GATHER_B4)
+            hipLaunchKernelGGL((qconv_igemm<BM, BN, WM, WN, GATHER_B4, false, true>), g, b, 0, stream, q);
+        else if (gather == GATHER_B8_ELEM)
+            hipLaunchKernelGGL((qconv_igemm<BM, BN, WM, WN, GATHER_B8_ELEM, false, true>), g, b, 0, stream, q);
+        else
+            return hipErrorInvalidValue;
+        return hipGetLastError();
+    }
     if (gather == GATHER_B8 && is_1x1)
         hipLaunchKernelGGL((qconv_igemm<BM, BN, WM, WN, GATHER_B8, true>), g, b, 0, stream, q);
     else if (gather == GATHER_B8)
@@ -1883,6 +1917,11 @@ int pipe_tile_choice(int64_t m, int32_t c_out, int64_t k, bool res) {
 }
 
 hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_t stream, int tile) {
+    if (p.int_rq) {   // integer-only requantization runs on the register-staged kernel
+        if (p.zw_red != 0) return hipErrorInvalidValue;
+        if (p.c_out <= 64) return launch_staged<64, 256, 1, 4>(p, gather, is_1x1, stream);
+        return launch_staged<128, 128, 2, 2>(p, gather, is_1x1, stream);
+    }
     if (gather == GATHER_C4 && tile < 0 && stem_ok(p)) return launch_stem(p, stream);
     if (gather == GATHER_B4S) {   // its packed layout is the streaming kernel's: no other tile
         if (p.c_out <= 64) return launch_stream<S64x128d6>(p, is_1x1, true, false, stream, true);

@@ -234,6 +234,37 @@ def test_host_prepack_asymmetric_weights(lib, x_type, w_type, z_w, c_in, epi):
         assert np.array_equal(lhs, rhs)
 
 
+@pytest.mark.parametrize("kw", [dict(epilogue=B.EPI_ADD_RELU | B.EPI_INT_REQUANT),
+                                dict(epilogue=B.EPI_RAW_INT32 | B.EPI_INT_REQUANT, y_type=B.INT32),
+                                dict(epilogue=B.EPI_RELU | B.EPI_INT_REQUANT, c_in=64, w_type=B.UINT8, z_w=3)])
+def test_integer_requant_unsupported_combinations(lib, kw):
+    d = conv_desc(**kw)
+    rc = lib.iqnn_qconv_fwd(ctypes.byref(d), ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.c_void_p(4096),
+                            ctypes.c_void_p(4096), None)
+    assert rc == 2
+
+
+def test_host_prepack_integer_multipliers(lib):
+    # the packed multiplier slot holds N << 16 | M with (M, N) = get_MN(M[c]) (FQ-ViT
+    # article, LayerNorm code), checked against the oracle's get_mn
+    rng = np.random.default_rng(21)
+    c_out, c_in = 40, 32
+    w = rng.integers(-127, 128, size=(c_out, 3, 3, c_in)).astype(np.int32)
+    s_w = np.exp(rng.uniform(np.log(1e-5), np.log(1e-1), c_out)).astype(np.float32)
+    s_in, s_out = np.float32(0.013), np.float32(0.07)
+    d = conv_desc(c_in=c_in, c_out=c_out, epilogue=B.EPI_RELU | B.EPI_INT_REQUANT)
+    buf = _host_pack(d, w, B.INT8, None, s_in, s_w, s_out)
+    ocp = 256
+    slots = buf[4 * ocp:8 * ocp].view(np.uint32)[:c_out]
+    want = [O.get_mn(m) for m in O.requant_multiplier(s_in, s_w, s_out)]
+    assert [(int(v) & 0xFFFF, int(v) >> 16) for v in slots] == want
+    assert lib.iqnn_qconv_maxpool_fwd(ctypes.byref(conv_desc(n=2, h=38, w=38, c_in=4, c_out=64, kh=7, kw=7,
+                                                             stride_h=2, stride_w=2, pad_h=0, pad_w=0,
+                                                             epilogue=B.EPI_RELU | B.EPI_INT_REQUANT)),
+                                      ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.c_void_p(4096), 3, 2, 1,
+                                      None) == 2
+
+
 def test_prepack_overflow_and_bad_scales(lib):
     d = conv_desc(c_in=16, c_out=16)
     w = np.full((16, 3, 3, 16), 127, np.int32)

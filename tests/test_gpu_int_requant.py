@@ -1,0 +1,79 @@
+"""GPU parity of the integer-only requantization (IQNN_EPI_INT_REQUANT): every output
+byte equals the oracle's direct accumulator followed by get_mn / requant_int
+("Quantization" blog, 量化模式: integer (power of two) quantization; FQ-ViT article,
+LayerNorm code: get_MN).  The layers cover the register-staged kernel's gathers:
+8-bit with C_in % 16 == 0 (3x3 and 1x1), the element gather (C_in % 16 != 0, the
+4-channel stem input), 4-bit activations, and a GEMM."""
+import numpy as np
+import pytest
+
+import oracle as O
+from integer_quantized_nn_amd import synth
+from parity_util import assert_bytes_equal, conv_codes, otype, require_gpu, to_bytes
+
+pytestmark = pytest.mark.gpu
+
+U8, I8, U4, I4 = synth.UINT8, synth.INT8, synth.UINT4, synth.INT4
+NONE, RELU = synth.EPI_NONE, synth.EPI_RELU
+INT_RQ = 16
+
+
+def oracle_int(case, x, w):
+    co = w.shape[0]
+    s_w = np.broadcast_to(np.atleast_1d(np.asarray(case.s_w, np.float32)), (co,))
+    bias_q = O.quantize_bias(case.bias, case.s_in, s_w)
+    acc = O.conv2d_acc(x, case.z_in, w, 0, case.stride, case.pad, bias_q)
+    mn = [O.get_mn(m) for m in O.requant_multiplier(case.s_in, s_w, case.s_out)]
+    m = np.array([a for a, _ in mn])
+    n = np.array([b for _, b in mn])
+    return O.requant_int(acc, m, n, case.epi, case.z_out, otype(case.y_type))
+
+
+CASES = [
+    # n, h, w, c_in, c_out, k, stride, pad, x_type, w_type, y_type, epi
+    (2, 9, 11, 64, 64, 3, 1, 1, U8, I8, U8, RELU),
+    (1, 13, 7, 128, 96, 1, 1, 0, U8, I8, I8, NONE),
+    (2, 8, 8, 48, 80, 3, 2, 1, I8, I8, U8, RELU),
+    (1, 10, 10, 24, 40, 3, 1, 1, U8, I8, U8, NONE),     # element gather, ragged channels
+    (2, 15, 15, 4, 64, 7, 2, 3, U8, I8, U8, RELU),      # stem-like 4-channel input
+    (2, 8, 8, 32, 64, 3, 1, 1, U4, I4, U4, RELU),       # 4-bit activations and output
+    (1, 7, 9, 64, 128, 3, 1, 1, U4, I4, I8, NONE),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "n%dh%dw%dci%dco%dk%ds%dp%d_x%dw%dy%de%d" % c)
+def test_conv_integer_requant(case):
+    torch = require_gpu()
+    from integer_quantized_nn_amd.layers import QConv
+    n, h, w, ci, co, k, s, p, xt, wt, yt, epi = case
+    c = synth.conv_case((hash(case) + 77) % 2 ** 31, n, h, w, ci, co, k, s, p, xt, wt, yt, epi)
+    x, wq, _ = conv_codes(c)
+    want = to_bytes(oracle_int(c, x, wq), yt)
+    conv = QConv(n, h, w, ci, co, k, s, p, xt, wt, yt, epi | INT_RQ, c.z_in, c.z_out, to_bytes(wq, wt), c.bias,
+                 c.s_in, c.s_w, c.s_out)
+    y = conv(torch.from_numpy(to_bytes(x, xt)).cuda())
+    torch.cuda.synchronize()
+    assert_bytes_equal(y.cpu().numpy(), want, str(case))
+    # discrimination: the 8-bit cases span many codes
+    if yt in (U8, I8):
+        assert len(np.unique(y.cpu().numpy())) >= 32
+
+
+def test_gemm_integer_requant():
+    torch = require_gpu()
+    from integer_quantized_nn_amd.layers import QGemm
+    rng = np.random.default_rng(8)
+    m, n, k = 211, 72, 160
+    a = rng.integers(0, 256, size=(m, k)).astype(np.int32)
+    b = rng.integers(-128, 128, size=(n, k)).astype(np.int32)
+    s_a, s_out = np.float32(0.02), np.float32(0.6)
+    s_b = rng.uniform(0.002, 0.004, n).astype(np.float32)
+    bias = rng.normal(0, 0.5, n).astype(np.float32)
+    acc = O.gemm_acc(a, 119, b, 0, O.quantize_bias(bias, s_a, s_b))
+    mn = [O.get_mn(v) for v in O.requant_multiplier(s_a, s_b, s_out)]
+    want = O.requant_int(acc, np.array([v[0] for v in mn]), np.array([v[1] for v in mn]), O.EPI_NONE, 0, O.INT8)
+    g = QGemm(m, n, k, U8, I8, I8, NONE | INT_RQ, 119, 0, to_bytes(b, I8), bias, s_a, s_b, s_out)
+    c = g(torch.from_numpy(to_bytes(a, U8)).cuda())
+    torch.cuda.synchronize()
+    assert_bytes_equal(c.cpu().numpy(), to_bytes(want, I8), "gemm integer requant")
+    assert len(np.unique(c.cpu().numpy())) >= 32

@@ -74,7 +74,7 @@ def test_asymmetric_weights_match_torch_conv2d(case):
     # zero point Z_W; the accumulator is sum (Q(I) - Z_I)(Q(W) - Z_W).  torch conv2d in
     # float64 on the centred operands is exact for these integer sums.
     n, h, w, ci, co, kh, kw, stride, pad = case
-    rng = np.random.default_rng(hash(("zw",) + case) % 2 ** 32)
+    rng = np.random.default_rng((hash(case) + 91) % 2 ** 32)
     for (wlo, whi, zw) in [(0, 255, 131), (0, 255, 0), (0, 15, 7), (-128, 127, -9), (-8, 7, 3)]:
         x = _rand_codes(rng, (n, h, w, ci), 0, 255)
         wt = _rand_codes(rng, (co, kh, kw, ci), wlo, whi)
