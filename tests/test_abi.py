@@ -107,6 +107,29 @@ def test_fused_conv_pool_rejects_other_shapes_before_launch(lib):
     assert lib.iqnn_qconv_maxpool_fwd(ctypes.byref(stem), P(4096), P(4096), None, 3, 2, 1, None) == 1
 
 
+def test_empty_and_oversized_inputs(lib):
+    P = ctypes.c_void_p
+    # empty tensors: nothing to read or write, no launch, no pointer needed
+    assert lib.iqnn_quantize(None, None, 0, 3, 1, None, None, 0, B.UINT8, None) == 0
+    assert lib.iqnn_dequantize(None, None, 0, 3, 1, None, None, 0, B.INT4, None) == 0
+    assert lib.iqnn_quantize_pad(None, None, 0, 8, 8, 3, 3, 4, None, None, 0, B.UINT8, None) == 0
+    # an empty batch or GEMM has no valid descriptor
+    g = B.GemmDesc()
+    g.m, g.n, g.k = 0, 16, 64
+    g.a_type, g.b_type, g.c_type, g.res_type, g.epilogue = B.UINT8, B.INT8, B.INT8, B.UINT8, B.EPI_NONE
+    assert lib.iqnn_qgemm_fwd(ctypes.byref(g), P(4096), P(4096), None, P(4096), None) == 1
+    # size limits, all reported before any launch
+    assert lib.iqnn_qconv_fwd(ctypes.byref(conv_desc(c_out=(1 << 24) + 16, kh=1, kw=1, pad_h=0, pad_w=0)),
+                              P(4096), P(4096), None, P(4096), None) == 2
+    huge = conv_desc(n=1 << 20, h=1 << 11, w=1 << 11, kh=1, kw=1, pad_h=0, pad_w=0)   # 2^42 output pixels
+    assert lib.iqnn_qconv_fwd(ctypes.byref(huge), P(4096), P(4096), None, P(4096), None) == 2
+    assert lib.iqnn_maxpool2d(P(4096), P(4096), 1 << 16, 512, 512, 16, 3, 1, 1, B.UINT8, None) == 2
+    assert lib.iqnn_quantize_pad(P(4096), P(4096), 1 << 16, 256, 256, 3, 0, 4, P(4096), P(4096), 0, B.UINT8,
+                                 None) == 2
+    g.m, g.k, g.b_type, g.z_b = 256, 96, B.UINT8, 9   # Z_B term needs K % 64 == 0
+    assert lib.iqnn_qgemm_fwd(ctypes.byref(g), P(4096), P(4096), None, P(4096), None) == 2
+
+
 def test_quantize_and_pool_argument_errors(lib):
     P = ctypes.c_void_p
     assert lib.iqnn_quantize(P(4096), P(4096), 1, 3, 1, P(4096), P(4096), 0, 9, None) == 1

@@ -33,6 +33,11 @@ SMALL = [
     (1, 4, 4, 256, 256, 3, 1, 1, U8, I8, U8, RELU, U8),
     (1, 3, 3, 64, 40, 3, 1, 2, U8, I8, U8, NONE, U8),
     (1, 1, 1, 1024, 2048, 1, 1, 0, U8, I8, U8, ADD_RELU, U8),
+    # degenerate: one input and one output channel on a 1x1 image, a kernel wider than
+    # its one-pixel-wide input, two 4-bit channels
+    (1, 1, 1, 1, 1, 1, 1, 0, U8, I8, U8, NONE, U8),
+    (2, 3, 1, 3, 5, 3, 1, 1, U8, I8, I8, RELU, U8),
+    (1, 1, 2, 16, 2, 1, 1, 0, U4, I4, U4, NONE, U4),
 ]
 
 
