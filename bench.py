@@ -350,7 +350,7 @@ def main():
         print("TRAFFIC " + json.dumps(rec))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+        print("bench.py measures one GPU only: there is no multi-GPU path (got --gpus %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
     import torch

@@ -53,7 +53,7 @@ extern "C" {
 typedef enum {
     IQNN_OK = 0,
     IQNN_ERR_INVALID_ARG = 1,  /* a size, type, zero point, scale or pointer is invalid */
-    IQNN_ERR_UNSUPPORTED = 2,  /* valid, but a combination this build does not implement */
+    IQNN_ERR_UNSUPPORTED = 2,  /* valid, but a combination the library does not implement */
     IQNN_ERR_ALIGNMENT = 3,    /* a pointer or row does not meet the documented alignment */
     IQNN_ERR_OVERFLOW = 4,     /* folded bias or accumulator bound would leave int32 */
     IQNN_ERR_HIP = 5           /* the HIP runtime reported an error */
