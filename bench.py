@@ -125,7 +125,9 @@ def bench_trunk(args):
     t0 = time.perf_counter()
     tr = synth.resnet50_trunk(seed=0, batch=args.batch)
     log("synthetic trunk ready in %.1f s" % (time.perf_counter() - t0))
-    net = QuantResNet50Trunk(tr)
+    # uint8 activation codes stored as int8 bytes q - 128 (zero points Z - 128): the same
+    # trunk byte for byte up to the sign bit, with no per-fragment sign flip in the kernels
+    net = QuantResNet50Trunk(tr, offset_codes=True)
     x = torch.from_numpy(tr.x).cuda()
     torch.cuda.synchronize()
     launches = net.launches()
@@ -201,7 +203,7 @@ def bench_trunk(args):
         "vs_baseline": None, "dtype": "int8", "data": "synthetic",
         "config": {"workload": "resnet50_trunk_b%d" % args.batch, "batch": args.batch, "image_hw": 224,
                    "convs": n_conv, "ops_per_step": step_ops,
-                   "activations": "uint8 asymmetric per-tensor", "weights": "int8 per-channel symmetric",
+                   "activations": "uint8 asymmetric per-tensor, stored as int8 bytes q - 128 (zero points Z - 128)", "weights": "int8 per-channel symmetric",
                    "step": "quantize fp32 input, 53 fused convs + max pooling (fused with the stem), "
                            "dequantize output"},
         "pct_int8_mfma_peak": value * 1e12 / PEAK_INT8_OPS,
@@ -212,7 +214,8 @@ def bench_trunk(args):
         "per_layer_us_tops": per_layer,
     }
     if not args.no_cpu_baseline:
-        final_codes = net.bufs[net.final].cpu().numpy()
+        # back to uint8 codes (the stored bytes are q - 128) for the comparison with the oracle
+        final_codes = net.bufs[net.final].cpu().numpy() ^ np.uint8(0x80 if net.offset_codes else 0)
         rec["cpu_baseline"] = cpu_baseline_trunk(tr, final_codes, args.cpu_seconds)
     else:
         rec["cpu_baseline"] = None

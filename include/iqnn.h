@@ -151,9 +151,11 @@ const char *iqnn_last_error(void);
  * 6: 64x128; 7..17 the persistent streaming kernel with 7: 64x128 (12-stage ring),
  * 8: 64x128 (6), 9: 128x128 (8), 10: 128x128 (4), 11: 64x256 (3), 12: 256x128 (6),
  * 13: 128x256 (6), 14: 128x128 (3, three blocks per CU), 15: 128x256 (3),
- * 16: 256x128 (3), 17: 256x256 (4).  Layers a configuration cannot take (4-bit
- * activations, C_in % 64 != 0, residual layouts it does not stream) keep a
- * configuration that can.  Every choice computes identical results; only speed differs.  The initial
+ * 16: 256x128 (3), 17: 256x256 (4); 18 the direct 3x3 kernel (64-channel 8-bit
+ * activations, 3x3 / stride 1 / pad 1 on 56-pixel rows, no residual) at any batch,
+ * where the automatic choice takes it from 512 two-row tiles up.  Layers a
+ * configuration cannot take (4-bit activations, C_in % 64 != 0, residual layouts it
+ * does not stream) keep a configuration that can.  Every choice computes identical results; only speed differs.  The initial
  * value is -1, or the integer in the environment variable IQNN_FORCE_TILE.  Returns
  * IQNN_ERR_INVALID_ARG for other values.  Process-wide and unsynchronised: set it
  * while no other thread launches. */

@@ -182,7 +182,6 @@ iqnn_status gemm_layer(const iqnn_gemm_desc* d, Layer* L) {
 }
 
 // Tile override for tuning sweeps (iqnn_set_conv_tile); starts from IQNN_FORCE_TILE.
-constexpr int kMaxTile = 17;
 int& tile_override() {
     static int t = [] {
         const char* e = std::getenv("IQNN_FORCE_TILE");

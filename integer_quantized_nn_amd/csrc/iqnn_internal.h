@@ -99,8 +99,12 @@ struct ConvParams {
     int32_t vec_store;        // C_out % 16 == 0: vector stores
 };
 
-// tile < 0 picks the pipelined kernel's tile configuration from the layer shape;
-// 0..4 force one (the IQNN_FORCE_TILE environment variable, for tuning sweeps).
+// tile < 0 picks the kernel and its tile configuration from the layer shape; 0..17
+// force a block configuration of the ring / streaming kernels, kTileDirect3x3 the
+// direct 3x3 kernel on the layers it takes (the IQNN_FORCE_TILE environment variable
+// or iqnn_set_conv_tile, for tuning sweeps and tests).
+constexpr int kTileDirect3x3 = 18;
+constexpr int kMaxTile = 18;
 hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_t stream, int tile);
 
 // The image stem (4-channel padding-free input, stride 2) fused with 3x3 / stride 2 /

@@ -175,18 +175,22 @@ __device__ __forceinline__ uint4 pack_bytes16(const ConvParams& p, const uint32_
 // 8-bit residual, 2 = never a residual, 3 = always a 4-bit residual.
 // INTRQ: integer-only requantization (mult[] holds N << 16 | M); compiled into the
 // register-staged kernel only, so the other kernels' register budgets never see it.
-template <bool BIAS = true, int ADDK = 0, bool INTRQ = false>
+// OUTK: 0 = output type and store width decided at run time; 1 = 8-bit codes, 2 = raw
+// int32, 3 = 4-bit codes, each with 16-channel vector stores (C_out % 16 == 0).  A
+// kernel that keeps most registers busy takes the one branch it needs.
+template <bool BIAS = true, int ADDK = 0, bool INTRQ = false, int OUTK = 0>
 __device__ __forceinline__ void epi_store16(const ConvParams& p, const v16i& acc, const int32_t* bias,
                                             const float* mult, uint32_t rw[4], int ocb, int64_t pix, bool add_rt,
                                             float m_res) {
     const bool add = (ADDK == 1 || ADDK == 3) ? true : (ADDK == 2 ? false : add_rt);
     const int64_t oidx = pix * p.c_out + ocb;   // element index of the first channel
-    if (p.epi == E_RAW) {
+    const bool vec = OUTK != 0 || p.vec_store;
+    if (OUTK == 2 || (OUTK == 0 && p.epi == E_RAW)) {
         int32_t a[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) a[j] = acc[j] + (BIAS ? bias[j] : 0);
         int32_t* yo = reinterpret_cast<int32_t*>(p.y) + oidx;
-        if (p.vec_store) {
+        if (vec) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 *reinterpret_cast<int4*>(yo + 4 * j) = make_int4(a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]);
@@ -195,6 +199,7 @@ __device__ __forceinline__ void epi_store16(const ConvParams& p, const v16i& acc
         }
         return;
     }
+    if constexpr (OUTK == 2) return;
     uint32_t b[16];
     if constexpr (INTRQ) {
         // integer-only requantization: mult[j] holds N << 16 | M; rne(a * M / 2^N) as
@@ -228,10 +233,10 @@ __device__ __forceinline__ void epi_store16(const ConvParams& p, const v16i& acc
         }
         round_codes16(p, v, b);
     }
-    if (p.y_type == T_INT8 || p.y_type == T_UINT8) {
+    if (OUTK == 1 || (OUTK == 0 && (p.y_type == T_INT8 || p.y_type == T_UINT8))) {
         const uint4 pk = pack_bytes16(p, b);
         const uint32_t ow[4] = {pk.x, pk.y, pk.z, pk.w};
-        if (p.vec_store) {
+        if (vec) {
             *reinterpret_cast<uint4*>(p.y + oidx) = pk;
         } else {
             for (int j = 0; j < 16 && ocb + j < p.c_out; ++j) p.y[oidx + j] = (uint8_t)(ow[j >> 2] >> (8 * (j & 3)));
@@ -240,7 +245,7 @@ __device__ __forceinline__ void epi_store16(const ConvParams& p, const v16i& acc
         uint32_t ow[2] = {0, 0};
 #pragma unroll
         for (int j = 0; j < 16; ++j) ow[j >> 3] |= (b[j] & 0xFu) << (4 * (j & 7));
-        if (p.vec_store) {
+        if (vec) {
             *reinterpret_cast<uint2*>(p.y + (oidx >> 1)) = make_uint2(ow[0], ow[1]);
         } else {
             for (int j = 0; j < 8 && ocb + 2 * j < p.c_out; ++j)
@@ -1875,6 +1880,222 @@ hipError_t launch_stem_pool(const ConvParams& p, uint8_t* yp, hipStream_t stream
     return hipGetLastError();
 }
 
+namespace {
+
+// ============================================================ direct 3x3 kernel
+//
+// qconv_direct3x3: 3x3 / stride 1 / pad 1 convolution of 64-channel 8-bit codes on rows
+// of W pixels (W <= 64), as a direct convolution.  A tile is two output rows of one image
+// (2W pixels, four 32-pixel MFMA blocks, one per wave; lanes past 2W compute a clamped
+// pixel and store nothing).  The four input rows the tile reads -- with the input
+// zero-point code in the padding, so the padded taps need no test -- are copied into
+// LDS once per tile by 16-byte DMA (slab rows of W+2 pixels x 64 bytes, the four
+// 16-byte slots of a pixel swizzled by bits 2-3 of its column, as the streaming
+// kernel's rows).  Three slab buffers: the slab of the tile after next is issued at
+// the start of a tile, two tiles ahead, and the wait for a slab leaves the newest
+// stores in flight.  Every wave holds
+// the A fragments of the block's 64 output channels for all K = 9 x 64 in registers
+// and reads its B fragment of tap (ky, kx), k-step ks straight from the slab: the
+// implicit GEMM's nine reads of every input row from L2 become one, and no weight
+// bytes move per tile.
+// OUTK: the epilogue's output kind (1 = 8-bit codes, 2 = raw int32, 3 = 4-bit codes).
+constexpr int kD3Buf = 16384;   // LDS bytes per slab buffer (4 rows of up to 62 pixels)
+constexpr int64_t kD3MinTiles = 512;
+
+template <int W, int OUTK, bool XORB>
+__global__ __launch_bounds__(256, 2) void qconv_direct3x3(const ConvParams p, int32_t n_tiles,
+                                                           int32_t tiles_per_img) {
+    constexpr int SW = W + 2;                       // slab columns: one pad column each side
+    constexpr int CHUNKS = 4 * SW * 4;              // 16-byte chunks of the four slab rows
+    constexpr int CPW = (CHUNKS + 255) / 256;       // DMA instructions per wave (64 chunks each)
+    static_assert(W % 2 == 0 && 2 * W <= 128, "two rows are at most four 32-pixel blocks");
+    static_assert(CPW * 4 * 1024 <= kD3Buf, "a slab fits one buffer");
+    __shared__ __attribute__((aligned(1024))) uint8_t slab[3][kD3Buf];
+    __shared__ __attribute__((aligned(16))) int32_t cbias[64];
+    __shared__ __attribute__((aligned(16))) float cmult[64];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int oc0 = (int)blockIdx.y * 64;
+    if ((int)blockIdx.x >= n_tiles) return;
+    if (tid < 64) {
+        cbias[tid] = p.bias[oc0 + tid];
+        cmult[tid] = p.mult[oc0 + tid];
+    }
+    // A fragments: packed rows oc0 + 32t + lane%32, K bytes 64 tap + 32 ks + 16 (lane/32)
+    v4i wa[2][9][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int tap = 0; tap < 9; ++tap)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                wa[t][tap][ks] = *reinterpret_cast<const v4i*>(p.w + (int64_t)(oc0 + 32 * t + (lane & 31)) * p.kp +
+                                                               64 * tap + 32 * ks + 16 * (lane >> 5));
+    __syncthreads();
+
+    const int h = p.h;
+    // Chunk q = (wave + 4j) * 64 + lane of a slab buffer (its bytes 16q..16q+15) is slab
+    // row q / (4 SW), column (q / 4) % SW, slot q % 4, and holds channel chunk
+    // slot ^ ((column >> 2) & 3) of input row oy0 - 1 + row, column - 1.  Per lane and DMA
+    // instruction j, fixed for the whole launch: the chunk's byte offset from the start
+    // of input row oy0 - 1, and its slab row minus one (iy - oy0), or a row no image has
+    // for the pad columns and the chunks past the slab.
+    int loff[CPW], rm1[CPW];
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+        const int q = (wave + 4 * j) * 64 + lane;   // < 4 * CPW * 64: inside the buffer
+        const int row = q / (SW * 4), rem = q - row * (SW * 4);
+        const int col = rem >> 2, slot = rem & 3;
+        const int chunk = slot ^ ((col >> 2) & 3);
+        const bool in_img_col = q < CHUNKS && col >= 1 && col <= W;
+        loff[j] = in_img_col ? (row * W + col - 1) * 64 + chunk * 16 : 0;
+        rm1[j] = in_img_col ? row - 1 : (1 << 30);   // h < 2^31 / 56 < 2^30
+    }
+    // Slab of tile `tile` into buffer `buf`: every lane issues its CPW DMA instructions
+    // (the waits count them), from the input where the chunk's row and column are in the
+    // image and from the 16 pad-code bytes of pad_row elsewhere.  Tiles never exceed the
+    // batch, so in-image rows and columns stay inside the n x h x W x 64 input.
+    auto issue = [&](int tile, int buf) {
+        const int n = tile / tiles_per_img;
+        const int oy0 = 2 * (tile - n * tiles_per_img);
+        const int64_t row0 = ((int64_t)n * h + oy0 - 1) * W * 64;   // input row oy0 - 1
+#pragma unroll
+        for (int j = 0; j < CPW; ++j) {
+            const void* src = (uint32_t)(oy0 + rm1[j]) < (uint32_t)h ? (const void*)(p.x + (row0 + loff[j]))
+                                                                     : (const void*)p.pad_row;
+            dma16_run<1>(lds_addr(&slab[buf][0]) + (wave + 4 * j) * 1024, &src);
+        }
+    };
+
+    const int frow = lane & 31;
+    const int i = min(wave * 32 + frow, 2 * W - 1);   // pixel of the row pair
+    const int r = i >= W ? 1 : 0, ox = i - r * W;
+    const bool px_ok = wave * 32 + frow < 2 * W;
+    const uint32_t bxor = XORB ? p.x_xor : 0u;
+    const int grid = (int)gridDim.x;
+    int buf = 0;
+    issue(blockIdx.x, 0);
+    if ((int)blockIdx.x + grid < n_tiles) issue(blockIdx.x + grid, 1);
+    bool stored = false;   // this wave issued the (at least two) stores of its previous tile
+    for (int tile = blockIdx.x; tile < n_tiles; tile += grid) {
+        // The memory counter retires loads and stores in issue order, so vmcnt <= N
+        // means all but the newest N operations are done.  Issued after this tile's
+        // slab: the next tile's slab (CPW DMA, if there is a next tile), the previous
+        // tile's stores (two or more, if any lane had a pixel) and possibly older stores:
+        // N = CPW + 2 waits for the slab and never for the newest stores.
+        if (tile + grid < n_tiles) {
+            if (stored) IQNN_WAIT_VM(CPW + 2);
+            else IQNN_WAIT_VM(CPW);
+        } else {
+            if (stored) IQNN_WAIT_VM(2);
+            else IQNN_WAIT_VM(0);
+        }
+        // every wave's part of the slab has landed, and every wave is done with the
+        // previous tile's buffer, which takes the slab of the tile after next
+        __builtin_amdgcn_s_barrier();
+        {
+            const int after = tile + 2 * grid;
+            if (after < n_tiles) issue(after, buf == 0 ? 2 : buf - 1);
+        }
+
+        v16i acc[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int ocl = t * 32 + (lane >> 5) * 16;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int4 bv = *reinterpret_cast<const int4*>(&cbias[ocl + 4 * q]);
+                acc[t][4 * q] = bv.x; acc[t][4 * q + 1] = bv.y; acc[t][4 * q + 2] = bv.z; acc[t][4 * q + 3] = bv.w;
+            }
+        }
+        const uint8_t* sb = &slab[buf][0];
+        // B fragment s = (tap, k-step) of this lane's pixel, read one step ahead of its
+        // two MFMAs (a scheduling barrier per step keeps the reads from piling up in
+        // registers next to the A fragments)
+        auto read_b = [&](int s) -> v4i {
+            const int tap = s >> 1, ks = s & 1;
+            const int ky = tap / 3, kx = tap - 3 * ky;
+            const int col = ox + kx;
+            return *reinterpret_cast<const v4i*>(sb + ((r + ky) * SW + col) * 64 +
+                                                 (((2 * ks + (lane >> 5)) ^ ((col >> 2) & 3)) << 4));
+        };
+        v4i fb = read_b(0);
+#pragma unroll
+        for (int s = 0; s < 18; ++s) {
+            v4i fn;
+            if (s + 1 < 18) fn = read_b(s + 1);
+            if constexpr (XORB) {
+                fb[0] ^= bxor; fb[1] ^= bxor; fb[2] ^= bxor; fb[3] ^= bxor;
+            }
+            acc[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wa[0][s >> 1][s & 1], fb, acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wa[1][s >> 1][s & 1], fb, acc[1], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (s + 1 < 18) fb = fn;
+        }
+        const int n = tile / tiles_per_img;
+        const int oy = 2 * (tile - n * tiles_per_img) + r;
+        const bool st = px_ok && oy < h;
+        stored = __builtin_amdgcn_ballot_w64(st) != 0;
+        if (st) {
+            const int64_t pix = ((int64_t)n * h + oy) * W + ox;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int ocl = t * 32 + (lane >> 5) * 16;
+                if (oc0 + ocl >= p.c_out) continue;
+                uint32_t rw[4] = {0, 0, 0, 0};
+                // multipliers read from LDS inside the epilogue: no register copy next to
+                // the 144 registers of A fragments
+                epi_store16<false, 2, false, OUTK>(p, acc[t], nullptr, &cmult[ocl], rw, oc0 + ocl, pix, false,
+                                                   0.0f);
+            }
+        }
+        buf = buf == 2 ? 0 : buf + 1;
+    }
+    // no DMA may still be writing this workgroup's LDS when it ends
+    IQNN_WAIT_VM(0);
+}
+
+}  // namespace
+
+// The direct 3x3 kernel's conditions: 8-bit activations with 64 channels, 3x3 / stride 1
+// / pad 1 on rows of 56 pixels (the instantiated width), C_out % 64 == 0, no residual,
+// the binary32 requant without the weight zero-point term.  The automatic choice also
+// asks for at least one two-row tile per workgroup slot (N x ceil(H / 2) >= 512), so
+// the per-workgroup weight load pays off.
+bool direct3x3_ok(const ConvParams& p, int gather, bool forced) {
+    if (gather != GATHER_B8 || p.c != 64 || p.kh != 3 || p.kw != 3 || p.sh != 1 || p.sw != 1) return false;
+    if (p.ph != 1 || p.pw != 1 || p.w_in != 56 || p.ow != 56 || p.oh != p.h) return false;
+    if (p.c_out % 64 != 0 || p.epi == E_ADD || p.epi == E_ADD_RELU || p.zw_red != 0 || p.int_rq) return false;
+    if (p.m >= ((int64_t)1 << 31)) return false;
+    return forced || (p.m / ((int64_t)p.oh * p.ow)) * ((p.oh + 1) / 2) >= kD3MinTiles;
+}
+
+hipError_t launch_direct3x3(const ConvParams& p, hipStream_t stream) {
+    const int64_t n_img = p.m / ((int64_t)p.oh * p.ow);
+    const int64_t tiles_per_img = (p.oh + 1) / 2;
+    const int64_t n_tiles = n_img * tiles_per_img;
+    if (n_tiles <= 0) return hipSuccess;
+    if (n_tiles >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    const int64_t oc_blocks = p.c_out / 64;
+    const int64_t per_block = std::min<int64_t>(n_tiles, std::max<int64_t>(1, 512 / oc_blocks));   // ~2 per CU
+    const dim3 grid((unsigned)per_block, (unsigned)oc_blocks);
+    const int32_t nt = (int32_t)n_tiles, tpi = (int32_t)tiles_per_img;
+    // signed activation codes are MFMA operands as they are; uint8 ones get the sign flip
+    const bool xorb = p.x_xor != 0;
+    if (p.epi == E_RAW) {
+        if (xorb) hipLaunchKernelGGL((qconv_direct3x3<56, 2, true>), grid, dim3(256), 0, stream, p, nt, tpi);
+        else hipLaunchKernelGGL((qconv_direct3x3<56, 2, false>), grid, dim3(256), 0, stream, p, nt, tpi);
+    } else if (p.y_type == T_INT8 || p.y_type == T_UINT8) {
+        if (xorb) hipLaunchKernelGGL((qconv_direct3x3<56, 1, true>), grid, dim3(256), 0, stream, p, nt, tpi);
+        else hipLaunchKernelGGL((qconv_direct3x3<56, 1, false>), grid, dim3(256), 0, stream, p, nt, tpi);
+    } else {
+        if (xorb) hipLaunchKernelGGL((qconv_direct3x3<56, 3, true>), grid, dim3(256), 0, stream, p, nt, tpi);
+        else hipLaunchKernelGGL((qconv_direct3x3<56, 3, false>), grid, dim3(256), 0, stream, p, nt, tpi);
+    }
+    return hipGetLastError();
+}
+
 bool pipe_eligible(int gather, int32_t c, int64_t k) {
     return (gather == GATHER_B8 && c % 64 == 0 && k % kPipeBK == 0) || gather == GATHER_C4;
 }
@@ -1917,6 +2138,11 @@ int pipe_tile_choice(int64_t m, int32_t c_out, int64_t k, bool res) {
 }
 
 hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_t stream, int tile) {
+    if (tile == kTileDirect3x3) {   // the direct kernel where it applies, else the automatic choice
+        if (direct3x3_ok(p, gather, true)) return launch_direct3x3(p, stream);
+        tile = -1;
+    }
+    if (tile < 0 && direct3x3_ok(p, gather, false)) return launch_direct3x3(p, stream);
     if (p.int_rq) {   // integer-only requantization runs on the register-staged kernel
         if (p.zw_red != 0) return hipErrorInvalidValue;
         if (p.c_out <= 64) return launch_staged<64, 256, 1, 4>(p, gather, is_1x1, stream);

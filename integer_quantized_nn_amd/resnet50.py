@@ -8,6 +8,14 @@ stage's first block, and a passive max pooling after the stem ("Quantization"
 blog, 量化激活函数).  One forward step is: quantize the fp32 input, 53 convs and
 one max pooling on one stream, dequantize the final output.  Every activation
 tensor keeps its own HBM buffer (the trunk needs a few GB at batch 256).
+
+Activations are uint8 codes with a per-tensor zero point (the article's asymmetric
+activation quantization).  With offset_codes the trunk stores every such code q as the
+int8 byte q - 128 with zero point Z - 128: the same real values, the same q - Z in every
+contraction, the same rounding decisions (rne(t) + Z and the clip bounds shift by the
+same 128), so every buffer holds the uint8 trunk's bytes XOR 0x80.  The kernels then
+take the activation bytes as signed MFMA operands directly instead of flipping the sign
+bit of every fragment.
 """
 import numpy as np
 import torch
@@ -25,13 +33,18 @@ class QuantResNet50Trunk:
     channels at a time.  A zero weight on the extra channel and the real-0 border make
     it the same convolution as the 3-channel padded one."""
 
-    def __init__(self, trunk, device="cuda", weight_codes=None, stream=None, fuse_stem_pool=True):
+    def __init__(self, trunk, device="cuda", weight_codes=None, stream=None, fuse_stem_pool=True,
+                 offset_codes=False):
         """trunk: synth.Trunk.  weight_codes: optional {layer name: OHWI int8 bytes};
         by default the float weights are quantized per output channel on the GPU.
         fuse_stem_pool: run the stem and the max pooling as one launch
-        (iqnn_qconv_maxpool_fwd), never writing the stem's output."""
+        (iqnn_qconv_maxpool_fwd), never writing the stem's output.  offset_codes:
+        store the uint8 activation codes as int8 bytes q - 128 (zero points Z - 128)."""
         self.trunk = trunk
         self.fuse_stem_pool = fuse_stem_pool
+        self.offset_codes = offset_codes
+        act, off = (B.INT8, 128) if offset_codes else (B.UINT8, 0)
+        self.act_type = act
         self.device = device
         n = trunk.batch
         self.convs = {}
@@ -52,22 +65,22 @@ class QuantResNet50Trunk:
             if layer is stem:   # padded 4-channel input, zero weights on the extra channel
                 w_bytes = np.pad(w_bytes.reshape(co, kh, kw, ci), ((0, 0), (0, 0), (0, 0), (0, STEM_PAD_CHANNELS - ci)))
                 h, w, ci, pad = h + 2 * pad, w + 2 * pad, STEM_PAD_CHANNELS, 0
-            conv = QConv(n, h, w, ci, co, kh, c.stride, pad, B.UINT8, B.INT8, B.UINT8, c.epi, c.z_in, c.z_out,
-                         w_bytes, c.bias, c.s_in, c.s_w, c.s_out, res_type=B.UINT8, z_res=c.z_res,
+            conv = QConv(n, h, w, ci, co, kh, c.stride, pad, act, B.INT8, act, c.epi, c.z_in - off, c.z_out - off,
+                         w_bytes, c.bias, c.s_in, c.s_w, c.s_out, res_type=act, z_res=c.z_res - off,
                          s_res=c.s_res, device=device, stream=stream)
             self.convs[layer.name] = conv
             self.shapes[layer.out] = conv.out_shape
             if layer.name == "stem":
                 oh, ow = conv.out_shape[1:3]
                 self.shapes["pool"] = (n, (oh + 2 - 3) // 2 + 1, (ow + 2 - 3) // 2 + 1, co)
-        self.bufs = {name: empty_codes(shape, B.UINT8, device) for name, shape in self.shapes.items()
+        self.bufs = {name: empty_codes(shape, act, device) for name, shape in self.shapes.items()
                      if not (fuse_stem_pool and name == "stem")}
         self.final = trunk.layers[-1].out
         s_f, z_f = trunk.qparams[self.final]
         self.final_scale = torch.tensor([s_f], dtype=torch.float32, device=device)
-        self.final_zp = torch.tensor([z_f], dtype=torch.int32, device=device)
+        self.final_zp = torch.tensor([z_f - off], dtype=torch.int32, device=device)
         self.in_scale = torch.tensor([trunk.s_in], dtype=torch.float32, device=device)
-        self.in_zp = torch.tensor([trunk.z_in], dtype=torch.int32, device=device)
+        self.in_zp = torch.tensor([trunk.z_in - off], dtype=torch.int32, device=device)
         self.out_f32 = torch.empty(self.shapes[self.final], dtype=torch.float32, device=device)
 
     def run_codes(self, stream=None, events=None):
@@ -88,15 +101,15 @@ class QuantResNet50Trunk:
                 events[i][1].record()
             if layer.name == "stem" and not self.fuse_stem_pool:
                 n, h, w, c = self.shapes["stem"]
-                maxpool2d(b["stem"], n, h, w, c, 3, 2, 1, B.UINT8, out=b["pool"], stream=stream)
+                maxpool2d(b["stem"], n, h, w, c, 3, 2, 1, self.act_type, out=b["pool"], stream=stream)
         return b[self.final]
 
     def step(self, x_f32, stream=None, events=None):
         """One full forward: quantize -> trunk -> dequantize.  Returns fp32 NHWC output."""
-        quantize_pad(x_f32, self.in_scale, self.in_zp, B.UINT8, self.stem_pad, STEM_PAD_CHANNELS,
+        quantize_pad(x_f32, self.in_scale, self.in_zp, self.act_type, self.stem_pad, STEM_PAD_CHANNELS,
                      out=self.bufs["input"], stream=stream)
         self.run_codes(stream, events)
-        dequantize(self.bufs[self.final], self.shapes[self.final], self.final_scale, self.final_zp, B.UINT8,
+        dequantize(self.bufs[self.final], self.shapes[self.final], self.final_scale, self.final_zp, self.act_type,
                    out=self.out_f32, stream=stream)
         return self.out_f32
 

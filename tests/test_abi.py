@@ -39,9 +39,9 @@ def test_version_and_status_strings(lib):
 
 
 def test_conv_tile_override_range(lib):
-    for t in (0, 17, -1):
+    for t in (0, 17, 18, -1):
         B.iqnn_set_conv_tile(t)
-    for bad in (-2, 18):
+    for bad in (-2, 19):
         with pytest.raises(B.IqnnError) as ei:
             B.iqnn_set_conv_tile(bad)
         assert ei.value.status == 1 and "tile" in str(ei.value)

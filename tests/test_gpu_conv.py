@@ -98,6 +98,60 @@ def test_stem_fused_max_pooling(n, hw, y_type, epi):
     assert_bytes_equal(y.cpu().numpy(), want, "stem+pool %s" % ((n, hw, y_type, epi),))
 
 
+# 64-channel 3x3 / stride 1 / pad 1 layers on 56-pixel rows (the direct kernel, forced at
+# any batch through tile 18: one slab of input rows per two output rows): odd heights (a
+# tile's second row outside the image), several 64-channel output blocks, signed codes,
+# raw accumulators, padding-dominated two-row images, and batches with more two-row tiles
+# than workgroups (each workgroup walks several tiles through its three slab buffers;
+# the oracle checks the listed images)
+DIRECT = [
+    # n, h, c_out, x_type, y_type, epi, images checked (None: all)
+    (2, 56, 64, U8, U8, RELU, None),
+    (1, 7, 128, U8, I8, NONE, None),
+    (3, 2, 64, I8, U8, RELU, None),
+    (1, 5, 192, U8, U8, NONE, None),
+    (2, 3, 64, U8, I32, RAW, None),
+    (20, 56, 64, U8, I32, RAW, (0, 19)),
+    (45, 55, 128, U8, U8, RELU, (0, 22, 44)),
+]
+
+
+@pytest.mark.parametrize("case", DIRECT, ids=lambda c: "n%dh%dco%d_x%dy%de%d" % c[:6])
+def test_conv_direct3x3_64ch(case):
+    require_gpu()
+    from integer_quantized_nn_amd import binding as B
+    n, h, co, xt, yt, epi, images = case
+    c = synth.conv_case(hash(case[:6]) % 2 ** 31, n, h, 56, 64, co, 3, 1, 1, xt, I8, yt, epi)
+    x, wc, _ = conv_codes(c)
+    B.iqnn_set_conv_tile(18)
+    try:
+        got = gpu_conv(c, x, wc, None)
+    finally:
+        B.iqnn_set_conv_tile(-1)
+    sel = list(images) if images is not None else None
+    want = to_bytes(oracle_conv(c, x, wc, None, sel), yt)
+    assert_bytes_equal(got if sel is None else got[sel], want, str(case))
+
+
+def test_conv_direct3x3_automatic_large_batch():
+    """From 512 two-row tiles the automatic choice takes the direct kernel: batch 80
+    of the 56x56 64->64 Conv_Relu layer, sampled images against the oracle, every image
+    against the streaming kernel (tile 11)."""
+    require_gpu()
+    from integer_quantized_nn_amd import binding as B
+    c = synth.conv_case(4242, 80, 56, 56, 64, 64, 3, 1, 1, U8, I8, U8, RELU)
+    x, wc, _ = conv_codes(c)
+    got = gpu_conv(c, x, wc, None)
+    images = [0, 1, 40, 79]
+    assert_bytes_equal(got[images], to_bytes(oracle_conv(c, x, wc, None, images), U8), "direct, batch 80")
+    B.iqnn_set_conv_tile(11)
+    try:
+        other = gpu_conv(c, x, wc, None)
+    finally:
+        B.iqnn_set_conv_tile(-1)
+    assert_bytes_equal(got, other, "direct vs streaming kernel, batch 80")
+
+
 # 8-bit layers with C_in % 64 == 0 (the pipelined kernel): ring depths that do not
 # divide the stage count, one-stage contractions, ragged pixel tails and channel
 # counts that are not multiples of any block

@@ -32,31 +32,35 @@ def _codes(tr):
     return x, w
 
 
-def _run_gpu(tr, x, w):
+def _run_gpu(tr, x, w, offset=False):
     import torch
     from integer_quantized_nn_amd.resnet50 import QuantResNet50Trunk
-    net = QuantResNet50Trunk(tr, weight_codes={k: O.pack(v, O.INT8) for k, v in w.items()})
+    net = QuantResNet50Trunk(tr, weight_codes={k: O.pack(v, O.INT8) for k, v in w.items()}, offset_codes=offset)
     # the trunk's input buffer is the image with the stem's border and a 4th channel,
     # all holding the input zero-point code
     p = net.stem_pad
     xp = np.pad(x, ((0, 0), (p, p), (p, p), (0, 1)), constant_values=tr.z_in)
-    net.bufs["input"].copy_(torch.from_numpy(O.pack(xp, O.UINT8)))
+    net.bufs["input"].copy_(torch.from_numpy(O.pack(xp, O.UINT8) ^ np.uint8(0x80 if offset else 0)))
     net.run_codes()
     torch.cuda.synchronize()
     return net
 
 
-def test_trunk_every_layer_small_batch():
-    """Batch 2 at 224x224: every intermediate tensor of both images, byte for byte."""
+@pytest.mark.parametrize("offset", [False, True], ids=["uint8", "offset_int8"])
+def test_trunk_every_layer_small_batch(offset):
+    """Batch 2 at 224x224: every intermediate tensor of both images, byte for byte.
+    With offset codes (uint8 code q stored as the int8 byte q - 128, zero points
+    shifted alike) every buffer holds the uint8 oracle's bytes XOR 0x80."""
     require_gpu()
     tr = synth.resnet50_trunk(seed=3, batch=2)
     x, w = _codes(tr)
-    net = _run_gpu(tr, x, w)
+    net = _run_gpu(tr, x, w, offset)
     ref = oracle_trunk(tr, x, w, [0, 1])
+    flip = np.uint8(0x80 if offset else 0)
     for name, buf in net.bufs.items():
         if name == "input":
             continue
-        assert_bytes_equal(buf.cpu().numpy(), O.pack(ref[name], O.UINT8), name)
+        assert_bytes_equal(buf.cpu().numpy(), O.pack(ref[name], O.UINT8) ^ flip, name)
 
 
 def test_trunk_full_batch_sampled_images():
@@ -69,29 +73,35 @@ def test_trunk_full_batch_sampled_images():
     images = [0, 255]
     ref = oracle_trunk(tr, x, w, images)
     final = tr.layers[-1].out
-    # the full step exactly as the benchmark runs it: float input, GPU-quantized weights
-    net = QuantResNet50Trunk(tr)
-    xd = torch.from_numpy(tr.x).cuda()
-    y = net.step(xd)
-    torch.cuda.synchronize()
-    got_codes = net.bufs[final].cpu().numpy()[images]
-    assert_bytes_equal(got_codes, O.pack(ref[final], O.UINT8), "trunk output codes")
     s_f, z_f = tr.qparams[final]
     want_f = O.dequantize(ref[final], s_f, z_f)
-    assert np.array_equal(y.cpu().numpy()[images].view(np.uint32), want_f.view(np.uint32))
+    xd = torch.from_numpy(tr.x).cuda()
+    # the full step as the benchmark runs it (float input, GPU-quantized weights), with
+    # uint8 codes and with the offset int8 storage the benchmark uses
+    for offset in (False, True):
+        net = QuantResNet50Trunk(tr, offset_codes=offset)
+        y = net.step(xd)
+        torch.cuda.synchronize()
+        got_codes = net.bufs[final].cpu().numpy()[images]
+        flip = np.uint8(0x80 if offset else 0)
+        assert_bytes_equal(got_codes, O.pack(ref[final], O.UINT8) ^ flip, "trunk output codes, offset %s" % offset)
+        assert np.array_equal(y.cpu().numpy()[images].view(np.uint32), want_f.view(np.uint32)), offset
+        del net, y
+        torch.cuda.empty_cache()
     # discrimination: the outputs span many codes and rarely saturate
     for name in ("stem", "l1.0.out", "l3.5.out", final):
         q = ref[name]
         assert len(np.unique(q)) >= 32 and (q == 255).mean() < 0.02, name
 
 
-def test_trunk_graph_replay_matches_eager():
+@pytest.mark.parametrize("offset", [False, True], ids=["uint8", "offset_int8"])
+def test_trunk_graph_replay_matches_eager(offset):
     """The step captured in a HIP graph and replayed three times, with other eager
     work and synchronisations in between, gives the eager step's bytes each time."""
     torch = require_gpu()
     from integer_quantized_nn_amd.resnet50 import QuantResNet50Trunk
     tr = synth.resnet50_trunk(seed=5, batch=2)
-    net = QuantResNet50Trunk(tr)
+    net = QuantResNet50Trunk(tr, offset_codes=offset)
     x = torch.from_numpy(tr.x).cuda()
     want = net.step(x).clone()
     want_codes = net.bufs[tr.layers[-1].out].clone()
