@@ -185,7 +185,7 @@ def bench_trunk(args):
     roof["frac"] = roof["achieved"] / roof["peak"]
     tr_bytes = measured_traffic("resnet50_trunk_b%d" % args.batch)
     roof["traffic"] = tr_bytes
-    roof["kernel"] = "qconv (qconv_stream / qconv_pipe / qconv_igemm; %d launches per step)" % n_conv
+    roof["kernel"] = "qconv (qconv_stem_pool / qconv_direct3x3 / qconv_stream; %d launches per step)" % n_conv
     roof["algorithmic_bytes_per_launch"] = bytes_per_launch
     roof["algorithmic_ops_per_launch"] = ops_per_launch
     roof["avg_launch_us"] = avg_dur * 1e6
