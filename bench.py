@@ -254,8 +254,9 @@ def bench_layer(args):
         y_bytes = n * oh * ow * co // (2 if c.y_type in (synth.UINT4, synth.INT4) else 1)
         nbytes = xd.numel() + w_bytes + y_bytes + (rd.numel() if rd is not None else 0)
         run = lambda: layer(xd, res=rd)
-    elif wl in ("vitl_fc1", "gemm_int8_256"):
-        g = synth.vitl_fc1() if wl == "vitl_fc1" else synth.gemm_int8_256()
+    elif wl in ("vitl_fc1", "vitl_fc1_2of4", "gemm_int8_256"):
+        sparse = wl == "vitl_fc1_2of4"   # weights magnitude-pruned to 2:4 along K, on the sparse MFMA
+        g = synth.vitl_fc1(sparse_2of4=sparse) if wl.startswith("vitl") else synth.gemm_int8_256()
         m, n, k = g.shape
         if g.b_codes is not None:
             b_bytes = O.pack(g.b_codes, O.INT8)
@@ -263,10 +264,13 @@ def bench_layer(args):
         else:
             b_bytes = quantize(torch.from_numpy(g.b).cuda(), g.s_b, 0, g.b_type, axis=0).cpu().numpy()
             a_dev = quantize(torch.from_numpy(g.a).cuda(), g.s_a, g.z_a, g.a_type)
-        layer = QGemm(m, n, k, g.a_type, g.b_type, g.c_type, g.epi, g.z_a, g.z_out, b_bytes, g.bias, g.s_a, g.s_b,
-                      g.s_out)
+        from integer_quantized_nn_amd import binding as IB
+        layer = QGemm(m, n, k, g.a_type, IB.INT8_2OF4 if sparse else g.b_type, g.c_type, g.epi, g.z_a, g.z_out,
+                      b_bytes, g.bias, g.s_a, g.s_b, g.s_out)
+        # ops: the dense problem's 2*M*N*K (with 2:4 weights half the products are with zero
+        # codes and the kernel skips them); bytes: 2:4 weights move kept codes + positions
         ops = 2 * m * n * k
-        nbytes = m * k + n * k + m * n
+        nbytes = m * k + (n * k // 2 + n * k // 8 if sparse else n * k) + m * n
         run = lambda: layer(a_dev)
     else:
         raise SystemExit("unknown workload " + wl)
@@ -315,7 +319,9 @@ def bench_layer(args):
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": span * 1e3 / args.steps,
             "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
-            "config": {"workload": wl, "ops": ops, "algorithmic_bytes": nbytes, "cache": "warm (inputs reused)"},
+            "config": {"workload": wl, "ops": ops, "algorithmic_bytes": nbytes, "cache": "warm (inputs reused)",
+                       **({"ops_note": "dense-equivalent 2*M*N*K; the 2:4 weights make half of the products "
+                                       "zero, which the sparse MFMA skips"} if wl.endswith("2of4") else {})},
             "pct_int8_mfma_peak": ops / avg / PEAK_INT8_OPS, "roofline": roof, "cpu_baseline": None}
 
 
@@ -327,7 +333,7 @@ def main():
     ap.add_argument("--batch", type=int, default=256)
     ap.add_argument("--workload", default="resnet50_trunk",
                     choices=["resnet50_trunk", "conv3x3_int8", "conv3x3_4bit", "conv3x3_uint8w", "conv3x3_intrq",
-                             "vitl_fc1", "gemm_int8_256"])
+                             "vitl_fc1", "vitl_fc1_2of4", "gemm_int8_256"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="trunk: time eager launches instead of one captured HIP graph per step")

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define IQNN_ABI_VERSION 2
+#define IQNN_ABI_VERSION 3
 
 typedef enum {
     IQNN_OK = 0,
@@ -66,7 +66,20 @@ typedef enum {
     IQNN_UINT8 = 1,
     IQNN_INT4 = 2,
     IQNN_UINT4 = 3,
-    IQNN_INT32 = 4   /* raw accumulator output only */
+    IQNN_INT32 = 4,  /* raw accumulator output only */
+    /* Weights only: INT8 codes, symmetric (z_w = 0), in which every group of four
+     * consecutive K positions (four consecutive input channels of one filter tap;
+     * four consecutive K of a GEMM row) holds at most two nonzero codes: 2:4
+     * structured sparsity (Horizon QAT talk, section 三: sparse plus quantized
+     * weights).  The codes are given dense (OHWI / [N][K], zeros included); prepack
+     * keeps two codes per group with their positions and fails with
+     * IQNN_ERR_INVALID_ARG naming the channel and group when a group has more than
+     * two nonzero codes.  The forward result is that of the same codes as INT8; the
+     * kernel contracts only the kept half (the sparse int8 MFMA).  Needs 8-bit
+     * activations, C_in % 64 == 0 (GEMM: K % 64 == 0), KH*KW <= 64, N*OH*OW < 2^31,
+     * the binary32 epilogue, and for ADD / ADD_RELU an 8-bit residual with
+     * C_out % 16 == 0; otherwise IQNN_ERR_UNSUPPORTED. */
+    IQNN_INT8_2OF4 = 5
 } iqnn_dtype;
 
 /* Fused epilogues (MegEngine 4-bit article, section 算子融合優化: Conv_Relu and
@@ -97,7 +110,8 @@ typedef enum {
 /* Convolution descriptor.  Dilation 1, groups 1.  Output size
  * OH = (H + 2*pad_h - KH)/stride_h + 1, OW likewise.
  * x_type: INT8, UINT8, INT4 or UINT4.  w_type: INT8, UINT8, INT4 or UINT4 with
- * the per-tensor weight zero point z_w (INT8 / INT4 with z_w = 0 are symmetric).
+ * the per-tensor weight zero point z_w (INT8 / INT4 with z_w = 0 are symmetric),
+ * or INT8_2OF4 (2:4-sparse symmetric INT8, see iqnn_dtype).
  * y_type: INT8, UINT8, INT4, UINT4, or INT32 with IQNN_EPI_RAW_INT32.
  * res_type: type of the residual for ADD / ADD_RELU (8- or 4-bit), else ignored.
  * z_in / z_out / z_res / z_w: zero points, within the code range of their type.

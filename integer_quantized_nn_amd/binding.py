@@ -15,6 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libiqnn.so")
 
 INT8, UINT8, INT4, UINT4, INT32 = 0, 1, 2, 3, 4
+INT8_2OF4 = 5          # weights only: 2:4-sparse symmetric int8 codes
 EPI_NONE, EPI_RELU, EPI_ADD, EPI_ADD_RELU, EPI_RAW_INT32 = 0, 1, 2, 3, 4
 EPI_INT_REQUANT = 16   # flag: integer-only requantization (with NONE or RELU)
 STATUS = {0: "IQNN_OK", 1: "IQNN_ERR_INVALID_ARG", 2: "IQNN_ERR_UNSUPPORTED", 3: "IQNN_ERR_ALIGNMENT",

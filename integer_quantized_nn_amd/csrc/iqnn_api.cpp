@@ -21,6 +21,15 @@
 
 namespace iqnn {
 
+int xcd_groups_override() {
+    static const int v = [] {
+        const char* e = std::getenv("IQNN_XCD_OC_GROUPS");
+        const int g = (e && *e) ? std::atoi(e) : 0;
+        return (g == 1 || g == 2 || g == 4 || g == 8) ? g : 0;
+    }();
+    return v;
+}
+
 PackGeom pack_geom(int64_t c_out, int64_t k) {
     PackGeom g;
     g.ocp = (int32_t)((c_out + kOcPad - 1) / kOcPad * kOcPad);
@@ -63,6 +72,7 @@ bool code_range(int32_t t, int32_t* lo, int32_t* hi) {
     }
 }
 bool is_code_type(int32_t t) { int32_t a, b; return code_range(t, &a, &b); }
+bool is_sparse(int32_t w_type) { return w_type == T_INT8_2OF4; }
 bool is_4bit(int32_t t) { return t == T_INT4 || t == T_UINT4; }
 bool in_range(int32_t t, int32_t z) {
     int32_t lo, hi;
@@ -111,8 +121,21 @@ iqnn_status check_layer(const Layer& L) {
     if (L.c_out > (1 << 24) || L.k > (1 << 24))
         return fail(IQNN_ERR_UNSUPPORTED, "C_out or K above 2^24");
     if (!is_code_type(L.x_type)) return fail(IQNN_ERR_INVALID_ARG, "activation type %d is not a code type", L.x_type);
-    if (!is_code_type(L.w_type)) return fail(IQNN_ERR_INVALID_ARG, "weight type %d is not a code type", L.w_type);
-    if (!in_range(L.w_type, L.z_w)) return fail(IQNN_ERR_INVALID_ARG, "z_w %d outside the weight code range", L.z_w);
+    if (is_sparse(L.w_type)) {
+        // 2:4 weights: symmetric int8 codes on the sparse streaming kernel
+        if (L.z_w != 0) return fail(IQNN_ERR_INVALID_ARG, "2:4 weights are symmetric int8 codes (z_w must be 0)");
+        const bool add = L.epi == E_ADD || L.epi == E_ADD_RELU;
+        const bool is_1x1 = L.kh == 1 && L.kw == 1;
+        if (is_4bit(L.x_type) || L.c % 64 != 0 || L.m >= ((int64_t)1 << 31) ||
+            (!is_1x1 && (int64_t)L.kh * L.kw > 64) || L.int_rq ||
+            (add && (is_4bit(L.res_type) || L.c_out % 16 != 0)))
+            return fail(IQNN_ERR_UNSUPPORTED,
+                        "2:4 weights need 8-bit activations, C_in %% 64 == 0, KH*KW <= 64, N*OH*OW < 2^31, the "
+                        "binary32 requantization and an 8-bit residual with C_out %% 16 == 0");
+    } else {
+        if (!is_code_type(L.w_type)) return fail(IQNN_ERR_INVALID_ARG, "weight type %d is not a code type", L.w_type);
+        if (!in_range(L.w_type, L.z_w)) return fail(IQNN_ERR_INVALID_ARG, "z_w %d outside the weight code range", L.z_w);
+    }
     if (zw_red(L) != 0) {
         // the per-pixel term rides on the streaming kernel's 8-bit gather
         const bool add = L.epi == E_ADD || L.epi == E_ADD_RELU;
@@ -238,6 +261,53 @@ bool b4_stream(const Layer& L) {
     return true;
 }
 
+// One output channel of 2:4 weights in the sparse kernel's layout (PackGeom): the
+// weights are stored as the LDS image of every (128-row channel tile, 64-K stage)
+// block, 5120 bytes each: 128 rows of 32 bytes of kept codes, then 128 rows of 8 bytes
+// of positions.  A row's kept codes are, for each group of four K positions, the two
+// kept codes in K order (zeros where fewer than two are nonzero); its 16-byte half h
+// (K [32h, 32h + 32) of the stage) sits at slot h ^ ((row >> 3) & 1) of the row (the
+// kernel's conflict-free LDS swizzle).  The positions of half h are the 32-bit word h,
+// group g of the half in bits 4g..4g+3.  More than two nonzero codes in a group is an
+// error (the weights are not 2:4 sparse).
+iqnn_status pack_sparse_row(const std::vector<int32_t>& row, const PackGeom& g, int32_t oc, int8_t* wp) {
+    const int64_t prow = packed_row_of_channel(oc);
+    const int64_t tile = prow / kSpRows, r = prow % kSpRows;
+    const int64_t nst = g.kp / 64;
+    const int64_t k = (int64_t)row.size();
+    for (int64_t s = 0; s < nst; ++s) {
+        int8_t* blk = wp + (tile * nst + s) * kSpBlock;
+        for (int64_t h = 0; h < 2; ++h) {
+            int8_t* vals = blk + r * 32 + ((h ^ ((r >> 3) & 1)) * 16);
+            uint32_t word = 0;
+            for (int64_t gi = 0; gi < 8; ++gi) {
+                const int64_t k0 = s * 64 + h * 32 + gi * 4;
+                int kept[2], n = 0;
+                for (int j = 0; j < 4; ++j) {
+                    const int32_t v = k0 + j < k ? row[(size_t)(k0 + j)] : 0;
+                    if (v == 0) continue;
+                    if (n == 2)
+                        return fail(IQNN_ERR_INVALID_ARG,
+                                    "2:4 weights: channel %d has more than two nonzero codes in K %lld..%lld", oc,
+                                    (long long)k0, (long long)k0 + 3);
+                    kept[n++] = j;
+                }
+                // fill with zero positions, keeping the two positions distinct and increasing
+                for (int j = 0; n < 2 && j < 4; ++j)
+                    if (!(n == 1 && kept[0] == j)) kept[n++] = j;
+                if (kept[0] > kept[1]) std::swap(kept[0], kept[1]);
+                for (int q = 0; q < 2; ++q) {
+                    const int64_t kk = k0 + kept[q];
+                    vals[2 * gi + q] = (int8_t)(kk < k ? row[(size_t)kk] : 0);
+                    word |= (uint32_t)kept[q] << (4 * gi + 2 * q);
+                }
+            }
+            std::memcpy(blk + kSpRows * 32 + r * 8 + h * 4, &word, 4);
+        }
+    }
+    return IQNN_OK;
+}
+
 // Writes the packed layer (layout in PackGeom) into host memory `dst` of g.bytes.
 iqnn_status prepack_into(const Layer& L, const void* w_host, const float* bias_host, float s_in,
                          const float* s_w_host, int per_channel, float s_out, float s_res, uint8_t* dst) {
@@ -272,7 +342,7 @@ iqnn_status prepack_into(const Layer& L, const void* w_host, const float* bias_h
         for (int64_t k = 0; k < L.k; ++k) {
             int64_t e = oc * L.k + k;
             int32_t v;
-            if (L.w_type == T_INT8) {
+            if (L.w_type == T_INT8 || is_sparse(L.w_type)) {
                 v = (int8_t)wb[e];
             } else if (L.w_type == T_UINT8) {
                 v = (int32_t)wb[e] - 128;   // held as q_W - 128
@@ -318,6 +388,11 @@ iqnn_status prepack_into(const Layer& L, const void* w_host, const float* bias_h
             }
         } else {
             mult[oc] = 1.0f;
+        }
+        if (is_sparse(L.w_type)) {
+            iqnn_status st = pack_sparse_row(row, g, (int32_t)oc, wp);
+            if (st != IQNN_OK) return st;
+            continue;
         }
         int8_t* dst = wp + (int64_t)packed_row_of_channel((int32_t)oc) * g.kp;
         for (int64_t k = 0; k < L.k; ++k) {
@@ -378,6 +453,8 @@ void conv_params(const Layer& L, const void* x, const void* packed, const void* 
     p.mult = reinterpret_cast<const float*>(static_cast<const uint8_t*>(packed) + (size_t)g.ocp * 4);
     p.m_res = reinterpret_cast<const float*>(static_cast<const uint8_t*>(packed) + (size_t)g.ocp * 8 + kHdrMres);
     p.pad_row = static_cast<const uint8_t*>(packed) + (size_t)g.ocp * 8 + kHdrPad;
+    // 2:4 weights: w_idx marks the sparse layout (the positions sit inside each block)
+    p.w_idx = is_sparse(L.w_type) ? static_cast<const uint8_t*>(packed) + g.w_off + kSpRows * 32 : nullptr;
     p.res = add ? static_cast<const uint8_t*>(res) : nullptr;
     p.y = static_cast<uint8_t*>(y);
     p.m = L.m;

@@ -8,7 +8,7 @@
 namespace iqnn {
 
 // Element types, same numbering as iqnn_dtype.
-enum : int32_t { T_INT8 = 0, T_UINT8 = 1, T_INT4 = 2, T_UINT4 = 3, T_INT32 = 4 };
+enum : int32_t { T_INT8 = 0, T_UINT8 = 1, T_INT4 = 2, T_UINT4 = 3, T_INT32 = 4, T_INT8_2OF4 = 5 };
 enum : int32_t { E_NONE = 0, E_RELU = 1, E_ADD = 2, E_ADD_RELU = 3, E_RAW = 4 };
 
 // Activation gather modes of the implicit-GEMM kernel.
@@ -25,6 +25,9 @@ enum : int32_t {
 //   [4*ocp, 8*ocp)        float  requant multiplier M[c]
 //   [8*ocp, 8*ocp+256)    header: float M_res at +0, 64 pad-code bytes at +64
 //   [w_off, w_off+ocp*kp) int8   weights, rows in kernel order, K padded to kp
+//   2:4 weights (T_INT8_2OF4) use the first 5/8 of that region instead, as blocks of
+//   kSpBlock bytes, one per (kSpRows-row channel tile, 64-K stage), tile-major: the
+//   sparse kernel's LDS image of the stage (kept codes, then positions)
 struct PackGeom {
     int32_t ocp;    // output channels padded to a multiple of kOcPad
     int32_t kp;     // K padded to a multiple of kKPad
@@ -35,6 +38,8 @@ struct PackGeom {
 constexpr int kOcPad = 256;   // largest block extent along output channels
 constexpr int kKPad = 64;     // one MFMA K step
 constexpr int kBK = 128;      // K elements staged per pipeline step
+constexpr int kSpRows = 128;                  // 2:4 weights: channel rows per block
+constexpr int kSpBlock = kSpRows * (32 + 8);  // 2:4 weights: bytes per (tile, stage) block
 
 PackGeom pack_geom(int64_t c_out, int64_t k);
 
@@ -71,6 +76,7 @@ struct ConvParams {
     int32_t group_px;         // pixel tiles per rasterization group (set by the launcher)
     int32_t gx;               // streaming kernel: workgroups per XCD (set by the launcher)
     int32_t px_chunk;         // streaming kernel: pixel tiles per XCD share (set by the launcher)
+    int32_t xo_groups;        // streaming kernel: channel-tile groups across the XCDs (set by the launcher)
     uint32_t pad_word;        // four copies of the staged padding byte
     uint32_t x_xor;           // 0x80808080 for UINT8 activations, else 0
     int32_t x_signed4;        // INT4 activations: sign-extend nibbles
@@ -79,6 +85,7 @@ struct ConvParams {
     int32_t zw_red;           // s_w - Z_w: coefficient of the per-pixel activation sum (0: none)
     const float* m_res;       // residual multiplier S_res/S_out (in the packed buffer)
     const uint8_t* pad_row;   // 64 bytes of the raw input zero-point code (in the packed buffer)
+    const uint8_t* w_idx;     // 2:4 weights: the positions of block 0 (non-null marks the 2:4 layout)
     // Epilogue constants (host-computed).  The requantized value is clipped to
     // [t_lo, t_hi] = [Q_MIN (or max(Q_MIN, Z_out) with ReLU), Q_MAX] - Z_out, then
     // out_magic = 1.5 * 2^23 + (Z_out minus its odd part) is added, which rounds to
@@ -101,11 +108,15 @@ struct ConvParams {
 
 // tile < 0 picks the kernel and its tile configuration from the layer shape; 0..17
 // force a block configuration of the ring / streaming kernels, kTileDirect3x3 the
-// direct 3x3 kernel on the layers it takes (the IQNN_FORCE_TILE environment variable
+// direct 3x3 kernel on the layers it takes (2:4-sparse layers always take their own
+// 128x128 configuration) (the IQNN_FORCE_TILE environment variable
 // or iqnn_set_conv_tile, for tuning sweeps and tests).
 constexpr int kTileDirect3x3 = 18;
 constexpr int kMaxTile = 18;
 hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_t stream, int tile);
+// Channel-tile groups of the streaming kernel's XCD split, forced for tuning sweeps
+// (IQNN_XCD_OC_GROUPS = 1, 2, 4 or 8); 0: the automatic rule.
+int xcd_groups_override();
 
 // The image stem (4-channel padding-free input, stride 2) fused with 3x3 / stride 2 /
 // pad 1 max pooling of its codes into yp [N][OH/2][OW/2][64].

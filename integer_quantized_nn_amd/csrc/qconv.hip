@@ -52,6 +52,7 @@ namespace iqnn {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* gbl_ptr_t;
@@ -1020,6 +1021,22 @@ __device__ __forceinline__ void dma4_seq(uint32_t lds, const void* const* src) {
     }
 }
 
+// 4-byte DMA of N = 1 or 2 256-byte instructions to consecutive LDS from one m0.
+template <int N>
+__device__ __forceinline__ void dma4_short(uint32_t lds, const void* const* src) {
+    static_assert(N == 1 || N == 2, "short 4-byte runs");
+    const uint32_t m = __builtin_amdgcn_readfirstlane(lds);
+    const char* q0 = static_cast<const char*>(src[0]);
+    if constexpr (N == 1) {
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(m), "v"(q0)
+                     : "memory", "m0");
+    } else {
+        const char* q1 = static_cast<const char*>(src[1]) - 256;
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\t"
+                     "global_load_lds_dword %2, off offset:256" ::"s"(m), "v"(q0), "v"(q1) : "memory", "m0");
+    }
+}
+
 // OCC_: workgroups per CU to compile for (0: as many as the LDS allows, at most 2);
 // 3 caps the kernel at 168 VGPRs.
 template <int BM_, int BN_, int WM_, int NST_, int OCC_ = 0>
@@ -1038,21 +1055,37 @@ struct StreamCfg {
 // to the contraction (one v_dot4 with ones per 16 bytes of a B fragment; lanes l and
 // l+32 hold the two K halves of pixel l%32) and zw_red times it is added to every
 // channel of the pixel before the epilogue.
-template <class C, bool IS1X1, bool RES, bool C4, bool B4 = false, bool ZW = false>
+// SP: 2:4 structured-sparse weights on the sparse MFMA (v_smfmac_i32_32x32x64_i8).  A
+// stage's 64 K positions of a weight row are 32 bytes of kept codes (two per group of
+// four K positions, in K order) and 8 bytes of 2-bit positions; lane half h of a
+// 32-row fragment holds the kept codes of K [32h, 32h + 32) and their 16 positions
+// (measured lane layout: kept code v pairs with B bytes 16h + 4*(v/2 % 4) + pos of
+// B lane half v/8), and the B operand is the two 16-byte activation fragments the
+// dense path reads for its two k-steps.  One sparse MFMA per stage replaces two.
+template <class C, bool IS1X1, bool RES, bool C4, bool B4 = false, bool ZW = false, bool SP = false>
 __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) {
     constexpr int BM = C::BM, BN = C::BN, WM = C::WM, NST = C::NST;
     constexpr int TM = C::TM, TN = C::TN;
     constexpr int BROW = B4 ? 32 : kPipeBK;           // bytes of an activation row per stage
-    constexpr int STAGE = BM * kPipeBK + BN * BROW;   // bytes of one ring slot
-    constexpr int A_INST = BM / 64;                   // weight rows: 16 per instruction per wave
+    constexpr int AROW = SP ? 32 : kPipeBK;           // bytes of a weight row per stage (2:4: kept codes)
+    constexpr int IROW = SP ? 8 : 0;                  // bytes of a weight row's sparse positions per stage
+    constexpr int A_BYTES = BM * (AROW + IROW);       // weight part of a ring slot
+    constexpr int RROW = B4 ? BM / 2 : BM;            // bytes of a residual row
+    constexpr int STAGE_K = A_BYTES + BN * BROW;
+    constexpr int STAGE = (RES && BN * RROW > STAGE_K) ? BN * RROW : STAGE_K;   // bytes of one ring slot
+    constexpr int A_INST = SP ? BM / 128 : BM / 64;   // weight rows: 32 (2:4) or 16 per instruction per wave
+    constexpr int I_INST = SP ? BM / 128 : 0;         // sparse positions: 32 rows per 4-byte instruction
     // activation rows per instruction: 16 (8-bit), 32 (4-bit), 4 (4-channel gather)
     constexpr int B_INST = C4 ? BN / 16 : (B4 ? BN / 128 : BN / 64);
-    constexpr int K_LOADS = A_INST + B_INST;          // DMA instructions per wave per stage
-    constexpr int RROW = B4 ? BM / 2 : BM;            // bytes of a residual row
+    constexpr int K_LOADS = A_INST + I_INST + B_INST;   // DMA instructions per wave per stage
     constexpr int R_INST = RES ? BN * RROW / 4096 : 0;   // residual: 1 KB per instruction per wave
     constexpr int D = NST - 1;                        // stages issued ahead
     static_assert(TM >= 1 && TN >= 1 && A_INST >= 1 && B_INST >= 1 && BN % 64 == 0, "tile shape");
-    static_assert(C4 || K_LOADS * 4096 == STAGE, "a stage is K_LOADS KB-instructions per wave");
+    static_assert(C4 || SP || K_LOADS * 4096 == STAGE, "a stage is K_LOADS KB-instructions per wave");
+    static_assert(!SP || ((A_INST + B_INST) * 4096 + I_INST * 1024 == STAGE_K && BM % 128 == 0),
+                  "a 2:4 stage: kept codes and activations in KB-instructions, positions in 256-byte ones");
+    static_assert(!SP || !(B4 || C4 || ZW), "2:4 weights take the 8-bit gather with symmetric weights");
+    static_assert(!(SP && RES) || 4 * K_LOADS * 1024 <= STAGE, "the padded residual stage fits a slot");
     static_assert(!(B4 && C4), "one gather mode");
     static_assert(NST >= 3, "ring depth");
     static_assert(D * K_LOADS <= 60, "DMA in flight must fit the 6-bit vmcnt");
@@ -1072,11 +1105,13 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
     const int wave_px = wave / WM;
 
     // ------------------------------------------------------------ schedule
+    // XCD x owns channel group x % xo_groups (n_oc of its channel tiles) and pixel share
+    // x / xo_groups: with more than one channel group an XCD's weights stay in its L2
     const int xcd = blockIdx.x & 7, widx = blockIdx.x >> 3;
-    const int n_oc = p.n_oc_tiles;
-    const int oc_t = widx % n_oc;
+    const int n_oc = p.n_oc_tiles / p.xo_groups;
+    const int oc_t = (xcd % p.xo_groups) * n_oc + widx % n_oc;
     const int member = widx / n_oc, members = p.gx / n_oc;
-    const int chunk0 = xcd * p.px_chunk;
+    const int chunk0 = (xcd / p.xo_groups) * p.px_chunk;
     const int chunk_len = min(p.px_chunk, p.n_px_tiles - chunk0);
     const int J = chunk_len > member ? (chunk_len - member + members - 1) / members : 0;
     if (J <= 0) return;
@@ -1101,10 +1136,22 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
     const int dslot = lane & 3;
     const uint8_t* padrow = p.pad_row;
     const int8_t* wsrc[A_INST];
+    const uint8_t* isrc[SP ? I_INST : 1];
 #pragma unroll
     for (int j = 0; j < A_INST; ++j) {
-        const int row = wave * (BM / 4) + 16 * j + drow;
-        wsrc[j] = p.w + (int64_t)(oc0 + row) * p.kp + (dslot ^ swz(row)) * 16;
+        if constexpr (SP) {   // the block is the stage's LDS image: straight 1 KB copies
+            wsrc[j] = p.w + (int64_t)oc_t * nst * kSpBlock + (wave * A_INST + j) * 1024 + lane * 16;
+        } else {
+            const int row = wave * (BM / 4) + 16 * j + drow;
+            wsrc[j] = p.w + (int64_t)(oc0 + row) * p.kp + (dslot ^ swz(row)) * 16;
+        }
+    }
+    if constexpr (SP) {   // positions follow the kept codes in the block: 256-byte copies
+        static_assert(!SP || BM == kSpRows, "2:4 blocks hold kSpRows channel rows");
+#pragma unroll
+        for (int j = 0; j < I_INST; ++j)
+            isrc[j] = reinterpret_cast<const uint8_t*>(p.w) + (int64_t)oc_t * nst * kSpBlock + BM * AROW +
+                      (wave * I_INST + j) * 256 + lane * 4;
     }
     // Per-tile state of the tile being issued.  Activation rows (B) are pixels:
     //   1x1:    prow = the pixel's row + its 16-byte segment; rows past the end point at
@@ -1219,8 +1266,14 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
             const int k0 = is_s * kPipeBK;
             const void* as[A_INST];
 #pragma unroll
-            for (int j = 0; j < A_INST; ++j) as[j] = wsrc[j] + k0;
-            dma16_seq<A_INST>(dst + wave * (BM / 4) * kPipeBK, as);
+            for (int j = 0; j < A_INST; ++j) as[j] = wsrc[j] + (SP ? (int64_t)is_s * kSpBlock : (int64_t)k0);
+            dma16_seq<A_INST>(dst + wave * (BM / 4) * AROW, as);
+            if constexpr (SP) {
+                const void* is[I_INST];
+#pragma unroll
+                for (int j = 0; j < I_INST; ++j) is[j] = isrc[j] + (int64_t)is_s * kSpBlock;
+                dma4_short<I_INST>(dst + BM * AROW + wave * (BM / 4) * IROW, is);
+            }
             const void* bs[B_INST];
             if constexpr (C4) {
                 const int32_t rows = is_s * (16 / p.kw);   // filter rows advanced since stage 0
@@ -1238,7 +1291,7 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
                     if constexpr (IS1X1) bs[i] = prow[i] + (k0 >> SH);
                     else bs[i] = ((tmask[i] >> tap) & 1) ? prow[i] + (tapoff >> SH) : padrow;
                 }
-                dma16_seq<B_INST>(dst + BM * kPipeBK + wave * (BN / 4) * BROW, bs);
+                dma16_seq<B_INST>(dst + A_BYTES + wave * (BN / 4) * BROW, bs);
             }
         }
         is_off = is_off + STAGE == NST * STAGE ? 0 : is_off + STAGE;
@@ -1353,19 +1406,91 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
         issue();
     };
 
+    // 2:4 weights: the fragments of one stage (kept codes, positions, both activation
+    // k-steps); two sets alternate so the next stage is read during this one's MFMAs
+    struct SpFrag {
+        v4i a[SP ? TM : 1];
+        int ix[SP ? TM : 1];
+        v4i b0[SP ? TN : 1], b1[SP ? TN : 1];
+    };
+    auto read_sp = [&](const uint8_t* cur, SpFrag& f) {
+        if constexpr (SP) {
+#pragma unroll
+            for (int t = 0; t < TM; ++t) {
+                const int row = wave_oc * C::WOC + 32 * t + frow;
+                f.a[t] = *reinterpret_cast<const v4i*>(cur + row * AROW + (((lane >> 5) ^ swz4(row)) * 16));
+                f.ix[t] = *reinterpret_cast<const int*>(cur + BM * AROW + row * IROW + (lane >> 5) * 4);
+            }
+#pragma unroll
+            for (int u = 0; u < TN; ++u) {
+                const uint8_t* brow = cur + A_BYTES + (wave_px * C::WPX + 32 * u) * kPipeBK;
+                f.b0[u] = *reinterpret_cast<const v4i*>(brow + foff0);
+                f.b1[u] = *reinterpret_cast<const v4i*>(brow + foff1);
+            }
+        }
+    };
+    auto smfmacs = [&](SpFrag& f, int lo, int hi) {
+        if constexpr (SP) {
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+#pragma unroll
+                for (int u = 0; u < TN; ++u)
+                    if (t * TN + u >= lo && t * TN + u < hi) {
+                        const v8i b = {f.b0[u][0], f.b0[u][1], f.b0[u][2], f.b0[u][3],
+                                       f.b1[u][0], f.b1[u][1], f.b1[u][2], f.b1[u][3]};
+                        acc[t][u] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(f.a[t], b, acc[t][u], f.ix[t], 0, 0);
+                    }
+        }
+    };
+    SpFrag fx, fy;
+
     for (int i = 0; i < D; ++i) issue();
     uint32_t cur_off = 0;
     auto advance = [&]() { cur_off = cur_off + STAGE == NST * STAGE ? 0 : cur_off + STAGE; };
     sync();
-    read_frags(ring + cur_off, foff0, fa0, fb0);
+    if constexpr (SP) read_sp(ring + cur_off, fx);
+    else read_frags(ring + cur_off, foff0, fa0, fb0);
 
     constexpr int NMF = TM * TN, NRD = TM + TN, HALF = NMF / 2;
     // residual epilogues run only with the residual stage (the host routes the rest to
     // qconv_pipe), so no global load of the epilogue is ever pending in the loop
     constexpr bool add = RES;
     const float m_res = RES ? *p.m_res : 0.0f;
+    // one 2:4 stage: the uint8 shift of its activation fragments, the first half of its
+    // MFMAs, the stage barrier (and the DMA refill), the next stage's fragment reads
+    // next to the second half
+    auto sp_stage = [&](SpFrag& f, SpFrag& nf, bool more, bool do_sync) {
+        if constexpr (SP) {
+#pragma unroll
+            for (int u = 0; u < TN; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    f.b0[u][i] ^= bxor;
+                    f.b1[u][i] ^= bxor;
+                }
+            __builtin_amdgcn_sched_barrier(0);
+            smfmacs(f, 0, HALF);
+            __builtin_amdgcn_sched_barrier(0);
+            advance();
+            if (do_sync) sync();
+            if (more) read_sp(ring + cur_off, nf);
+            smfmacs(f, HALF, NMF);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
     for (int j = 0; j < J; ++j) {
         const bool last_tile = j + 1 == J;
+        if constexpr (SP) {
+            for (int s = 0; s < nst; s += 2) {
+                const bool end0 = s + 1 == nst;
+                sp_stage(fx, fy, !end0, !(last_tile && end0 && !RES));
+                if (!end0) {
+                    const bool end1 = s + 2 == nst;
+                    sp_stage(fy, fx, !end1, !(last_tile && end1 && !RES));
+                }
+            }
+        } else
         for (int s = 0; s < nst; ++s) {
             const uint8_t* cur = ring + cur_off;
             shift_b(fb0, 0);
@@ -1436,10 +1561,43 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
             advance();
             if (!last_tile) sync();
         }
-        if (!last_tile) read_frags(ring + cur_off, foff0, fa0, fb0);
+        if (!last_tile) {
+            if constexpr (SP) read_sp(ring + cur_off, fx);
+            else read_frags(ring + cur_off, foff0, fa0, fb0);
+        }
     }
     // no DMA may still be writing this workgroup's LDS when it ends
     IQNN_WAIT_VM(0);
+}
+
+// Persistent schedule of the streaming kernel over the 8 XCDs (workgroup ids are dealt
+// round-robin, so workgroup i runs on XCD i % 8).  The channel tiles are split into
+// xo_groups groups (1, 2, 4 or 8, dividing the tile count) and the pixel tiles into
+// 8 / xo_groups shares; XCD x takes group x % xo_groups and share x / xo_groups.  Its
+// workgroups, about occ per CU (32 CUs per XCD) and a multiple of its channel tiles,
+// each keep one channel tile and walk a strided run of the share's pixel tiles.
+// xo_groups > 1 keeps an XCD's weights (its channel groups' rows) resident in its 4 MB
+// L2 when all of a layer's weights are too large for that; the rule takes the
+// smallest split that brings them to at most kXcdWeightBytes.
+constexpr int64_t kXcdWeightBytes = 2 << 20;
+void stream_schedule(ConvParams& q, int occ) {
+    const int n_oc_all = q.n_oc_tiles;
+    int xo = 1;
+    const int forced = xcd_groups_override();
+    if (forced > 0) {
+        xo = forced;
+    } else {
+        const int64_t w_bytes = (int64_t)q.c_out * q.kp * (q.w_idx ? 5 : 8) / 8;
+        while (xo < 8 && w_bytes / xo > kXcdWeightBytes && n_oc_all % (2 * xo) == 0) xo *= 2;
+    }
+    while (xo > 1 && n_oc_all % xo != 0) xo /= 2;
+    q.xo_groups = xo;
+    const int n_oc = n_oc_all / xo;
+    const int shares = 8 / xo;
+    q.px_chunk = (int32_t)((q.n_px_tiles + shares - 1) / shares);
+    int per = n_oc * std::max(1, occ * 32 / n_oc);
+    per = (int)std::min<int64_t>(per, (int64_t)q.px_chunk * n_oc);
+    q.gx = per;
 }
 
 template <class C>
@@ -1451,14 +1609,8 @@ hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bo
     if (n_px <= 0) return hipSuccess;
     if (p.m >= ((int64_t)1 << 31) || (!is_1x1 && !c4 && p.kh * p.kw > 64)) return hipErrorInvalidValue;
     q.n_px_tiles = (int32_t)n_px;
-    q.px_chunk = (int32_t)((n_px + 7) / 8);
-    // workgroups per XCD: a multiple of the channel tiles, about OCC per CU (32 CUs per
-    // XCD), no more than there are tiles in one XCD's share
-    const int n_oc = q.n_oc_tiles;
-    int per = n_oc * std::max(1, C::OCC * 32 / n_oc);
-    per = std::min<int64_t>(per, (int64_t)q.px_chunk * n_oc);
-    q.gx = per;
-    dim3 g((unsigned)(8 * per)), b(256);
+    stream_schedule(q, C::OCC);
+    dim3 g((unsigned)(8 * q.gx)), b(256);
     if (b4) {   // 4-bit activations: the 64x128 and 128x128 configurations only
         if constexpr (C::OCC < 3 && C::BN == 128 && ((C::BM == 64 && C::NST == 6) || (C::BM == 128 && C::NST == 4))) {
             const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;
@@ -1509,6 +1661,51 @@ hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bo
     else
         hipLaunchKernelGGL((qconv_stream<C, false, false, false>), g, b, 0, stream, q);
     return hipGetLastError();
+}
+
+// Block configuration of the 2:4 kernel: a stage is 40 bytes per weight row (kept
+// codes + positions) and 64 per pixel row.
+template <int BM_, int BN_, int WM_, int NST_>
+struct StreamCfg2of4 {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = 4 / WM_, NST = NST_;
+    static constexpr int WOC = BM / WM, WPX = BN / WN;
+    static constexpr int TM = WOC / 32, TN = WPX / 32;
+    static constexpr int STAGE = BM * 40 + BN * kPipeBK;
+    static constexpr int LDS = NST * STAGE + 8 * BM;
+    static constexpr int OCC = 160 * 1024 / LDS >= 2 ? 2 : 1;
+};
+
+// 2:4-sparse weights: 128x128 blocks, two per CU (199-236 VGPRs), the schedule of the
+// dense streaming kernel.  Without a residual the 13 KB stages allow a ring of 6 (five
+// stages in flight); the residual stage needs 16 KB slots, so a ring of 4.
+template <class C>
+hipError_t launch_stream_2of4_cfg(const ConvParams& p, bool is_1x1, hipStream_t stream) {
+    ConvParams q = p;
+    q.n_oc_tiles = (p.c_out + C::BM - 1) / C::BM;
+    const int64_t n_px = (p.m + C::BN - 1) / C::BN;
+    if (n_px <= 0) return hipSuccess;
+    if (p.m >= ((int64_t)1 << 31) || (!is_1x1 && p.kh * p.kw > 64)) return hipErrorInvalidValue;
+    q.n_px_tiles = (int32_t)n_px;
+    stream_schedule(q, C::OCC);
+    dim3 g((unsigned)(8 * q.gx)), b(256);
+    const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;
+    if constexpr (C::NST * C::BN * C::BM + 8 * C::BM <= 80 * 1024) {   // residual slots fit two per CU
+        if (is_1x1 && add) hipLaunchKernelGGL((qconv_stream<C, true, true, false, false, false, true>), g, b, 0, stream, q);
+        else if (add) hipLaunchKernelGGL((qconv_stream<C, false, true, false, false, false, true>), g, b, 0, stream, q);
+    } else if (add) {
+        return hipErrorInvalidValue;
+    }
+    if (!add) {
+        if (is_1x1) hipLaunchKernelGGL((qconv_stream<C, true, false, false, false, false, true>), g, b, 0, stream, q);
+        else hipLaunchKernelGGL((qconv_stream<C, false, false, false, false, false, true>), g, b, 0, stream, q);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_stream_2of4(const ConvParams& p, bool is_1x1, hipStream_t stream) {
+    const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;
+    if (add) return launch_stream_2of4_cfg<StreamCfg2of4<128, 128, 2, 4>>(p, is_1x1, stream);
+    return launch_stream_2of4_cfg<StreamCfg2of4<128, 128, 2, 6>>(p, is_1x1, stream);
 }
 
 // ============================================================ stem kernel
@@ -2138,6 +2335,13 @@ int pipe_tile_choice(int64_t m, int32_t c_out, int64_t k, bool res) {
 }
 
 hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_t stream, int tile) {
+    if (p.w_idx) {   // 2:4 weights: their packed layout is the sparse streaming kernel's
+        const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;
+        const bool res_prefetch = add && p.vec_store && (p.res_type == T_INT8 || p.res_type == T_UINT8);
+        if (gather != GATHER_B8 || !pipe_eligible(gather, p.c, p.k) || p.zw_red != 0 || (add && !res_prefetch))
+            return hipErrorInvalidValue;
+        return launch_stream_2of4(p, is_1x1, stream);
+    }
     if (tile == kTileDirect3x3) {   // the direct kernel where it applies, else the automatic choice
         if (direct3x3_ok(p, gather, true)) return launch_direct3x3(p, stream);
         tile = -1;

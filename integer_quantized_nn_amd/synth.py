@@ -193,22 +193,37 @@ def conv3x3_4bit(seed=0, n=64, hw=28, c=128):
                      name="conv3x3_4bit")
 
 
-def vitl_fc1(seed=0, m=64 * 197, k=1024, n=4096, outlier_frac=0.02, outlier_max=40.0):
+def prune_2of4(w):
+    """Magnitude pruning to 2:4 structured sparsity along the last axis: in every group
+    of four consecutive entries the two of largest |w| are kept (the earlier one on a
+    tie), the other two set to 0.  The last axis must be a multiple of 4."""
+    g = w.reshape(-1, 4)
+    order = np.argsort(-np.abs(g), axis=1, kind="stable")
+    keep = np.zeros(g.shape, bool)
+    np.put_along_axis(keep, order[:, :2], True, axis=1)
+    return np.where(keep, g, np.float32(0)).reshape(w.shape).astype(w.dtype)
+
+
+def vitl_fc1(seed=0, m=64 * 197, k=1024, n=4096, outlier_frac=0.02, outlier_max=40.0, sparse_2of4=False):
     """ViT-L MLP fc1 as a GEMM: N(0,1) activations with 2% of channels scaled by U[1,40]
     (the FQ-ViT article's inter-channel range observation), uint8 per-tensor min-max;
-    int8 per-channel weights N(0, 0.02); per-channel requant to int8, no activation."""
+    int8 per-channel weights N(0, 0.02); per-channel requant to int8, no activation.
+    sparse_2of4: the float weights magnitude-pruned to 2:4 along K before quantization."""
     rng = np.random.default_rng(seed)
     a = rng.standard_normal((m, k), dtype=np.float32)
     n_out = int(round(outlier_frac * k))
     ch = rng.choice(k, size=n_out, replace=False)
     a[:, ch] *= rng.uniform(1.0, outlier_max, size=n_out).astype(np.float32)
     b = rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
+    if sparse_2of4:
+        b = prune_2of4(b)
     bias = rng.standard_normal(n, dtype=np.float32) * np.float32(0.1)
     s_a, z_a = minmax_qparams(a.min(), a.max(), UINT8)
     s_b = sym_scales(b, 0, INT8)
     cal = a[:197].astype(np.float64) @ b.astype(np.float64).T + bias
     s_out = f32(float(np.abs(cal).max()) / 127)
-    return GemmCase("vitl_fc1", a, None, b, None, bias, s_a, z_a, s_b, s_out, 0, UINT8, INT8, INT8, EPI_NONE)
+    return GemmCase("vitl_fc1_2of4" if sparse_2of4 else "vitl_fc1", a, None, b, None, bias, s_a, z_a, s_b, s_out, 0,
+                    UINT8, INT8, INT8, EPI_NONE)
 
 
 # ------------------------------------------------------------ ResNet-50 trunk

@@ -9,7 +9,8 @@ import oracle as O
 LIB_T = {"INT8": 0, "UINT8": 1, "INT4": 2, "UINT4": 3, "INT32": 4}
 # oracle numbering, matched by name (the two sides define their own constants)
 ORC_T = {"INT8": O.INT8, "UINT8": O.UINT8, "INT4": O.INT4, "UINT4": O.UINT4, "INT32": O.INT32}
-T_NAME = {0: "INT8", 1: "UINT8", 2: "INT4", 3: "UINT4", 4: "INT32"}
+T_NAME = {0: "INT8", 1: "UINT8", 2: "INT4", 3: "UINT4", 4: "INT32",
+          5: "INT8"}   # IQNN_INT8_2OF4: 2:4-sparse weights are dense INT8 codes to the oracle
 EPI_NAME = {0: "NONE", 1: "RELU", 2: "ADD", 3: "ADD_RELU", 4: "RAW"}
 ORC_EPI = {"NONE": O.EPI_NONE, "RELU": O.EPI_RELU, "ADD": O.EPI_ADD, "ADD_RELU": O.EPI_ADD_RELU, "RAW": O.EPI_RAW}
 
