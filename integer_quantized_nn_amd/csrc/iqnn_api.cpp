@@ -35,7 +35,8 @@ PackGeom pack_geom(int64_t c_out, int64_t k) {
     g.ocp = (int32_t)((c_out + kOcPad - 1) / kOcPad * kOcPad);
     g.kp = (int32_t)((k + kKPad - 1) / kKPad * kKPad);
     g.w_off = (int64_t)g.ocp * 8 + 256;
-    g.bytes = g.w_off + (int64_t)g.ocp * g.kp;
+    g.t_off = g.w_off + (int64_t)g.ocp * g.kp;
+    g.bytes = g.t_off + (int64_t)g.ocp * g.kp;
     return g;
 }
 
@@ -410,6 +411,20 @@ iqnn_status prepack_into(const Layer& L, const void* w_host, const float* bias_h
             return fail(IQNN_ERR_INVALID_ARG, "residual multiplier is not a normal float in [FLT_MIN, 1e20]");
         mres[0] = m;
     }
+    if (!is_sparse(L.w_type)) {
+        // tile-order copy for the streaming kernel: block (row / 64, stage) holds, for
+        // each of its 64 rows, the stage's four 16-byte K segments at slots q ^ swz(row)
+        const int64_t nst = g.kp / 64;
+        int8_t* tp = reinterpret_cast<int8_t*>(dst + g.t_off);
+        for (int64_t r = 0; r < g.ocp; ++r) {
+            const int64_t sw = (r >> 2) & 3;
+            for (int64_t s = 0; s < nst; ++s) {
+                int8_t* blk = tp + ((r / 64) * nst + s) * 4096 + (r % 64) * 64;
+                for (int64_t q = 0; q < 4; ++q)
+                    std::memcpy(blk + q * 16, wp + r * g.kp + s * 64 + (q ^ sw) * 16, 16);
+            }
+        }
+    }
     return ok();
 }
 
@@ -449,6 +464,7 @@ void conv_params(const Layer& L, const void* x, const void* packed, const void* 
     std::memset(&p, 0, sizeof p);
     p.x = static_cast<const uint8_t*>(x);
     p.w = reinterpret_cast<const int8_t*>(static_cast<const uint8_t*>(packed) + g.w_off);
+    p.w_tiled = reinterpret_cast<const int8_t*>(static_cast<const uint8_t*>(packed) + g.t_off);
     p.bias = static_cast<const int32_t*>(packed);
     p.mult = reinterpret_cast<const float*>(static_cast<const uint8_t*>(packed) + (size_t)g.ocp * 4);
     p.m_res = reinterpret_cast<const float*>(static_cast<const uint8_t*>(packed) + (size_t)g.ocp * 8 + kHdrMres);

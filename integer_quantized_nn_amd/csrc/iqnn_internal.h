@@ -28,10 +28,15 @@ enum : int32_t {
 //   2:4 weights (T_INT8_2OF4) use the first 5/8 of that region instead, as blocks of
 //   kSpBlock bytes, one per (kSpRows-row channel tile, 64-K stage), tile-major: the
 //   sparse kernel's LDS image of the stage (kept codes, then positions)
+//   [t_off, t_off+ocp*kp) int8   the same weights in tile order for the streaming
+//                                kernel: 4 KB blocks, one per (64-row group, 64-K
+//                                stage), group-major; a block is the stage's LDS image
+//                                (row r's 16-byte K segment q at slot q ^ ((r >> 2) & 3))
 struct PackGeom {
     int32_t ocp;    // output channels padded to a multiple of kOcPad
     int32_t kp;     // K padded to a multiple of kKPad
     int64_t w_off;
+    int64_t t_off;
     int64_t bytes;
 };
 
@@ -60,6 +65,7 @@ constexpr int kHdrPad = 64;     // 64 bytes of the input zero-point code (the pa
 struct ConvParams {
     const uint8_t* x;
     const int8_t* w;          // packed weights [ocp][kp]
+    const int8_t* w_tiled;    // the same weights in 64-row, 64-K blocks (streaming kernel)
     const int32_t* bias;      // [ocp]
     const float* mult;        // [ocp]
     const uint8_t* res;       // residual codes or nullptr

@@ -1141,9 +1141,9 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
     for (int j = 0; j < A_INST; ++j) {
         if constexpr (SP) {   // the block is the stage's LDS image: straight 1 KB copies
             wsrc[j] = p.w + (int64_t)oc_t * nst * kSpBlock + (wave * A_INST + j) * 1024 + lane * 16;
-        } else {
-            const int row = wave * (BM / 4) + 16 * j + drow;
-            wsrc[j] = p.w + (int64_t)(oc0 + row) * p.kp + (dslot ^ swz(row)) * 16;
+        } else {   // 16 rows of the tile-order copy: one contiguous 1 KB piece of a 4 KB block
+            const int row0 = oc0 + wave * (BM / 4) + 16 * j;
+            wsrc[j] = p.w_tiled + ((int64_t)(row0 >> 6) * nst) * 4096 + (row0 & 63) * 64 + lane * 16;
         }
     }
     if constexpr (SP) {   // positions follow the kept codes in the block: 256-byte copies
@@ -1266,7 +1266,7 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
             const int k0 = is_s * kPipeBK;
             const void* as[A_INST];
 #pragma unroll
-            for (int j = 0; j < A_INST; ++j) as[j] = wsrc[j] + (SP ? (int64_t)is_s * kSpBlock : (int64_t)k0);
+            for (int j = 0; j < A_INST; ++j) as[j] = wsrc[j] + (int64_t)is_s * (SP ? kSpBlock : 4096);
             dma16_seq<A_INST>(dst + wave * (BM / 4) * AROW, as);
             if constexpr (SP) {
                 const void* is[I_INST];
