@@ -103,34 +103,28 @@ __device__ __forceinline__ int32_t code_at(const uint32_t* w, int j, int32_t qty
     return nib;
 }
 
-// One thread per 16 elements; QT and PC (per-channel parameters) fixed per
-// instantiation.
+// One thread per 4 elements, so a wave's float4 stores are 1 KB contiguous; QT and
+// PC (per-channel parameters) fixed per instantiation.
 template <int QT, bool PC>
 __global__ __launch_bounds__(256) void dequantize_kernel(const DequantParams p) {
-    const int64_t chunk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t e0 = chunk * 16;
+    const int64_t e0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
     if (e0 >= p.total) return;
-    const int n = (int)((p.total - e0) < 16 ? (p.total - e0) : 16);
+    const int n = (int)((p.total - e0) < 4 ? (p.total - e0) : 4);
     constexpr bool four = QT == T_INT4 || QT == T_UINT4;
-    uint32_t w[4] = {0, 0, 0, 0};
-    if (n == 16) {
-        if (four) {
-            uint2 v = *reinterpret_cast<const uint2*>(p.q + e0 / 2);
-            w[0] = v.x; w[1] = v.y;
-        } else {
-            uint4 v = *reinterpret_cast<const uint4*>(p.q + e0);
-            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-        }
+    uint32_t w[1] = {0};
+    if (n == 4) {
+        if (four) w[0] = *reinterpret_cast<const uint16_t*>(p.q + e0 / 2);
+        else w[0] = *reinterpret_cast<const uint32_t*>(p.q + e0);
     } else {
         const int nb = four ? n / 2 : n;
         const uint8_t* src = p.q + (four ? e0 / 2 : e0);
-        for (int j = 0; j < nb; ++j) w[j >> 2] |= (uint32_t)src[j] << (8 * (j & 3));
+        for (int j = 0; j < nb; ++j) w[0] |= (uint32_t)src[j] << (8 * j);
     }
-    float out[16];
+    float out[4];
     if (PC) {
         ChanCursor cur(e0, p.ch, p.inner);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int j = 0; j < 4; ++j) {
             float centred = (float)(code_at(w, j, QT) - p.zp[cur.c]);
             out[j] = centred * p.scale[cur.c];
             cur.next(p.ch, p.inner);
@@ -139,15 +133,13 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const DequantParams p) 
         const float s = p.scale[0];
         const int32_t z = p.zp[0];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int j = 0; j < 4; ++j) {
             float centred = (float)(code_at(w, j, QT) - z);
             out[j] = centred * s;
         }
     }
-    if (n == 16) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<float4*>(p.x + e0 + 4 * j) = make_float4(out[4 * j], out[4 * j + 1], out[4 * j + 2], out[4 * j + 3]);
+    if (n == 4) {
+        *reinterpret_cast<float4*>(p.x + e0) = make_float4(out[0], out[1], out[2], out[3]);
     } else {
         for (int j = 0; j < n; ++j) p.x[e0 + j] = out[j];
     }
@@ -252,7 +244,7 @@ hipError_t launch_quantize(const QuantParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_dequantize(const DequantParams& p, hipStream_t stream) {
-    const int64_t chunks = (p.total + 15) / 16;
+    const int64_t chunks = (p.total + 3) / 4;
     if (chunks == 0) return hipSuccess;
     const int64_t blocks = (chunks + 255) / 256;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;

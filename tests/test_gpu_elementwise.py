@@ -81,25 +81,28 @@ def test_maxpool_parity(dt):
 
 
 @pytest.mark.parametrize("per_channel", [False, True])
-def test_quantize_pad_parity(per_channel):
-    # padded layout == oracle quantize of the interior, zero-point code everywhere else
+@pytest.mark.parametrize("shape", [(3, 11, 9, 3), (2, 7, 12, 3), (2, 5, 8, 4), (1, 3, 1400, 3)],
+                         ids=["c3", "c3_w12", "c4", "long_row"])
+def test_quantize_pad_parity(per_channel, shape):
+    """Padded layout == oracle quantize of the interior, zero-point code everywhere else,
+    for 3- and 4-channel images, long rows and several paddings / padded channel counts."""
     torch = require_gpu()
     from integer_quantized_nn_amd.layers import quantize_pad
-    rng = np.random.default_rng(400 + per_channel)
-    x = (rng.standard_normal((3, 11, 9, 3)) * 2).astype(np.float32)
+    n, h, w, c = shape
+    rng = np.random.default_rng(400 + per_channel + w)
+    x = (rng.standard_normal(shape) * 2).astype(np.float32)
     if per_channel:
-        s, z = np.array([0.02, 0.03, 0.05], np.float32), np.array([100, 7, 255], np.int32)
+        s = np.array([0.02, 0.03, 0.05, 0.04][:c], np.float32)
+        z = np.array([100, 7, 255, 31][:c], np.int32)
     else:
         s, z = np.float32(0.021), 119
-    for pad, cp in ((3, 4), (0, 3), (1, 8)):
+    for pad, cp in ((3, 4), (0, max(c, 3)), (1, 8)):
         q = O.quantize(x, s, z, O.UINT8)
-        zc = np.broadcast_to(np.atleast_1d(z), (3,)) if per_channel else np.full(3, z)
-        want = np.empty((3, 11 + 2 * pad, 9 + 2 * pad, cp), np.int32)
-        want[...] = zc[0] if not per_channel else 0
-        if per_channel:
-            # border pixels take each channel's zero point, extra channels the first one's
-            want[..., :3] = zc
-            want[..., 3:] = zc[0]
-        want[:, pad:pad + 11, pad:pad + 9, :3] = q
+        zc = np.broadcast_to(np.atleast_1d(z), (c,)) if per_channel else np.full(c, z)
+        want = np.empty((n, h + 2 * pad, w + 2 * pad, cp), np.int32)
+        # border pixels take each channel's zero point, extra channels the first one's
+        want[..., :c] = zc
+        want[..., c:] = zc[0]
+        want[:, pad:pad + h, pad:pad + w, :c] = q
         got = quantize_pad(torch.from_numpy(x).cuda(), s, z, 1, pad, cp).cpu().numpy()
         assert_bytes_equal(got, O.pack(want, O.UINT8), "quantize_pad pad=%d cp=%d" % (pad, cp))
