@@ -1039,12 +1039,13 @@ __device__ __forceinline__ void dma4_short(uint32_t lds, const void* const* src)
 
 // OCC_: workgroups per CU to compile for (0: as many as the LDS allows, at most 2);
 // 3 caps the kernel at 168 VGPRs.
-template <int BM_, int BN_, int WM_, int NST_, int OCC_ = 0>
+// BROW_: bytes of an activation row per stage (32 for packed 4-bit activations).
+template <int BM_, int BN_, int WM_, int NST_, int OCC_ = 0, int BROW_ = kPipeBK>
 struct StreamCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = 4 / WM_, NST = NST_;
     static constexpr int WOC = BM / WM, WPX = BN / WN;
     static constexpr int TM = WOC / 32, TN = WPX / 32;
-    static constexpr int STAGE = (BM + BN) * kPipeBK;
+    static constexpr int STAGE = BM * kPipeBK + BN * BROW_;
     static constexpr int LDS = NST * STAGE + 8 * BM;
     static constexpr int LDS_FIT = 160 * 1024 / LDS;   // 160 KB of LDS per CU
     static constexpr int OCC = OCC_ > 0 ? OCC_ : (LDS_FIT >= 2 ? 2 : 1);
@@ -1600,6 +1601,25 @@ void stream_schedule(ConvParams& q, int occ) {
     q.gx = per;
 }
 
+// 4-bit activations (packed rows streamed to LDS): the 64x128 and 128x128 blocks.
+template <class C>
+hipError_t launch_stream_b4(const ConvParams& p, bool is_1x1, hipStream_t stream) {
+    ConvParams q = p;
+    q.n_oc_tiles = (p.c_out + C::BM - 1) / C::BM;
+    const int64_t n_px = (p.m + C::BN - 1) / C::BN;
+    if (n_px <= 0) return hipSuccess;
+    if (p.m >= ((int64_t)1 << 31) || (!is_1x1 && p.kh * p.kw > 64)) return hipErrorInvalidValue;
+    q.n_px_tiles = (int32_t)n_px;
+    stream_schedule(q, C::OCC);
+    dim3 g((unsigned)(8 * q.gx)), b(256);
+    const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;
+    if (is_1x1 && add) hipLaunchKernelGGL((qconv_stream<C, true, true, false, true>), g, b, 0, stream, q);
+    else if (is_1x1) hipLaunchKernelGGL((qconv_stream<C, true, false, false, true>), g, b, 0, stream, q);
+    else if (add) hipLaunchKernelGGL((qconv_stream<C, false, true, false, true>), g, b, 0, stream, q);
+    else hipLaunchKernelGGL((qconv_stream<C, false, false, false, true>), g, b, 0, stream, q);
+    return hipGetLastError();
+}
+
 template <class C>
 hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bool c4, hipStream_t stream,
                          bool b4 = false, bool zw = false) {
@@ -1611,17 +1631,7 @@ hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bo
     q.n_px_tiles = (int32_t)n_px;
     stream_schedule(q, C::OCC);
     dim3 g((unsigned)(8 * q.gx)), b(256);
-    if (b4) {   // 4-bit activations: the 64x128 and 128x128 configurations only
-        if constexpr (C::OCC < 3 && C::BN == 128 && ((C::BM == 64 && C::NST == 6) || (C::BM == 128 && C::NST == 4))) {
-            const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;
-            if (is_1x1 && add) hipLaunchKernelGGL((qconv_stream<C, true, true, false, true>), g, b, 0, stream, q);
-            else if (is_1x1) hipLaunchKernelGGL((qconv_stream<C, true, false, false, true>), g, b, 0, stream, q);
-            else if (add) hipLaunchKernelGGL((qconv_stream<C, false, true, false, true>), g, b, 0, stream, q);
-            else hipLaunchKernelGGL((qconv_stream<C, false, false, false, true>), g, b, 0, stream, q);
-            return hipGetLastError();
-        }
-        return hipErrorInvalidValue;
-    }
+    if (b4) return hipErrorInvalidValue;   // 4-bit activations: launch_stream_b4
     if (zw) {   // asymmetric weights: the 64x256 and 128x128 configurations only
         if constexpr (C::OCC < 3 && ((C::BN == 256 && C::BM == 64 && C::NST == 3) ||
                                      (C::BN == 128 && C::BM == 128 && C::NST == 4))) {
@@ -2354,8 +2364,8 @@ hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_
     }
     if (gather == GATHER_C4 && tile < 0 && stem_ok(p)) return launch_stem(p, stream);
     if (gather == GATHER_B4S) {   // its packed layout is the streaming kernel's: no other tile
-        if (p.c_out <= 64) return launch_stream<S64x128d6>(p, is_1x1, true, false, stream, true);
-        return launch_stream<S128x128d4>(p, is_1x1, true, false, stream, true);
+        if (p.c_out <= 64) return launch_stream_b4<S64x128d6>(p, is_1x1, stream);
+        return launch_stream_b4<S128x128d4>(p, is_1x1, stream);
     }
     if (p.zw_red != 0) {   // asymmetric weights ride on the streaming kernel only
         const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;
