@@ -123,11 +123,13 @@ def bench_trunk(args):
     from integer_quantized_nn_amd.resnet50 import QuantResNet50Trunk
 
     t0 = time.perf_counter()
-    tr = synth.resnet50_trunk(seed=0, batch=args.batch)
+    sparse = args.workload == "resnet50_trunk_2of4"   # 2:4-pruned weights after the stem
+    tr = synth.resnet50_trunk(seed=0, batch=args.batch, sparse_2of4=sparse)
     log("synthetic trunk ready in %.1f s" % (time.perf_counter() - t0))
     # uint8 activation codes stored as int8 bytes q - 128 (zero points Z - 128): the same
     # trunk byte for byte up to the sign bit, with no per-fragment sign flip in the kernels
-    net = QuantResNet50Trunk(tr, offset_codes=True)
+    net = QuantResNet50Trunk(tr, offset_codes=True, sparse_2of4=sparse)
+    wl_name = ("resnet50_trunk_2of4_b%d" if sparse else "resnet50_trunk_b%d") % args.batch
     x = torch.from_numpy(tr.x).cuda()
     torch.cuda.synchronize()
     launches = net.launches()
@@ -183,7 +185,7 @@ def bench_trunk(args):
         roof = {"bound": "mfma", "achieved": ops_per_launch / avg_dur / 1e12, "peak": PEAK_INT8_OPS / 1e12,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    tr_bytes = measured_traffic("resnet50_trunk_b%d" % args.batch)
+    tr_bytes = measured_traffic(wl_name)
     roof["traffic"] = tr_bytes
     roof["kernel"] = "qconv (qconv_stem_pool / qconv_direct3x3 / qconv_stream; %d launches per step)" % n_conv
     roof["algorithmic_bytes_per_launch"] = bytes_per_launch
@@ -201,9 +203,10 @@ def bench_trunk(args):
         "metric": METRIC, "value": value, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int8", "data": "synthetic",
-        "config": {"workload": "resnet50_trunk_b%d" % args.batch, "batch": args.batch, "image_hw": 224,
+        "config": {"workload": wl_name, "batch": args.batch, "image_hw": 224,
                    "convs": n_conv, "ops_per_step": step_ops,
-                   "activations": "uint8 asymmetric per-tensor, stored as int8 bytes q - 128 (zero points Z - 128)", "weights": "int8 per-channel symmetric",
+                   "activations": "uint8 asymmetric per-tensor, stored as int8 bytes q - 128 (zero points Z - 128)", "weights": "int8 per-channel symmetric" + (
+                       ", 2:4-pruned after the stem (sparse MFMA; ops counted as the dense 2*M*N*K)" if sparse else ""),
                    "step": "quantize fp32 input, 53 fused convs + max pooling (fused with the stem), "
                            "dequantize output"},
         "pct_int8_mfma_peak": value * 1e12 / PEAK_INT8_OPS,
@@ -332,7 +335,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--batch", type=int, default=256)
     ap.add_argument("--workload", default="resnet50_trunk",
-                    choices=["resnet50_trunk", "conv3x3_int8", "conv3x3_4bit", "conv3x3_uint8w", "conv3x3_intrq",
+                    choices=["resnet50_trunk", "resnet50_trunk_2of4", "conv3x3_int8", "conv3x3_4bit", "conv3x3_uint8w", "conv3x3_intrq",
                              "vitl_fc1", "vitl_fc1_2of4", "gemm_int8_256"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
@@ -377,7 +380,7 @@ def main():
         torch.cuda.synchronize()
         log("calibration copy: %d bytes read, %d bytes written" % (n, n))
         del src, dst
-    rec = bench_trunk(args) if args.workload == "resnet50_trunk" else bench_layer(args)
+    rec = bench_trunk(args) if args.workload.startswith("resnet50_trunk") else bench_layer(args)
     print(json.dumps(rec), flush=True)
 
 

@@ -34,12 +34,15 @@ class QuantResNet50Trunk:
     it the same convolution as the 3-channel padded one."""
 
     def __init__(self, trunk, device="cuda", weight_codes=None, stream=None, fuse_stem_pool=True,
-                 offset_codes=False):
+                 offset_codes=False, sparse_2of4=False):
         """trunk: synth.Trunk.  weight_codes: optional {layer name: OHWI int8 bytes};
         by default the float weights are quantized per output channel on the GPU.
         fuse_stem_pool: run the stem and the max pooling as one launch
         (iqnn_qconv_maxpool_fwd), never writing the stem's output.  offset_codes:
-        store the uint8 activation codes as int8 bytes q - 128 (zero points Z - 128)."""
+        store the uint8 activation codes as int8 bytes q - 128 (zero points Z - 128).
+        sparse_2of4: run the convs after the stem with their weights as 2:4-sparse
+        codes (IQNN_INT8_2OF4; the trunk's weights must be 2:4, as drawn by
+        synth.resnet50_trunk(sparse_2of4=True)), except the 64-channel 3x3 convs."""
         self.trunk = trunk
         self.fuse_stem_pool = fuse_stem_pool
         self.offset_codes = offset_codes
@@ -65,7 +68,11 @@ class QuantResNet50Trunk:
             if layer is stem:   # padded 4-channel input, zero weights on the extra channel
                 w_bytes = np.pad(w_bytes.reshape(co, kh, kw, ci), ((0, 0), (0, 0), (0, 0), (0, STEM_PAD_CHANNELS - ci)))
                 h, w, ci, pad = h + 2 * pad, w + 2 * pad, STEM_PAD_CHANNELS, 0
-            conv = QConv(n, h, w, ci, co, kh, c.stride, pad, act, B.INT8, act, c.epi, c.z_in - off, c.z_out - off,
+            # the 64-channel 3x3 convs keep the dense codes: their direct kernel (weights
+            # held in registers) beats the sparse streaming kernel on them
+            sparse = sparse_2of4 and layer is not stem and not (kh == 3 and ci == 64)
+            w_type = B.INT8_2OF4 if sparse else B.INT8
+            conv = QConv(n, h, w, ci, co, kh, c.stride, pad, act, w_type, act, c.epi, c.z_in - off, c.z_out - off,
                          w_bytes, c.bias, c.s_in, c.s_w, c.s_out, res_type=act, z_res=c.z_res - off,
                          s_res=c.s_res, device=device, stream=stream)
             self.convs[layer.name] = conv

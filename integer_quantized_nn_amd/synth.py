@@ -253,13 +253,15 @@ class Trunk:
         return sum(l.case.ops(self.batch, *l.in_hw) for l in self.layers)
 
 
-def resnet50_trunk(seed=0, batch=256, hw=224, calib_images=1):
+def resnet50_trunk(seed=0, batch=256, hw=224, calib_images=1, sparse_2of4=False):
     """The 53 convolutions of ResNet-50 (bottleneck stages 3-4-6-3, stride on the 3x3
     conv, 1x1 stride-s downsample without ReLU), random He-normal weights, uint8
     activations and int8 per-channel weights.
 
     Output scales come from a float forward of the unquantized trunk over the first
-    `calib_images` images (max rule; min-max for the downsample outputs)."""
+    `calib_images` images (max rule; min-max for the downsample outputs).
+    sparse_2of4: the float weights of every conv after the stem are magnitude-pruned
+    to 2:4 along the input channels as they are drawn (before calibration)."""
     import torch
     import torch.nn.functional as F
     rng = np.random.default_rng(seed)
@@ -293,6 +295,8 @@ def resnet50_trunk(seed=0, batch=256, hw=224, calib_images=1):
         sigma = np.float32(np.sqrt(2.0 / fan_in))
         w = rng.standard_normal((co, k, k, ci), dtype=np.float32) * sigma
         b = rng.standard_normal(co, dtype=np.float32) * np.float32(0.1) * sigma
+        if sparse_2of4 and name != "stem":
+            w = prune_2of4(w)
         params.append((w, b))
     zps = [int(rng.integers(0, 17)) for _ in specs]
 

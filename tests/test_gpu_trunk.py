@@ -32,10 +32,11 @@ def _codes(tr):
     return x, w
 
 
-def _run_gpu(tr, x, w, offset=False):
+def _run_gpu(tr, x, w, offset=False, sparse=False):
     import torch
     from integer_quantized_nn_amd.resnet50 import QuantResNet50Trunk
-    net = QuantResNet50Trunk(tr, weight_codes={k: O.pack(v, O.INT8) for k, v in w.items()}, offset_codes=offset)
+    net = QuantResNet50Trunk(tr, weight_codes={k: O.pack(v, O.INT8) for k, v in w.items()}, offset_codes=offset,
+                             sparse_2of4=sparse)
     # the trunk's input buffer is the image with the stem's border and a 4th channel,
     # all holding the input zero-point code
     p = net.stem_pad
@@ -61,6 +62,26 @@ def test_trunk_every_layer_small_batch(offset):
         if name == "input":
             continue
         assert_bytes_equal(buf.cpu().numpy(), O.pack(ref[name], O.UINT8) ^ flip, name)
+
+
+def test_trunk_2of4_every_layer_small_batch():
+    """The trunk with 2:4-pruned weights after the stem, the convs after the stem on the
+    sparse kernel but the 64-channel 3x3 ones (direct kernel on the same codes), offset
+    int8 storage, batch 3: every intermediate tensor against the oracle's dense
+    convolutions of the same codes."""
+    require_gpu()
+    tr = synth.resnet50_trunk(seed=6, batch=3, sparse_2of4=True)
+    x, w = _codes(tr)
+    for l in tr.layers[1:]:
+        assert np.all((w[l.name].reshape(-1, 4) != 0).sum(axis=1) <= 2), l.name
+    net = _run_gpu(tr, x, w, True, sparse=True)
+    ref = oracle_trunk(tr, x, w, [0, 1, 2])
+    for name, buf in net.bufs.items():
+        if name == "input":
+            continue
+        assert_bytes_equal(buf.cpu().numpy(), O.pack(ref[name], O.UINT8) ^ np.uint8(0x80), name)
+    for name in ("l1.0.out", "l3.5.out", tr.layers[-1].out):
+        assert len(np.unique(ref[name])) >= 32, name
 
 
 def test_trunk_full_batch_sampled_images():
