@@ -1622,7 +1622,7 @@ hipError_t launch_stream_b4(const ConvParams& p, bool is_1x1, hipStream_t stream
 
 template <class C>
 hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bool c4, hipStream_t stream,
-                         bool b4 = false, bool zw = false) {
+                         bool zw = false) {
     ConvParams q = p;
     q.n_oc_tiles = (p.c_out + C::BM - 1) / C::BM;
     const int64_t n_px = (p.m + C::BN - 1) / C::BN;
@@ -1631,7 +1631,6 @@ hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bo
     q.n_px_tiles = (int32_t)n_px;
     stream_schedule(q, C::OCC);
     dim3 g((unsigned)(8 * q.gx)), b(256);
-    if (b4) return hipErrorInvalidValue;   // 4-bit activations: launch_stream_b4
     if (zw) {   // asymmetric weights: the 64x256 and 128x128 configurations only
         if constexpr (C::OCC < 3 && ((C::BN == 256 && C::BM == 64 && C::NST == 3) ||
                                      (C::BN == 128 && C::BM == 128 && C::NST == 4))) {
@@ -2372,8 +2371,8 @@ hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_
         const bool res_prefetch = add && p.vec_store && (p.res_type == T_INT8 || p.res_type == T_UINT8);
         if (gather != GATHER_B8 || !pipe_eligible(gather, p.c, p.k) || (add && !res_prefetch))
             return hipErrorInvalidValue;
-        if (p.c_out <= 64) return launch_stream<S64x256d3>(p, is_1x1, res_prefetch, false, stream, false, true);
-        return launch_stream<S128x128d4>(p, is_1x1, res_prefetch, false, stream, false, true);
+        if (p.c_out <= 64) return launch_stream<S64x256d3>(p, is_1x1, res_prefetch, false, stream, true);
+        return launch_stream<S128x128d4>(p, is_1x1, res_prefetch, false, stream, true);
     }
     if (pipe_eligible(gather, p.c, p.k)) {
         const bool c4 = gather == GATHER_C4;

@@ -89,6 +89,18 @@ def test_gemm_2of4_ragged():
     assert_bytes_equal(got, to_bytes(oracle_gemm(g, a, b), g.c_type), "gemm 1000x256x384")
 
 
+@pytest.mark.parametrize("m,k,n", [(1, 64, 128), (2, 128, 16), (129, 64, 300)])
+def test_gemm_2of4_edges(m, k, n):
+    """One row and one stage, a 16-channel output (a partly empty 128-channel block),
+    ragged rows with channels spanning three blocks."""
+    require_gpu()
+    g = synth.vitl_fc1(seed=m + k + n, m=m, k=k, n=n, sparse_2of4=True)
+    a = O.quantize(g.a, g.s_a, g.z_a, O.UINT8)
+    b = O.quantize(g.b, g.s_b, 0, O.INT8, axis=0)
+    got = _gpu_gemm_2of4(g, a, b)
+    assert_bytes_equal(got, to_bytes(oracle_gemm(g, a, b), g.c_type), "gemm %dx%dx%d" % (m, k, n))
+
+
 def test_gemm_2of4_vitl_fc1_full_size():
     """ViT-L fc1 (12608 x 1024 -> 4096) with 2:4-pruned weights, sampled rows including
     the first 197 and the ragged tail."""
