@@ -92,3 +92,24 @@ def test_vitl_fc1_full_size_sampled_rows():
     assert_bytes_equal(got[rows], want, "vitl fc1")
     q = O.unpack(got[rows], O.INT8)
     assert len(np.unique(q)) >= 64 and (np.abs(q) >= 127).mean() < 0.01
+
+
+@pytest.mark.parametrize("n,k,sparse", [(4096, 2048, False), (8192, 2048, False), (3328, 2048, False),
+                                        (8192, 2048, True)],
+                         ids=["w8MB_4groups", "w16MB_8groups", "odd_tiles_1group", "sp10MB_8groups"])
+def test_gemm_xcd_channel_groups(n, k, sparse):
+    """Layers whose weights exceed 2 MB split their channel tiles across the XCDs (2, 4
+    or 8 groups, so an XCD's share is at most 2 MB; a tile count the split does not
+    divide keeps one group).  Every output byte of a 300-row GEMM against the oracle."""
+    require_gpu()
+    import torch
+    from integer_quantized_nn_amd import binding as IB
+    from integer_quantized_nn_amd.layers import QGemm
+    g = synth.vitl_fc1(seed=n + k, m=300, k=k, n=n, sparse_2of4=sparse)
+    a = O.quantize(g.a, g.s_a, g.z_a, O.UINT8)
+    b = O.quantize(g.b, g.s_b, 0, O.INT8, axis=0)
+    layer = QGemm(300, n, k, g.a_type, IB.INT8_2OF4 if sparse else IB.INT8, g.c_type, g.epi, g.z_a, g.z_out,
+                  to_bytes(b, g.b_type), g.bias, g.s_a, g.s_b, g.s_out)
+    got = layer(torch.from_numpy(to_bytes(a, g.a_type)).cuda())
+    torch.cuda.synchronize()
+    assert_bytes_equal(got.cpu().numpy(), to_bytes(oracle_gemm(g, a, b), g.c_type), "gemm 300x%dx%d" % (k, n))
