@@ -256,7 +256,9 @@ def bench_layer(args):
         w_bytes = co * 9 * ci // (2 if c.w_type in (synth.UINT4, synth.INT4) else 1)
         y_bytes = n * oh * ow * co // (2 if c.y_type in (synth.UINT4, synth.INT4) else 1)
         nbytes = xd.numel() + w_bytes + y_bytes + (rd.numel() if rd is not None else 0)
-        run = lambda: layer(xd, res=rd)
+        ins = [(xd, rd)]
+        run_on = lambda i, o: layer(ins[i][0], res=ins[i][1], out=o)
+        out_shape, out_type = layer.out_shape, c.y_type
     elif wl in ("vitl_fc1", "vitl_fc1_2of4", "gemm_int8_256"):
         sparse = wl == "vitl_fc1_2of4"   # weights magnitude-pruned to 2:4 along K, on the sparse MFMA
         g = synth.vitl_fc1(sparse_2of4=sparse) if wl.startswith("vitl") else synth.gemm_int8_256()
@@ -274,9 +276,26 @@ def bench_layer(args):
         # codes and the kernel skips them); bytes: 2:4 weights move kept codes + positions
         ops = 2 * m * n * k
         nbytes = m * k + (n * k // 2 + n * k // 8 if sparse else n * k) + m * n
-        run = lambda: layer(a_dev)
+        ins = [(a_dev, None)]
+        run_on = lambda i, o: layer(ins[i][0], out=o)
+        out_shape, out_type = layer.out_shape, g.c_type
     else:
         raise SystemExit("unknown workload " + wl)
+    # --cold: rotate enough input / output sets (at least 4, over 256 MB in all) that
+    # every launch reads and writes HBM rather than the 256 MB Infinity Cache
+    from integer_quantized_nn_amd.layers import empty_codes
+    set_bytes = nbytes
+    n_sets = max(4, -(-(300 << 20) // set_bytes)) if args.cold else 1
+    for _ in range(n_sets - 1):
+        ins.append(tuple(t.clone() if t is not None else None for t in ins[0]))
+    outs = [empty_codes(out_shape, out_type) for _ in range(n_sets)]
+    step_no = [0]
+
+    def run():
+        i = step_no[0] % n_sets
+        step_no[0] += 1
+        return run_on(i, outs[i])
+
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(max(args.warmup, 1)):
@@ -322,7 +341,9 @@ def bench_layer(args):
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": span * 1e3 / args.steps,
             "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
-            "config": {"workload": wl, "ops": ops, "algorithmic_bytes": nbytes, "cache": "warm (inputs reused)",
+            "config": {"workload": wl, "ops": ops, "algorithmic_bytes": nbytes,
+                       "cache": ("cold (%d rotating input/output sets, %.0f MB in all)" % (n_sets, n_sets * set_bytes / 1e6)
+                                 if args.cold else "warm (inputs reused)"),
                        **({"ops_note": "dense-equivalent 2*M*N*K; the 2:4 weights make half of the products "
                                        "zero, which the sparse MFMA skips"} if wl.endswith("2of4") else {})},
             "pct_int8_mfma_peak": ops / avg / PEAK_INT8_OPS, "roofline": roof, "cpu_baseline": None}
@@ -337,6 +358,8 @@ def main():
     ap.add_argument("--workload", default="resnet50_trunk",
                     choices=["resnet50_trunk", "resnet50_trunk_2of4", "conv3x3_int8", "conv3x3_4bit", "conv3x3_uint8w", "conv3x3_intrq",
                              "vitl_fc1", "vitl_fc1_2of4", "gemm_int8_256"])
+    ap.add_argument("--cold", action="store_true",
+                    help="single-layer workloads: rotate input/output sets (> 256 MB) so every launch misses the caches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="trunk: time eager launches instead of one captured HIP graph per step")
