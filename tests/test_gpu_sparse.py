@@ -35,8 +35,7 @@ CASES = [
 
 def sparse_case(case):
     n, h, w, ci, co, k, s, p, xt, yt, epi = case
-    c = synth.conv_case(hash(case) % 2 ** 31, n, h, w, ci, co, k, s, p, xt, I8, yt, epi,
-                        res_type=U8 if epi == ADD_RELU else U8)
+    c = synth.conv_case(hash(case) % 2 ** 31, n, h, w, ci, co, k, s, p, xt, I8, yt, epi, res_type=U8)
     c.w = synth.prune_2of4(c.w)
     return c
 
