@@ -2108,7 +2108,7 @@ namespace {
 constexpr int kD3Buf = 16384;   // LDS bytes per slab buffer (4 rows of up to 62 pixels)
 constexpr int64_t kD3MinTiles = 512;
 
-template <int W, int OUTK, bool XORB>
+template <int W, int OUTK, bool XORB, bool INTRQ = false>
 __global__ __launch_bounds__(256, 2) void qconv_direct3x3(const ConvParams p, int32_t n_tiles,
                                                            int32_t tiles_per_img) {
     constexpr int SW = W + 2;                       // slab columns: one pad column each side
@@ -2252,7 +2252,7 @@ __global__ __launch_bounds__(256, 2) void qconv_direct3x3(const ConvParams p, in
                 uint32_t rw[4] = {0, 0, 0, 0};
                 // multipliers read from LDS inside the epilogue: no register copy next to
                 // the 144 registers of A fragments
-                epi_store16<false, 2, false, OUTK>(p, acc[t], nullptr, &cmult[ocl], rw, oc0 + ocl, pix, false,
+                epi_store16<false, 2, INTRQ, OUTK>(p, acc[t], nullptr, &cmult[ocl], rw, oc0 + ocl, pix, false,
                                                    0.0f);
             }
         }
@@ -2272,7 +2272,8 @@ __global__ __launch_bounds__(256, 2) void qconv_direct3x3(const ConvParams p, in
 bool direct3x3_ok(const ConvParams& p, int gather, bool forced) {
     if (gather != GATHER_B8 || p.c != 64 || p.kh != 3 || p.kw != 3 || p.sh != 1 || p.sw != 1) return false;
     if (p.ph != 1 || p.pw != 1 || p.w_in != 56 || p.ow != 56 || p.oh != p.h) return false;
-    if (p.c_out % 64 != 0 || p.epi == E_ADD || p.epi == E_ADD_RELU || p.zw_red != 0 || p.int_rq) return false;
+    if (p.c_out % 64 != 0 || p.epi == E_ADD || p.epi == E_ADD_RELU || p.zw_red != 0) return false;
+    if (p.int_rq && p.y_type != T_INT8 && p.y_type != T_UINT8) return false;   // 8-bit codes only
     if (p.m >= ((int64_t)1 << 31)) return false;
     return forced || (p.m / ((int64_t)p.oh * p.ow)) * ((p.oh + 1) / 2) >= kD3MinTiles;
 }
@@ -2289,7 +2290,10 @@ hipError_t launch_direct3x3(const ConvParams& p, hipStream_t stream) {
     const int32_t nt = (int32_t)n_tiles, tpi = (int32_t)tiles_per_img;
     // signed activation codes are MFMA operands as they are; uint8 ones get the sign flip
     const bool xorb = p.x_xor != 0;
-    if (p.epi == E_RAW) {
+    if (p.int_rq) {   // integer-only requantization to 8-bit codes
+        if (xorb) hipLaunchKernelGGL((qconv_direct3x3<56, 1, true, true>), grid, dim3(256), 0, stream, p, nt, tpi);
+        else hipLaunchKernelGGL((qconv_direct3x3<56, 1, false, true>), grid, dim3(256), 0, stream, p, nt, tpi);
+    } else if (p.epi == E_RAW) {
         if (xorb) hipLaunchKernelGGL((qconv_direct3x3<56, 2, true>), grid, dim3(256), 0, stream, p, nt, tpi);
         else hipLaunchKernelGGL((qconv_direct3x3<56, 2, false>), grid, dim3(256), 0, stream, p, nt, tpi);
     } else if (p.y_type == T_INT8 || p.y_type == T_UINT8) {

@@ -77,3 +77,44 @@ def test_gemm_integer_requant():
     torch.cuda.synchronize()
     assert_bytes_equal(c.cpu().numpy(), to_bytes(want, I8), "gemm integer requant")
     assert len(np.unique(c.cpu().numpy())) >= 32
+
+
+@pytest.mark.parametrize("h,co,xt,yt,epi", [(6, 64, U8, U8, RELU), (5, 128, I8, I8, NONE), (2, 64, U8, I8, RELU)])
+def test_direct3x3_integer_requant(h, co, xt, yt, epi):
+    """The direct 3x3 kernel with the integer-only epilogue (forced through tile 18):
+    64-channel 3x3 convs on 56-pixel rows, odd and two-row heights, one and two
+    64-channel output blocks, uint8 and int8 codes."""
+    torch = require_gpu()
+    from integer_quantized_nn_amd import binding as B
+    from integer_quantized_nn_amd.layers import QConv
+    c = synth.conv_case(h * 1000 + co + xt, 2, h, 56, 64, co, 3, 1, 1, xt, I8, yt, epi)
+    x, wq, _ = conv_codes(c)
+    want = to_bytes(oracle_int(c, x, wq), yt)
+    conv = QConv(2, h, 56, 64, co, 3, 1, 1, xt, I8, yt, epi | INT_RQ, c.z_in, c.z_out, to_bytes(wq, I8), c.bias,
+                 c.s_in, c.s_w, c.s_out)
+    B.iqnn_set_conv_tile(18)
+    try:
+        y = conv(torch.from_numpy(to_bytes(x, xt)).cuda())
+        torch.cuda.synchronize()
+    finally:
+        B.iqnn_set_conv_tile(-1)
+    assert_bytes_equal(y.cpu().numpy(), want, "direct 3x3 integer requant h=%d co=%d" % (h, co))
+
+
+def test_integer_requant_3x3_workload_sampled_images():
+    """The 3x3 workload (N=32, 56x56, 64 -> 64, Conv_Relu to uint8) with the integer-only
+    epilogue, on the kernel the library picks for it (the direct 3x3 kernel), against
+    the oracle on sampled whole images."""
+    torch = require_gpu()
+    from integer_quantized_nn_amd.layers import QConv
+    c = synth.conv3x3_int8()
+    x, wq, _ = conv_codes(c)
+    n, h, w, ci = x.shape
+    conv = QConv(n, h, w, ci, c.c_out, 3, 1, 1, c.x_type, I8, c.y_type, c.epi | INT_RQ, c.z_in, c.z_out,
+                 to_bytes(wq, I8), c.bias, c.s_in, c.s_w, c.s_out)
+    y = conv(torch.from_numpy(to_bytes(x, c.x_type)).cuda())
+    torch.cuda.synchronize()
+    images = [0, 13, 31]
+    want = to_bytes(oracle_int(c, x[images], wq), c.y_type)
+    assert_bytes_equal(y.cpu().numpy()[images], want, "3x3 workload, integer requant")
+    assert len(np.unique(y.cpu().numpy())) >= 64
