@@ -235,8 +235,10 @@ def bench_layer(args):
     from integer_quantized_nn_amd.layers import QConv, QGemm, quantize
 
     wl = args.workload
-    if wl in ("conv3x3_int8", "conv3x3_4bit", "conv3x3_uint8w", "conv3x3_intrq"):
+    if wl in ("conv3x3_int8", "conv3x3_4bit", "conv3x3_uint8w", "conv3x3_intrq", "conv3x3_2of4"):
         c = synth.conv3x3_4bit() if wl == "conv3x3_4bit" else synth.conv3x3_int8()
+        if wl == "conv3x3_2of4":   # float weights magnitude-pruned to 2:4 along the input channels
+            c.w = synth.prune_2of4(c.w)
         n, h, w, ci = c.x.shape
         co = c.c_out
         w_type, s_w, z_w = c.w_type, c.s_w, 0
@@ -247,6 +249,9 @@ def bench_layer(args):
         else:
             wq = quantize(torch.from_numpy(c.w).cuda(), c.s_w, 0, c.w_type, axis=0).cpu().numpy()
         epi = c.epi | (16 if wl == "conv3x3_intrq" else 0)   # integer-only requantization flag
+        if wl == "conv3x3_2of4":
+            from integer_quantized_nn_amd import binding as IB
+            w_type = IB.INT8_2OF4
         layer = QConv(n, h, w, ci, co, 3, c.stride, c.pad, c.x_type, w_type, c.y_type, epi, c.z_in, c.z_out,
                       wq, c.bias, c.s_in, s_w, c.s_out, res_type=c.res_type, z_res=c.z_res, s_res=c.s_res, z_w=z_w)
         xd = quantize(torch.from_numpy(c.x).cuda(), c.s_in, c.z_in, c.x_type)
@@ -254,6 +259,8 @@ def bench_layer(args):
         ops = c.ops(n, h, w)
         oh, ow = layer.out_shape[1:3]
         w_bytes = co * 9 * ci // (2 if c.w_type in (synth.UINT4, synth.INT4) else 1)
+        if wl == "conv3x3_2of4":
+            w_bytes = w_bytes * 5 // 8   # kept codes + positions
         y_bytes = n * oh * ow * co // (2 if c.y_type in (synth.UINT4, synth.INT4) else 1)
         nbytes = xd.numel() + w_bytes + y_bytes + (rd.numel() if rd is not None else 0)
         ins = [(xd, rd)]
@@ -356,7 +363,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--batch", type=int, default=256)
     ap.add_argument("--workload", default="resnet50_trunk",
-                    choices=["resnet50_trunk", "resnet50_trunk_2of4", "conv3x3_int8", "conv3x3_4bit", "conv3x3_uint8w", "conv3x3_intrq",
+                    choices=["resnet50_trunk", "resnet50_trunk_2of4", "conv3x3_int8", "conv3x3_2of4", "conv3x3_4bit", "conv3x3_uint8w", "conv3x3_intrq",
                              "vitl_fc1", "vitl_fc1_2of4", "gemm_int8_256"])
     ap.add_argument("--cold", action="store_true",
                     help="single-layer workloads: rotate input/output sets (> 256 MB) so every launch misses the caches")

@@ -2108,7 +2108,10 @@ namespace {
 constexpr int kD3Buf = 16384;   // LDS bytes per slab buffer (4 rows of up to 62 pixels)
 constexpr int64_t kD3MinTiles = 512;
 
-template <int W, int OUTK, bool XORB, bool INTRQ = false>
+// SP: 2:4-sparse weights (one tap of 64 input channels is one 64-K stage of the 2:4
+// blocks): per channel block and tap a 16-byte fragment of kept codes and its 32-bit
+// positions in registers, one sparse MFMA per tap on the tap's two k-step fragments.
+template <int W, int OUTK, bool XORB, bool INTRQ = false, bool SP = false>
 __global__ __launch_bounds__(256, 2) void qconv_direct3x3(const ConvParams p, int32_t n_tiles,
                                                            int32_t tiles_per_img) {
     constexpr int SW = W + 2;                       // slab columns: one pad column each side
@@ -2128,16 +2131,28 @@ __global__ __launch_bounds__(256, 2) void qconv_direct3x3(const ConvParams p, in
         cbias[tid] = p.bias[oc0 + tid];
         cmult[tid] = p.mult[oc0 + tid];
     }
-    // A fragments: packed rows oc0 + 32t + lane%32, K bytes 64 tap + 32 ks + 16 (lane/32)
-    v4i wa[2][9][2];
+    // A fragments: packed rows oc0 + 32t + lane%32, K bytes 64 tap + 32 ks + 16 (lane/32);
+    // 2:4 weights: that row's kept codes of K half lane/32 of stage `tap` and their
+    // positions, from the (128-row tile, stage) block
+    v4i wa[2][9][SP ? 1 : 2];
+    int wix[SP ? 2 : 1][SP ? 9 : 1];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int tap = 0; tap < 9; ++tap)
+        for (int tap = 0; tap < 9; ++tap) {
+            const int row = oc0 + 32 * t + (lane & 31);
+            if constexpr (SP) {
+                const int rr = row % kSpRows, hh = lane >> 5;
+                const int8_t* blk = p.w + ((int64_t)(row / kSpRows) * (p.kp / kPipeBK) + tap) * kSpBlock;
+                wa[t][tap][0] = *reinterpret_cast<const v4i*>(blk + rr * 32 + ((hh ^ ((rr >> 3) & 1)) * 16));
+                wix[t][tap] = *reinterpret_cast<const int*>(blk + kSpRows * 32 + rr * 8 + hh * 4);
+            } else {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                wa[t][tap][ks] = *reinterpret_cast<const v4i*>(p.w + (int64_t)(oc0 + 32 * t + (lane & 31)) * p.kp +
-                                                               64 * tap + 32 * ks + 16 * (lane >> 5));
+                for (int ks = 0; ks < 2; ++ks)
+                    wa[t][tap][ks] = *reinterpret_cast<const v4i*>(p.w + (int64_t)row * p.kp + 64 * tap + 32 * ks +
+                                                                   16 * (lane >> 5));
+            }
+        }
     __syncthreads();
 
     const int h = p.h;
@@ -2226,18 +2241,43 @@ __global__ __launch_bounds__(256, 2) void qconv_direct3x3(const ConvParams p, in
             return *reinterpret_cast<const v4i*>(sb + ((r + ky) * SW + col) * 64 +
                                                  (((2 * ks + (lane >> 5)) ^ ((col >> 2) & 3)) << 4));
         };
-        v4i fb = read_b(0);
+        if constexpr (SP) {
+            // one tap per step: its two k-step fragments are the sparse MFMA's B operand
+            v4i f0 = read_b(0), f1 = read_b(1);
 #pragma unroll
-        for (int s = 0; s < 18; ++s) {
-            v4i fn;
-            if (s + 1 < 18) fn = read_b(s + 1);
-            if constexpr (XORB) {
-                fb[0] ^= bxor; fb[1] ^= bxor; fb[2] ^= bxor; fb[3] ^= bxor;
+            for (int tap = 0; tap < 9; ++tap) {
+                v4i n0, n1;
+                if (tap + 1 < 9) {
+                    n0 = read_b(2 * tap + 2);
+                    n1 = read_b(2 * tap + 3);
+                }
+                if constexpr (XORB) {
+                    f0[0] ^= bxor; f0[1] ^= bxor; f0[2] ^= bxor; f0[3] ^= bxor;
+                    f1[0] ^= bxor; f1[1] ^= bxor; f1[2] ^= bxor; f1[3] ^= bxor;
+                }
+                const v8i fb8 = {f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
+                acc[0] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(wa[0][tap][0], fb8, acc[0], wix[0][tap], 0, 0);
+                acc[1] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(wa[1][tap][0], fb8, acc[1], wix[1][tap], 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                if (tap + 1 < 9) {
+                    f0 = n0;
+                    f1 = n1;
+                }
             }
-            acc[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wa[0][s >> 1][s & 1], fb, acc[0], 0, 0, 0);
-            acc[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wa[1][s >> 1][s & 1], fb, acc[1], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            if (s + 1 < 18) fb = fn;
+        } else {
+            v4i fb = read_b(0);
+#pragma unroll
+            for (int s = 0; s < 18; ++s) {
+                v4i fn;
+                if (s + 1 < 18) fn = read_b(s + 1);
+                if constexpr (XORB) {
+                    fb[0] ^= bxor; fb[1] ^= bxor; fb[2] ^= bxor; fb[3] ^= bxor;
+                }
+                acc[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wa[0][s >> 1][s & 1], fb, acc[0], 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wa[1][s >> 1][s & 1], fb, acc[1], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                if (s + 1 < 18) fb = fn;
+            }
         }
         const int n = tile / tiles_per_img;
         const int oy = 2 * (tile - n * tiles_per_img) + r;
@@ -2274,6 +2314,7 @@ bool direct3x3_ok(const ConvParams& p, int gather, bool forced) {
     if (p.ph != 1 || p.pw != 1 || p.w_in != 56 || p.ow != 56 || p.oh != p.h) return false;
     if (p.c_out % 64 != 0 || p.epi == E_ADD || p.epi == E_ADD_RELU || p.zw_red != 0) return false;
     if (p.int_rq && p.y_type != T_INT8 && p.y_type != T_UINT8) return false;   // 8-bit codes only
+    if (p.w_idx && p.epi != E_RAW && p.y_type != T_INT8 && p.y_type != T_UINT8) return false;
     if (p.m >= ((int64_t)1 << 31)) return false;
     return forced || (p.m / ((int64_t)p.oh * p.ow)) * ((p.oh + 1) / 2) >= kD3MinTiles;
 }
@@ -2290,7 +2331,15 @@ hipError_t launch_direct3x3(const ConvParams& p, hipStream_t stream) {
     const int32_t nt = (int32_t)n_tiles, tpi = (int32_t)tiles_per_img;
     // signed activation codes are MFMA operands as they are; uint8 ones get the sign flip
     const bool xorb = p.x_xor != 0;
-    if (p.int_rq) {   // integer-only requantization to 8-bit codes
+    if (p.w_idx) {   // 2:4 weights: 8-bit codes or raw int32
+        if (p.epi == E_RAW) {
+            if (xorb) hipLaunchKernelGGL((qconv_direct3x3<56, 2, true, false, true>), grid, dim3(256), 0, stream, p, nt, tpi);
+            else hipLaunchKernelGGL((qconv_direct3x3<56, 2, false, false, true>), grid, dim3(256), 0, stream, p, nt, tpi);
+        } else {
+            if (xorb) hipLaunchKernelGGL((qconv_direct3x3<56, 1, true, false, true>), grid, dim3(256), 0, stream, p, nt, tpi);
+            else hipLaunchKernelGGL((qconv_direct3x3<56, 1, false, false, true>), grid, dim3(256), 0, stream, p, nt, tpi);
+        }
+    } else if (p.int_rq) {   // integer-only requantization to 8-bit codes
         if (xorb) hipLaunchKernelGGL((qconv_direct3x3<56, 1, true, true>), grid, dim3(256), 0, stream, p, nt, tpi);
         else hipLaunchKernelGGL((qconv_direct3x3<56, 1, false, true>), grid, dim3(256), 0, stream, p, nt, tpi);
     } else if (p.epi == E_RAW) {
@@ -2353,6 +2402,7 @@ hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_
         const bool res_prefetch = add && p.vec_store && (p.res_type == T_INT8 || p.res_type == T_UINT8);
         if (gather != GATHER_B8 || !pipe_eligible(gather, p.c, p.k) || p.zw_red != 0 || (add && !res_prefetch))
             return hipErrorInvalidValue;
+        if (direct3x3_ok(p, gather, tile == kTileDirect3x3)) return launch_direct3x3(p, stream);
         return launch_stream_2of4(p, is_1x1, stream);
     }
     if (tile == kTileDirect3x3) {   // the direct kernel where it applies, else the automatic choice

@@ -42,7 +42,7 @@ class QuantResNet50Trunk:
         store the uint8 activation codes as int8 bytes q - 128 (zero points Z - 128).
         sparse_2of4: run the convs after the stem with their weights as 2:4-sparse
         codes (IQNN_INT8_2OF4; the trunk's weights must be 2:4, as drawn by
-        synth.resnet50_trunk(sparse_2of4=True)), except the 64-channel 3x3 convs."""
+        synth.resnet50_trunk(sparse_2of4=True))."""
         self.trunk = trunk
         self.fuse_stem_pool = fuse_stem_pool
         self.offset_codes = offset_codes
@@ -68,10 +68,7 @@ class QuantResNet50Trunk:
             if layer is stem:   # padded 4-channel input, zero weights on the extra channel
                 w_bytes = np.pad(w_bytes.reshape(co, kh, kw, ci), ((0, 0), (0, 0), (0, 0), (0, STEM_PAD_CHANNELS - ci)))
                 h, w, ci, pad = h + 2 * pad, w + 2 * pad, STEM_PAD_CHANNELS, 0
-            # the 64-channel 3x3 convs keep the dense codes: their direct kernel (weights
-            # held in registers) beats the sparse streaming kernel on them
-            sparse = sparse_2of4 and layer is not stem and not (kh == 3 and ci == 64)
-            w_type = B.INT8_2OF4 if sparse else B.INT8
+            w_type = B.INT8_2OF4 if (sparse_2of4 and layer is not stem) else B.INT8
             conv = QConv(n, h, w, ci, co, kh, c.stride, pad, act, w_type, act, c.epi, c.z_in - off, c.z_out - off,
                          w_bytes, c.bias, c.s_in, c.s_w, c.s_out, res_type=act, z_res=c.z_res - off,
                          s_res=c.s_res, device=device, stream=stream)

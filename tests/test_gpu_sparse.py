@@ -51,10 +51,29 @@ def test_conv_2of4_small_shapes(case):
     assert_bytes_equal(got, want, str(case))
 
 
+@pytest.mark.parametrize("h,co,xt,yt,epi", [(6, 64, U8, U8, RELU), (5, 128, I8, I8, NONE), (2, 64, U8, I32, RAW)])
+def test_conv_2of4_direct3x3(h, co, xt, yt, epi):
+    """2:4 weights on the direct 3x3 kernel (forced through tile 18): 64-channel 3x3
+    convs on 56-pixel rows, odd and two-row heights, one and two output blocks, uint8
+    and int8 codes, raw int32."""
+    require_gpu()
+    from integer_quantized_nn_amd import binding as B
+    c = synth.conv_case(h * 100 + co + xt, 2, h, 56, 64, co, 3, 1, 1, xt, I8, yt, epi)
+    c.w = synth.prune_2of4(c.w)
+    x, wc, res = conv_codes(c)
+    want = to_bytes(oracle_conv(c, x, wc, res), yt)
+    B.iqnn_set_conv_tile(18)
+    try:
+        got = gpu_conv(c, x, wc, res, w_type=SP)
+    finally:
+        B.iqnn_set_conv_tile(-1)
+    assert_bytes_equal(got, want, "direct 2:4 h=%d co=%d" % (h, co))
+
+
 def test_conv_2of4_equals_dense_kernel_on_the_3x3_workload():
     """The 3x3 workload (N=32, 56x56, 64 -> 64, Conv_Relu to uint8) with 2:4-pruned
-    weights: the sparse kernel against the oracle on sampled whole images and against
-    the dense kernel on every byte."""
+    weights (the direct kernel's sparse variant): against the oracle on sampled whole
+    images and against the dense kernel on every byte."""
     require_gpu()
     c = synth.conv3x3_int8()
     c.w = synth.prune_2of4(c.w)

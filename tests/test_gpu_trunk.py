@@ -65,10 +65,9 @@ def test_trunk_every_layer_small_batch(offset):
 
 
 def test_trunk_2of4_every_layer_small_batch():
-    """The trunk with 2:4-pruned weights after the stem, the convs after the stem on the
-    sparse kernel but the 64-channel 3x3 ones (direct kernel on the same codes), offset
-    int8 storage, batch 3: every intermediate tensor against the oracle's dense
-    convolutions of the same codes."""
+    """The trunk with 2:4-pruned weights after the stem, every conv after the stem on the
+    sparse kernels, offset int8 storage, batch 3: every intermediate tensor against the
+    oracle's dense convolutions of the same codes."""
     require_gpu()
     tr = synth.resnet50_trunk(seed=6, batch=3, sparse_2of4=True)
     x, w = _codes(tr)
