@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "int8/int4 quantized conv+GEMM TOPS and % of int8 MFMA peak, bit-exact"
 PEAK_INT8_OPS = 5.0e15      # MI355X dense int8 MFMA, ops/s
 PEAK_HBM = 8.0e12           # MI355X HBM3E, bytes/s
+PEAK_FP6_OPS = 10.1e15      # MI355X dense FP6 MFMA, ops/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qconv_resnet50_trunk_b256_traffic.md")
 
 
@@ -235,8 +236,10 @@ def bench_layer(args):
     from integer_quantized_nn_amd.layers import QConv, QGemm, quantize
 
     wl = args.workload
-    if wl in ("conv3x3_int8", "conv3x3_4bit", "conv3x3_uint8w", "conv3x3_intrq", "conv3x3_2of4"):
-        c = synth.conv3x3_4bit() if wl == "conv3x3_4bit" else synth.conv3x3_int8()
+    fp6 = wl == "conv3x3_4bit_fp6"   # the 4-bit layer on the FP6 MFMA (weights and activations as BF6)
+    peak_ops = PEAK_FP6_OPS if fp6 else PEAK_INT8_OPS
+    if wl in ("conv3x3_int8", "conv3x3_4bit", "conv3x3_4bit_fp6", "conv3x3_uint8w", "conv3x3_intrq", "conv3x3_2of4"):
+        c = synth.conv3x3_4bit() if wl.startswith("conv3x3_4bit") else synth.conv3x3_int8()
         if wl == "conv3x3_2of4":   # float weights magnitude-pruned to 2:4 along the input channels
             c.w = synth.prune_2of4(c.w)
         n, h, w, ci = c.x.shape
@@ -254,6 +257,9 @@ def bench_layer(args):
             w_type = IB.INT8_2OF4
         layer = QConv(n, h, w, ci, co, 3, c.stride, c.pad, c.x_type, w_type, c.y_type, epi, c.z_in, c.z_out,
                       wq, c.bias, c.s_in, s_w, c.s_out, res_type=c.res_type, z_res=c.z_res, s_res=c.s_res, z_w=z_w)
+        if fp6:
+            from integer_quantized_nn_amd import binding as IB
+            IB.iqnn_set_conv_tile(19)
         xd = quantize(torch.from_numpy(c.x).cuda(), c.s_in, c.z_in, c.x_type)
         rd = quantize(torch.from_numpy(c.res).cuda(), c.s_res, c.z_res, c.res_type) if c.res is not None else None
         ops = c.ops(n, h, w)
@@ -336,18 +342,18 @@ def bench_layer(args):
     if spin0.elapsed_time(t_begin) * 1e-3 < enqueued:
         print("warning: the spin kernel ended before every timed step was enqueued", file=sys.stderr)
     ai = ops / nbytes
-    if ai < PEAK_INT8_OPS / PEAK_HBM:
+    if ai < peak_ops / PEAK_HBM:
         roof = {"bound": "hbm", "achieved": nbytes / avg / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": ops / avg / 1e12, "peak": PEAK_INT8_OPS / 1e12, "unit": "TFLOP/s"}
+        roof = {"bound": "mfma", "achieved": ops / avg / 1e12, "peak": peak_ops / 1e12, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(wl)
     roof["avg_launch_us"] = avg * 1e6
-    roof["mfma_frac"] = ops / avg / PEAK_INT8_OPS
+    roof["mfma_frac"] = ops / avg / peak_ops
     return {"metric": METRIC, "value": ops * args.steps / span / 1e12, "unit": "TOPS", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": span * 1e3 / args.steps,
             "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf6" if fp6 else "int8", "data": "synthetic",
             "config": {"workload": wl, "ops": ops, "algorithmic_bytes": nbytes,
                        "cache": ("cold (%d rotating input/output sets, %.0f MB in all)" % (n_sets, n_sets * set_bytes / 1e6)
                                  if args.cold else "warm (inputs reused)"),
@@ -363,7 +369,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--batch", type=int, default=256)
     ap.add_argument("--workload", default="resnet50_trunk",
-                    choices=["resnet50_trunk", "resnet50_trunk_2of4", "conv3x3_int8", "conv3x3_2of4", "conv3x3_4bit", "conv3x3_uint8w", "conv3x3_intrq",
+                    choices=["resnet50_trunk", "resnet50_trunk_2of4", "conv3x3_int8", "conv3x3_2of4", "conv3x3_4bit", "conv3x3_4bit_fp6", "conv3x3_uint8w", "conv3x3_intrq",
                              "vitl_fc1", "vitl_fc1_2of4", "gemm_int8_256"])
     ap.add_argument("--cold", action="store_true",
                     help="single-layer workloads: rotate input/output sets (> 256 MB) so every launch misses the caches")

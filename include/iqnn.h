@@ -167,7 +167,11 @@ const char *iqnn_last_error(void);
  * 13: 128x256 (6), 14: 128x128 (3, three blocks per CU), 15: 128x256 (3),
  * 16: 256x128 (3), 17: 256x256 (4); 18 the direct 3x3 kernel (64-channel 8-bit
  * activations, 3x3 / stride 1 / pad 1 on 56-pixel rows, no residual) at any batch,
- * where the automatic choice takes it from 512 two-row tiles up.  Layers a
+ * where the automatic choice takes it from 512 two-row tiles up; 19 the FP6 path for
+ * 4-bit activations with symmetric INT4 weights and 64*K < 2^24: weights and
+ * activations as BF6 (e3m2) codes on the f8f6f4 MFMA with fp32 accumulation of
+ * integers, exact (the 4-bit inference article's case for 4-bit compute; CDNA4 has
+ * no 4-bit integer MFMA), other layers as with -1.  Layers a
  * configuration cannot take (4-bit activations, C_in % 64 != 0, residual layouts it
  * does not stream) keep a configuration that can.  Every choice computes identical results; only speed differs.  The initial
  * value is -1, or the integer in the environment variable IQNN_FORCE_TILE.  Returns

@@ -232,7 +232,6 @@ bool c4_path(const Layer& L) {
 // K of the packed weights and of the kernel's loop.
 int64_t kdim(const Layer& L) { return c4_path(L) ? (int64_t)L.kh * c4_kwp(L) * 4 : L.k; }
 
-int64_t packed_size(const Layer& L) { return pack_geom(L.c_out, kdim(L)).bytes; }
 
 // Staged K position of logical K index k.  4-bit activations are unpacked in
 // 16-element segments as [0,2,4,6, 1,3,5,7, 8,10,12,14, 9,11,13,15] (low nibbles of
@@ -309,7 +308,49 @@ iqnn_status pack_sparse_row(const std::vector<int32_t>& row, const PackGeom& g, 
     return IQNN_OK;
 }
 
-// Writes the packed layer (layout in PackGeom) into host memory `dst` of g.bytes.
+// 4-bit streaming layers with INT4 weights also carry a BF6 copy of their weights for
+// the FP6 MFMA path (chosen with kTileFp6), after the standard layout: int32 bias[ocp]
+// (the folded bias plus the activation shift -- 8 for UINT4, 0 for INT4 -- times the
+// channel's weight sum, since the path contracts q - 8) and 4 KB blocks per (64-row
+// group, 64-K stage), group-major: 64-byte rows (the kernel's LDS image) whose 8-byte
+// unit u (0-5: the 24 bytes of K half u / 3, 32 six-bit codes in K order) sits at unit
+// u ^ ((row >> 2) & 7).  The fp32 accumulation is exact while 64 * K < 2^24.
+bool b4f6(const Layer& L) { return b4_stream(L) && L.w_type == T_INT4 && L.z_w == 0 && 64 * L.k < (1 << 24); }
+int64_t f6_bias_off(const Layer& L) { return pack_geom(L.c_out, kdim(L)).bytes; }
+int64_t f6_w_off(const Layer& L) {
+    const PackGeom g = pack_geom(L.c_out, kdim(L));
+    return g.bytes + (int64_t)g.ocp * 4;
+}
+int64_t packed_size(const Layer& L) {
+    const PackGeom g = pack_geom(L.c_out, kdim(L));
+    return g.bytes + (b4f6(L) ? (int64_t)g.ocp * 4 + (int64_t)g.ocp * g.kp : 0);
+}
+
+// BF6 (e3m2) code of an integer in [-8, 8] (every one of them is exact).
+uint32_t bf6_host(int v) {
+    static const uint32_t mag[9] = {0, 12, 16, 18, 20, 21, 22, 23, 24};
+    return (v < 0 ? 32u : 0u) | mag[v < 0 ? -v : v];
+}
+
+// One channel's BF6 codes into the FP6 blocks (see b4f6).
+void put_f6_row(const std::vector<int32_t>& row, int64_t k, int64_t prow, int64_t nst, uint8_t* blocks) {
+    for (int64_t s = 0; s < nst; ++s) {
+        uint8_t* rp = blocks + ((prow / 64) * nst + s) * 4096 + (prow % 64) * 64;
+        for (int64_t h = 0; h < 2; ++h) {
+            uint8_t bytes[24] = {0};
+            for (int v = 0; v < 32; ++v) {
+                const int64_t kk = s * 64 + h * 32 + v;
+                const uint32_t code = bf6_host(kk < k ? row[(size_t)kk] : 0);
+                for (int b = 0; b < 6; ++b)
+                    if ((code >> b) & 1u) bytes[(6 * v + b) / 8] |= (uint8_t)(1u << ((6 * v + b) % 8));
+            }
+            for (int i = 0; i < 3; ++i)
+                std::memcpy(rp + (((3 * h + i) ^ ((prow >> 2) & 7)) * 8), bytes + 8 * i, 8);
+        }
+    }
+}
+
+// Writes the packed layer (layout in PackGeom) into host memory `dst` of packed_size(L).
 iqnn_status prepack_into(const Layer& L, const void* w_host, const float* bias_host, float s_in,
                          const float* s_w_host, int per_channel, float s_out, float s_res, uint8_t* dst) {
     const PackGeom g = pack_geom(L.c_out, kdim(L));
@@ -323,7 +364,10 @@ iqnn_status prepack_into(const Layer& L, const void* w_host, const float* bias_h
     if (add && !scale_ok(s_res)) return fail(IQNN_ERR_INVALID_ARG, "residual scale must be positive and finite");
     if (std::fegetround() != FE_TONEAREST) return fail(IQNN_ERR_INVALID_ARG, "host rounding mode is not nearest-even");
 
-    std::memset(dst, 0, (size_t)g.bytes);
+    std::memset(dst, 0, (size_t)packed_size(L));
+    const bool f6 = b4f6(L);
+    int32_t* bias_f6 = f6 ? reinterpret_cast<int32_t*>(dst + f6_bias_off(L)) : nullptr;
+    uint8_t* blocks_f6 = f6 ? dst + f6_w_off(L) : nullptr;
     int32_t* bias = reinterpret_cast<int32_t*>(dst);
     float* mult = reinterpret_cast<float*>(dst + (size_t)g.ocp * 4);
     float* mres = reinterpret_cast<float*>(dst + (size_t)g.ocp * 8 + kHdrMres);
@@ -375,6 +419,13 @@ iqnn_status prepack_into(const Layer& L, const void* w_host, const float* bias_h
         if (mx * abs_sum + (fold < 0 ? -fold : fold) + (red < 0 ? -red : red) * mx * L.k > INT32_MAX)
             return fail(IQNN_ERR_OVERFLOW, "accumulator of channel %lld may leave int32", (long long)oc);
         bias[oc] = (int32_t)fold;
+        if (f6) {   // the FP6 path contracts (q - 8) for UINT4 activations
+            const int64_t f = fold + (L.x_type == T_UINT4 ? 8 : 0) * sum;
+            if (f < INT32_MIN || f > INT32_MAX)
+                return fail(IQNN_ERR_OVERFLOW, "folded bias of channel %lld leaves int32", (long long)oc);
+            bias_f6[oc] = (int32_t)f;   // physical channel order, like the folded bias
+            put_f6_row(row, L.k, packed_row_of_channel((int32_t)oc), g.kp / 64, blocks_f6);
+        }
         if (!raw) {
             const float m = sw_in / s_out;
             if (!normal_ok(m) || m > 1e20f)
@@ -432,9 +483,9 @@ iqnn_status prepack_host(const Layer& L, const void* w_host, const float* bias_h
                          const float* s_w_host, int per_channel, float s_out, float s_res, void* packed_host,
                          size_t packed_bytes) {
     if (!w_host || !s_w_host || !packed_host) return fail(IQNN_ERR_INVALID_ARG, "null weight, scale or output pointer");
-    const PackGeom g = pack_geom(L.c_out, kdim(L));
-    if ((int64_t)packed_bytes < g.bytes)
-        return fail(IQNN_ERR_INVALID_ARG, "packed buffer has %zu bytes, needs %lld", packed_bytes, (long long)g.bytes);
+    const int64_t need = packed_size(L);
+    if ((int64_t)packed_bytes < need)
+        return fail(IQNN_ERR_INVALID_ARG, "packed buffer has %zu bytes, needs %lld", packed_bytes, (long long)need);
     return prepack_into(L, w_host, bias_host, s_in, s_w_host, per_channel, s_out, s_res,
                         static_cast<uint8_t*>(packed_host));
 }
@@ -443,11 +494,11 @@ iqnn_status prepack_dev(const Layer& L, const void* w_host, const float* bias_ho
                         const float* s_w_host, int per_channel, float s_out, float s_res, void* packed_dev,
                         size_t packed_bytes, hipStream_t stream) {
     if (!w_host || !s_w_host || !packed_dev) return fail(IQNN_ERR_INVALID_ARG, "null weight, scale or output pointer");
-    const PackGeom g = pack_geom(L.c_out, kdim(L));
-    if ((int64_t)packed_bytes < g.bytes)
-        return fail(IQNN_ERR_INVALID_ARG, "packed buffer has %zu bytes, needs %lld", packed_bytes, (long long)g.bytes);
+    const int64_t need = packed_size(L);
+    if ((int64_t)packed_bytes < need)
+        return fail(IQNN_ERR_INVALID_ARG, "packed buffer has %zu bytes, needs %lld", packed_bytes, (long long)need);
     if (!aligned(packed_dev, 256)) return fail(IQNN_ERR_ALIGNMENT, "packed buffer must be 256-byte aligned");
-    std::vector<uint8_t> buf((size_t)g.bytes);
+    std::vector<uint8_t> buf((size_t)need);
     iqnn_status s = prepack_into(L, w_host, bias_host, s_in, s_w_host, per_channel, s_out, s_res, buf.data());
     if (s != IQNN_OK) return s;
     hipError_t e = hipMemcpyAsync(packed_dev, buf.data(), buf.size(), hipMemcpyHostToDevice, stream);
@@ -457,7 +508,8 @@ iqnn_status prepack_dev(const Layer& L, const void* w_host, const float* bias_ho
 }
 
 // Kernel parameters of a validated layer and its pointers.
-void conv_params(const Layer& L, const void* x, const void* packed, const void* res, void* y, ConvParams& p) {
+void conv_params(const Layer& L, const void* x, const void* packed, const void* res, void* y, ConvParams& p,
+                 bool f6 = false) {
     const bool add = L.epi == E_ADD || L.epi == E_ADD_RELU;
     const PackGeom g = pack_geom(L.c_out, kdim(L));
     const bool c4 = c4_path(L);
@@ -516,6 +568,11 @@ void conv_params(const Layer& L, const void* x, const void* packed, const void* 
         p.res_xor = L.res_type == T_INT8 ? 0x80808080u : (L.res_type == T_INT4 ? 0x88888888u : 0u);
     }
     p.vec_store = L.c_out % 16 == 0;
+    if (f6) {   // the layer's BF6 region (see b4f6)
+        p.bias = reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(packed) + f6_bias_off(L));
+        p.w_tiled = reinterpret_cast<const int8_t*>(static_cast<const uint8_t*>(packed) + f6_w_off(L));
+        p.f6 = 1;
+    }
 }
 
 iqnn_status forward(const Layer& L, const void* x, const void* packed, const void* res, void* y, hipStream_t stream) {
@@ -527,7 +584,7 @@ iqnn_status forward(const Layer& L, const void* x, const void* packed, const voi
     if (!aligned(packed, 256)) return fail(IQNN_ERR_ALIGNMENT, "packed buffer must be 256-byte aligned");
     const bool c4 = c4_path(L);
     ConvParams p;
-    conv_params(L, x, packed, res, y, p);
+    conv_params(L, x, packed, res, y, p, forced_tile() == kTileFp6 && b4f6(L));
     const int gather = is_4bit(L.x_type) ? (b4_stream(L) ? GATHER_B4S : GATHER_B4)
                                           : (L.c % 16 == 0 ? GATHER_B8 : (c4 ? GATHER_C4 : GATHER_B8_ELEM));
     const bool is_1x1 = gather != GATHER_B8_ELEM && gather != GATHER_C4 && L.kh == 1 && L.kw == 1 && L.sh == 1 && L.sw == 1 &&

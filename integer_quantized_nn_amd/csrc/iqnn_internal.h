@@ -110,6 +110,8 @@ struct ConvParams {
     float res_zf;
     uint32_t res_xor;
     int32_t vec_store;        // C_out % 16 == 0: vector stores
+    int32_t f6;               // 4-bit streaming layer on the FP6 MFMA: bias and w_tiled point at the
+                              // layer's BF6 region (set by the host, forced with kTileFp6)
 };
 
 // tile < 0 picks the kernel and its tile configuration from the layer shape; 0..17
@@ -118,7 +120,8 @@ struct ConvParams {
 // 128x128 configuration) (the IQNN_FORCE_TILE environment variable
 // or iqnn_set_conv_tile, for tuning sweeps and tests).
 constexpr int kTileDirect3x3 = 18;
-constexpr int kMaxTile = 18;
+constexpr int kTileFp6 = 19;   // 4-bit layers with INT4 weights: the FP6 MFMA path
+constexpr int kMaxTile = 19;
 hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_t stream, int tile);
 // Channel-tile groups of the streaming kernel's XCD split, forced for tuning sweeps
 // (IQNN_XCD_OC_GROUPS = 1, 2, 4 or 8); 0: the automatic rule.

@@ -54,6 +54,16 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// BF6 (e3m2: sign, 3 exponent bits with bias 3, 2 mantissa bits) code of an integer in
+// [-8, 8]; all of them are exact: 1 = 2^0, 3 = 2^1 * 1.5, 5 = 2^2 * 1.25, 7 = 2^2 * 1.75.
+__device__ __forceinline__ uint32_t bf6_code(int v) {
+    const int m = v < 0 ? -v : v;
+    const uint32_t mag = m == 0 ? 0u : (m == 1 ? 12u : (m == 2 ? 16u : (m == 3 ? 18u : (m == 4 ? 20u :
+                         (m == 5 ? 21u : (m == 6 ? 22u : (m == 7 ? 23u : 24u)))))));
+    return (v < 0 ? 32u : 0u) | mag;
+}
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
@@ -1063,7 +1073,15 @@ struct StreamCfg {
 // (measured lane layout: kept code v pairs with B bytes 16h + 4*(v/2 % 4) + pos of
 // B lane half v/8), and the B operand is the two 16-byte activation fragments the
 // dense path reads for its two k-steps.  One sparse MFMA per stage replaces two.
-template <class C, bool IS1X1, bool RES, bool C4, bool B4 = false, bool ZW = false, bool SP = false>
+// F6: 4-bit operands on the FP6 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4, both operands
+// BF6 e3m2, unit scales): the INT4 weights come as BF6 codes from their own tile-order
+// copy (64-byte LDS rows, 48 bytes used, 8-byte units swizzled by bits 2-4 of the row),
+// the packed 4-bit activation rows are turned into BF6 per stage through a 256-entry
+// table of code pairs (UINT4 codes shifted by -8, the shift folded into the bias), and
+// one MFMA per stage accumulates in fp32, which is exact for these integers (a partial
+// sum stays below 2^24); the epilogue converts it to int32 and adds the bias.
+template <class C, bool IS1X1, bool RES, bool C4, bool B4 = false, bool ZW = false, bool SP = false,
+          bool F6 = false>
 __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) {
     constexpr int BM = C::BM, BN = C::BN, WM = C::WM, NST = C::NST;
     constexpr int TM = C::TM, TN = C::TN;
@@ -1087,6 +1105,7 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
                   "a 2:4 stage: kept codes and activations in KB-instructions, positions in 256-byte ones");
     static_assert(!SP || !(B4 || C4 || ZW), "2:4 weights take the 8-bit gather with symmetric weights");
     static_assert(!(SP && RES) || 4 * K_LOADS * 1024 <= STAGE, "the padded residual stage fits a slot");
+    static_assert(!F6 || (B4 && !SP && !ZW && !C4), "the FP6 path takes packed 4-bit activations");
     static_assert(!(B4 && C4), "one gather mode");
     static_assert(NST >= 3, "ring depth");
     static_assert(D * K_LOADS <= 60, "DMA in flight must fit the 6-bit vmcnt");
@@ -1098,6 +1117,7 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
     __shared__ __attribute__((aligned(1024))) uint8_t ring[NST * STAGE];
     __shared__ __attribute__((aligned(16))) int32_t cbias[BM];
     __shared__ __attribute__((aligned(16))) float cmult[BM];
+    __shared__ __attribute__((aligned(16))) uint32_t f6tab[F6 ? 256 : 1];   // byte -> BF6 code pair
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1122,6 +1142,13 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
     if (tid < BM) {
         cbias[tid] = p.bias[oc0 + tid];
         cmult[tid] = p.mult[oc0 + tid];
+    }
+    if constexpr (F6) {
+        // the two codes of a byte: low nibble (even element) in bits 0-5, high in 6-11
+        const int lo = tid & 15, hi = tid >> 4;
+        const int vlo = p.x_signed4 ? (lo >= 8 ? lo - 16 : lo) : lo - 8;
+        const int vhi = p.x_signed4 ? (hi >= 8 ? hi - 16 : hi) : hi - 8;
+        f6tab[tid] = bf6_code(vlo) | (bf6_code(vhi) << 6);
     }
     __syncthreads();
 
@@ -1329,8 +1356,18 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
     // accumulators start from the folded bias of their channels: lane half h of channel
     // block t holds channels ocl(t) .. ocl(t)+15 of the block
     v16i acc[TM][TN];
+    v16f accf[F6 ? TM : 1][F6 ? TN : 1];
     int32_t ssum[ZW ? TN : 1];
     auto init_acc = [&]() {
+        if constexpr (F6) {
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+#pragma unroll
+                for (int u = 0; u < TN; ++u)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) accf[t][u][q] = 0.0f;
+            return;
+        }
         if constexpr (ZW) {
 #pragma unroll
             for (int u = 0; u < TN; ++u) ssum[u] = 0;
@@ -1445,11 +1482,54 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
     };
     SpFrag fx, fy;
 
+    // FP6 path: the fragments of one stage (BF6 weight codes, packed 4-bit activations)
+    struct F6Frag {
+        v8i a[F6 ? TM : 1];
+        uint4 b[F6 ? TN : 1];
+    };
+    auto read_f6 = [&](const uint8_t* cur, F6Frag& f) {
+        if constexpr (F6) {
+#pragma unroll
+            for (int t = 0; t < TM; ++t) {
+                const int row = wave_oc * C::WOC + 32 * t + frow;
+                const uint8_t* rp = cur + row * kPipeBK;
+                const int sw = (row >> 2) & 7, u0 = 3 * (lane >> 5);
+                const uint2 d0 = *reinterpret_cast<const uint2*>(rp + ((u0 ^ sw) << 3));
+                const uint2 d1 = *reinterpret_cast<const uint2*>(rp + (((u0 + 1) ^ sw) << 3));
+                const uint2 d2 = *reinterpret_cast<const uint2*>(rp + (((u0 + 2) ^ sw) << 3));
+                f.a[t] = v8i{(int)d0.x, (int)d0.y, (int)d1.x, (int)d1.y, (int)d2.x, (int)d2.y, 0, 0};
+            }
+#pragma unroll
+            for (int u = 0; u < TN; ++u)
+                f.b[u] = *reinterpret_cast<const uint4*>(cur + BM * kPipeBK + (wave_px * C::WPX + 32 * u) * 32 + b4off);
+        }
+    };
+    // 32 packed 4-bit codes (16 bytes) -> 32 BF6 codes, code v at bits 6v..6v+5
+    auto to_bf6 = [&](const uint4& raw) -> v8i {
+        const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+        uint32_t pr[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) pr[q] = f6tab[(wd[q >> 2] >> (8 * (q & 3))) & 0xFFu];
+        v8i o;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const uint32_t* P = pr + 8 * g;
+            o[3 * g] = (int)(P[0] | (P[1] << 12) | (P[2] << 24));
+            o[3 * g + 1] = (int)((P[2] >> 8) | (P[3] << 4) | (P[4] << 16) | (P[5] << 28));
+            o[3 * g + 2] = (int)((P[5] >> 4) | (P[6] << 8) | (P[7] << 20));
+        }
+        o[6] = 0;
+        o[7] = 0;
+        return o;
+    };
+    F6Frag gx, gy;
+
     for (int i = 0; i < D; ++i) issue();
     uint32_t cur_off = 0;
     auto advance = [&]() { cur_off = cur_off + STAGE == NST * STAGE ? 0 : cur_off + STAGE; };
     sync();
     if constexpr (SP) read_sp(ring + cur_off, fx);
+    else if constexpr (F6) read_f6(ring + cur_off, gx);
     else read_frags(ring + cur_off, foff0, fa0, fb0);
 
     constexpr int NMF = TM * TN, NRD = TM + TN, HALF = NMF / 2;
@@ -1480,9 +1560,48 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
         }
     };
 
+    // one FP6 stage: the activations to BF6, the first half of the MFMAs, the barrier
+    // (and the DMA refill), the next stage's reads next to the second half
+    auto f6_stage = [&](F6Frag& f, F6Frag& nf, bool more, bool do_sync) {
+        if constexpr (F6) {
+            v8i b6[TN];
+#pragma unroll
+            for (int u = 0; u < TN; ++u) b6[u] = to_bf6(f.b[u]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+#pragma unroll
+                for (int u = 0; u < TN; ++u)
+                    if (t * TN + u < HALF)
+                        accf[t][u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[t], b6[u], accf[t][u], 3, 3,
+                                                                                     0, 127, 0, 127);
+            __builtin_amdgcn_sched_barrier(0);
+            advance();
+            if (do_sync) sync();
+            if (more) read_f6(ring + cur_off, nf);
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+#pragma unroll
+                for (int u = 0; u < TN; ++u)
+                    if (t * TN + u >= HALF)
+                        accf[t][u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[t], b6[u], accf[t][u], 3, 3,
+                                                                                     0, 127, 0, 127);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
     for (int j = 0; j < J; ++j) {
         const bool last_tile = j + 1 == J;
-        if constexpr (SP) {
+        if constexpr (F6) {
+            for (int s = 0; s < nst; s += 2) {
+                const bool end0 = s + 1 == nst;
+                f6_stage(gx, gy, !end0, !(last_tile && end0 && !RES));
+                if (!end0) {
+                    const bool end1 = s + 2 == nst;
+                    f6_stage(gy, gx, !end1, !(last_tile && end1 && !RES));
+                }
+            }
+        } else if constexpr (SP) {
             for (int s = 0; s < nst; s += 2) {
                 const bool end0 = s + 1 == nst;
                 sp_stage(fx, fy, !end0, !(last_tile && end0 && !RES));
@@ -1554,7 +1673,14 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
                         rtile + pl * RROW + (((ocl >> 5) ^ rswz(pl, RROW / 16)) << 4) + ((ocl >> 4) & 1) * 8);
                     rw[0] = v.x; rw[1] = v.y;
                 }
-                epi_store16<false, RES ? (B4 ? 3 : 1) : 2>(p, acc[t][u], nullptr, mult, rw, ocb, pix, add, m_res);
+                if constexpr (F6) {   // fp32 sums of integers below 2^24: exact conversion
+                    v16i ai;
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) ai[q] = (int)accf[t][u][q];
+                    epi_store16<true, RES ? 3 : 2>(p, ai, &cbias[ocl], mult, rw, ocb, pix, add, m_res);
+                } else {
+                    epi_store16<false, RES ? (B4 ? 3 : 1) : 2>(p, acc[t][u], nullptr, mult, rw, ocb, pix, add, m_res);
+                }
             }
         }
         init_acc();
@@ -1564,6 +1690,7 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
         }
         if (!last_tile) {
             if constexpr (SP) read_sp(ring + cur_off, fx);
+            else if constexpr (F6) read_f6(ring + cur_off, gx);
             else read_frags(ring + cur_off, foff0, fa0, fb0);
         }
     }
@@ -1604,6 +1731,7 @@ void stream_schedule(ConvParams& q, int occ) {
 // 4-bit activations (packed rows streamed to LDS): the 64x128 and 128x128 blocks.
 template <class C>
 hipError_t launch_stream_b4(const ConvParams& p, bool is_1x1, hipStream_t stream) {
+    const bool f6 = p.f6 != 0;   // INT4 weights as BF6 on the FP6 MFMA
     ConvParams q = p;
     q.n_oc_tiles = (p.c_out + C::BM - 1) / C::BM;
     const int64_t n_px = (p.m + C::BN - 1) / C::BN;
@@ -1613,6 +1741,13 @@ hipError_t launch_stream_b4(const ConvParams& p, bool is_1x1, hipStream_t stream
     stream_schedule(q, C::OCC);
     dim3 g((unsigned)(8 * q.gx)), b(256);
     const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;
+    if (f6) {
+        if (is_1x1 && add) hipLaunchKernelGGL((qconv_stream<C, true, true, false, true, false, false, true>), g, b, 0, stream, q);
+        else if (is_1x1) hipLaunchKernelGGL((qconv_stream<C, true, false, false, true, false, false, true>), g, b, 0, stream, q);
+        else if (add) hipLaunchKernelGGL((qconv_stream<C, false, true, false, true, false, false, true>), g, b, 0, stream, q);
+        else hipLaunchKernelGGL((qconv_stream<C, false, false, false, true, false, false, true>), g, b, 0, stream, q);
+        return hipGetLastError();
+    }
     if (is_1x1 && add) hipLaunchKernelGGL((qconv_stream<C, true, true, false, true>), g, b, 0, stream, q);
     else if (is_1x1) hipLaunchKernelGGL((qconv_stream<C, true, false, false, true>), g, b, 0, stream, q);
     else if (add) hipLaunchKernelGGL((qconv_stream<C, false, true, false, true>), g, b, 0, stream, q);
@@ -2372,6 +2507,7 @@ using S64x128d12 = StreamCfg<64, 128, 1, 12>;
 using S64x128d6 = StreamCfg<64, 128, 1, 6>;
 using S128x128d8 = StreamCfg<128, 128, 2, 8>;
 using S128x128d4 = StreamCfg<128, 128, 2, 4>;
+using S128x128w1d4 = StreamCfg<128, 128, 1, 4>;
 using S64x256d3 = StreamCfg<64, 256, 1, 3>;
 using S256x128d6 = StreamCfg<256, 128, 2, 6>;
 using S128x256d6 = StreamCfg<128, 256, 2, 6>;
@@ -2397,6 +2533,8 @@ int pipe_tile_choice(int64_t m, int32_t c_out, int64_t k, bool res) {
 }
 
 hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_t stream, int tile) {
+    if (p.f6 && gather != GATHER_B4S) return hipErrorInvalidValue;
+    if (tile == kTileFp6) tile = -1;   // the FP6 path is chosen by the host (ConvParams::f6)
     if (p.w_idx) {   // 2:4 weights: their packed layout is the sparse streaming kernel's
         const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;
         const bool res_prefetch = add && p.vec_store && (p.res_type == T_INT8 || p.res_type == T_UINT8);
@@ -2418,6 +2556,9 @@ hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_
     if (gather == GATHER_C4 && tile < 0 && stem_ok(p)) return launch_stem(p, stream);
     if (gather == GATHER_B4S) {   // its packed layout is the streaming kernel's: no other tile
         if (p.c_out <= 64) return launch_stream_b4<S64x128d6>(p, is_1x1, stream);
+        // FP6: one wave per 128 channels x 32 pixels, so each activation fragment turned
+        // into BF6 feeds four MFMAs
+        if (p.f6) return launch_stream_b4<S128x128w1d4>(p, is_1x1, stream);
         return launch_stream_b4<S128x128d4>(p, is_1x1, stream);
     }
     if (p.zw_red != 0) {   // asymmetric weights ride on the streaming kernel only

@@ -39,9 +39,9 @@ def test_version_and_status_strings(lib):
 
 
 def test_conv_tile_override_range(lib):
-    for t in (0, 17, 18, -1):
+    for t in (0, 17, 18, 19, -1):
         B.iqnn_set_conv_tile(t)
-    for bad in (-2, 19):
+    for bad in (-2, 20):
         with pytest.raises(B.IqnnError) as ei:
             B.iqnn_set_conv_tile(bad)
         assert ei.value.status == 1 and "tile" in str(ei.value)
@@ -300,3 +300,52 @@ def test_prepack_overflow_and_bad_scales(lib):
     with pytest.raises(B.IqnnError) as e:   # multiplier underflows to a denormal
         _host_pack(d, w, B.INT8, None, np.float32(1e-20), np.full(16, 1e-20, np.float32), 1e10)
     assert e.value.status == 1
+
+
+def _bf6_value(code):
+    """Real value of a BF6 (e3m2) code: sign, 3 exponent bits (bias 3), 2 mantissa bits."""
+    sign = -1 if code & 32 else 1
+    e, m = (code >> 2) & 7, code & 3
+    return sign * (m / 4 * 2.0 ** -2 if e == 0 else (1 + m / 4) * 2.0 ** (e - 3))
+
+
+@pytest.mark.parametrize("x_type,c_out", [(B.UINT4, 96), (B.INT4, 64)])
+def test_host_prepack_fp6_region(lib, x_type, c_out):
+    """4-bit streaming layers with INT4 weights carry a BF6 copy of the weights and a
+    bias for the FP6 path after the standard layout: the copy decodes to the weight
+    codes, and the bias is the folded bias plus 8 * sum(W) for UINT4 activations (the
+    path contracts q - 8)."""
+    rng = np.random.default_rng(c_out)
+    c_in, k = 64, 9 * 64
+    w = rng.integers(-8, 8, size=(c_out, 3, 3, c_in)).astype(np.int32)
+    bias = rng.normal(0, 0.3, c_out).astype(np.float32)
+    s_w = rng.uniform(0.01, 0.05, c_out).astype(np.float32)
+    z_in = 5 if x_type == B.UINT4 else 0
+    d = conv_desc(x_type=x_type, w_type=B.INT4, y_type=B.UINT4, c_in=c_in, c_out=c_out, epilogue=B.EPI_RELU,
+                  z_in=z_in, z_out=1)
+    buf = _host_pack(d, w, B.INT4, bias, np.float32(0.05), s_w, np.float32(0.07))
+    ocp, kp = 256, (k + 63) // 64 * 64
+    std_bytes = 8 * ocp + 256 + 2 * ocp * kp
+    assert buf.size == std_bytes + 4 * ocp + ocp * kp
+    folded = buf[:4 * ocp].view(np.int32)[:c_out].astype(np.int64)
+    bias_f6 = buf[std_bytes:std_bytes + 4 * ocp].view(np.int32)[:c_out]
+    shift = 8 if x_type == B.UINT4 else 0
+    assert np.array_equal(bias_f6, folded + shift * w.reshape(c_out, -1).sum(axis=1))
+    # blocks: 4 KB per (64-row group, stage); row R's 8-byte unit u at u ^ ((R >> 2) & 7)
+    nst = kp // 64
+    blocks = buf[std_bytes + 4 * ocp:].reshape(ocp // 64, nst, 64, 64)
+    rows = []
+    for c in range(c_out):
+        b, r32 = divmod(c, 32)
+        h, j, r = r32 // 16, (r32 // 4) % 4, r32 % 4
+        rows.append(32 * b + 8 * j + 4 * h + r)
+    logical = w.reshape(c_out, -1)
+    for c in range(0, c_out, 7):
+        R = rows[c]
+        for s in range(nst):
+            rowbytes = blocks[R // 64, s, R % 64]
+            for h in range(2):
+                half = b"".join(bytes(rowbytes[8 * ((3 * h + i) ^ ((R >> 2) & 7)):][:8]) for i in range(3))
+                bits = int.from_bytes(half, "little")
+                vals = [_bf6_value((bits >> (6 * v)) & 63) for v in range(32)]
+                assert vals == list(logical[c, s * 64 + 32 * h:s * 64 + 32 * h + 32]), (c, s, h)

@@ -221,6 +221,66 @@ def test_conv_4bit_streaming(case):
     assert_bytes_equal(gpu_conv(c, x, wc, res), want, str(case))
 
 
+@pytest.mark.parametrize("case", B4S, ids=lambda c: "n%dh%dw%dci%dco%dk%ds%dp%d_x%dy%de%d" % c[:11])
+def test_conv_4bit_fp6_path(case):
+    """The same 4-bit layers on the FP6 MFMA path (forced through tile 19): INT4 weights
+    and the activations as BF6 codes, fp32 accumulation of integers, every byte equal to
+    the oracle's."""
+    require_gpu()
+    from integer_quantized_nn_amd import binding as B
+    n, h, w, ci, co, k, s, p, xt, yt, epi, rt = case
+    c = synth.conv_case(hash(case) % 2 ** 31 + 1, n, h, w, ci, co, k, s, p, xt, I4, yt, epi, res_type=rt)
+    x, wc, res = conv_codes(c)
+    want = to_bytes(oracle_conv(c, x, wc, res), yt)
+    B.iqnn_set_conv_tile(19)
+    try:
+        got = gpu_conv(c, x, wc, res)
+    finally:
+        B.iqnn_set_conv_tile(-1)
+    assert_bytes_equal(got, want, "fp6 " + str(case))
+
+
+def test_conv_4bit_fp6_adversarial_codes():
+    """Every 4-bit code, including -8 weights and the extreme activations 0 and 15, on
+    the FP6 path."""
+    require_gpu()
+    from integer_quantized_nn_amd import binding as B
+    rng = np.random.default_rng(43)
+    for (xt, yt, rt) in [(U4, U4, U4), (I4, I4, I4)]:
+        c = synth.conv_case(9, 3, 5, 6, 64, 64, 3, 1, 1, xt, I4, yt, ADD_RELU, res_type=rt)
+        xlo, xhi = O.qrange(otype(xt))
+        rlo, rhi = O.qrange(otype(rt))
+        x = rng.integers(xlo, xhi + 1, size=c.x.shape).astype(np.int32)
+        w = rng.integers(-8, 8, size=c.w.shape).astype(np.int32)
+        r = rng.integers(rlo, rhi + 1, size=c.res.shape).astype(np.int32)
+        c.z_in = int(xhi) if xt == U4 else 0
+        want = to_bytes(oracle_conv(c, x, w, r), yt)
+        B.iqnn_set_conv_tile(19)
+        try:
+            got = gpu_conv(c, x, w, r)
+        finally:
+            B.iqnn_set_conv_tile(-1)
+        assert_bytes_equal(got, want, "fp6 adversarial x%d" % xt)
+
+
+def test_conv_4bit_fp6_workload_sampled_images():
+    """The 4-bit workload (N=64, 28x28, 128 -> 128, Conv_Add_Relu, UINT4 in / out /
+    residual, INT4 weights) on the FP6 path, against the oracle on sampled images and
+    against the int8 path on every byte."""
+    require_gpu()
+    from integer_quantized_nn_amd import binding as B
+    c = synth.conv3x3_4bit()
+    x, wc, res = conv_codes(c)
+    B.iqnn_set_conv_tile(19)
+    try:
+        got = gpu_conv(c, x, wc, res)
+    finally:
+        B.iqnn_set_conv_tile(-1)
+    assert_bytes_equal(got, gpu_conv(c, x, wc, res), "fp6 vs int8 path")
+    images = [0, 31, 63]
+    assert_bytes_equal(got[images], to_bytes(oracle_conv(c, x, wc, res, images=images), c.y_type), "fp6 vs oracle")
+
+
 def test_conv_adversarial_codes_and_padding():
     # every code of each type, including -128 / 255 / -8 / 15, on tiny images where
     # most taps read padding
