@@ -1728,10 +1728,10 @@ void stream_schedule(ConvParams& q, int occ) {
     q.gx = per;
 }
 
-// 4-bit activations (packed rows streamed to LDS): the 64x128 and 128x128 blocks.
-template <class C>
+// 4-bit activations (packed rows streamed to LDS): the 64x128 and 128x128 blocks; F6:
+// INT4 weights as BF6 on the FP6 MFMA (ConvParams::f6 set by the host).
+template <class C, bool F6>
 hipError_t launch_stream_b4(const ConvParams& p, bool is_1x1, hipStream_t stream) {
-    const bool f6 = p.f6 != 0;   // INT4 weights as BF6 on the FP6 MFMA
     ConvParams q = p;
     q.n_oc_tiles = (p.c_out + C::BM - 1) / C::BM;
     const int64_t n_px = (p.m + C::BN - 1) / C::BN;
@@ -1741,17 +1741,10 @@ hipError_t launch_stream_b4(const ConvParams& p, bool is_1x1, hipStream_t stream
     stream_schedule(q, C::OCC);
     dim3 g((unsigned)(8 * q.gx)), b(256);
     const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;
-    if (f6) {
-        if (is_1x1 && add) hipLaunchKernelGGL((qconv_stream<C, true, true, false, true, false, false, true>), g, b, 0, stream, q);
-        else if (is_1x1) hipLaunchKernelGGL((qconv_stream<C, true, false, false, true, false, false, true>), g, b, 0, stream, q);
-        else if (add) hipLaunchKernelGGL((qconv_stream<C, false, true, false, true, false, false, true>), g, b, 0, stream, q);
-        else hipLaunchKernelGGL((qconv_stream<C, false, false, false, true, false, false, true>), g, b, 0, stream, q);
-        return hipGetLastError();
-    }
-    if (is_1x1 && add) hipLaunchKernelGGL((qconv_stream<C, true, true, false, true>), g, b, 0, stream, q);
-    else if (is_1x1) hipLaunchKernelGGL((qconv_stream<C, true, false, false, true>), g, b, 0, stream, q);
-    else if (add) hipLaunchKernelGGL((qconv_stream<C, false, true, false, true>), g, b, 0, stream, q);
-    else hipLaunchKernelGGL((qconv_stream<C, false, false, false, true>), g, b, 0, stream, q);
+    if (is_1x1 && add) hipLaunchKernelGGL((qconv_stream<C, true, true, false, true, false, false, F6>), g, b, 0, stream, q);
+    else if (is_1x1) hipLaunchKernelGGL((qconv_stream<C, true, false, false, true, false, false, F6>), g, b, 0, stream, q);
+    else if (add) hipLaunchKernelGGL((qconv_stream<C, false, true, false, true, false, false, F6>), g, b, 0, stream, q);
+    else hipLaunchKernelGGL((qconv_stream<C, false, false, false, true, false, false, F6>), g, b, 0, stream, q);
     return hipGetLastError();
 }
 
@@ -2555,11 +2548,13 @@ hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_
     }
     if (gather == GATHER_C4 && tile < 0 && stem_ok(p)) return launch_stem(p, stream);
     if (gather == GATHER_B4S) {   // its packed layout is the streaming kernel's: no other tile
-        if (p.c_out <= 64) return launch_stream_b4<S64x128d6>(p, is_1x1, stream);
+        if (p.c_out <= 64)
+            return p.f6 ? launch_stream_b4<S64x128d6, true>(p, is_1x1, stream)
+                        : launch_stream_b4<S64x128d6, false>(p, is_1x1, stream);
         // FP6: one wave per 128 channels x 32 pixels, so each activation fragment turned
         // into BF6 feeds four MFMAs
-        if (p.f6) return launch_stream_b4<S128x128w1d4>(p, is_1x1, stream);
-        return launch_stream_b4<S128x128d4>(p, is_1x1, stream);
+        if (p.f6) return launch_stream_b4<S128x128w1d4, true>(p, is_1x1, stream);
+        return launch_stream_b4<S128x128d4, false>(p, is_1x1, stream);
     }
     if (p.zw_red != 0) {   // asymmetric weights ride on the streaming kernel only
         const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;

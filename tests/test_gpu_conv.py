@@ -281,6 +281,46 @@ def test_conv_4bit_fp6_workload_sampled_images():
     assert_bytes_equal(got[images], to_bytes(oracle_conv(c, x, wc, res, images=images), c.y_type), "fp6 vs oracle")
 
 
+def test_conv_4bit_fp6_path_reads_only_its_own_region():
+    """The FP6 path is the one that runs under tile 19: with the int8 weights and the
+    int32 bias of the packed layer overwritten it still matches the oracle, and the
+    default path still does with the BF6 region overwritten instead."""
+    require_gpu()
+    import torch
+    from integer_quantized_nn_amd import binding as B
+    from integer_quantized_nn_amd.layers import QConv
+    c = synth.conv_case(77, 1, 13, 7, 128, 128, 3, 1, 1, U4, I4, U4, ADD_RELU, res_type=U4)
+    x, wc, res = conv_codes(c)
+    want = to_bytes(oracle_conv(c, x, wc, res), c.y_type)
+    ocp, kp = 256, 9 * 128
+    std_bytes = 8 * ocp + 256 + 2 * ocp * kp          # bias, multipliers, scalars, int8 weights, tile-order copy
+    xd = torch.from_numpy(to_bytes(x, c.x_type)).cuda()
+    rd = torch.from_numpy(to_bytes(res, c.res_type)).cuda()
+
+    def layer():
+        conv = QConv(1, 13, 7, 128, 128, 3, c.stride, c.pad, c.x_type, I4, c.y_type, c.epi, c.z_in, c.z_out,
+                     to_bytes(wc, I4), c.bias, c.s_in, c.s_w, c.s_out, res_type=c.res_type, z_res=c.z_res,
+                     s_res=c.s_res)
+        assert conv.packed.numel() == std_bytes + 4 * ocp + ocp * kp
+        return conv
+
+    conv = layer()
+    conv.packed[:4 * ocp].fill_(0x5A)
+    conv.packed[8 * ocp + 256:std_bytes].fill_(0x5A)
+    B.iqnn_set_conv_tile(19)
+    try:
+        got = conv(xd, res=rd)
+        torch.cuda.synchronize()
+    finally:
+        B.iqnn_set_conv_tile(-1)
+    assert_bytes_equal(got.cpu().numpy(), want, "fp6 path with the int8 region overwritten")
+    conv = layer()
+    conv.packed[std_bytes:].fill_(0x5A)
+    got = conv(xd, res=rd)
+    torch.cuda.synchronize()
+    assert_bytes_equal(got.cpu().numpy(), want, "default path with the BF6 region overwritten")
+
+
 def test_conv_adversarial_codes_and_padding():
     # every code of each type, including -128 / 255 / -8 / 15, on tiny images where
     # most taps read padding
