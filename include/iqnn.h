@@ -55,7 +55,7 @@ typedef enum {
     IQNN_ERR_INVALID_ARG = 1,  /* a size, type, zero point, scale or pointer is invalid */
     IQNN_ERR_UNSUPPORTED = 2,  /* valid, but a combination the library does not implement */
     IQNN_ERR_ALIGNMENT = 3,    /* a pointer or row does not meet the documented alignment */
-    IQNN_ERR_OVERFLOW = 4,     /* folded bias or accumulator bound would leave int32 */
+    IQNN_ERR_OVERFLOW = 4,     /* folded bias or accumulator bound would leave int32; a range too wide for binary32 */
     IQNN_ERR_HIP = 5           /* the HIP runtime reported an error */
 } iqnn_status;
 
@@ -180,6 +180,23 @@ const char *iqnn_last_error(void);
 iqnn_status iqnn_set_conv_tile(int32_t tile);
 
 /* ------------------------------------------------------- quantize / dequantize */
+
+/* Quantization parameters of a tensor from its real range [minv, maxv] (host, pure
+ * function).  MinMax uniform quantization (FQ-ViT article, §3.1); the Horizon QAT
+ * talk (section 三) fixes a scale from the real min / max over the INT8 range.
+ * Every step is one binary32 operation rounded to nearest even:
+ *   symmetric (signed qtype only): S = max(|minv|, |maxv|) / Q_MAX, Z = 0;
+ *   asymmetric: the range is widened to hold 0 (mn = min(minv, 0), mx = max(maxv, 0)),
+ *   S = (mx - mn) / (Q_MAX - Q_MIN), Z = clip(Q_MIN - rne(mn / S), Q_MIN, Q_MAX),
+ *   so the real 0 has the exact code Z.
+ * A scale below the smallest normal binary32 (a zero range) is replaced by 1, so every
+ * value of such a tensor quantizes to Z.  qtype: INT8, UINT8, INT4, UINT4.  Errors:
+ * IQNN_ERR_INVALID_ARG for null outputs, non-finite bounds, minv > maxv, another
+ * qtype, or symmetric with an unsigned qtype; IQNN_ERR_OVERFLOW when mx - mn is not a
+ * finite binary32.  Outputs are written only on success. */
+iqnn_status iqnn_choose_qparams(float minv, float maxv, int32_t qtype, int symmetric, float *scale,
+                                int32_t *zp);
+
 
 /* Quantize fp32 -> codes.  x viewed as [outer][ch][inner]; with per_channel the
  * scale and zero point of element (o, c, i) are scale_dev[c], zp_dev[c], else

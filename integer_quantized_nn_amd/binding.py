@@ -64,6 +64,7 @@ def lib():
         "iqnn_status_str": (ctypes.c_char_p, [I]),
         "iqnn_last_error": (ctypes.c_char_p, []),
         "iqnn_set_conv_tile": (I, [I32]),
+        "iqnn_choose_qparams": (I, [F, F, I32, I, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)]),
         "iqnn_quantize": (I, [P, P, I64, I64, I64, P, P, I, I32, P]),
         "iqnn_dequantize": (I, [P, P, I64, I64, I64, P, P, I, I32, P]),
         "iqnn_quantize_pad": (I, [P, P, I32, I32, I32, I32, I32, I32, P, P, I, I32, P]),
@@ -123,6 +124,14 @@ def iqnn_abi_version():
 
 def iqnn_set_conv_tile(tile):
     _check(lib().iqnn_set_conv_tile(int(tile)))
+
+
+def iqnn_choose_qparams(vmin, vmax, qtype, symmetric=False):
+    """(scale, zero point) of a real range [vmin, vmax]: binary32 scale, int zero point."""
+    s, z = ctypes.c_float(), ctypes.c_int32()
+    _check(lib().iqnn_choose_qparams(float(vmin), float(vmax), int(qtype), int(bool(symmetric)),
+                                     ctypes.byref(s), ctypes.byref(z)))
+    return np.float32(s.value), int(z.value)
 
 
 def iqnn_quantize(x, q, outer, ch, inner, scale, zp, per_channel, qtype, stream=None):

@@ -646,6 +646,34 @@ iqnn_status iqnn_set_conv_tile(int32_t tile) {
     return ok();
 }
 
+iqnn_status iqnn_choose_qparams(float minv, float maxv, int32_t qtype, int symmetric, float* scale,
+                                int32_t* zp) {
+    int32_t lo, hi;
+    if (!code_range(qtype, &lo, &hi)) return fail(IQNN_ERR_INVALID_ARG, "choose_qparams: type %d is not a code type", qtype);
+    if (!scale || !zp) return fail(IQNN_ERR_INVALID_ARG, "choose_qparams: null output");
+    if (!std::isfinite(minv) || !std::isfinite(maxv) || minv > maxv)
+        return fail(IQNN_ERR_INVALID_ARG, "choose_qparams: range [%g, %g] is not a finite interval", minv, maxv);
+    if (symmetric && lo >= 0) return fail(IQNN_ERR_INVALID_ARG, "choose_qparams: symmetric parameters need a signed type");
+    const float mn = minv < 0.0f ? minv : 0.0f, mx = maxv > 0.0f ? maxv : 0.0f;
+    float s;
+    if (symmetric) {
+        s = std::max(std::fabs(minv), std::fabs(maxv)) / (float)hi;
+    } else {
+        const float width = mx - mn;
+        if (!std::isfinite(width)) return fail(IQNN_ERR_OVERFLOW, "choose_qparams: range width overflows binary32");
+        s = width / (float)(hi - lo);
+    }
+    if (!(s >= std::numeric_limits<float>::min())) s = 1.0f;
+    int32_t z = 0;
+    if (!symmetric) {
+        const int64_t t = (int64_t)std::nearbyint(mn / s);
+        z = (int32_t)std::min<int64_t>(std::max<int64_t>(lo - t, lo), hi);
+    }
+    *scale = s;
+    *zp = z;
+    return ok();
+}
+
 iqnn_status iqnn_quantize(const float* x_dev, void* q_dev, int64_t outer, int64_t ch, int64_t inner,
                           const float* scale_dev, const int32_t* zp_dev, int per_channel, int32_t qtype,
                           void* stream) {

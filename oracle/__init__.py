@@ -10,7 +10,7 @@ for the page passage each step follows.
 Codes are numpy int32 arrays holding one logical code per element (4-bit codes
 unpacked); pack()/unpack() convert to and from the byte layout.  The integer-only
 requantization (get_mn, requant_int) is written here directly in numpy int64 /
-Python integers.
+Python integers, and choose_qparams in numpy binary32 scalars.
 
 Parity pins: every function here is pinned by tests/test_oracle_*.py against
 worked values printed on the pages, closed forms, library routines
@@ -103,6 +103,34 @@ def _per_channel_arrays(scale, zp, ch):
         scale = np.broadcast_to(scale, (ch,)).astype(np.float32)
         zp = np.broadcast_to(zp, (ch,)).astype(np.int32)
     return _c(scale, np.float32), _c(zp, np.int32), int(per_channel)
+
+
+def choose_qparams(vmin, vmax, qtype, symmetric=False):
+    """Quantization parameters from a real range (FQ-ViT article, §3.1, MinMax uniform
+    quantization; Horizon QAT talk, section 三: a fixed scale from the real min / max
+    over the code range).  Each step is one binary32 operation (numpy float32 scalars,
+    round to nearest even):
+      symmetric (signed types): S = max(|min|, |max|) / Q_MAX, Z = 0;
+      asymmetric: widen the range to hold 0, S = (max - min) / (Q_MAX - Q_MIN),
+      Z = clip(Q_MIN - rne(min / S)), so the real 0 gets the exact code Z.
+    A scale that is zero or below the smallest normal binary32 becomes 1 (every value
+    of a zero-range tensor is then the code Z).  Returns (np.float32 S, int Z)."""
+    f = np.float32
+    q_min, q_max = qrange(qtype)
+    lo_real, hi_real = f(vmin), f(vmax)
+    if symmetric:
+        assert q_min < 0, "symmetric parameters need a signed type"
+        scale = f(max(abs(lo_real), abs(hi_real))) / f(q_max)
+    else:
+        lo_real = lo_real if lo_real < f(0) else f(0)
+        hi_real = hi_real if hi_real > f(0) else f(0)
+        scale = (hi_real - lo_real) / f(q_max - q_min)
+    if not scale >= np.finfo(np.float32).tiny:
+        scale = f(1)
+    if symmetric:
+        return f(scale), 0
+    zero = q_min - int(np.rint(lo_real / scale))
+    return f(scale), int(min(max(zero, q_min), q_max))
 
 
 def _axis_view(shape, axis):
