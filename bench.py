@@ -193,6 +193,9 @@ def bench_trunk(args):
     roof["algorithmic_ops_per_launch"] = ops_per_launch
     roof["avg_launch_us"] = avg_dur * 1e6
     roof["mfma_frac"] = ops_per_launch / avg_dur / PEAK_INT8_OPS
+    if roof["bound"] == "hbm":   # the same bytes against what a plain copy reaches on this GPU
+        roof["measured_copy_gbs"] = measure_copy_gbs()
+        roof["frac_of_measured_copy"] = roof["achieved"] / roof["measured_copy_gbs"]
 
     value = step_ops / (ms_per_step * 1e-3) / 1e12
     per_layer = {}
@@ -224,6 +227,24 @@ def bench_trunk(args):
     else:
         rec["cpu_baseline"] = None
     return rec
+
+
+def measure_copy_gbs(mib=1024, reps=5):
+    """Best rate of a device-to-device copy (bytes read + written per second, GB/s):
+    the HBM rate a plain streaming kernel reaches on this GPU."""
+    import torch
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    best = float("inf")
+    for _ in range(reps + 1):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b) * 1e-3)
+    del src, dst
+    return 2.0 * (mib << 20) / best / 1e9
 
 
 # --------------------------------------------------------- single layers
