@@ -258,6 +258,8 @@ def bench_layer(args):
 
     wl = args.workload
     fp6 = wl == "conv3x3_4bit_fp6"   # the 4-bit layer on the FP6 MFMA (weights and activations as BF6)
+    # kernel configuration of every timed call: the FP6 path, or --tile / --xcd-groups
+    cfg = (19, 0) if fp6 else ((args.tile, args.xcd_groups) if (args.tile >= 0 or args.xcd_groups) else None)
     peak_ops = PEAK_FP6_OPS if fp6 else PEAK_INT8_OPS
     if wl in ("conv3x3_int8", "conv3x3_4bit", "conv3x3_4bit_fp6", "conv3x3_uint8w", "conv3x3_intrq", "conv3x3_2of4"):
         c = synth.conv3x3_4bit() if wl.startswith("conv3x3_4bit") else synth.conv3x3_int8()
@@ -278,9 +280,6 @@ def bench_layer(args):
             w_type = IB.INT8_2OF4
         layer = QConv(n, h, w, ci, co, 3, c.stride, c.pad, c.x_type, w_type, c.y_type, epi, c.z_in, c.z_out,
                       wq, c.bias, c.s_in, s_w, c.s_out, res_type=c.res_type, z_res=c.z_res, s_res=c.s_res, z_w=z_w)
-        if fp6:
-            from integer_quantized_nn_amd import binding as IB
-            IB.iqnn_set_conv_tile(19)
         xd = quantize(torch.from_numpy(c.x).cuda(), c.s_in, c.z_in, c.x_type)
         rd = quantize(torch.from_numpy(c.res).cuda(), c.s_res, c.z_res, c.res_type) if c.res is not None else None
         ops = c.ops(n, h, w)
@@ -291,7 +290,7 @@ def bench_layer(args):
         y_bytes = n * oh * ow * co // (2 if c.y_type in (synth.UINT4, synth.INT4) else 1)
         nbytes = xd.numel() + w_bytes + y_bytes + (rd.numel() if rd is not None else 0)
         ins = [(xd, rd)]
-        run_on = lambda i, o: layer(ins[i][0], res=ins[i][1], out=o)
+        run_on = lambda i, o: layer(ins[i][0], res=ins[i][1], out=o, cfg=cfg)
         out_shape, out_type = layer.out_shape, c.y_type
     elif wl in ("vitl_fc1", "vitl_fc1_2of4", "gemm_int8_256"):
         sparse = wl == "vitl_fc1_2of4"   # weights magnitude-pruned to 2:4 along K, on the sparse MFMA
@@ -311,7 +310,7 @@ def bench_layer(args):
         ops = 2 * m * n * k
         nbytes = m * k + (n * k // 2 + n * k // 8 if sparse else n * k) + m * n
         ins = [(a_dev, None)]
-        run_on = lambda i, o: layer(ins[i][0], out=o)
+        run_on = lambda i, o: layer(ins[i][0], out=o, cfg=cfg)
         out_shape, out_type = layer.out_shape, g.c_type
     else:
         raise SystemExit("unknown workload " + wl)
@@ -398,6 +397,10 @@ def main():
     ap.add_argument("--no-graph", action="store_true",
                     help="trunk: time eager launches instead of one captured HIP graph per step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--tile", type=int, default=-1,
+                    help="single-layer workloads: force this kernel configuration (iqnn_kernel_cfg.tile)")
+    ap.add_argument("--xcd-groups", type=int, default=0,
+                    help="single-layer workloads: force this many channel-tile groups across the XCDs")
     ap.add_argument("--traffic-db", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="print the TRAFFIC record of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) made "
                          "with --calib-copy-mib and exit (no GPU needed)")

@@ -31,11 +31,13 @@
  *              row-major (weight layout), C = A * B^T stored [M][N].  4-bit tensors
  *              pack two consecutive elements of the flattened tensor per byte:
  *              element 2j in bits 0-3, element 2j+1 in bits 4-7; INT4 is two's
- *              complement.  Weights are symmetric (Z_w = 0).
+ *              complement.  Weight codes carry a per-tensor zero point z_w / z_b
+ *              (INT8 / INT4 with zero point 0 are symmetric).
  *   Rounding   Every round is round-half-to-even ("Quantization" blog, 量化算子).
  *              Floating point is IEEE binary32, one rounding per operation, no
  *              fused multiply-add, so results are bit-exact and reproducible.
- *   Threading  The library keeps no mutable global state; calls on different
+ *   Threading  The library keeps no mutable global state: every choice a call
+ *              makes depends only on its arguments, and calls on different
  *              streams or threads are independent.
  */
 #ifndef IQNN_H
@@ -48,7 +50,7 @@
 extern "C" {
 #endif
 
-#define IQNN_ABI_VERSION 3
+#define IQNN_ABI_VERSION 4
 
 typedef enum {
     IQNN_OK = 0,
@@ -158,26 +160,35 @@ const char *iqnn_status_str(iqnn_status status);
  * stays valid until the next library call on the same thread. */
 const char *iqnn_last_error(void);
 
-/* Tuning knob: fix the block configuration of the 8-bit conv / GEMM kernels for
- * every later launch in this process.  tile = -1 restores the automatic per-layer
- * choice.  0..6 select the ring kernel with blocks of (channels x pixels) 0: 64x256,
- * 1: 128x128, 2: 128x256, 3: 256x128, 4: 256x256, 5: 128x128 (3-stage ring),
- * 6: 64x128; 7..17 the persistent streaming kernel with 7: 64x128 (12-stage ring),
- * 8: 64x128 (6), 9: 128x128 (8), 10: 128x128 (4), 11: 64x256 (3), 12: 256x128 (6),
- * 13: 128x256 (6), 14: 128x128 (3, three blocks per CU), 15: 128x256 (3),
- * 16: 256x128 (3), 17: 256x256 (4); 18 the direct 3x3 kernel (64-channel 8-bit
- * activations, 3x3 / stride 1 / pad 1 on 56-pixel rows, no residual) at any batch,
- * where the automatic choice takes it from 512 two-row tiles up; 19 the FP6 path for
- * 4-bit activations with symmetric INT4 weights and 64*K < 2^24: weights and
- * activations as BF6 (e3m2) codes on the f8f6f4 MFMA with fp32 accumulation of
- * integers, exact (the 4-bit inference article's case for 4-bit compute; CDNA4 has
- * no 4-bit integer MFMA), other layers as with -1.  Layers a
- * configuration cannot take (4-bit activations, C_in % 64 != 0, residual layouts it
- * does not stream) keep a configuration that can.  Every choice computes identical results; only speed differs.  The initial
- * value is -1, or the integer in the environment variable IQNN_FORCE_TILE.  Returns
- * IQNN_ERR_INVALID_ARG for other values.  Process-wide and unsynchronised: set it
- * while no other thread launches. */
-iqnn_status iqnn_set_conv_tile(int32_t tile);
+/* Kernel configuration of one forward call (iqnn_qconv_fwd_cfg, iqnn_qgemm_fwd_cfg):
+ * for tuning sweeps and for tests that run every block configuration.  Every choice
+ * computes identical results; only speed differs.
+ *   tile = -1: the automatic per-layer choice (what iqnn_qconv_fwd / iqnn_qgemm_fwd do).
+ *     0..6   the ring kernel with blocks of (channels x pixels) 0: 64x256, 1: 128x128,
+ *            2: 128x256, 3: 256x128, 4: 256x256, 5: 128x128 (3-stage ring), 6: 64x128;
+ *     7..17  the persistent streaming kernel, four waves per workgroup: 7: 64x128
+ *            (12-stage ring), 8: 64x128 (6), 9: 128x128 (8), 10: 128x128 (4), 11: 64x256
+ *            (3), 12: 256x128 (6), 13: 128x256 (6), 14: 128x128 (3, three blocks per
+ *            CU), 15: 128x256 (3), 16: 256x128 (3), 17: 256x256 (4);
+ *     18     the direct 3x3 kernel (64-channel 8-bit activations, 3x3 / stride 1 /
+ *            pad 1 on 56-pixel rows, no residual) at any batch, where the automatic
+ *            choice takes it from 512 two-row tiles up;
+ *     19     the FP6 path for 4-bit activations with symmetric INT4 weights and
+ *            64*K < 2^24: weights and activations as BF6 (e3m2) codes on the f8f6f4
+ *            MFMA with fp32 accumulation of integers, exact (the 4-bit inference
+ *            article's case for 4-bit compute; CDNA4 has no 4-bit integer MFMA);
+ *     20..23 the streaming kernel with eight waves per workgroup, one workgroup per
+ *            CU: 20: 256x256 (4-stage ring), 21: 128x512 (3), 22: 256x128 (4),
+ *            23: 512x128 (3).
+ *   Layers a configuration cannot take (4-bit activations, C_in % 64 != 0, residual
+ *   layouts it does not stream) keep a configuration that can.
+ *   xcd_groups = 0: the automatic split of the streaming kernel's channel tiles across
+ *     the eight XCDs; 1, 2, 4 or 8 force that many channel-tile groups.
+ * Other values are IQNN_ERR_INVALID_ARG (before any launch). */
+typedef struct {
+    int32_t tile;
+    int32_t xcd_groups;
+} iqnn_kernel_cfg;
 
 /* ------------------------------------------------------- quantize / dequantize */
 
@@ -295,6 +306,12 @@ iqnn_status iqnn_qconv_fwd(const iqnn_conv_desc *desc, const void *x_dev,
                            const void *packed_dev, const void *res_dev, void *y_dev,
                            void *stream);
 
+/* iqnn_qconv_fwd with an explicit kernel configuration (see iqnn_kernel_cfg); cfg NULL
+ * is the automatic choice.  Same results, arguments and errors. */
+iqnn_status iqnn_qconv_fwd_cfg(const iqnn_conv_desc *desc, const void *x_dev,
+                               const void *packed_dev, const void *res_dev, void *y_dev,
+                               const iqnn_kernel_cfg *cfg, void *stream);
+
 /* Quantized conv followed by max pooling of its output codes, fused: the conv's
  * output is never written, only y_dev = maxpool(conv(x)) [N][PH][PW][C_out] with
  * PH = (OH + 2*pool_pad - pool_k)/pool_stride + 1, PW likewise.  Max pooling is
@@ -304,7 +321,8 @@ iqnn_status iqnn_qconv_fwd(const iqnn_conv_desc *desc, const void *x_dev,
  * shape class -- 8-bit activations with C_in == 4 and no padding (an input from
  * iqnn_quantize_pad), stride 2, KH <= 8, KW <= 8, C_out == 64 with 8-bit codes,
  * Conv or Conv_Relu, symmetric weights (or z_w equal to the weight shift), OH even,
- * OW % 16 == 0, OW <= 128, pool 3x3 stride 2 padding 1; IQNN_ERR_UNSUPPORTED
+ * OW % 16 == 0, OW <= 128, N*H*W*4 input bytes divisible by 16 (the kernel moves whole
+ * 16-byte units), pool 3x3 stride 2 padding 1; IQNN_ERR_UNSUPPORTED
  * otherwise (validated before any launch).  Alignment: x, y 16 bytes; packed 256. */
 iqnn_status iqnn_qconv_maxpool_fwd(const iqnn_conv_desc *desc, const void *x_dev,
                                    const void *packed_dev, void *y_dev, int32_t pool_k,
@@ -333,6 +351,11 @@ iqnn_status iqnn_qgemm_prepack_host(const iqnn_gemm_desc *desc, const void *b_ho
 iqnn_status iqnn_qgemm_fwd(const iqnn_gemm_desc *desc, const void *a_dev,
                            const void *packed_dev, const void *res_dev, void *c_dev,
                            void *stream);
+
+/* iqnn_qgemm_fwd with an explicit kernel configuration (see iqnn_kernel_cfg). */
+iqnn_status iqnn_qgemm_fwd_cfg(const iqnn_gemm_desc *desc, const void *a_dev,
+                               const void *packed_dev, const void *res_dev, void *c_dev,
+                               const iqnn_kernel_cfg *cfg, void *stream);
 
 /* -------------------------------------------------------------------- pooling */
 

@@ -38,6 +38,15 @@ class ConvDesc(ctypes.Structure):
                 (self.w + 2 * self.pad_w - self.kw) // self.stride_w + 1)
 
 
+class KernelCfg(ctypes.Structure):
+    """iqnn_kernel_cfg: tile (-1 automatic) and xcd_groups (0 automatic) of one call."""
+    _fields_ = [("tile", ctypes.c_int32), ("xcd_groups", ctypes.c_int32)]
+
+
+def kernel_cfg(tile=-1, xcd_groups=0):
+    return KernelCfg(int(tile), int(xcd_groups))
+
+
 class GemmDesc(ctypes.Structure):
     _fields_ = [("m", ctypes.c_int64), ("n", ctypes.c_int64), ("k", ctypes.c_int64)] + \
                [(n, ctypes.c_int32) for n in ("a_type", "b_type", "c_type", "res_type", "epilogue",
@@ -58,12 +67,11 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     P, I, I32, I64, F, SZ = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int64,
                              ctypes.c_float, ctypes.c_size_t)
-    CD, GD = ctypes.POINTER(ConvDesc), ctypes.POINTER(GemmDesc)
+    CD, GD, KC = ctypes.POINTER(ConvDesc), ctypes.POINTER(GemmDesc), ctypes.POINTER(KernelCfg)
     sig = {
         "iqnn_abi_version": (I, []),
         "iqnn_status_str": (ctypes.c_char_p, [I]),
         "iqnn_last_error": (ctypes.c_char_p, []),
-        "iqnn_set_conv_tile": (I, [I32]),
         "iqnn_choose_qparams": (I, [F, F, I32, I, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)]),
         "iqnn_quantize": (I, [P, P, I64, I64, I64, P, P, I, I32, P]),
         "iqnn_dequantize": (I, [P, P, I64, I64, I64, P, P, I, I32, P]),
@@ -72,11 +80,13 @@ def lib():
         "iqnn_qconv_prepack": (I, [CD, P, P, F, P, I, F, F, P, SZ, P]),
         "iqnn_qconv_prepack_host": (I, [CD, P, P, F, P, I, F, F, P, SZ]),
         "iqnn_qconv_fwd": (I, [CD, P, P, P, P, P]),
+        "iqnn_qconv_fwd_cfg": (I, [CD, P, P, P, P, KC, P]),
         "iqnn_qconv_maxpool_fwd": (I, [CD, P, P, P, I32, I32, I32, P]),
         "iqnn_qgemm_packed_size": (SZ, [GD]),
         "iqnn_qgemm_prepack": (I, [GD, P, P, F, P, I, F, F, P, SZ, P]),
         "iqnn_qgemm_prepack_host": (I, [GD, P, P, F, P, I, F, F, P, SZ]),
         "iqnn_qgemm_fwd": (I, [GD, P, P, P, P, P]),
+        "iqnn_qgemm_fwd_cfg": (I, [GD, P, P, P, P, KC, P]),
         "iqnn_maxpool2d": (I, [P, P, I32, I32, I32, I32, I32, I32, I32, I32, P]),
     }
     for name, (res, args) in sig.items():
@@ -120,10 +130,6 @@ def _stream(stream, like=None):
 
 def iqnn_abi_version():
     return lib().iqnn_abi_version()
-
-
-def iqnn_set_conv_tile(tile):
-    _check(lib().iqnn_set_conv_tile(int(tile)))
 
 
 def iqnn_choose_qparams(vmin, vmax, qtype, symmetric=False):
@@ -180,6 +186,20 @@ def iqnn_qconv_fwd(desc, x, packed, res, y, stream=None):
     _check(lib().iqnn_qconv_fwd(ctypes.byref(desc), _dev(x), _dev(packed), _dev(res), _dev(y), _stream(stream, y)))
 
 
+def iqnn_qconv_fwd_cfg(desc, x, packed, res, y, cfg, stream=None):
+    """cfg: a KernelCfg, a (tile, xcd_groups) pair, or None (automatic)."""
+    _check(lib().iqnn_qconv_fwd_cfg(ctypes.byref(desc), _dev(x), _dev(packed), _dev(res), _dev(y), _cfg(cfg),
+                                    _stream(stream, y)))
+
+
+def _cfg(cfg):
+    if cfg is None:
+        return None
+    if not isinstance(cfg, KernelCfg):
+        cfg = KernelCfg(*(int(v) for v in cfg))
+    return ctypes.byref(cfg)
+
+
 def iqnn_qconv_maxpool_fwd(desc, x, packed, y, pool_k, pool_stride, pool_pad, stream=None):
     _check(lib().iqnn_qconv_maxpool_fwd(ctypes.byref(desc), _dev(x), _dev(packed), _dev(y), pool_k, pool_stride,
                                         pool_pad, _stream(stream, y)))
@@ -213,6 +233,11 @@ def iqnn_qgemm_prepack_host(desc, b_host, bias_host, s_a, s_b_host, per_channel,
 
 def iqnn_qgemm_fwd(desc, a, packed, res, c, stream=None):
     _check(lib().iqnn_qgemm_fwd(ctypes.byref(desc), _dev(a), _dev(packed), _dev(res), _dev(c), _stream(stream, c)))
+
+
+def iqnn_qgemm_fwd_cfg(desc, a, packed, res, c, cfg, stream=None):
+    _check(lib().iqnn_qgemm_fwd_cfg(ctypes.byref(desc), _dev(a), _dev(packed), _dev(res), _dev(c), _cfg(cfg),
+                                    _stream(stream, c)))
 
 
 def iqnn_maxpool2d(x, y, n, h, w, c, k, stride, pad, dtype, stream=None):

@@ -21,15 +21,6 @@
 
 namespace iqnn {
 
-int xcd_groups_override() {
-    static const int v = [] {
-        const char* e = std::getenv("IQNN_XCD_OC_GROUPS");
-        const int g = (e && *e) ? std::atoi(e) : 0;
-        return (g == 1 || g == 2 || g == 4 || g == 8) ? g : 0;
-    }();
-    return v;
-}
-
 PackGeom pack_geom(int64_t c_out, int64_t k) {
     PackGeom g;
     g.ocp = (int32_t)((c_out + kOcPad - 1) / kOcPad * kOcPad);
@@ -205,17 +196,20 @@ iqnn_status gemm_layer(const iqnn_gemm_desc* d, Layer* L) {
     return check_layer(*L);
 }
 
-// Tile override for tuning sweeps (iqnn_set_conv_tile); starts from IQNN_FORCE_TILE.
-int& tile_override() {
-    static int t = [] {
-        const char* e = std::getenv("IQNN_FORCE_TILE");
-        if (!e || !*e) return -1;
-        int v = std::atoi(e);
-        return (v >= 0 && v <= kMaxTile) ? v : -1;
-    }();
-    return t;
+// The kernel configuration of one forward call (iqnn_kernel_cfg; NULL: automatic).
+iqnn_status read_cfg(const iqnn_kernel_cfg* cfg, int* tile, int* xcd_groups) {
+    *tile = -1;
+    *xcd_groups = 0;
+    if (!cfg) return IQNN_OK;
+    if (cfg->tile < -1 || cfg->tile > kMaxTile)
+        return fail(IQNN_ERR_INVALID_ARG, "kernel configuration: tile %d outside -1..%d", cfg->tile, kMaxTile);
+    const int g = cfg->xcd_groups;
+    if (g != 0 && g != 1 && g != 2 && g != 4 && g != 8)
+        return fail(IQNN_ERR_INVALID_ARG, "kernel configuration: xcd_groups %d is not 0, 1, 2, 4 or 8", g);
+    *tile = cfg->tile;
+    *xcd_groups = g;
+    return IQNN_OK;
 }
-int forced_tile() { return tile_override(); }
 
 // The 4-channel gather of the pipelined kernel: 8-bit activations with exactly 4
 // channels and no padding (the input carries its own border, see
@@ -575,7 +569,10 @@ void conv_params(const Layer& L, const void* x, const void* packed, const void* 
     }
 }
 
-iqnn_status forward(const Layer& L, const void* x, const void* packed, const void* res, void* y, hipStream_t stream) {
+iqnn_status forward(const Layer& L, const void* x, const void* packed, const void* res, void* y,
+                    const iqnn_kernel_cfg* cfg, hipStream_t stream) {
+    int tile, xcd_groups;
+    if (iqnn_status st = read_cfg(cfg, &tile, &xcd_groups); st != IQNN_OK) return st;
     const bool add = L.epi == E_ADD || L.epi == E_ADD_RELU;
     if (!x || !packed || !y) return fail(IQNN_ERR_INVALID_ARG, "null input, packed or output pointer");
     if (add && !res) return fail(IQNN_ERR_INVALID_ARG, "ADD / ADD_RELU epilogue needs a residual");
@@ -584,12 +581,13 @@ iqnn_status forward(const Layer& L, const void* x, const void* packed, const voi
     if (!aligned(packed, 256)) return fail(IQNN_ERR_ALIGNMENT, "packed buffer must be 256-byte aligned");
     const bool c4 = c4_path(L);
     ConvParams p;
-    conv_params(L, x, packed, res, y, p, forced_tile() == kTileFp6 && b4f6(L));
+    conv_params(L, x, packed, res, y, p, tile == kTileFp6 && b4f6(L));
+    p.xcd_force = xcd_groups;
     const int gather = is_4bit(L.x_type) ? (b4_stream(L) ? GATHER_B4S : GATHER_B4)
                                           : (L.c % 16 == 0 ? GATHER_B8 : (c4 ? GATHER_C4 : GATHER_B8_ELEM));
     const bool is_1x1 = gather != GATHER_B8_ELEM && gather != GATHER_C4 && L.kh == 1 && L.kw == 1 && L.sh == 1 && L.sw == 1 &&
                         L.ph == 0 && L.pw == 0;
-    hipError_t e = launch_qconv(p, gather, is_1x1, stream, forced_tile());
+    hipError_t e = launch_qconv(p, gather, is_1x1, stream, tile);
     if (e != hipSuccess) return fail(IQNN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }
@@ -614,7 +612,7 @@ iqnn_status forward_pool(const Layer& L, const void* x, const void* packed, void
     if (!stem_pool_ok(p))
         return fail(IQNN_ERR_UNSUPPORTED,
                     "fused pooling needs a stride-2 stem with KH <= 8, 64 8-bit output channels, even OH, "
-                    "OW %% 16 == 0 and OW <= 128");
+                    "OW %% 16 == 0, OW <= 128 and an input of N*H*W*4 bytes divisible by 16");
     hipError_t e = launch_stem_pool(p, static_cast<uint8_t*>(y_pool), stream);
     if (e != hipSuccess) return fail(IQNN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -639,12 +637,6 @@ const char* iqnn_status_str(iqnn_status s) {
 }
 
 const char* iqnn_last_error(void) { return g_err.c_str(); }
-
-iqnn_status iqnn_set_conv_tile(int32_t tile) {
-    if (tile < -1 || tile > kMaxTile) return fail(IQNN_ERR_INVALID_ARG, "tile %d outside -1..%d", tile, kMaxTile);
-    tile_override() = tile;
-    return ok();
-}
 
 iqnn_status iqnn_choose_qparams(float minv, float maxv, int32_t qtype, int symmetric, float* scale,
                                 int32_t* zp) {
@@ -759,10 +751,15 @@ iqnn_status iqnn_qconv_prepack_host(const iqnn_conv_desc* desc, const void* w_ho
 
 iqnn_status iqnn_qconv_fwd(const iqnn_conv_desc* desc, const void* x_dev, const void* packed_dev,
                            const void* res_dev, void* y_dev, void* stream) {
+    return iqnn_qconv_fwd_cfg(desc, x_dev, packed_dev, res_dev, y_dev, nullptr, stream);
+}
+
+iqnn_status iqnn_qconv_fwd_cfg(const iqnn_conv_desc* desc, const void* x_dev, const void* packed_dev,
+                               const void* res_dev, void* y_dev, const iqnn_kernel_cfg* cfg, void* stream) {
     Layer L;
     iqnn_status s = conv_layer(desc, &L);
     if (s != IQNN_OK) return s;
-    return forward(L, x_dev, packed_dev, res_dev, y_dev, static_cast<hipStream_t>(stream));
+    return forward(L, x_dev, packed_dev, res_dev, y_dev, cfg, static_cast<hipStream_t>(stream));
 }
 
 iqnn_status iqnn_qconv_maxpool_fwd(const iqnn_conv_desc* desc, const void* x_dev, const void* packed_dev,
@@ -803,10 +800,15 @@ iqnn_status iqnn_qgemm_prepack_host(const iqnn_gemm_desc* desc, const void* b_ho
 
 iqnn_status iqnn_qgemm_fwd(const iqnn_gemm_desc* desc, const void* a_dev, const void* packed_dev,
                            const void* res_dev, void* c_dev, void* stream) {
+    return iqnn_qgemm_fwd_cfg(desc, a_dev, packed_dev, res_dev, c_dev, nullptr, stream);
+}
+
+iqnn_status iqnn_qgemm_fwd_cfg(const iqnn_gemm_desc* desc, const void* a_dev, const void* packed_dev,
+                               const void* res_dev, void* c_dev, const iqnn_kernel_cfg* cfg, void* stream) {
     Layer L;
     iqnn_status s = gemm_layer(desc, &L);
     if (s != IQNN_OK) return s;
-    return forward(L, a_dev, packed_dev, res_dev, c_dev, static_cast<hipStream_t>(stream));
+    return forward(L, a_dev, packed_dev, res_dev, c_dev, cfg, static_cast<hipStream_t>(stream));
 }
 
 iqnn_status iqnn_maxpool2d(const void* x_dev, void* y_dev, int32_t n, int32_t h, int32_t w, int32_t c, int32_t k,

@@ -83,6 +83,7 @@ struct ConvParams {
     int32_t gx;               // streaming kernel: workgroups per XCD (set by the launcher)
     int32_t px_chunk;         // streaming kernel: pixel tiles per XCD share (set by the launcher)
     int32_t xo_groups;        // streaming kernel: channel-tile groups across the XCDs (set by the launcher)
+    int32_t xcd_force;        // 1, 2, 4 or 8: channel-tile groups asked for by the caller; 0: automatic
     uint32_t pad_word;        // four copies of the staged padding byte
     uint32_t x_xor;           // 0x80808080 for UINT8 activations, else 0
     int32_t x_signed4;        // INT4 activations: sign-extend nibbles
@@ -115,17 +116,13 @@ struct ConvParams {
 };
 
 // tile < 0 picks the kernel and its tile configuration from the layer shape; 0..17
-// force a block configuration of the ring / streaming kernels, kTileDirect3x3 the
-// direct 3x3 kernel on the layers it takes (2:4-sparse layers always take their own
-// 128x128 configuration) (the IQNN_FORCE_TILE environment variable
-// or iqnn_set_conv_tile, for tuning sweeps and tests).
+// and 20..23 force a block configuration of the ring / streaming kernels,
+// kTileDirect3x3 the direct 3x3 kernel on the layers it takes (2:4-sparse layers always
+// take their own 128x128 configuration).  The caller's iqnn_kernel_cfg, per call.
 constexpr int kTileDirect3x3 = 18;
 constexpr int kTileFp6 = 19;   // 4-bit layers with INT4 weights: the FP6 MFMA path
-constexpr int kMaxTile = 19;
+constexpr int kMaxTile = 23;
 hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_t stream, int tile);
-// Channel-tile groups of the streaming kernel's XCD split, forced for tuning sweeps
-// (IQNN_XCD_OC_GROUPS = 1, 2, 4 or 8); 0: the automatic rule.
-int xcd_groups_override();
 
 // The image stem (4-channel padding-free input, stride 2) fused with 3x3 / stride 2 /
 // pad 1 max pooling of its codes into yp [N][OH/2][OW/2][64].

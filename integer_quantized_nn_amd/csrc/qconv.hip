@@ -1050,16 +1050,21 @@ __device__ __forceinline__ void dma4_short(uint32_t lds, const void* const* src)
 // OCC_: workgroups per CU to compile for (0: as many as the LDS allows, at most 2);
 // 3 caps the kernel at 168 VGPRs.
 // BROW_: bytes of an activation row per stage (32 for packed 4-bit activations).
-template <int BM_, int BN_, int WM_, int NST_, int OCC_ = 0, int BROW_ = kPipeBK>
+// NW_: waves per workgroup, WM_ of them along channels.  Eight waves make one block
+// per CU whose weight rows are fetched once for twice the pixels of a four-wave block,
+// with two waves per SIMD as before.
+template <int BM_, int BN_, int WM_, int NST_, int OCC_ = 0, int BROW_ = kPipeBK, int NW_ = 4>
 struct StreamCfg {
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = 4 / WM_, NST = NST_;
+    static constexpr int NW = NW_;
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = NW_ / WM_, NST = NST_;
     static constexpr int WOC = BM / WM, WPX = BN / WN;
     static constexpr int TM = WOC / 32, TN = WPX / 32;
     static constexpr int STAGE = BM * kPipeBK + BN * BROW_;
     static constexpr int LDS = NST * STAGE + 8 * BM;
     static constexpr int LDS_FIT = 160 * 1024 / LDS;   // 160 KB of LDS per CU
-    static constexpr int OCC = OCC_ > 0 ? OCC_ : (LDS_FIT >= 2 ? 2 : 1);
+    static constexpr int OCC = OCC_ > 0 ? OCC_ : (LDS_FIT >= 2 && NW_ == 4 ? 2 : 1);
     static_assert(OCC <= LDS_FIT, "LDS for the requested occupancy");
+    static_assert(WM * WN == NW && (NW == 4 || NW == 8), "four or eight waves");
 };
 
 // ZW: asymmetric weights.  The per-pixel sum of the activation operands is kept next
@@ -1080,10 +1085,12 @@ struct StreamCfg {
 // table of code pairs (UINT4 codes shifted by -8, the shift folded into the bias), and
 // one MFMA per stage accumulates in fp32, which is exact for these integers (a partial
 // sum stays below 2^24); the epilogue converts it to int32 and adds the bias.
+// OUTK: 1 = 8-bit output codes with 16-channel vector stores, fixed at compile time
+// (the requantizing epilogue without run-time type branches); 0 = decided at run time.
 template <class C, bool IS1X1, bool RES, bool C4, bool B4 = false, bool ZW = false, bool SP = false,
-          bool F6 = false>
-__global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) {
-    constexpr int BM = C::BM, BN = C::BN, WM = C::WM, NST = C::NST;
+          bool F6 = false, int OUTK = 0>
+__global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvParams p) {
+    constexpr int BM = C::BM, BN = C::BN, WM = C::WM, NST = C::NST, NW = C::NW;
     constexpr int TM = C::TM, TN = C::TN;
     constexpr int BROW = B4 ? 32 : kPipeBK;           // bytes of an activation row per stage
     constexpr int AROW = SP ? 32 : kPipeBK;           // bytes of a weight row per stage (2:4: kept codes)
@@ -1092,19 +1099,23 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
     constexpr int RROW = B4 ? BM / 2 : BM;            // bytes of a residual row
     constexpr int STAGE_K = A_BYTES + BN * BROW;
     constexpr int STAGE = (RES && BN * RROW > STAGE_K) ? BN * RROW : STAGE_K;   // bytes of one ring slot
-    constexpr int A_INST = SP ? BM / 128 : BM / 64;   // weight rows: 32 (2:4) or 16 per instruction per wave
-    constexpr int I_INST = SP ? BM / 128 : 0;         // sparse positions: 32 rows per 4-byte instruction
-    // activation rows per instruction: 16 (8-bit), 32 (4-bit), 4 (4-channel gather)
-    constexpr int B_INST = C4 ? BN / 16 : (B4 ? BN / 128 : BN / 64);
-    constexpr int K_LOADS = A_INST + I_INST + B_INST;   // DMA instructions per wave per stage
-    constexpr int R_INST = RES ? BN * RROW / 4096 : 0;   // residual: 1 KB per instruction per wave
+    // DMA instructions per wave per stage.  Weight rows: 32 (2:4) or 16 per instruction;
+    // sparse positions: 32 rows per 4-byte instruction; activation rows: 16 (8-bit),
+    // 32 (4-bit), 4 (4-channel gather) per instruction; residual: 1 KB per instruction
+    constexpr int A_INST = SP ? BM / 128 : BM / (16 * NW);
+    constexpr int I_INST = SP ? BM / 128 : 0;
+    constexpr int B_INST = C4 ? BN / (4 * NW) : (B4 ? BN / (32 * NW) : BN / (16 * NW));
+    constexpr int K_LOADS = A_INST + I_INST + B_INST;
+    constexpr int R_INST = RES ? BN * RROW / (1024 * NW) : 0;
     constexpr int D = NST - 1;                        // stages issued ahead
     static_assert(TM >= 1 && TN >= 1 && A_INST >= 1 && B_INST >= 1 && BN % 64 == 0, "tile shape");
-    static_assert(C4 || SP || K_LOADS * 4096 == STAGE, "a stage is K_LOADS KB-instructions per wave");
+    static_assert(C4 || SP || K_LOADS * 1024 * NW == STAGE, "a stage is K_LOADS KB-instructions per wave");
+    static_assert(NW == 4 || !(SP || C4 || B4 || F6), "eight-wave blocks take the dense 8-bit gather");
+    static_assert(BM <= 64 * NW, "one thread per channel loads the channel tables");
     static_assert(!SP || ((A_INST + B_INST) * 4096 + I_INST * 1024 == STAGE_K && BM % 128 == 0),
                   "a 2:4 stage: kept codes and activations in KB-instructions, positions in 256-byte ones");
     static_assert(!SP || !(B4 || C4 || ZW), "2:4 weights take the 8-bit gather with symmetric weights");
-    static_assert(!(SP && RES) || 4 * K_LOADS * 1024 <= STAGE, "the padded residual stage fits a slot");
+    static_assert(!(SP && RES) || NW * K_LOADS * 1024 <= STAGE, "the padded residual stage fits a slot");
     static_assert(!F6 || (B4 && !SP && !ZW && !C4), "the FP6 path takes packed 4-bit activations");
     static_assert(!(B4 && C4), "one gather mode");
     static_assert(NST >= 3, "ring depth");
@@ -1170,7 +1181,7 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
         if constexpr (SP) {   // the block is the stage's LDS image: straight 1 KB copies
             wsrc[j] = p.w + (int64_t)oc_t * nst * kSpBlock + (wave * A_INST + j) * 1024 + lane * 16;
         } else {   // 16 rows of the tile-order copy: one contiguous 1 KB piece of a 4 KB block
-            const int row0 = oc0 + wave * (BM / 4) + 16 * j;
+            const int row0 = oc0 + wave * (BM / NW) + 16 * j;
             wsrc[j] = p.w_tiled + ((int64_t)(row0 >> 6) * nst) * 4096 + (row0 & 63) * 64 + lane * 16;
         }
     }
@@ -1203,7 +1214,7 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
             // lane%16 = tap jj of slot s, holding K segment s ^ swz(row)
 #pragma unroll
             for (int i = 0; i < B_INST; ++i) {
-                const int row = wave * (BN / 4) + 4 * i + (lane >> 4);
+                const int row = wave * (BN / NW) + 4 * i + (lane >> 4);
                 const int slot = (lane >> 2) & 3, jj = lane & 3;
                 const int tap0 = (slot ^ swz(row)) * 4 + jj;
                 const int ky0 = tap0 / p.kw, kx0 = tap0 - ky0 * p.kw;
@@ -1222,7 +1233,7 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
             for (int i = 0; i < B_INST; ++i) {
                 // 8-bit: 16 rows of 64 bytes per instruction, lane -> row lane/4, slot lane%4;
                 // 4-bit: 32 rows of 32 bytes, lane -> row lane/2, half lane%2
-                const int row = B4 ? wave * (BN / 4) + 32 * i + (lane >> 1) : wave * (BN / 4) + 16 * i + drow;
+                const int row = B4 ? wave * (BN / NW) + 32 * i + (lane >> 1) : wave * (BN / NW) + 16 * i + drow;
                 const int64_t pix = px0 + row;
                 const int32_t seg = B4 ? ((lane & 1) ^ swz4(row)) * 16 : (dslot ^ swz(row)) * 16;
                 constexpr int SH = B4 ? 1 : 0;   // element offset -> byte offset
@@ -1287,7 +1298,7 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
                     const void* ps[NPAD];
 #pragma unroll
                     for (int i = 0; i < NPAD; ++i) ps[i] = p.res;
-                    dma16_seq<NPAD>(dst + 4 * R_INST * 1024 + wave * NPAD * 1024, ps);
+                    dma16_seq<NPAD>(dst + NW * R_INST * 1024 + wave * NPAD * 1024, ps);
                 }
             }
         } else {
@@ -1295,12 +1306,12 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
             const void* as[A_INST];
 #pragma unroll
             for (int j = 0; j < A_INST; ++j) as[j] = wsrc[j] + (int64_t)is_s * (SP ? kSpBlock : 4096);
-            dma16_seq<A_INST>(dst + wave * (BM / 4) * AROW, as);
+            dma16_seq<A_INST>(dst + wave * (BM / NW) * AROW, as);
             if constexpr (SP) {
                 const void* is[I_INST];
 #pragma unroll
                 for (int j = 0; j < I_INST; ++j) is[j] = isrc[j] + (int64_t)is_s * kSpBlock;
-                dma4_short<I_INST>(dst + BM * AROW + wave * (BM / 4) * IROW, is);
+                dma4_short<I_INST>(dst + BM * AROW + wave * (BM / NW) * IROW, is);
             }
             const void* bs[B_INST];
             if constexpr (C4) {
@@ -1311,7 +1322,7 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
                     if (coff[i] >= 0 && cky[i] + rows < p.kh) src = p.x + (int64_t)(coff[i] + rows * p.w_in) * 4;
                     bs[i] = src;
                 }
-                dma4_seq<B_INST>(dst + (BM + wave * (BN / 4)) * kPipeBK, bs);
+                dma4_seq<B_INST>(dst + (BM + wave * (BN / NW)) * kPipeBK, bs);
             } else {
                 constexpr int SH = B4 ? 1 : 0;
 #pragma unroll
@@ -1319,7 +1330,7 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
                     if constexpr (IS1X1) bs[i] = prow[i] + (k0 >> SH);
                     else bs[i] = ((tmask[i] >> tap) & 1) ? prow[i] + (tapoff >> SH) : padrow;
                 }
-                dma16_seq<B_INST>(dst + A_BYTES + wave * (BN / 4) * BROW, bs);
+                dma16_seq<B_INST>(dst + A_BYTES + wave * (BN / NW) * BROW, bs);
             }
         }
         is_off = is_off + STAGE == NST * STAGE ? 0 : is_off + STAGE;
@@ -1679,7 +1690,8 @@ __global__ __launch_bounds__(256, C::OCC) void qconv_stream(const ConvParams p) 
                     for (int q = 0; q < 16; ++q) ai[q] = (int)accf[t][u][q];
                     epi_store16<true, RES ? 3 : 2>(p, ai, &cbias[ocl], mult, rw, ocb, pix, add, m_res);
                 } else {
-                    epi_store16<false, RES ? (B4 ? 3 : 1) : 2>(p, acc[t][u], nullptr, mult, rw, ocb, pix, add, m_res);
+                    epi_store16<false, RES ? (B4 ? 3 : 1) : 2, false, OUTK>(p, acc[t][u], nullptr, mult, rw, ocb, pix,
+                                                                            add, m_res);
                 }
             }
         }
@@ -1711,7 +1723,7 @@ constexpr int64_t kXcdWeightBytes = 2 << 20;
 void stream_schedule(ConvParams& q, int occ) {
     const int n_oc_all = q.n_oc_tiles;
     int xo = 1;
-    const int forced = xcd_groups_override();
+    const int forced = q.xcd_force;
     if (forced > 0) {
         xo = forced;
     } else {
@@ -1748,9 +1760,18 @@ hipError_t launch_stream_b4(const ConvParams& p, bool is_1x1, hipStream_t stream
     return hipGetLastError();
 }
 
+// A block reads weight rows [oc0, oc0 + BM) of the packed layer, whose channels are
+// padded to a multiple of kOcPad: blocks wider than that need the padded count to be a
+// multiple of their width, or the last block would read past the packed buffer.
+bool block_fits_packed(int32_t c_out, int bm) {
+    const int64_t ocp = ((int64_t)c_out + kOcPad - 1) / kOcPad * kOcPad;
+    return bm <= kOcPad ? kOcPad % bm == 0 : ocp % bm == 0;
+}
+
 template <class C>
 hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bool c4, hipStream_t stream,
                          bool zw = false) {
+    if (!block_fits_packed(p.c_out, C::BM)) return hipErrorInvalidValue;
     ConvParams q = p;
     q.n_oc_tiles = (p.c_out + C::BM - 1) / C::BM;
     const int64_t n_px = (p.m + C::BN - 1) / C::BN;
@@ -1758,7 +1779,7 @@ hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bo
     if (p.m >= ((int64_t)1 << 31) || (!is_1x1 && !c4 && p.kh * p.kw > 64)) return hipErrorInvalidValue;
     q.n_px_tiles = (int32_t)n_px;
     stream_schedule(q, C::OCC);
-    dim3 g((unsigned)(8 * q.gx)), b(256);
+    dim3 g((unsigned)(8 * q.gx)), b(64 * C::NW);
     if (zw) {   // asymmetric weights: the 64x256 and 128x128 configurations only
         if constexpr (C::OCC < 3 && ((C::BN == 256 && C::BM == 64 && C::NST == 3) ||
                                      (C::BN == 128 && C::BM == 128 && C::NST == 4))) {
@@ -1772,7 +1793,7 @@ hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bo
         }
         return hipErrorInvalidValue;
     }
-    if constexpr ((C::NST - 1) * (C::BM / 64 + C::BN / 16) <= 60 && C::OCC < 3) {
+    if constexpr (C::NW == 4 && (C::NST - 1) * (C::BM / 64 + C::BN / 16) <= 60 && C::OCC < 3) {
         if (c4) {
             hipLaunchKernelGGL((qconv_stream<C, false, false, true>), g, b, 0, stream, q);
             return hipGetLastError();
@@ -1781,20 +1802,30 @@ hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bo
         return hipErrorInvalidValue;
     }
     // the residual rides in the stream when a tile of it fits one stage
-    constexpr bool kResStage = C::BM * C::BN / 4096 <= C::BM / 64 + C::BN / 64 && C::OCC < 3;
+    constexpr bool kResStage = C::BM * C::BN <= (C::BM + C::BN) * kPipeBK && C::OCC < 3;
     const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;
     if (add && !(kResStage && res_prefetch)) return hipErrorInvalidValue;
+    // 8-bit codes stored 16 channels at a time: the epilogue compiled for that output
+    const bool out8 = p.epi != E_RAW && (p.y_type == T_INT8 || p.y_type == T_UINT8) && p.vec_store;
     if constexpr (kResStage) {
         if (res_prefetch) {
-            if (is_1x1)
+            if (is_1x1 && out8)
+                hipLaunchKernelGGL((qconv_stream<C, true, true, false, false, false, false, false, 1>), g, b, 0, stream, q);
+            else if (is_1x1)
                 hipLaunchKernelGGL((qconv_stream<C, true, true, false>), g, b, 0, stream, q);
+            else if (out8)
+                hipLaunchKernelGGL((qconv_stream<C, false, true, false, false, false, false, false, 1>), g, b, 0, stream, q);
             else
                 hipLaunchKernelGGL((qconv_stream<C, false, true, false>), g, b, 0, stream, q);
             return hipGetLastError();
         }
     }
-    if (is_1x1)
+    if (is_1x1 && out8)
+        hipLaunchKernelGGL((qconv_stream<C, true, false, false, false, false, false, false, 1>), g, b, 0, stream, q);
+    else if (is_1x1)
         hipLaunchKernelGGL((qconv_stream<C, true, false, false>), g, b, 0, stream, q);
+    else if (out8)
+        hipLaunchKernelGGL((qconv_stream<C, false, false, false, false, false, false, false, 1>), g, b, 0, stream, q);
     else
         hipLaunchKernelGGL((qconv_stream<C, false, false, false>), g, b, 0, stream, q);
     return hipGetLastError();
@@ -1804,6 +1835,7 @@ hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bo
 // codes + positions) and 64 per pixel row.
 template <int BM_, int BN_, int WM_, int NST_>
 struct StreamCfg2of4 {
+    static constexpr int NW = 4;
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = 4 / WM_, NST = NST_;
     static constexpr int WOC = BM / WM, WPX = BN / WN;
     static constexpr int TM = WOC / 32, TN = WPX / 32;
@@ -1967,12 +1999,15 @@ __global__ __launch_bounds__(256, 3) void qconv_stem(const ConvParams p, int32_t
 // The stem kernel's conditions (see qconv_stem): 4-channel gather with 8-tap rows,
 // stride 2, at most kStemKH filter rows, C_out <= 64 in 16-channel groups, whole
 // 128-pixel tiles per image, an even input width (8-byte aligned slab reads), a
-// slab that fits one buffer, no residual.
+// slab that fits one buffer, no residual, and an input of whole 16-byte units: the
+// slab DMA moves 16 bytes per lane from a 16-byte aligned start, and a unit that ran
+// past the end of the input (N*H*W*4 = 8 mod 16) would still hold needed bytes.
 bool stem_ok(const ConvParams& p) {
     if (p.kw != 8 || p.sh != 2 || p.sw != 2 || p.kh > kStemKH || p.c_out > 64 || !p.vec_store) return false;
     if (p.epi == E_ADD || p.epi == E_ADD_RELU) return false;
     const int64_t ohw = (int64_t)p.oh * p.ow;
     if (ohw % kStemBN != 0 || p.w_in % 2 != 0 || p.m >= ((int64_t)1 << 31)) return false;
+    if ((p.m / ohw) * p.h * (int64_t)p.w_in * 4 % 16 != 0) return false;
     const int64_t out_rows = (kStemBN - 1 + p.ow - 1) / p.ow + 1;   // output rows one tile can touch
     const int64_t max_rows = 2 * (out_rows - 1) + p.kh;
     return max_rows * p.w_in * 4 + 16 <= kStemBuf;
@@ -2508,6 +2543,11 @@ using S128x128d3o3 = StreamCfg<128, 128, 2, 3, 3>;
 using S128x256d3 = StreamCfg<128, 256, 2, 3>;
 using S256x128d3 = StreamCfg<256, 128, 2, 3>;
 using S256x256d4 = StreamCfg<256, 256, 2, 4>;
+// eight waves per workgroup, one workgroup per CU (each wave 128 channels x 64 or 32 pixels)
+using W256x256d4 = StreamCfg<256, 256, 2, 4, 1, kPipeBK, 8>;
+using W128x512d3 = StreamCfg<128, 512, 1, 3, 1, kPipeBK, 8>;
+using W256x128d4 = StreamCfg<256, 128, 2, 4, 1, kPipeBK, 8>;
+using W512x128d3 = StreamCfg<512, 128, 4, 3, 1, kPipeBK, 8>;
 
 // Automatic tile, all on the streaming kernel at two blocks per CU: 256x128 blocks
 // (each wave 128 channels x 64 pixels: 0.75 KB of fragment reads per MFMA) for the
@@ -2569,6 +2609,10 @@ hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_
         const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;
         const bool res_prefetch = add && p.vec_store && (p.res_type == T_INT8 || p.res_type == T_UINT8);
         if (tile < 0) tile = pipe_tile_choice(p.m, p.c_out, p.k, res_prefetch);
+        // eight-wave blocks stream neither a residual stage nor the 4-channel gather
+        if (tile >= 20 && (add || c4)) tile = p.c_out <= 64 ? 11 : 10;
+        // 512-channel blocks need C_out padded to 256 to be a multiple of 512
+        if (tile == 23 && !block_fits_packed(p.c_out, 512)) tile = 20;
         // the streaming kernel takes a residual only as a stage of its stream, decodes
         // pixel indices in 32 bits and keeps a 64-bit mask of in-image filter taps
         const bool stream_ok = p.m < ((int64_t)1 << 31) && (is_1x1 || c4 || p.kh * p.kw <= 64);
@@ -2595,7 +2639,11 @@ hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_
         case 14: return launch_stream<S128x128d3o3>(p, is_1x1, res_prefetch, c4, stream);
         case 15: return launch_stream<S128x256d3>(p, is_1x1, res_prefetch, c4, stream);
         case 16: return launch_stream<S256x128d3>(p, is_1x1, res_prefetch, c4, stream);
-        default: return launch_stream<S256x256d4>(p, is_1x1, res_prefetch, c4, stream);
+        case 17: return launch_stream<S256x256d4>(p, is_1x1, res_prefetch, c4, stream);
+        case 20: return launch_stream<W256x256d4>(p, is_1x1, res_prefetch, c4, stream);
+        case 21: return launch_stream<W128x512d3>(p, is_1x1, res_prefetch, c4, stream);
+        case 22: return launch_stream<W256x128d4>(p, is_1x1, res_prefetch, c4, stream);
+        default: return launch_stream<W512x128d3>(p, is_1x1, res_prefetch, c4, stream);
         }
     }
     if (p.c_out <= 64) return launch_staged<64, 256, 1, 4>(p, gather, is_1x1, stream);

@@ -108,10 +108,14 @@ class QConv:
         B.iqnn_qconv_prepack(d, w_bytes, bias, s_in, s_w, s_w.size > 1, s_out, s_res, self.packed, stream)
         self.y_type = y_type
 
-    def __call__(self, x, res=None, out=None, stream=None):
+    def __call__(self, x, res=None, out=None, stream=None, cfg=None):
+        """cfg: kernel configuration (tile, xcd_groups) of this call; None: automatic."""
         if out is None:
             out = empty_codes(self.out_shape, self.y_type, x.device)
-        B.iqnn_qconv_fwd(self.desc, x, self.packed, res, out, stream)
+        if cfg is None:
+            B.iqnn_qconv_fwd(self.desc, x, self.packed, res, out, stream)
+        else:
+            B.iqnn_qconv_fwd_cfg(self.desc, x, self.packed, res, out, cfg, stream)
         return out
 
     def pool_shape(self, k=3, stride=2, pad=1):
@@ -142,8 +146,11 @@ class QGemm:
         B.iqnn_qgemm_prepack(d, b_bytes, bias, s_a, s_b, s_b.size > 1, s_out, s_res, self.packed, stream)
         self.c_type = c_type
 
-    def __call__(self, a, res=None, out=None, stream=None):
+    def __call__(self, a, res=None, out=None, stream=None, cfg=None):
         if out is None:
             out = empty_codes(self.out_shape, self.c_type, a.device)
-        B.iqnn_qgemm_fwd(self.desc, a, self.packed, res, out, stream)
+        if cfg is None:
+            B.iqnn_qgemm_fwd(self.desc, a, self.packed, res, out, stream)
+        else:
+            B.iqnn_qgemm_fwd_cfg(self.desc, a, self.packed, res, out, cfg, stream)
         return out

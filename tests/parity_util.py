@@ -84,8 +84,9 @@ def oracle_conv(case, x, w, res, images=None, z_w=0, s_w=None):
                    case.z_res, z_w=z_w)
 
 
-def gpu_conv(case, x, w, res, stream=None, w_type=None, z_w=0, s_w=None):
-    """libiqnn output bytes (numpy) for the whole batch."""
+def gpu_conv(case, x, w, res, stream=None, w_type=None, z_w=0, s_w=None, cfg=None):
+    """libiqnn output bytes (numpy) for the whole batch; cfg: (tile, xcd_groups) of the
+    call (iqnn_qconv_fwd_cfg), None for the automatic choice."""
     import torch
     from integer_quantized_nn_amd.layers import QConv
     n, h, wd, ci = x.shape
@@ -97,7 +98,7 @@ def gpu_conv(case, x, w, res, stream=None, w_type=None, z_w=0, s_w=None):
                  z_w=z_w)
     xd = torch.from_numpy(to_bytes(x, case.x_type)).cuda()
     rd = torch.from_numpy(to_bytes(res, case.res_type)).cuda() if res is not None else None
-    y = conv(xd, res=rd, stream=stream)
+    y = conv(xd, res=rd, stream=stream, cfg=cfg)
     torch.cuda.synchronize()
     return y.cpu().numpy()
 
@@ -118,7 +119,7 @@ def oracle_gemm(case, a, b, rows=None):
                    oepi(case.epi))
 
 
-def gpu_gemm(case, a, b, stream=None):
+def gpu_gemm(case, a, b, stream=None, cfg=None):
     import torch
     from integer_quantized_nn_amd.layers import QGemm
     m, k = a.shape
@@ -126,6 +127,6 @@ def gpu_gemm(case, a, b, stream=None):
     g = QGemm(m, n, k, case.a_type, case.b_type, case.c_type, case.epi, case.z_a, case.z_out,
               to_bytes(b, case.b_type), case.bias, case.s_a, case.s_b, case.s_out, stream=stream)
     ad = torch.from_numpy(to_bytes(a, case.a_type)).cuda()
-    c = g(ad, stream=stream)
+    c = g(ad, stream=stream, cfg=cfg)
     torch.cuda.synchronize()
     return c.cpu().numpy()

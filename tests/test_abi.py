@@ -33,19 +33,33 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert B.iqnn_abi_version() == 3
+    assert B.iqnn_abi_version() == 4
     assert lib.iqnn_status_str(0) == b"IQNN_OK"
     assert lib.iqnn_status_str(4) == b"IQNN_ERR_OVERFLOW"
 
 
-def test_conv_tile_override_range(lib):
-    for t in (0, 17, 18, 19, -1):
-        B.iqnn_set_conv_tile(t)
-    for bad in (-2, 20):
+def test_kernel_cfg_is_validated_before_launch(lib):
+    """iqnn_qconv_fwd_cfg / iqnn_qgemm_fwd_cfg reject a tile outside -1..23 and an XCD
+    group count other than 0, 1, 2, 4, 8 before touching any pointer (null device
+    pointers here: reaching a launch would fail differently), and the library exports
+    no process-wide tuning knob any more."""
+    d = conv_desc()
+    g = B.GemmDesc()
+    g.m, g.n, g.k = 64, 64, 64
+    g.a_type, g.b_type, g.c_type, g.res_type, g.epilogue = B.INT8, B.INT8, B.INT8, B.INT8, B.EPI_NONE
+    for bad, word in (((-2, 0), "tile"), ((24, 0), "tile"), ((-1, 3), "xcd_groups"), ((10, 16), "xcd_groups")):
         with pytest.raises(B.IqnnError) as ei:
-            B.iqnn_set_conv_tile(bad)
-        assert ei.value.status == 1 and "tile" in str(ei.value)
-    B.iqnn_set_conv_tile(-1)
+            B.iqnn_qconv_fwd_cfg(d, 0, 0, None, 0, bad, stream=0)
+        assert ei.value.status == 1 and word in str(ei.value), str(ei.value)
+        with pytest.raises(B.IqnnError) as ei:
+            B.iqnn_qgemm_fwd_cfg(g, 0, 0, None, 0, bad, stream=0)
+        assert ei.value.status == 1 and word in str(ei.value), str(ei.value)
+    # a valid configuration passes validation and fails on the null pointers instead
+    for ok in ((-1, 0), (0, 1), (23, 8), (19, 2)):
+        with pytest.raises(B.IqnnError) as ei:
+            B.iqnn_qconv_fwd_cfg(d, 0, 0, None, 0, ok, stream=0)
+        assert ei.value.status == 1 and "null" in str(ei.value), str(ei.value)
+    assert not hasattr(lib, "iqnn_set_conv_tile")
 
 
 def conv_desc(**kw):
@@ -349,3 +363,16 @@ def test_host_prepack_fp6_region(lib, x_type, c_out):
                 bits = int.from_bytes(half, "little")
                 vals = [_bf6_value((bits >> (6 * v)) & 63) for v in range(32)]
                 assert vals == list(logical[c, s * 64 + 32 * h:s * 64 + 32 * h + 32]), (c, s, h)
+
+
+def test_fused_stem_pool_rejects_inputs_of_partial_16_byte_units(lib):
+    """iqnn_qconv_maxpool_fwd moves its input in whole 16-byte units, so an input of
+    N*H*W*4 = 8 mod 16 bytes (N = 1, 37x38x4) is UNSUPPORTED, decided from the
+    descriptor before any pointer is used (the addresses here are aligned stand-ins
+    that are never dereferenced)."""
+    d = conv_desc(n=1, h=37, w=38, c_in=4, c_out=64, kh=7, kw=7, stride_h=2, stride_w=2, pad_h=0, pad_w=0,
+                  y_type=B.UINT8, epilogue=B.EPI_RELU)
+    fake = 1 << 20
+    with pytest.raises(B.IqnnError) as ei:
+        B.iqnn_qconv_maxpool_fwd(d, fake, fake, fake, 3, 2, 1, stream=0)
+    assert ei.value.status == 2 and "16" in str(ei.value), str(ei.value)

@@ -76,6 +76,38 @@ def test_conv_four_channel_padded_input(hw, k, stride, co):
     assert_bytes_equal(y.cpu().numpy(), want, "c4 %s" % ((hw, k, stride, co),))
 
 
+@pytest.mark.parametrize("n", [1, 2])
+def test_stem_input_not_whole_16_byte_units(n):
+    """A 31x32 image padded to 37x38x4: with N = 1 the input is 5624 bytes (8 mod 16),
+    which the slab kernels of the stem cannot read in whole 16-byte units, so
+    iqnn_qconv_fwd takes the 4-channel streaming gather and iqnn_qconv_maxpool_fwd
+    reports UNSUPPORTED; with N = 2 (11248 bytes) both run the stem kernels.  Every
+    computed byte against the oracle, including the last pixel of the last image."""
+    torch = require_gpu()
+    from integer_quantized_nn_amd import binding as B
+    from integer_quantized_nn_amd.layers import QConv
+    h, w = 31, 32
+    c = synth.conv_case(3700 + n, n, h, w, 3, 64, 7, 2, 3, U8, I8, U8, RELU)
+    x, wc, _ = conv_codes(c)
+    conv_ref = oracle_conv(c, x, wc, None)
+    xp = np.pad(x, ((0, 0), (3, 3), (3, 3), (0, 1)), constant_values=c.z_in)
+    wp = np.pad(wc, ((0, 0), (0, 0), (0, 0), (0, 1)))
+    conv = QConv(n, h + 6, w + 6, 4, 64, 7, 2, 0, U8, I8, U8, RELU, c.z_in, c.z_out,
+                 to_bytes(wp, I8), c.bias, c.s_in, c.s_w, c.s_out)
+    xd = torch.from_numpy(to_bytes(xp, U8)).cuda()
+    y = conv(xd)
+    torch.cuda.synchronize()
+    assert_bytes_equal(y.cpu().numpy(), to_bytes(conv_ref, U8), "stem n=%d" % n)
+    if n == 1:
+        with pytest.raises(B.IqnnError) as ei:
+            conv.conv_maxpool(xd)
+        assert ei.value.status == 2 and "16" in str(ei.value)
+    else:
+        yp = conv.conv_maxpool(xd)
+        torch.cuda.synchronize()
+        assert_bytes_equal(yp.cpu().numpy(), to_bytes(O.maxpool2d(conv_ref, 3, 2, 1), U8), "stem+pool n=%d" % n)
+
+
 @pytest.mark.parametrize("n,hw,y_type,epi", [(2, (32, 32), U8, RELU), (3, (48, 64), I8, NONE), (1, (16, 224), U8, NONE),
                                           (2, (224, 224), U8, RELU), (1, (40, 64), I8, RELU)])
 def test_stem_fused_max_pooling(n, hw, y_type, epi):
@@ -123,11 +155,7 @@ def test_conv_direct3x3_64ch(case):
     n, h, co, xt, yt, epi, images = case
     c = synth.conv_case(hash(case[:6]) % 2 ** 31, n, h, 56, 64, co, 3, 1, 1, xt, I8, yt, epi)
     x, wc, _ = conv_codes(c)
-    B.iqnn_set_conv_tile(18)
-    try:
-        got = gpu_conv(c, x, wc, None)
-    finally:
-        B.iqnn_set_conv_tile(-1)
+    got = gpu_conv(c, x, wc, None, cfg=(18, 0))
     sel = list(images) if images is not None else None
     want = to_bytes(oracle_conv(c, x, wc, None, sel), yt)
     assert_bytes_equal(got if sel is None else got[sel], want, str(case))
@@ -144,11 +172,7 @@ def test_conv_direct3x3_automatic_large_batch():
     got = gpu_conv(c, x, wc, None)
     images = [0, 1, 40, 79]
     assert_bytes_equal(got[images], to_bytes(oracle_conv(c, x, wc, None, images), U8), "direct, batch 80")
-    B.iqnn_set_conv_tile(11)
-    try:
-        other = gpu_conv(c, x, wc, None)
-    finally:
-        B.iqnn_set_conv_tile(-1)
+    other = gpu_conv(c, x, wc, None, cfg=(11, 0))
     assert_bytes_equal(got, other, "direct vs streaming kernel, batch 80")
 
 
@@ -166,35 +190,30 @@ PIPE = [
 ]
 
 
-@pytest.mark.parametrize("tile", range(18))
+@pytest.mark.parametrize("tile", list(range(18)) + [20, 21, 22, 23])
 def test_conv_every_tile(tile):
-    """Each block tile of the pipelined kernel (forced through iqnn_set_conv_tile)
-    gives the oracle's bytes on the same layers, and so does the 4-channel gather on
-    the tiles it is built for."""
+    """Each block tile of the pipelined and streaming kernels (forced per call through
+    iqnn_qconv_fwd_cfg) gives the oracle's bytes on the same layers, and so does the
+    4-channel gather on the tiles it is built for."""
     torch = require_gpu()
-    from integer_quantized_nn_amd import binding as B
     from integer_quantized_nn_amd.layers import QConv
-    B.iqnn_set_conv_tile(tile)
-    try:
-        for i, (n, h, w, ci, co, k, s, p, epi) in enumerate(PIPE):
-            c = synth.conv_case(1000 + 17 * i, n, h, w, ci, co, k, s, p, U8, I8, U8, epi, res_type=U8)
-            x, wc, res = conv_codes(c)
-            want = to_bytes(oracle_conv(c, x, wc, res), U8)
-            assert_bytes_equal(gpu_conv(c, x, wc, res), want, "tile %d %s" % (tile, PIPE[i]))
-        if tile in (0, 1, 6, 8, 10, 12):
-            h, w, k, st, co = 21, 19, 7, 2, 64 if tile != 1 else 128
-            c = synth.conv_case(77 + tile, 2, h, w, 3, co, k, st, 3, U8, I8, U8, RELU)
-            x, wc, _ = conv_codes(c)
-            want = to_bytes(oracle_conv(c, x, wc, None), U8)
-            xp = np.pad(x, ((0, 0), (3, 3), (3, 3), (0, 1)), constant_values=c.z_in)
-            wp = np.pad(wc, ((0, 0), (0, 0), (0, 0), (0, 1)))
-            conv = QConv(2, h + 6, w + 6, 4, co, k, st, 0, U8, I8, U8, RELU, c.z_in, c.z_out,
-                         to_bytes(wp, I8), c.bias, c.s_in, c.s_w, c.s_out)
-            y = conv(torch.from_numpy(to_bytes(xp, U8)).cuda())
-            torch.cuda.synchronize()
-            assert_bytes_equal(y.cpu().numpy(), want, "tile %d four-channel gather" % tile)
-    finally:
-        B.iqnn_set_conv_tile(-1)
+    for i, (n, h, w, ci, co, k, s, p, epi) in enumerate(PIPE):
+        c = synth.conv_case(1000 + 17 * i, n, h, w, ci, co, k, s, p, U8, I8, U8, epi, res_type=U8)
+        x, wc, res = conv_codes(c)
+        want = to_bytes(oracle_conv(c, x, wc, res), U8)
+        assert_bytes_equal(gpu_conv(c, x, wc, res, cfg=(tile, 0)), want, "tile %d %s" % (tile, PIPE[i]))
+    if tile in (0, 1, 6, 8, 10, 12):
+        h, w, k, st, co = 21, 19, 7, 2, 64 if tile != 1 else 128
+        c = synth.conv_case(77 + tile, 2, h, w, 3, co, k, st, 3, U8, I8, U8, RELU)
+        x, wc, _ = conv_codes(c)
+        want = to_bytes(oracle_conv(c, x, wc, None), U8)
+        xp = np.pad(x, ((0, 0), (3, 3), (3, 3), (0, 1)), constant_values=c.z_in)
+        wp = np.pad(wc, ((0, 0), (0, 0), (0, 0), (0, 1)))
+        conv = QConv(2, h + 6, w + 6, 4, co, k, st, 0, U8, I8, U8, RELU, c.z_in, c.z_out,
+                     to_bytes(wp, I8), c.bias, c.s_in, c.s_w, c.s_out)
+        y = conv(torch.from_numpy(to_bytes(xp, U8)).cuda(), cfg=(tile, 0))
+        torch.cuda.synchronize()
+        assert_bytes_equal(y.cpu().numpy(), want, "tile %d four-channel gather" % tile)
 
 
 # 4-bit activations with C_in % 64 == 0 (the streaming kernel's 4-bit path): both
@@ -232,11 +251,7 @@ def test_conv_4bit_fp6_path(case):
     c = synth.conv_case(hash(case) % 2 ** 31 + 1, n, h, w, ci, co, k, s, p, xt, I4, yt, epi, res_type=rt)
     x, wc, res = conv_codes(c)
     want = to_bytes(oracle_conv(c, x, wc, res), yt)
-    B.iqnn_set_conv_tile(19)
-    try:
-        got = gpu_conv(c, x, wc, res)
-    finally:
-        B.iqnn_set_conv_tile(-1)
+    got = gpu_conv(c, x, wc, res, cfg=(19, 0))
     assert_bytes_equal(got, want, "fp6 " + str(case))
 
 
@@ -255,11 +270,7 @@ def test_conv_4bit_fp6_adversarial_codes():
         r = rng.integers(rlo, rhi + 1, size=c.res.shape).astype(np.int32)
         c.z_in = int(xhi) if xt == U4 else 0
         want = to_bytes(oracle_conv(c, x, w, r), yt)
-        B.iqnn_set_conv_tile(19)
-        try:
-            got = gpu_conv(c, x, w, r)
-        finally:
-            B.iqnn_set_conv_tile(-1)
+        got = gpu_conv(c, x, w, r, cfg=(19, 0))
         assert_bytes_equal(got, want, "fp6 adversarial x%d" % xt)
 
 
@@ -271,11 +282,7 @@ def test_conv_4bit_fp6_workload_sampled_images():
     from integer_quantized_nn_amd import binding as B
     c = synth.conv3x3_4bit()
     x, wc, res = conv_codes(c)
-    B.iqnn_set_conv_tile(19)
-    try:
-        got = gpu_conv(c, x, wc, res)
-    finally:
-        B.iqnn_set_conv_tile(-1)
+    got = gpu_conv(c, x, wc, res, cfg=(19, 0))
     assert_bytes_equal(got, gpu_conv(c, x, wc, res), "fp6 vs int8 path")
     images = [0, 31, 63]
     assert_bytes_equal(got[images], to_bytes(oracle_conv(c, x, wc, res, images=images), c.y_type), "fp6 vs oracle")
@@ -307,12 +314,8 @@ def test_conv_4bit_fp6_path_reads_only_its_own_region():
     conv = layer()
     conv.packed[:4 * ocp].fill_(0x5A)
     conv.packed[8 * ocp + 256:std_bytes].fill_(0x5A)
-    B.iqnn_set_conv_tile(19)
-    try:
-        got = conv(xd, res=rd)
-        torch.cuda.synchronize()
-    finally:
-        B.iqnn_set_conv_tile(-1)
+    got = conv(xd, res=rd, cfg=(19, 0))
+    torch.cuda.synchronize()
     assert_bytes_equal(got.cpu().numpy(), want, "fp6 path with the int8 region overwritten")
     conv = layer()
     conv.packed[std_bytes:].fill_(0x5A)

@@ -92,12 +92,8 @@ def test_direct3x3_integer_requant(h, co, xt, yt, epi):
     want = to_bytes(oracle_int(c, x, wq), yt)
     conv = QConv(2, h, 56, 64, co, 3, 1, 1, xt, I8, yt, epi | INT_RQ, c.z_in, c.z_out, to_bytes(wq, I8), c.bias,
                  c.s_in, c.s_w, c.s_out)
-    B.iqnn_set_conv_tile(18)
-    try:
-        y = conv(torch.from_numpy(to_bytes(x, xt)).cuda())
-        torch.cuda.synchronize()
-    finally:
-        B.iqnn_set_conv_tile(-1)
+    y = conv(torch.from_numpy(to_bytes(x, xt)).cuda(), cfg=(18, 0))
+    torch.cuda.synchronize()
     assert_bytes_equal(y.cpu().numpy(), want, "direct 3x3 integer requant h=%d co=%d" % (h, co))
 
 

@@ -62,11 +62,7 @@ def test_conv_2of4_direct3x3(h, co, xt, yt, epi):
     c.w = synth.prune_2of4(c.w)
     x, wc, res = conv_codes(c)
     want = to_bytes(oracle_conv(c, x, wc, res), yt)
-    B.iqnn_set_conv_tile(18)
-    try:
-        got = gpu_conv(c, x, wc, res, w_type=SP)
-    finally:
-        B.iqnn_set_conv_tile(-1)
+    got = gpu_conv(c, x, wc, res, w_type=SP, cfg=(18, 0))
     assert_bytes_equal(got, want, "direct 2:4 h=%d co=%d" % (h, co))
 
 

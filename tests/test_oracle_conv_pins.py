@@ -235,13 +235,37 @@ def test_accumulator_overflow_is_reported():
         O.conv2d_acc(x, 0, wt)
 
 
-def test_maxpool_matches_torch():
-    rng = np.random.default_rng(20)
-    for (n, h, w, c, k, s, p) in [(2, 9, 8, 5, 3, 2, 1), (1, 7, 7, 3, 3, 1, 1), (1, 6, 5, 2, 2, 2, 0)]:
-        x = _rand_codes(rng, (n, h, w, c), 0, 255)
-        ref = F.max_pool2d(torch.from_numpy(x.astype(np.float64)).permute(0, 3, 1, 2), k, s, p)
-        ref = np.rint(ref.permute(0, 2, 3, 1).numpy()).astype(np.int32)
-        assert np.array_equal(O.maxpool2d(x, k, s, p), ref)
+def _torch_maxpool(x, k, s, p):
+    # torch pads with -inf: a tap outside the image can never be the maximum
+    ref = F.max_pool2d(torch.from_numpy(x.astype(np.float64)).permute(0, 3, 1, 2), k, s, p)
+    return np.rint(ref.permute(0, 2, 3, 1).numpy()).astype(np.int32)
+
+
+@pytest.mark.parametrize("lo,hi", [(0, 255), (-128, 127), (-8, 7), (-128, -1)],
+                         ids=["uint8", "int8", "int4", "negative_only"])
+def test_maxpool_matches_torch(lo, hi):
+    """Max pooling of codes ("Quantization" blog, 量化激活函数: passive, the max of the
+    codes) against torch max_pool2d.  Signed codes matter: with unsigned codes a tap
+    outside the image read as code 0 could never change the max, with negative codes it
+    would."""
+    rng = np.random.default_rng(20 + abs(lo) + hi)
+    for (n, h, w, c, k, s, p) in [(2, 9, 8, 5, 3, 2, 1), (1, 7, 7, 3, 3, 1, 1), (1, 6, 5, 2, 2, 2, 0),
+                                   (1, 4, 4, 3, 3, 2, 1), (2, 1, 1, 4, 3, 2, 1)]:
+        x = _rand_codes(rng, (n, h, w, c), lo, hi)
+        assert np.array_equal(O.maxpool2d(x, k, s, p), _torch_maxpool(x, k, s, p))
+
+
+def test_maxpool_border_windows_of_negative_codes():
+    """All-negative windows at the borders: every output of a 3x3 / stride 2 / pad 1
+    pooling of a constant -100 image is -100 (a border window holds only 4 or 6 image
+    taps), and a single -1 surrounded by -128 is found from every window that holds it."""
+    x = np.full((1, 5, 6, 2), -100, np.int32)
+    assert np.all(O.maxpool2d(x, 3, 2, 1) == -100)
+    x = np.full((1, 5, 5, 1), -128, np.int32)
+    x[0, 0, 0, 0] = -1
+    y = O.maxpool2d(x, 3, 2, 1)
+    assert y[0, 0, 0, 0] == -1 and np.all(y.reshape(-1)[1:] == -128)
+    assert np.array_equal(y, _torch_maxpool(x, 3, 2, 1))
 
 
 def _exact_real_output(x, z_in, s_in, wt, s_w, bias, res, z_res, s_res, stride, pad):
