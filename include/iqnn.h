@@ -368,6 +368,19 @@ iqnn_status iqnn_maxpool2d(const void *x_dev, void *y_dev, int32_t n, int32_t h,
                            int32_t c, int32_t k, int32_t stride, int32_t pad, int32_t dtype,
                            void *stream);
 
+/* ------------------------------------------------------- measurement helpers */
+
+/* Calibration launches for reporting the kernels above against what this GPU
+ * reaches, not part of the operator.  iqnn_probe_empty launches an empty kernel
+ * (launch overhead).  iqnn_probe_mfma_rate launches `blocks` workgroups of four
+ * waves, each wave running `iters` rounds of eight independent int8 32x32x32 MFMAs
+ * from registers (2 * 32 * 32 * 32 * 8 * iters * 4 * blocks operations), and writes
+ * blocks * 256 int32 sums to sink_dev (caller-owned device memory, 4-byte aligned).
+ * Both are asynchronous on `stream`.  Errors: INVALID_ARG (non-positive iters /
+ * blocks, null sink), ALIGNMENT, HIP. */
+iqnn_status iqnn_probe_empty(void *stream);
+iqnn_status iqnn_probe_mfma_rate(int32_t iters, int32_t blocks, int32_t *sink_dev, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -88,6 +88,8 @@ def lib():
         "iqnn_qgemm_fwd": (I, [GD, P, P, P, P, P]),
         "iqnn_qgemm_fwd_cfg": (I, [GD, P, P, P, P, KC, P]),
         "iqnn_maxpool2d": (I, [P, P, I32, I32, I32, I32, I32, I32, I32, I32, P]),
+        "iqnn_probe_empty": (I, [P]),
+        "iqnn_probe_mfma_rate": (I, [I32, I32, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -238,6 +240,14 @@ def iqnn_qgemm_fwd(desc, a, packed, res, c, stream=None):
 def iqnn_qgemm_fwd_cfg(desc, a, packed, res, c, cfg, stream=None):
     _check(lib().iqnn_qgemm_fwd_cfg(ctypes.byref(desc), _dev(a), _dev(packed), _dev(res), _dev(c), _cfg(cfg),
                                     _stream(stream, c)))
+
+
+def iqnn_probe_empty(stream=None):
+    _check(lib().iqnn_probe_empty(_stream(stream)))
+
+
+def iqnn_probe_mfma_rate(iters, blocks, sink, stream=None):
+    _check(lib().iqnn_probe_mfma_rate(int(iters), int(blocks), _dev(sink), _stream(stream, sink)))
 
 
 def iqnn_maxpool2d(x, y, n, h, w, c, k, stride, pad, dtype, stream=None):

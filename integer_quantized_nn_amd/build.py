@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libiqnn.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["qconv.hip", "elementwise.hip", "iqnn_api.cpp"]
+SOURCES = ["qconv.hip", "elementwise.hip", "probe.hip", "iqnn_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -811,6 +811,21 @@ iqnn_status iqnn_qgemm_fwd_cfg(const iqnn_gemm_desc* desc, const void* a_dev, co
     return forward(L, a_dev, packed_dev, res_dev, c_dev, cfg, static_cast<hipStream_t>(stream));
 }
 
+iqnn_status iqnn_probe_empty(void* stream) {
+    hipError_t e = launch_probe_empty(static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(IQNN_ERR_HIP, "probe launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+iqnn_status iqnn_probe_mfma_rate(int32_t iters, int32_t blocks, int32_t* sink_dev, void* stream) {
+    if (iters <= 0 || blocks <= 0 || !sink_dev)
+        return fail(IQNN_ERR_INVALID_ARG, "probe: iters and blocks must be positive and sink_dev non-null");
+    if (!aligned(sink_dev, 4)) return fail(IQNN_ERR_ALIGNMENT, "probe: sink_dev must be 4-byte aligned");
+    hipError_t e = launch_probe_mfma_rate(iters, blocks, sink_dev, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(IQNN_ERR_HIP, "probe launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 iqnn_status iqnn_maxpool2d(const void* x_dev, void* y_dev, int32_t n, int32_t h, int32_t w, int32_t c, int32_t k,
                            int32_t stride, int32_t pad, int32_t dtype, void* stream) {
     if (dtype != T_INT8 && dtype != T_UINT8) return fail(IQNN_ERR_UNSUPPORTED, "maxpool: 8-bit codes only");

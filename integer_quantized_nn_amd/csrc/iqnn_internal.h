@@ -163,6 +163,12 @@ struct QuantPadParams {
 };
 hipError_t launch_quantize_pad(const QuantPadParams& p, hipStream_t stream);
 
+// Calibration kernels (probe.hip): an empty launch, and `blocks` workgroups of four
+// waves running `iters` rounds of eight independent int8 MFMAs each (sink: blocks*256
+// int32 results).
+hipError_t launch_probe_empty(hipStream_t stream);
+hipError_t launch_probe_mfma_rate(int32_t iters, int32_t blocks, int32_t* sink, hipStream_t stream);
+
 struct PoolParams {
     const uint8_t* x;
     uint8_t* y;

@@ -108,14 +108,22 @@ class QuantResNet50Trunk:
                 maxpool2d(b["stem"], n, h, w, c, 3, 2, 1, self.act_type, out=b["pool"], stream=stream)
         return b[self.final]
 
-    def step(self, x_f32, stream=None, events=None):
-        """One full forward: quantize -> trunk -> dequantize.  Returns fp32 NHWC output."""
+    def quantize_input(self, x_f32, stream=None):
+        """The step's first launch: the fp32 image into the stem's padded 4-channel codes."""
         quantize_pad(x_f32, self.in_scale, self.in_zp, self.act_type, self.stem_pad, STEM_PAD_CHANNELS,
                      out=self.bufs["input"], stream=stream)
-        self.run_codes(stream, events)
+
+    def dequantize_output(self, stream=None):
+        """The step's last launch: the final codes back to fp32 (self.out_f32)."""
         dequantize(self.bufs[self.final], self.shapes[self.final], self.final_scale, self.final_zp, self.act_type,
                    out=self.out_f32, stream=stream)
         return self.out_f32
+
+    def step(self, x_f32, stream=None, events=None):
+        """One full forward: quantize -> trunk -> dequantize.  Returns fp32 NHWC output."""
+        self.quantize_input(x_f32, stream)
+        self.run_codes(stream, events)
+        return self.dequantize_output(stream)
 
     def capture(self, x_f32):
         """Record one step on x_f32 (a fixed device buffer) into a HIP graph, so a
@@ -133,6 +141,38 @@ class QuantResNet50Trunk:
         with torch.cuda.graph(g):
             self.step(x_f32)
         return g
+
+    def capture_parts(self, x_f32):
+        """The step as three HIP graphs -- quantize, the 53 convs with the pooling, and
+        dequantize -- so a caller can record events between them and time the conv
+        section of each replayed step on its own.  Replaying the three in order equals
+        one step."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):   # warm the capture stream once, eagerly
+            self.step(x_f32)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = [torch.cuda.CUDAGraph() for _ in range(3)]
+        with torch.cuda.graph(graphs[0]):
+            self.quantize_input(x_f32)
+        with torch.cuda.graph(graphs[1]):
+            self.run_codes()
+        with torch.cuda.graph(graphs[2]):
+            self.dequantize_output()
+        return graphs
+
+    def launch_layer(self, i, stream=None):
+        """Launch conv i of the step alone, on the buffers of the step (the stem with its
+        fused pooling when the trunk fuses it)."""
+        layer = self.trunk.layers[i]
+        b = self.bufs
+        conv = self.convs[layer.name]
+        if layer.name == "stem" and self.fuse_stem_pool:
+            conv.conv_maxpool(b[layer.src], 3, 2, 1, out=b["pool"], stream=stream)
+        else:
+            res = b[layer.res_src] if layer.res_src is not None else None
+            conv(b[layer.src], res=res, out=b[layer.out], stream=stream)
 
     def launches(self):
         """(kernel family, algorithmic ops, algorithmic bytes) of every launch in one step.

@@ -49,6 +49,7 @@ def _load():
     F = ctypes.c_float
     sig = {
         "iqo_num_threads": (I, []),
+        "iqo_set_num_threads": (None, [I]),
         "iqo_quantize": (I, [P, P, I64, I64, I64, P, P, I, I]),
         "iqo_dequantize": (I, [P, P, I64, I64, I64, P, P, I]),
         "iqo_pack": (I, [P, P, I64, I]),
@@ -89,6 +90,11 @@ def _c(a, dtype):
 
 def num_threads():
     return _load().iqo_num_threads()
+
+
+def set_num_threads(n):
+    """Threads of the oracle's OpenMP loops from now on (timing only; results are the same)."""
+    _load().iqo_set_num_threads(int(n))
 
 
 def qrange(qtype):

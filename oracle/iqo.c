@@ -34,6 +34,16 @@ int iqo_num_threads(void) {
 #endif
 }
 
+/* Threads of the OpenMP loops that follow (n >= 1); for timing the oracle on one core
+ * and on all of them.  Results do not depend on it (integer sums are exact). */
+void iqo_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Code ranges.
  * "Quantization" blog, section 量化模式 (quantization modes): symmetric mode clips
  * to int8, asymmetric mode to uint8; section 量化参数选择 notes that int8 really

@@ -37,6 +37,7 @@ enum { IQO_EPI_NONE = 0, IQO_EPI_RELU = 1, IQO_EPI_ADD = 2, IQO_EPI_ADD_RELU = 3
 enum { IQO_OK = 0, IQO_EINVAL = 1, IQO_EOVERFLOW = 2 };
 
 int iqo_num_threads(void);
+void iqo_set_num_threads(int n);
 
 /* [Q_MIN, Q_MAX] of a code type. */
 int iqo_qrange(int qtype, int32_t *qmin, int32_t *qmax);

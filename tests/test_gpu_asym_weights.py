@@ -54,18 +54,16 @@ def test_conv_asymmetric_weights(case):
 
 def test_conv3x3_asymmetric_weights_full_size():
     """The ResNet 3x3 workload (N=32 56x56 64->64, Conv_Relu) with UINT8 weights and a
-    per-tensor weight zero point; whole sampled images against the oracle."""
+    per-tensor weight zero point; every output byte against the oracle."""
     require_gpu()
     c = synth.conv3x3_int8(seed=0)
     x, _, _ = conv_codes(c)
     wq, s_w, z_w = asym_weights(c, U8)
     assert z_w not in (0, 128)
     got = gpu_conv(c, x, wq, None, w_type=U8, z_w=z_w, s_w=s_w)
-    images = [0, 13, 31]
-    want = to_bytes(oracle_conv(c, x, wq, None, images, z_w=z_w, s_w=s_w), c.y_type)
-    assert_bytes_equal(got[images], want, "conv3x3 uint8 weights")
-    q = got[images]
-    assert len(np.unique(q)) >= 64
+    want = to_bytes(oracle_conv(c, x, wq, None, z_w=z_w, s_w=s_w), c.y_type)
+    assert_bytes_equal(got, want, "conv3x3 uint8 weights")
+    assert len(np.unique(got)) >= 64
 
 
 def test_gemm_asymmetric_weights():

@@ -78,19 +78,17 @@ def test_gemm_epilogue_fma_canaries():
     assert np.array_equal(got, np.rint(t_unf[sel]).astype(np.int32))
 
 
-def test_vitl_fc1_full_size_sampled_rows():
+def test_vitl_fc1_full_size():
     """ViT-L fc1: 12608x1024 -> 4096, uint8 activations with outlier channels, int8
-    per-channel weights, per-channel requant to int8.  The GPU computes all rows; the
-    oracle recomputes a sample that includes the first 197 rows and the ragged tail."""
+    per-channel weights, per-channel requant to int8.  Every output byte against the
+    oracle (53 G multiply-adds on the host cores)."""
     require_gpu()
     c = synth.vitl_fc1(seed=0)
     a, b = gemm_codes(c)
     got = gpu_gemm(c, a, b)
-    rng = np.random.default_rng(1)
-    rows = np.unique(np.concatenate([np.arange(197), np.arange(12608 - 70, 12608), rng.choice(12608, 200, False)]))
-    want = to_bytes(oracle_gemm(c, a, b, rows), c.c_type)
-    assert_bytes_equal(got[rows], want, "vitl fc1")
-    q = O.unpack(got[rows], O.INT8)
+    want = to_bytes(oracle_gemm(c, a, b), c.c_type)
+    assert_bytes_equal(got, want, "vitl fc1")
+    q = O.unpack(got, O.INT8)
     assert len(np.unique(q)) >= 64 and (np.abs(q) >= 127).mean() < 0.01
 
 

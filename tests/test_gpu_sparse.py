@@ -68,8 +68,8 @@ def test_conv_2of4_direct3x3(h, co, xt, yt, epi):
 
 def test_conv_2of4_equals_dense_kernel_on_the_3x3_workload():
     """The 3x3 workload (N=32, 56x56, 64 -> 64, Conv_Relu to uint8) with 2:4-pruned
-    weights (the direct kernel's sparse variant): against the oracle on sampled whole
-    images and against the dense kernel on every byte."""
+    weights (the direct kernel's sparse variant): every output byte against the oracle
+    and against the dense kernel."""
     require_gpu()
     c = synth.conv3x3_int8()
     c.w = synth.prune_2of4(c.w)
@@ -77,9 +77,8 @@ def test_conv_2of4_equals_dense_kernel_on_the_3x3_workload():
     got = gpu_conv(c, x, wc, res, w_type=SP)
     dense = gpu_conv(c, x, wc, res, w_type=I8)
     assert_bytes_equal(got, dense, "sparse vs dense kernel")
-    images = [0, 17, 31]
-    want = to_bytes(oracle_conv(c, x, wc, res, images=images), c.y_type)
-    assert_bytes_equal(got[images], want, "sparse vs oracle")
+    want = to_bytes(oracle_conv(c, x, wc, res), c.y_type)
+    assert_bytes_equal(got, want, "sparse vs oracle")
     assert len(np.unique(got)) >= 64
 
 
@@ -116,14 +115,12 @@ def test_gemm_2of4_edges(m, k, n):
 
 
 def test_gemm_2of4_vitl_fc1_full_size():
-    """ViT-L fc1 (12608 x 1024 -> 4096) with 2:4-pruned weights, sampled rows including
-    the first 197 and the ragged tail."""
+    """ViT-L fc1 (12608 x 1024 -> 4096) with 2:4-pruned weights: every output byte
+    against the oracle's dense product of the same codes."""
     require_gpu()
     g = synth.vitl_fc1(sparse_2of4=True)
     a = O.quantize(g.a, g.s_a, g.z_a, O.UINT8)
     b = O.quantize(g.b, g.s_b, 0, O.INT8, axis=0)
     got = _gpu_gemm_2of4(g, a, b)
-    rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([np.arange(197), np.arange(12608 - 70, 12608), rng.choice(12608, 200, False)]))
-    assert_bytes_equal(got[rows], to_bytes(oracle_gemm(g, a, b, rows=rows), g.c_type), "fc1 2:4")
+    assert_bytes_equal(got, to_bytes(oracle_gemm(g, a, b), g.c_type), "fc1 2:4")
     assert len(np.unique(got)) >= 64 and (np.abs(got.view(np.int8).astype(int)) == 127).mean() < 0.01
