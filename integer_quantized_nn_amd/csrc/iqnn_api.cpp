@@ -255,6 +255,16 @@ bool b4_stream(const Layer& L) {
     return true;
 }
 
+// 4-bit streaming layers with INT4 weights and more than 64 output channels keep their
+// weights packed in the tile-order copy: per (64-row group, 64-K stage) a 2 KB block of
+// 32-byte rows, each the stage's 64 codes two per byte in K order (low nibble first, the
+// layout of a 4-bit activation row), the row's 16-byte halves swapped on rows with bit 3
+// set (the kernel's LDS swizzle).  The kernel unpacks them on chip as 16 * w, so its
+// accumulator bound is 16 times the int8 path's (checked at prepack).
+bool w4_packed(const Layer& L) {
+    return b4_stream(L) && L.w_type == T_INT4 && L.z_w == 0 && L.c_out > 64;
+}
+
 // One output channel of 2:4 weights in the sparse kernel's layout (PackGeom): the
 // weights are stored as the LDS image of every (128-row channel tile, 64-K stage)
 // block, 5120 bytes each: 128 rows of 32 bytes of kept codes, then 128 rows of 8 bytes
@@ -360,6 +370,7 @@ iqnn_status prepack_into(const Layer& L, const void* w_host, const float* bias_h
 
     std::memset(dst, 0, (size_t)packed_size(L));
     const bool f6 = b4f6(L);
+    const bool w4 = w4_packed(L);
     int32_t* bias_f6 = f6 ? reinterpret_cast<int32_t*>(dst + f6_bias_off(L)) : nullptr;
     uint8_t* blocks_f6 = f6 ? dst + f6_w_off(L) : nullptr;
     int32_t* bias = reinterpret_cast<int32_t*>(dst);
@@ -375,6 +386,7 @@ iqnn_status prepack_into(const Layer& L, const void* w_host, const float* bias_h
     const int64_t mx = L.x_type == T_UINT4 ? 15 : (L.x_type == T_INT4 ? 8 : 128);
     const uint8_t* wb = static_cast<const uint8_t*>(w_host);
     std::vector<int32_t> row((size_t)L.k);
+    std::vector<int32_t> wrows(w4 ? (size_t)(L.c_out * L.k) : 0);   // every channel's codes (packed copy)
 
     for (int64_t oc = 0; oc < L.c_out; ++oc) {
         int64_t sum = 0, abs_sum = 0;
@@ -391,6 +403,7 @@ iqnn_status prepack_into(const Layer& L, const void* w_host, const float* bias_h
                 if (L.w_type == T_INT4 && v >= 8) v -= 16;
             }
             row[(size_t)k] = v;
+            if (w4) wrows[(size_t)(oc * L.k + k)] = v;
             sum += v;
             abs_sum += v < 0 ? -v : v;
         }
@@ -412,6 +425,9 @@ iqnn_status prepack_into(const Layer& L, const void* w_host, const float* bias_h
             return fail(IQNN_ERR_OVERFLOW, "folded bias of channel %lld leaves int32", (long long)oc);
         if (mx * abs_sum + (fold < 0 ? -fold : fold) + (red < 0 ? -red : red) * mx * L.k > INT32_MAX)
             return fail(IQNN_ERR_OVERFLOW, "accumulator of channel %lld may leave int32", (long long)oc);
+        if (w4 && 16 * (mx * abs_sum + (fold < 0 ? -fold : fold)) > INT32_MAX)
+            return fail(IQNN_ERR_OVERFLOW, "accumulator of channel %lld may leave int32 on the packed INT4 path "
+                        "(16 times the bound)", (long long)oc);
         bias[oc] = (int32_t)fold;
         if (f6) {   // the FP6 path contracts (q - 8) for UINT4 activations
             const int64_t f = fold + (L.x_type == T_UINT4 ? 8 : 0) * sum;
@@ -456,7 +472,25 @@ iqnn_status prepack_into(const Layer& L, const void* w_host, const float* bias_h
             return fail(IQNN_ERR_INVALID_ARG, "residual multiplier is not a normal float in [FLT_MIN, 1e20]");
         mres[0] = m;
     }
-    if (!is_sparse(L.w_type)) {
+    if (w4) {
+        // packed INT4 tile-order copy (see w4_packed): block (row / 64, stage), 32 bytes
+        // per row, half h at slot h ^ ((row >> 3) & 1)
+        const int64_t nst = g.kp / 64;
+        uint8_t* tp = dst + g.t_off;
+        for (int64_t oc = 0; oc < L.c_out; ++oc) {
+            const int64_t r = packed_row_of_channel((int32_t)oc);
+            for (int64_t s = 0; s < nst; ++s) {
+                uint8_t* rowp = tp + ((r / 64) * nst + s) * 2048 + (r % 64) * 32;
+                for (int64_t i = 0; i < 64; ++i) {
+                    const int64_t k = s * 64 + i;
+                    const uint32_t code = k < L.k ? (uint32_t)wrows[(size_t)(oc * L.k + k)] & 0xFu : 0u;
+                    const int64_t byte = i / 2, half = byte / 16;
+                    const int64_t at = ((half ^ ((r >> 3) & 1)) * 16) + (byte % 16);
+                    rowp[at] |= (uint8_t)(code << (4 * (i & 1)));
+                }
+            }
+        }
+    } else if (!is_sparse(L.w_type)) {
         // tile-order copy for the streaming kernel: block (row / 64, stage) holds, for
         // each of its 64 rows, the stage's four 16-byte K segments at slots q ^ swz(row)
         const int64_t nst = g.kp / 64;
@@ -583,6 +617,7 @@ iqnn_status forward(const Layer& L, const void* x, const void* packed, const voi
     ConvParams p;
     conv_params(L, x, packed, res, y, p, tile == kTileFp6 && b4f6(L));
     p.xcd_force = xcd_groups;
+    p.w4 = w4_packed(L) && !p.f6;
     const int gather = is_4bit(L.x_type) ? (b4_stream(L) ? GATHER_B4S : GATHER_B4)
                                           : (L.c % 16 == 0 ? GATHER_B8 : (c4 ? GATHER_C4 : GATHER_B8_ELEM));
     const bool is_1x1 = gather != GATHER_B8_ELEM && gather != GATHER_C4 && L.kh == 1 && L.kw == 1 && L.sh == 1 && L.sw == 1 &&

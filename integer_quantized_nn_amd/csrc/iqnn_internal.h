@@ -111,6 +111,7 @@ struct ConvParams {
     float res_zf;
     uint32_t res_xor;
     int32_t vec_store;        // C_out % 16 == 0: vector stores
+    int32_t w4;               // 4-bit streaming layer whose tile-order copy holds packed INT4 weights
     int32_t f6;               // 4-bit streaming layer on the FP6 MFMA: bias and w_tiled point at the
                               // layer's BF6 region (set by the host, forced with kTileFp6)
 };

@@ -1087,13 +1087,21 @@ struct StreamCfg {
 // sum stays below 2^24); the epilogue converts it to int32 and adds the bias.
 // OUTK: 1 = 8-bit output codes with 16-channel vector stores, fixed at compile time
 // (the requantizing epilogue without run-time type branches); 0 = decided at run time.
+// S4: 4-bit activations are INT4 (sign-extended when unpacked), else UINT4.
+// W4: INT4 weights stay packed (two codes per byte, natural K order like an activation
+// row) in the tile-order copy and in LDS: 32 bytes per weight row and stage.  A lane
+// unpacks its A fragment by keeping each nibble in the high half of its byte -- the
+// byte (w << 4) is the two's-complement int8 16*w, no sign extension needed -- so the
+// contraction accumulates 16 * acc; the accumulators start from 16 * bias and are
+// shifted right by 4 before the epilogue, which is exact (every term is a multiple
+// of 16).
 template <class C, bool IS1X1, bool RES, bool C4, bool B4 = false, bool ZW = false, bool SP = false,
-          bool F6 = false, int OUTK = 0>
+          bool F6 = false, int OUTK = 0, bool S4 = false, bool W4 = false>
 __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvParams p) {
     constexpr int BM = C::BM, BN = C::BN, WM = C::WM, NST = C::NST, NW = C::NW;
     constexpr int TM = C::TM, TN = C::TN;
     constexpr int BROW = B4 ? 32 : kPipeBK;           // bytes of an activation row per stage
-    constexpr int AROW = SP ? 32 : kPipeBK;           // bytes of a weight row per stage (2:4: kept codes)
+    constexpr int AROW = (SP || W4) ? 32 : kPipeBK;   // bytes of a weight row per stage (2:4: kept codes; packed INT4)
     constexpr int IROW = SP ? 8 : 0;                  // bytes of a weight row's sparse positions per stage
     constexpr int A_BYTES = BM * (AROW + IROW);       // weight part of a ring slot
     constexpr int RROW = B4 ? BM / 2 : BM;            // bytes of a residual row
@@ -1102,7 +1110,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
     // DMA instructions per wave per stage.  Weight rows: 32 (2:4) or 16 per instruction;
     // sparse positions: 32 rows per 4-byte instruction; activation rows: 16 (8-bit),
     // 32 (4-bit), 4 (4-channel gather) per instruction; residual: 1 KB per instruction
-    constexpr int A_INST = SP ? BM / 128 : BM / (16 * NW);
+    constexpr int A_INST = SP ? BM / 128 : (W4 ? BM / (32 * NW) : BM / (16 * NW));
     constexpr int I_INST = SP ? BM / 128 : 0;
     constexpr int B_INST = C4 ? BN / (4 * NW) : (B4 ? BN / (32 * NW) : BN / (16 * NW));
     constexpr int K_LOADS = A_INST + I_INST + B_INST;
@@ -1117,6 +1125,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
     static_assert(!SP || !(B4 || C4 || ZW), "2:4 weights take the 8-bit gather with symmetric weights");
     static_assert(!(SP && RES) || NW * K_LOADS * 1024 <= STAGE, "the padded residual stage fits a slot");
     static_assert(!F6 || (B4 && !SP && !ZW && !C4), "the FP6 path takes packed 4-bit activations");
+    static_assert(!W4 || (B4 && !F6 && A_INST * 32 * NW == BM), "packed INT4 weights: 4-bit streaming, whole KB");
     static_assert(!(B4 && C4), "one gather mode");
     static_assert(NST >= 3, "ring depth");
     static_assert(D * K_LOADS <= 60, "DMA in flight must fit the 6-bit vmcnt");
@@ -1151,7 +1160,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
     auto tile_px0 = [&](int j) -> int64_t { return (int64_t)(chunk0 + member + j * members) * BN; };
 
     if (tid < BM) {
-        cbias[tid] = p.bias[oc0 + tid];
+        cbias[tid] = W4 ? p.bias[oc0 + tid] * 16 : p.bias[oc0 + tid];
         cmult[tid] = p.mult[oc0 + tid];
     }
     if constexpr (F6) {
@@ -1180,6 +1189,9 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
     for (int j = 0; j < A_INST; ++j) {
         if constexpr (SP) {   // the block is the stage's LDS image: straight 1 KB copies
             wsrc[j] = p.w + (int64_t)oc_t * nst * kSpBlock + (wave * A_INST + j) * 1024 + lane * 16;
+        } else if constexpr (W4) {   // 32 packed rows: one contiguous 1 KB piece of a 2 KB block
+            const int row0 = oc0 + wave * (BM / NW) + 32 * j;
+            wsrc[j] = p.w_tiled + ((int64_t)(row0 >> 6) * nst) * 2048 + (row0 & 63) * 32 + lane * 16;
         } else {   // 16 rows of the tile-order copy: one contiguous 1 KB piece of a 4 KB block
             const int row0 = oc0 + wave * (BM / NW) + 16 * j;
             wsrc[j] = p.w_tiled + ((int64_t)(row0 >> 6) * nst) * 4096 + (row0 & 63) * 64 + lane * 16;
@@ -1305,7 +1317,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
             const int k0 = is_s * kPipeBK;
             const void* as[A_INST];
 #pragma unroll
-            for (int j = 0; j < A_INST; ++j) as[j] = wsrc[j] + (int64_t)is_s * (SP ? kSpBlock : 4096);
+            for (int j = 0; j < A_INST; ++j) as[j] = wsrc[j] + (int64_t)is_s * (SP ? kSpBlock : (W4 ? 2048 : 4096));
             dma16_seq<A_INST>(dst + wave * (BM / NW) * AROW, as);
             if constexpr (SP) {
                 const void* is[I_INST];
@@ -1402,22 +1414,44 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
     // 4-bit: a lane's 16 bytes of a pixel row hold its half of both k-steps (8 bytes
     // each), read once per stage at k-step 0 and unpacked per k-step
     uint4 b4raw[B4 ? TN : 1];
+    // packed INT4 weights: a lane's 16 bytes of a weight row, both k-steps, likewise
+    uint4 a4raw[W4 ? TM : 1];
     const int b4off = (((lane >> 5) ^ swz4(frow)) * 16) + frow * 32;
-    const int x_signed4 = p.x_signed4;
+    constexpr int x_signed4 = S4 ? 1 : 0;
     auto read_frags = [&](const uint8_t* cur, int fo, v4i (&fa)[TM], v4i (&fb)[TN]) {
+        if constexpr (W4) {
+            if (fo == foff0) {
 #pragma unroll
-        for (int t = 0; t < TM; ++t)
-            fa[t] = *reinterpret_cast<const v4i*>(cur + (wave_oc * C::WOC + 32 * t) * kPipeBK + fo);
+                for (int t = 0; t < TM; ++t)
+                    a4raw[t] = *reinterpret_cast<const uint4*>(cur + (wave_oc * C::WOC + 32 * t) * 32 + b4off);
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+                fa[t] = *reinterpret_cast<const v4i*>(cur + (wave_oc * C::WOC + 32 * t) * kPipeBK + fo);
+        }
         if constexpr (B4) {
             if (fo == foff0) {
 #pragma unroll
                 for (int u = 0; u < TN; ++u)
-                    b4raw[u] = *reinterpret_cast<const uint4*>(cur + BM * kPipeBK + (wave_px * C::WPX + 32 * u) * 32 + b4off);
+                    b4raw[u] = *reinterpret_cast<const uint4*>(cur + A_BYTES + (wave_px * C::WPX + 32 * u) * 32 + b4off);
             }
         } else {
 #pragma unroll
             for (int u = 0; u < TN; ++u)
                 fb[u] = *reinterpret_cast<const v4i*>(cur + (BM + wave_px * C::WPX + 32 * u) * kPipeBK + fo);
+        }
+    };
+    // the A fragments of k-step kk from packed INT4 weights: nibble j of each byte in
+    // its high half, the int8 16*w (the same element order as the activation unpack)
+    auto unpack_a = [&](v4i (&fa)[TM], int kk) {
+        if constexpr (W4) {
+#pragma unroll
+            for (int t = 0; t < TM; ++t) {
+                const uint32_t w0 = kk == 0 ? a4raw[t].x : a4raw[t].z, w1 = kk == 0 ? a4raw[t].y : a4raw[t].w;
+                fa[t][0] = (int)((w0 << 4) & 0xF0F0F0F0u); fa[t][1] = (int)(w0 & 0xF0F0F0F0u);
+                fa[t][2] = (int)((w1 << 4) & 0xF0F0F0F0u); fa[t][3] = (int)(w1 & 0xF0F0F0F0u);
+            }
         }
     };
     // make the B fragments of k-step kk MFMA-ready: the uint8 shift (XOR 0x80), or the
@@ -1512,7 +1546,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
             }
 #pragma unroll
             for (int u = 0; u < TN; ++u)
-                f.b[u] = *reinterpret_cast<const uint4*>(cur + BM * kPipeBK + (wave_px * C::WPX + 32 * u) * 32 + b4off);
+                f.b[u] = *reinterpret_cast<const uint4*>(cur + A_BYTES + (wave_px * C::WPX + 32 * u) * 32 + b4off);
         }
     };
     // 32 packed 4-bit codes (16 bytes) -> 32 BF6 codes, code v at bits 6v..6v+5
@@ -1625,6 +1659,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
         for (int s = 0; s < nst; ++s) {
             const uint8_t* cur = ring + cur_off;
             shift_b(fb0, 0);
+            unpack_a(fa0, 0);
             __builtin_amdgcn_sched_barrier(0);
             mfmas(fa0, fb0, 0, NMF);
             read_frags(cur, foff1, fa1, fb1);
@@ -1637,6 +1672,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
             if (NRD > NMF) __builtin_amdgcn_sched_group_barrier(0x100, NRD - NMF, 0);
             __builtin_amdgcn_sched_barrier(0);
             shift_b(fb1, 1);
+            unpack_a(fa1, 1);
             mfmas(fa1, fb1, 0, HALF);
             __builtin_amdgcn_sched_barrier(0);
             advance();
@@ -1689,6 +1725,9 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
 #pragma unroll
                     for (int q = 0; q < 16; ++q) ai[q] = (int)accf[t][u][q];
                     epi_store16<true, RES ? 3 : 2>(p, ai, &cbias[ocl], mult, rw, ocb, pix, add, m_res);
+                } else if constexpr (W4) {   // 16 * acc: back to acc, exactly
+                    const v16i a = acc[t][u] >> 4;
+                    epi_store16<false, RES ? 3 : 2, false, OUTK>(p, a, nullptr, mult, rw, ocb, pix, add, m_res);
                 } else {
                     epi_store16<false, RES ? (B4 ? 3 : 1) : 2, false, OUTK>(p, acc[t][u], nullptr, mult, rw, ocb, pix,
                                                                             add, m_res);
@@ -1742,6 +1781,18 @@ void stream_schedule(ConvParams& q, int occ) {
 
 // 4-bit activations (packed rows streamed to LDS): the 64x128 and 128x128 blocks; F6:
 // INT4 weights as BF6 on the FP6 MFMA (ConvParams::f6 set by the host).
+template <class C, bool F6, bool S4 = false, bool W4 = false>
+hipError_t launch_stream_b4_k(const ConvParams& q, dim3 g, dim3 b, bool is_1x1, hipStream_t stream) {
+    const bool add = q.epi == E_ADD || q.epi == E_ADD_RELU;
+    if (is_1x1 && add) hipLaunchKernelGGL((qconv_stream<C, true, true, false, true, false, false, F6, 0, S4, W4>), g, b, 0, stream, q);
+    else if (is_1x1) hipLaunchKernelGGL((qconv_stream<C, true, false, false, true, false, false, F6, 0, S4, W4>), g, b, 0, stream, q);
+    else if (add) hipLaunchKernelGGL((qconv_stream<C, false, true, false, true, false, false, F6, 0, S4, W4>), g, b, 0, stream, q);
+    else hipLaunchKernelGGL((qconv_stream<C, false, false, false, true, false, false, F6, 0, S4, W4>), g, b, 0, stream, q);
+    return hipGetLastError();
+}
+
+// F6: the FP6 path; otherwise the activations' signedness and the packed INT4 weights
+// (ConvParams::w4, set by the host) select the compiled variant.
 template <class C, bool F6>
 hipError_t launch_stream_b4(const ConvParams& p, bool is_1x1, hipStream_t stream) {
     ConvParams q = p;
@@ -1752,12 +1803,19 @@ hipError_t launch_stream_b4(const ConvParams& p, bool is_1x1, hipStream_t stream
     q.n_px_tiles = (int32_t)n_px;
     stream_schedule(q, C::OCC);
     dim3 g((unsigned)(8 * q.gx)), b(256);
-    const bool add = p.epi == E_ADD || p.epi == E_ADD_RELU;
-    if (is_1x1 && add) hipLaunchKernelGGL((qconv_stream<C, true, true, false, true, false, false, F6>), g, b, 0, stream, q);
-    else if (is_1x1) hipLaunchKernelGGL((qconv_stream<C, true, false, false, true, false, false, F6>), g, b, 0, stream, q);
-    else if (add) hipLaunchKernelGGL((qconv_stream<C, false, true, false, true, false, false, F6>), g, b, 0, stream, q);
-    else hipLaunchKernelGGL((qconv_stream<C, false, false, false, true, false, false, F6>), g, b, 0, stream, q);
-    return hipGetLastError();
+    if constexpr (F6) {
+        return launch_stream_b4_k<C, true>(q, g, b, is_1x1, stream);
+    } else {
+        if (p.w4) {
+            if constexpr (C::BM % 128 == 0) {
+                return p.x_signed4 ? launch_stream_b4_k<C, false, true, true>(q, g, b, is_1x1, stream)
+                                   : launch_stream_b4_k<C, false, false, true>(q, g, b, is_1x1, stream);
+            }
+            return hipErrorInvalidValue;
+        }
+        return p.x_signed4 ? launch_stream_b4_k<C, false, true>(q, g, b, is_1x1, stream)
+                           : launch_stream_b4_k<C, false, false>(q, g, b, is_1x1, stream);
+    }
 }
 
 // A block reads weight rows [oc0, oc0 + BM) of the packed layer, whose channels are
@@ -2549,7 +2607,8 @@ using W128x512d3 = StreamCfg<128, 512, 1, 3, 1, kPipeBK, 8>;
 using W256x128d4 = StreamCfg<256, 128, 2, 4, 1, kPipeBK, 8>;
 using W512x128d3 = StreamCfg<512, 128, 4, 3, 1, kPipeBK, 8>;
 
-// Automatic tile, all on the streaming kernel at two blocks per CU: 256x128 blocks
+// Automatic tile (per-layer sweeps over the trunk's shapes at batch 256 chose these),
+// mostly on the streaming kernel at two blocks per CU: 256x128 blocks
 // (each wave 128 channels x 64 pixels: 0.75 KB of fragment reads per MFMA) for the
 // wide, deep contractions (C_out >= 256, K >= 1024, no residual); 128x128 blocks
 // for the rest.  C_out <= 64: 64x256 blocks (each wave 64 x 64: 1 KB of fragment
@@ -2559,7 +2618,11 @@ using W512x128d3 = StreamCfg<512, 128, 4, 3, 1, kPipeBK, 8>;
 // run 128x128 blocks three to a CU, and C_out >= 512 takes the 256x128 blocks at any K.
 int pipe_tile_choice(int64_t m, int32_t c_out, int64_t k, bool res) {
     (void)m;
+    // very deep contractions of 512+ channels: one 8-wave 256x128 block per CU
+    if (!res && c_out >= 512 && k >= 4096) return 22;
     if (!res && c_out >= 128 && (k >= 4096 || k == kPipeBK)) return 14;
+    // 128-channel contractions of at least 1024: 128x128 blocks three to a CU
+    if (!res && c_out == 128 && k >= 1024) return 14;
     if (!res && c_out >= 256 && (k >= 1024 || c_out >= 512)) return 16;
     if (c_out <= 64) return (k == kPipeBK || k >= 576) ? 11 : 8;
     return 10;

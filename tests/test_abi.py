@@ -376,3 +376,39 @@ def test_fused_stem_pool_rejects_inputs_of_partial_16_byte_units(lib):
     with pytest.raises(B.IqnnError) as ei:
         B.iqnn_qconv_maxpool_fwd(d, fake, fake, fake, 3, 2, 1, stream=0)
     assert ei.value.status == 2 and "16" in str(ei.value), str(ei.value)
+
+
+@pytest.mark.parametrize("x_type,c_out,epi", [(B.UINT4, 96, B.EPI_RELU), (B.INT4, 128, B.EPI_ADD_RELU)])
+def test_host_prepack_packed_int4_weights(lib, x_type, c_out, epi):
+    """4-bit streaming layers with INT4 weights and more than 64 output channels keep the
+    weights packed (two codes per byte) in the tile-order copy the kernel reads: 2 KB per
+    (64-row group, 64-K stage), 32 bytes per row in K order with the low nibble first,
+    the row's 16-byte halves swapped on rows with bit 3 set.  Decoding the blocks gives
+    back every weight code (in the documented row permutation)."""
+    rng = np.random.default_rng(c_out + 7)
+    c_in, k = 64, 9 * 64
+    w = rng.integers(-8, 8, size=(c_out, 3, 3, c_in)).astype(np.int32)
+    d = conv_desc(x_type=x_type, w_type=B.INT4, y_type=B.UINT4, c_in=c_in, c_out=c_out, epilogue=epi,
+                  z_in=3 if x_type == B.UINT4 else 0, z_out=1, res_type=B.UINT4, z_res=2)
+    buf = _host_pack(d, w, B.INT4, None, np.float32(0.05), np.full(c_out, 0.02, np.float32), np.float32(0.07),
+                     np.float32(0.03))
+    ocp, kp = 256, k
+    t_off = 8 * ocp + 256 + ocp * kp
+    nst = kp // 64
+    blocks = buf[t_off:t_off + ocp * kp // 2].reshape(ocp // 64, nst, 64, 32)
+    logical = w.reshape(c_out, -1)
+    for c in range(c_out):
+        b, r32 = divmod(c, 32)
+        h, j, r = r32 // 16, (r32 // 4) % 4, r32 % 4
+        R = 32 * b + 8 * j + 4 * h + r
+        for s in range(nst):
+            row = blocks[R // 64, s, R % 64]
+            sw = (R >> 3) & 1
+            nat = np.concatenate([row[16 * (0 ^ sw):16 * (0 ^ sw) + 16], row[16 * (1 ^ sw):16 * (1 ^ sw) + 16]])
+            codes = np.empty(64, np.int32)
+            codes[0::2] = nat & 0xF
+            codes[1::2] = nat >> 4
+            codes[codes >= 8] -= 16
+            assert np.array_equal(codes, logical[c, 64 * s:64 * s + 64]), (c, s)
+    # the rest of the tile-order region and the padding rows stay zero
+    assert not buf[t_off + ocp * kp // 2:t_off + ocp * kp].any()
