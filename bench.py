@@ -262,6 +262,23 @@ def make_layer(torch, wl, cfg=None):
                             c.stride, c.pad, ro, c.s_res, c.z_res)
                 return O.pack(y, OT[c.y_type]), time.perf_counter() - t0
             rec["oracle"] = oracle_out
+    elif wl == "resnet50_stem_pool":
+        # the trunk's stem with its max pooling fused: 256 x 224x224x3 -> 7x7/2 conv, 64
+        # channels, ReLU -> 3x3/2 pad 1 pooling; the input as the trunk feeds it (padded
+        # 4-channel offset codes q - 128 from iqnn_quantize_pad)
+        from integer_quantized_nn_amd.layers import quantize_pad
+        c = synth.conv_case(41, 256, 224, 224, 3, 64, 7, 2, 3, synth.UINT8, synth.INT8, synth.UINT8,
+                            synth.EPI_RELU, name="stem")
+        n, h, w, ci = c.x.shape
+        wq = quantize(torch.from_numpy(c.w).cuda(), c.s_w, 0, c.w_type, axis=0).cpu().numpy()
+        wq = np.pad(wq.reshape(64, 7, 7, ci), ((0, 0), (0, 0), (0, 0), (0, 1)))
+        layer = QConv(n, h + 6, w + 6, 4, 64, 7, 2, 0, IB.INT8, IB.INT8, IB.INT8, c.epi, c.z_in - 128,
+                      c.z_out - 128, wq, c.bias, c.s_in, c.s_w, c.s_out)
+        xd = quantize_pad(torch.from_numpy(c.x).cuda(), c.s_in, c.z_in - 128, IB.INT8, 3, 4)
+        pshape = layer.pool_shape(3, 2, 1)
+        rec.update(ops=c.ops(n, h, w), nbytes=xd.numel() + 64 * 7 * 7 * 4 + int(np.prod(pshape)),
+                   ins=[(xd, None)], out_shape=pshape, out_type=synth.INT8,
+                   run=lambda i, o: layer.conv_maxpool(rec["ins"][i][0], out=o))
     elif wl in ("vitl_fc1", "vitl_fc1_2of4", "gemm_int8_256"):
         sparse = wl == "vitl_fc1_2of4"   # weights magnitude-pruned to 2:4 along K, on the sparse MFMA
         g = synth.vitl_fc1(sparse_2of4=sparse) if wl.startswith("vitl") else synth.gemm_int8_256()
@@ -555,6 +572,7 @@ def main():
     ap.add_argument("--workload", default="resnet50_trunk",
                     choices=["resnet50_trunk", "resnet50_trunk_2of4", "conv3x3_int8", "conv3x3_2of4", "conv3x3_4bit",
                              "conv3x3_4bit_fp6", "conv3x3_uint8w", "conv3x3_intrq", "resnet50_l3_conv3x3",
+                             "resnet50_stem_pool",
                              "vitl_fc1", "vitl_fc1_2of4", "gemm_int8_256"])
     ap.add_argument("--cold", action="store_true",
                     help="single-layer workloads: rotate input/output sets (> 256 MB) so every launch misses the caches")

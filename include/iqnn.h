@@ -320,9 +320,10 @@ iqnn_status iqnn_qconv_fwd_cfg(const iqnn_conv_desc *desc, const void *x_dev,
  * bytes equal iqnn_qconv_fwd followed by iqnn_maxpool2d.  Supported: the image stem
  * shape class -- 8-bit activations with C_in == 4 and no padding (an input from
  * iqnn_quantize_pad), stride 2, KH <= 8, KW <= 8, C_out == 64 with 8-bit codes,
- * Conv or Conv_Relu, symmetric weights (or z_w equal to the weight shift), OH even,
- * OW % 16 == 0, OW <= 128, N*H*W*4 input bytes divisible by 16 (the kernel moves whole
- * 16-byte units), pool 3x3 stride 2 padding 1; IQNN_ERR_UNSUPPORTED
+ * Conv or Conv_Relu, symmetric weights (or z_w equal to the weight shift), an even
+ * input width W, OH and OW even, OW <= 248, (KH+2)*W*4 <= 9200 (two output rows' input
+ * rows fit one 9 KB LDS buffer), N*H*W*4 input bytes divisible by 16 (the kernel moves
+ * whole 16-byte units), pool 3x3 stride 2 padding 1; IQNN_ERR_UNSUPPORTED
  * otherwise (validated before any launch).  Alignment: x, y 16 bytes; packed 256. */
 iqnn_status iqnn_qconv_maxpool_fwd(const iqnn_conv_desc *desc, const void *x_dev,
                                    const void *packed_dev, void *y_dev, int32_t pool_k,

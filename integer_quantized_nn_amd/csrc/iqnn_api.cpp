@@ -646,8 +646,9 @@ iqnn_status forward_pool(const Layer& L, const void* x, const void* packed, void
     conv_params(L, x, packed, nullptr, nullptr, p);
     if (!stem_pool_ok(p))
         return fail(IQNN_ERR_UNSUPPORTED,
-                    "fused pooling needs a stride-2 stem with KH <= 8, 64 8-bit output channels, even OH, "
-                    "OW %% 16 == 0, OW <= 128 and an input of N*H*W*4 bytes divisible by 16");
+                    "fused pooling needs a stride-2 stem with KH <= 8, 64 8-bit output channels, an even "
+                    "input width, even OH and OW, OW <= 248, (KH+2)*W*4 <= 9200 and an input of N*H*W*4 "
+                    "bytes divisible by 16");
     hipError_t e = launch_stem_pool(p, static_cast<uint8_t*>(y_pool), stream);
     if (e != hipSuccess) return fail(IQNN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();

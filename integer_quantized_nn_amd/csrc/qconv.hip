@@ -975,6 +975,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // loads sit in one asm statement so nothing can use m0 in between; m0 takes one wait
 // state before the first load reads it.  The LDS address is wave-uniform;
 // readfirstlane pins it to an SGPR even when the compiler has parked it in a VGPR.
+// One 16-byte-per-lane LDS DMA from a wave-uniform base address (SGPR pair) plus a
+// per-lane unsigned 32-bit byte offset; the same m0 rules as dma16_run.
+__device__ __forceinline__ void dma16_sbase(uint32_t lds, const void* sbase, uint32_t voff) {
+    const uint32_t m = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void dma16_run(uint32_t lds, const void* const* src) {
     static_assert(N >= 1 && N <= 4, "16-byte runs of 1..4 KB");
@@ -2083,47 +2091,58 @@ hipError_t launch_stem(const ConvParams& p, hipStream_t stream) {
 // ============================================================ stem + max pooling
 //
 // qconv_stem_pool: the stem convolution of qconv_stem followed by max pooling 3x3,
-// stride 2, padding 1 over its output codes, without writing the convolution's output
-// to memory.  Max pooling is passive on codes ("Quantization" blog, 量化激活函数), so
-// pooling the codes computed here -- the same contraction and the same epilogue
-// arithmetic as qconv_stem -- gives the bytes of pooling the stored stem output.
-// A workgroup owns pooled rows [r0, r1) of one image and NW = 2*OW/32 waves.  For
-// pooled row r it computes stem rows 2r and 2r+1 (wave w: pixels 32w..32w+31 of the
-// row pair, one MFMA block) into a ring of three LDS row slots (row sr in slot
-// sr % 3), where row 2r-1 is still held from row r-1 (at the start of a band it is
-// computed first), then pools row r out of LDS: thread t takes pooled pixel t/8,
-// channels 8(t%8)..8(t%8)+7.  The input rows of a row pair (one contiguous byte range)
-// are copied into LDS with 16-byte DMA kSpAhead pairs ahead, through a ring of
-// kSpAhead+1 slab buffers; every wave issues exactly kSpCpw(NW) DMA instructions per
-// slab (chunks past the end repeat the last chunk: the same bytes to the same place),
-// so "slab r landed" is vmcnt <= (kSpAhead-1)*kSpCpw while later slabs are in flight.
+// stride 2, padding 1, without writing the convolution's output.  The requantizing
+// epilogue y(a) = clip(rne(float(a) * M[c]) + Z_out) is a non-decreasing function of
+// the int32 accumulator a of channel c (M[c] > 0, and the conversion, the product, the
+// rounding and the clip each preserve order), so the max of y over a pooling window is
+// y of the max of a over it: the kernel pools the accumulators and requantizes only
+// the pooled values -- a quarter of the stem's outputs -- and the bytes equal those of
+// pooling the stored stem codes (max pooling is passive on codes, "Quantization" blog,
+// 量化激活函数).
+// Wave g of a workgroup owns pooled columns 31g .. 31g+30 of one image; the workgroup
+// owns a band of pooled rows.  For every stem row, lane l (j = l % 32, pooled column
+// c = 31g + j) computes two MFMA blocks: stem column 2c-1 (block 0) and 2c (block 1),
+// each for all 64 channels.  The window of pooled column c is stem columns 2c-1, 2c,
+// 2c+1, and 2c+1 is block 0 of lane l+1, shuffled over; lanes 31 and 63 only feed
+// their left neighbour.  Out-of-image window columns are replaced by an in-image
+// column of the same window (column -1 by column 0), which leaves the max unchanged.
+// The window's stem rows are 2r-1, 2r, 2r+1; row 2r+1 stays in registers as the next
+// pooled row's first row.  The input rows of a stem row pair are one contiguous byte
+// range, copied into LDS with 16-byte DMA kSpAhead pairs ahead through kSpSlabs slab
+// buffers; every wave issues exactly kSpCpw(NW) DMA instructions per slab (chunks past
+// the end repeat the last chunk: the same bytes to the same place), so "slab r landed"
+// is vmcnt <= (kSpAhead-1)*kSpCpw while the later slabs are in flight.
 constexpr int kSpBuf = 9216;       // LDS bytes per slab buffer
 constexpr int kSpAhead = 3;        // row pairs in flight
 constexpr int kSpSlabs = kSpAhead + 1;
-constexpr int kSpMaxOW = 128;      // stem output width limit (8 waves)
+constexpr int kSpColsPerWave = 31; // pooled columns per wave
+constexpr int kSpMaxWaves = 4;     // pooled width limit 124
 constexpr int kSpCpw(int nw) { return (kSpBuf / 1024 + nw - 1) / nw; }
-
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 struct StemPoolArgs {
     uint8_t* yp;                   // pooled output [N][PH][PW][64]
     int32_t ph, pw;                // pooled height, width
     int32_t band, n_bands;         // pooled rows per workgroup, workgroups per image
-    uint32_t bias;                 // 0x80808080 for signed codes (unsigned order == signed order)
-    int64_t in_bytes;              // size of the input tensor
+    int64_t in_bytes;              // size of the input tensor (whole 16-byte units)
 };
 
-template <int NW>
-__global__ __launch_bounds__(64 * NW, 2) void qconv_stem_pool(const ConvParams p, const StemPoolArgs a) {
+// KH: filter rows (0: p.kh at run time); XX: the input bytes take the XOR with p.x_xor
+// (unsigned codes), without it they are used as they are; FIX: the odd part of Z_out
+// added to each rounded code (0 or 1 = p.out_fix, -1: p.out_fix read at run time), so
+// that no branch splits the loop body.
+template <int NW, int KH, bool XX, int FIX>
+__global__ __launch_bounds__(64 * NW, NW == 1 ? 1 : 2) void qconv_stem_pool(const ConvParams p, const StemPoolArgs a) {
     constexpr int CPW = kSpCpw(NW);
+    constexpr int KR = KH > 0 ? KH : kStemKH;   // filter rows held in registers
     static_assert((kSpAhead - 1) * CPW <= 60, "DMA in flight must fit the 6-bit vmcnt");
+    static_assert(KR <= kStemKH, "filter rows");
     __shared__ __attribute__((aligned(1024))) uint8_t slab[kSpSlabs][kSpBuf];
-    __shared__ __attribute__((aligned(16))) uint8_t rows[3][kSpMaxOW * 64];
     __shared__ __attribute__((aligned(16))) int32_t cbias[64];
     __shared__ __attribute__((aligned(16))) float cmult[64];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kh = KH > 0 ? KH : p.kh;
     const int n = (int)blockIdx.x / a.n_bands;
     const int r0 = ((int)blockIdx.x - n * a.n_bands) * a.band;
     const int r1 = min(a.ph, r0 + a.band);
@@ -2132,96 +2151,124 @@ __global__ __launch_bounds__(64 * NW, 2) void qconv_stem_pool(const ConvParams p
         cbias[tid] = p.bias[tid];
         cmult[tid] = p.mult[tid];
     }
-    v4i wa[2][kStemKH];
+    v4i wa[2][KR];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int ky = 0; ky < kStemKH; ++ky)
-            wa[t][ky] = ky < p.kh ? *reinterpret_cast<const v4i*>(p.w + (int64_t)(32 * t + (lane & 31)) * p.kp +
-                                                                  32 * ky + 16 * (lane >> 5))
-                                  : v4i{0, 0, 0, 0};
+        for (int ky = 0; ky < KR; ++ky)
+            wa[t][ky] = ky < kh ? *reinterpret_cast<const v4i*>(p.w + (int64_t)(32 * t + (lane & 31)) * p.kp +
+                                                               32 * ky + 16 * (lane >> 5))
+                                : v4i{0, 0, 0, 0};
     __syncthreads();
 
-    const int ow = p.ow, oh = p.oh;
+    const int ow = p.ow;
     const int64_t row_bytes = (int64_t)p.w_in * 4;
-    // copy input rows [2*sr0, 2*sr0 + nrows) of image n into slab buffer `buf`
+    // copy input rows [2*sr0, 2*sr0 + nrows) of image n into slab buffer `buf`: chunk j
+    // is 1 KB from the wave-uniform address p.x + base + 1024 j, each lane 16 bytes at
+    // its own offset (the input is below 2 GB, so 32-bit offsets reach all of it)
+    const uint32_t in_bytes = (uint32_t)a.in_bytes;
     auto issue = [&](int sr0, int nrows, int buf) {
-        const int64_t start = ((int64_t)n * p.h + 2 * (int64_t)sr0) * row_bytes;
-        const int64_t base = start & ~(int64_t)15;
-        const int chunks = (int)((start - base + nrows * row_bytes + 1023) >> 10);   // <= kSpBuf / 1024
+        const uint32_t start = (uint32_t)(((int64_t)n * p.h + 2 * (int64_t)sr0) * row_bytes);
+        const uint32_t base = start & ~15u;
+        const int chunks = (int)((start - base + (uint32_t)(nrows * row_bytes) + 1023) >> 10);   // <= kSpBuf / 1024
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
             const int j = min(wave + i * NW, chunks - 1);
-            const int64_t off = base + j * 1024 + lane * 16;
-            const void* src = off + 16 <= a.in_bytes ? (const void*)(p.x + off) : (const void*)p.x;
-            dma16_run<1>(lds_addr(&slab[buf][0]) + j * 1024, &src);
+            const uint32_t c0 = base + (uint32_t)j * 1024;
+            uint32_t voff = c0 + (uint32_t)lane * 16;
+            // a unit past the end of the input holds no needed byte (the input is whole
+            // 16-byte units): it reads the first unit instead
+            if (c0 + 1024 > in_bytes) voff = voff + 16 <= in_bytes ? voff : 0u;
+            dma16_sbase(lds_addr(&slab[buf][0]) + j * 1024, p.x, voff);
         }
     };
-    // stem pixels (this lane's column of the wave's block) of the rows starting at sr0,
-    // from slab buffer `buf`, into the row slots; pixel indices >= limit are not stored
-    const int frow = lane & 31;
-    const uint32_t bxor = p.x_xor;
-    auto compute = [&](int sr0, int buf, int limit) {
-        if (wave * 32 >= limit) return;
-        const int idx = wave * 32 + frow;
-        const int dr = idx >= ow ? 1 : 0;
-        const int ox = idx - dr * ow;
+    // This lane's pooled column pc and its two stem columns u (block 0) and u + 1
+    // (block 1), u = 2pc - 1 clamped into [0, OW-1].  Column u + 1 sits 8 bytes after
+    // column u, so a filter row of both blocks is three 8-byte units.  Clamping changes
+    // nothing that is used: at pc = 0 the blocks are columns 0 and 1 (the window's
+    // in-image columns are 0 and 1); a clamped u = OW-1 only occurs on lanes past the
+    // pooled width, whose block 1 (the partial column OW, read inside the slab) is never
+    // used, while their block 0 -- used by the lane to their left -- is unclamped.
+    const int jl = lane & 31;
+    const int pc = kSpColsPerWave * wave + jl;
+    const uint32_t u = (uint32_t)min(max(2 * pc - 1, 0), ow - 1);
+    const uint32_t bxor = XX ? p.x_xor : 0u;
+    // accumulators of stem row sr (slab buffer `buf` starts at input row 2*sr0): blocks
+    // b (stem columns u, u + 1) x channel halves t, the first MFMA adding to the bias
+    auto stem_row = [&](int sr, int sr0, int buf, v16i (&acc)[2][2]) {
         const int64_t start = ((int64_t)n * p.h + 2 * (int64_t)sr0) * row_bytes;
-        const uint32_t b0 = (uint32_t)(start & 15) + (uint32_t)(2 * dr * row_bytes) + ox * 8 + 16 * (lane >> 5);
+        const uint32_t rb = (uint32_t)(start & 15) + (uint32_t)(2 * (sr - sr0) * row_bytes) + 16 * (lane >> 5) + 8 * u;
         const uint2* sv = reinterpret_cast<const uint2*>(&slab[buf][0]);
-        v16i acc[2];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int ocl = t * 32 + (lane >> 5) * 16;
+        for (int ky = 0; ky < KR; ++ky) {
+            if (ky == 0 || KH > 0 || ky < kh) {   // kh >= 1
+                const uint32_t ad = (rb + ky * (uint32_t)row_bytes) >> 3;
+                const uint2 q0 = sv[ad], q1 = sv[ad + 1], q2 = sv[ad + 2];
+                v4i f0, f1;
+                if constexpr (XX) {
+                    const uint32_t m0 = q1.x ^ bxor, m1 = q1.y ^ bxor;
+                    f0 = v4i{(int)(q0.x ^ bxor), (int)(q0.y ^ bxor), (int)m0, (int)m1};
+                    f1 = v4i{(int)m0, (int)m1, (int)(q2.x ^ bxor), (int)(q2.y ^ bxor)};
+                } else {
+                    f0 = v4i{(int)q0.x, (int)q0.y, (int)q1.x, (int)q1.y};
+                    f1 = v4i{(int)q1.x, (int)q1.y, (int)q2.x, (int)q2.y};
+                }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int4 bv = *reinterpret_cast<const int4*>(&cbias[ocl + 4 * q]);
-                acc[t][4 * q] = bv.x; acc[t][4 * q + 1] = bv.y; acc[t][4 * q + 2] = bv.z; acc[t][4 * q + 3] = bv.w;
+                for (int t = 0; t < 2; ++t) {
+                    if (ky == 0) {   // both blocks start from the bias of channels ocl .. ocl+15
+                        const int ocl = t * 32 + (lane >> 5) * 16;
+                        v16i bias;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int4 bv = *reinterpret_cast<const int4*>(&cbias[ocl + 4 * q]);
+                            bias[4 * q] = bv.x; bias[4 * q + 1] = bv.y; bias[4 * q + 2] = bv.z; bias[4 * q + 3] = bv.w;
+                        }
+                        acc[0][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wa[t][ky], f0, bias, 0, 0, 0);
+                        acc[1][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wa[t][ky], f1, bias, 0, 0, 0);
+                    } else {
+                        acc[0][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wa[t][ky], f0, acc[0][t], 0, 0, 0);
+                        acc[1][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wa[t][ky], f1, acc[1][t], 0, 0, 0);
+                    }
+                }
             }
-        }
-#pragma unroll
-        for (int ky = 0; ky < kStemKH; ++ky) {
-            if (ky < p.kh) {
-                const uint32_t ad = (b0 + ky * (uint32_t)row_bytes) >> 3;   // 8-byte units
-                const uint2 lo = sv[ad], hi = sv[ad + 1];
-                v4i fb = {(int)(lo.x ^ bxor), (int)(lo.y ^ bxor), (int)(hi.x ^ bxor), (int)(hi.y ^ bxor)};
-                acc[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wa[0][ky], fb, acc[0], 0, 0, 0);
-                acc[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wa[1][ky], fb, acc[1], 0, 0, 0);
-            }
-        }
-        if (idx >= limit) return;
-        uint8_t* dst = &rows[(sr0 + dr) % 3][ox * 64];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int ocb = t * 32 + (lane >> 5) * 16;
-            float v[16];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 mv = *reinterpret_cast<const float4*>(&cmult[ocb + 4 * q]);
-                v[4 * q] = (float)acc[t][4 * q] * mv.x;
-                v[4 * q + 1] = (float)acc[t][4 * q + 1] * mv.y;
-                v[4 * q + 2] = (float)acc[t][4 * q + 2] * mv.z;
-                v[4 * q + 3] = (float)acc[t][4 * q + 3] * mv.w;
-            }
-            uint32_t b[16];
-            round_codes16(p, v, b);
-            *reinterpret_cast<uint4*>(dst + ocb) = pack_bytes16(p, b);
         }
     };
 
-    const int kr = p.kh + 2;   // input rows of a stem row pair
-    if (r0 > 0) {   // stem row 2*r0 - 1, the band's first pooled row's upper tap row
-        issue(2 * r0 - 1, p.kh, 0);
+    const int kr = kh + 2;   // input rows of a stem row pair
+    const bool store = jl < kSpColsPerWave && pc < a.pw;
+    // requantized bytes of pooled maxima h (channel halves t, 16 channels each)
+    auto requant = [&](const int32_t (&h)[2][16], uint4 (&pk)[2]) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int ocb = t * 32 + (lane >> 5) * 16;
+            uint32_t bb[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const float v = (float)h[t][q] * cmult[ocb + q];
+                bb[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_fmed3f(v, p.t_lo, p.t_hi) + p.out_magic) +
+                        (FIX < 0 ? p.out_fix : (uint32_t)FIX);
+            }
+            pk[t] = pack_bytes16(p, bb);
+        }
+    };
+    auto put = [&](int r, const uint4 (&pk)[2]) {
+        uint8_t* dst = a.yp + (((int64_t)n * a.ph + r) * a.pw + pc) * 64 + (lane >> 5) * 16;
+        *reinterpret_cast<uint4*>(dst) = pk[0];
+        *reinterpret_cast<uint4*>(dst + 32) = pk[1];
+    };
+
+    v16i carry[2][2], next[2][2];   // stem rows 2r-1 and 2r+1 of pooled row r
+    if (r0 > 0) {                    // the band's first pooled row's upper stem row
+        issue(2 * r0 - 1, kh, 0);
         IQNN_WAIT_VM_LGKM0(0);
         __builtin_amdgcn_s_barrier();
-        compute(2 * r0 - 1, 0, ow);
+        stem_row(2 * r0 - 1, 2 * r0 - 1, 0, carry);
         __syncthreads();   // slab 0 is free again
     }
     for (int i = 0; i < kSpAhead && r0 + i < r1; ++i) issue(2 * (r0 + i), kr, (r0 + i) % kSpSlabs);
-    const int pc = tid >> 3, g8 = (tid & 7) * 8;   // pooled column, channel offset
     for (int r = r0; r < r1; ++r) {
-        // this pair's slab has landed (the later ones may be in flight), every wave is
-        // done with the slab refilled below and with the row slots this pair overwrites
+        // this pair's slab has landed (the later ones may be in flight), and every wave
+        // is done with the slab refilled below
         if (r + kSpAhead - 1 < r1) {
             IQNN_WAIT_VM_LGKM0((kSpAhead - 1) * CPW);
         } else {
@@ -2229,37 +2276,35 @@ __global__ __launch_bounds__(64 * NW, 2) void qconv_stem_pool(const ConvParams p
         }
         __builtin_amdgcn_s_barrier();
         if (r + kSpAhead < r1) issue(2 * (r + kSpAhead), kr, (r + kSpAhead) % kSpSlabs);
-        compute(2 * r, r % kSpSlabs, 2 * ow);
-        __syncthreads();
-        // max pooling of row r: rows 2r-1..2r+1, columns 2c-1..2c+1 inside the image
-        if (pc < a.pw) {
-            u16x2 me[2], mo[2];
+        const int buf = r % kSpSlabs;
+        v16i vm[2][2];
+        stem_row(2 * r, 2 * r, buf, vm);
+        if (r > 0) {   // stem row -1 lies outside the image
 #pragma unroll
-            for (int d = 0; d < 2; ++d) { me[d] = u16x2{0, 0}; mo[d] = u16x2{0, 0}; }
+            for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int dy = -1; dy <= 1; ++dy) {
-                const int sr = 2 * r + dy;
-                if (sr < 0 || sr >= oh) continue;
-                const uint8_t* rowp = &rows[sr % 3][0];
+                for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int dx = -1; dx <= 1; ++dx) {
-                    const int sx = 2 * pc + dx;
-                    if (sx < 0 || sx >= ow) continue;
-                    const uint2 v = *reinterpret_cast<const uint2*>(rowp + sx * 64 + g8);
-                    const uint32_t vw[2] = {v.x ^ a.bias, v.y ^ a.bias};
-#pragma unroll
-                    for (int d = 0; d < 2; ++d) {
-                        me[d] = __builtin_elementwise_max(me[d], __builtin_bit_cast(u16x2, vw[d] & 0x00FF00FFu));
-                        mo[d] = __builtin_elementwise_max(mo[d], __builtin_bit_cast(u16x2, (vw[d] >> 8) & 0x00FF00FFu));
-                    }
-                }
-            }
-            uint32_t o[2];
-#pragma unroll
-            for (int d = 0; d < 2; ++d)
-                o[d] = (__builtin_bit_cast(uint32_t, me[d]) | (__builtin_bit_cast(uint32_t, mo[d]) << 8)) ^ a.bias;
-            *reinterpret_cast<uint2*>(a.yp + (((int64_t)n * a.ph + r) * a.pw + pc) * 64 + g8) = make_uint2(o[0], o[1]);
+                    for (int q = 0; q < 16; ++q) vm[b][t][q] = max(vm[b][t][q], carry[b][t][q]);
         }
+        stem_row(2 * r + 1, 2 * r, buf, next);   // row 2r+1 < OH: OH is even
+        // columns 2c-1 (block 0), 2c (block 1) and 2c+1 (block 0 of the next lane)
+        int32_t h[2][16];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int32_t v0 = max(vm[0][t][q], next[0][t][q]);
+                const int32_t v1 = max(vm[1][t][q], next[1][t][q]);
+                h[t][q] = max(max(v0, v1), __shfl_down(v0, 1, 64));
+            }
+        uint4 pk[2];
+        requant(h, pk);
+        if (store) put(r, pk);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) carry[b][t] = next[b][t];
     }
     // no DMA may still be writing this workgroup's LDS when it ends
     IQNN_WAIT_VM(0);
@@ -2267,14 +2312,23 @@ __global__ __launch_bounds__(64 * NW, 2) void qconv_stem_pool(const ConvParams p
 
 }  // namespace
 
-// The fused stem + pooling kernel's conditions: the stem kernel's (stem_ok), exactly
-// 64 output channels of 8-bit codes without residual, an even output height and a
-// width that is a multiple of 16 (a row pair is whole 32-pixel blocks) up to
-// kSpMaxOW, and the input rows of a stem row pair within one slab buffer.
+// The fused stem + pooling kernel's conditions: the stem's 4-channel gather with 8-tap
+// rows, stride 2 and at most kStemKH filter rows; 64 output channels of an 8-bit type
+// with a requantizing Conv / Conv_Relu epilogue; an even input width (8-byte aligned
+// slab reads); an even stem output height and width (pooled size = half the stem size,
+// so only the window column / row -1 leaves the image); a pooled width of at most
+// kSpMaxWaves * 31 columns; the input rows of a stem row pair within one slab buffer;
+// and an input of whole 16-byte units (the slab DMA moves 16 bytes per lane) below 2 GB
+// (32-bit offsets).
 bool stem_pool_ok(const ConvParams& p) {
-    if (!stem_ok(p) || p.c_out != 64 || p.epi == E_RAW) return false;
+    if (p.kw != 8 || p.sh != 2 || p.sw != 2 || p.kh < 1 || p.kh > kStemKH || p.c_out != 64 || !p.vec_store)
+        return false;
+    if (p.epi != E_NONE && p.epi != E_RELU) return false;
     if (p.y_type != T_UINT8 && p.y_type != T_INT8) return false;
-    if (p.oh % 2 != 0 || p.ow % 16 != 0 || p.ow > kSpMaxOW) return false;
+    if (p.w_in % 2 != 0 || p.m >= ((int64_t)1 << 31) || p.oh <= 0 || p.ow <= 0) return false;
+    if (p.oh % 2 != 0 || p.ow % 2 != 0 || p.ow / 2 > kSpMaxWaves * kSpColsPerWave) return false;
+    const int64_t in_bytes = (p.m / ((int64_t)p.oh * p.ow)) * p.h * (int64_t)p.w_in * 4;
+    if (in_bytes % 16 != 0 || in_bytes >= ((int64_t)1 << 31)) return false;
     return (int64_t)(p.kh + 2) * p.w_in * 4 + 16 <= kSpBuf;
 }
 
@@ -2286,22 +2340,28 @@ hipError_t launch_stem_pool(const ConvParams& p, uint8_t* yp, hipStream_t stream
     a.yp = yp;
     a.ph = p.oh / 2;
     a.pw = p.ow / 2;
-    a.n_bands = 2;   // two workgroups per image: about two per CU at batch 256
+    // about 1024 workgroups in all (four per CU, the LDS limit), bands of >= 4 rows
+    a.n_bands = (int)std::max<int64_t>(1, std::min<int64_t>((1024 + n_img - 1) / n_img, (a.ph + 3) / 4));
     a.band = (a.ph + a.n_bands - 1) / a.n_bands;
-    a.bias = p.y_type == T_INT8 ? 0x80808080u : 0u;
+    a.n_bands = (a.ph + a.band - 1) / a.band;
     a.in_bytes = n_img * p.h * (int64_t)p.w_in * 4;
     const int64_t grid = n_img * a.n_bands;
     if (grid >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-    const dim3 g((unsigned)grid), b((unsigned)(4 * p.ow));
-    switch (p.ow / 16) {   // waves: 2*OW/32
-    case 1: hipLaunchKernelGGL(qconv_stem_pool<1>, g, b, 0, stream, p, a); break;
-    case 2: hipLaunchKernelGGL(qconv_stem_pool<2>, g, b, 0, stream, p, a); break;
-    case 3: hipLaunchKernelGGL(qconv_stem_pool<3>, g, b, 0, stream, p, a); break;
-    case 4: hipLaunchKernelGGL(qconv_stem_pool<4>, g, b, 0, stream, p, a); break;
-    case 5: hipLaunchKernelGGL(qconv_stem_pool<5>, g, b, 0, stream, p, a); break;
-    case 6: hipLaunchKernelGGL(qconv_stem_pool<6>, g, b, 0, stream, p, a); break;
-    case 7: hipLaunchKernelGGL(qconv_stem_pool<7>, g, b, 0, stream, p, a); break;
-    case 8: hipLaunchKernelGGL(qconv_stem_pool<8>, g, b, 0, stream, p, a); break;
+    const int nw = (a.pw + kSpColsPerWave - 1) / kSpColsPerWave;
+    const dim3 g((unsigned)grid), b((unsigned)(64 * nw));
+    // the image stem (7 filter rows, signed input codes) takes a kernel with every choice
+    // fixed at compile time; other shapes the one that reads them at run time
+    const int fast = (p.kh == 7 && p.x_xor == 0u) ? 1 + (int)(p.out_fix & 1u) : 0;
+    switch (nw * 3 + fast) {
+#define IQNN_STEM_POOL_NW(NW_)                                                                          \
+    case NW_ * 3: hipLaunchKernelGGL((qconv_stem_pool<NW_, 0, true, -1>), g, b, 0, stream, p, a); break; \
+    case NW_ * 3 + 1: hipLaunchKernelGGL((qconv_stem_pool<NW_, 7, false, 0>), g, b, 0, stream, p, a); break; \
+    case NW_ * 3 + 2: hipLaunchKernelGGL((qconv_stem_pool<NW_, 7, false, 1>), g, b, 0, stream, p, a); break;
+    IQNN_STEM_POOL_NW(1)
+    IQNN_STEM_POOL_NW(2)
+    IQNN_STEM_POOL_NW(3)
+    IQNN_STEM_POOL_NW(4)
+#undef IQNN_STEM_POOL_NW
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

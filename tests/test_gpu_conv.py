@@ -109,10 +109,15 @@ def test_stem_input_not_whole_16_byte_units(n):
 
 
 @pytest.mark.parametrize("n,hw,y_type,epi", [(2, (32, 32), U8, RELU), (3, (48, 64), I8, NONE), (1, (16, 224), U8, NONE),
-                                          (2, (224, 224), U8, RELU), (1, (40, 64), I8, RELU)])
+                                          (2, (224, 224), U8, RELU), (1, (40, 64), I8, RELU),
+                                          (1, (20, 36), I8, NONE), (2, (16, 248), U8, RELU),
+                                          (3, (100, 132), I8, RELU), (1, (28, 124), U8, NONE)])
 def test_stem_fused_max_pooling(n, hw, y_type, epi):
     """iqnn_qconv_maxpool_fwd (the stem conv and 3x3/2 pad 1 max pooling in one launch)
-    equals the oracle's conv followed by the oracle's max pooling, byte for byte."""
+    equals the oracle's conv followed by the oracle's max pooling, byte for byte.  The
+    shapes span one to three waves of 31 pooled columns (pooled widths 8, 9, 16, 31,
+    33, 56, 62), bands of pooled rows whose first row takes its upper stem row from the
+    band above, a short last band, and signed codes whose window maxima are negative."""
     torch = require_gpu()
     from integer_quantized_nn_amd.layers import QConv
     h, w = hw
@@ -128,6 +133,29 @@ def test_stem_fused_max_pooling(n, hw, y_type, epi):
     torch.cuda.synchronize()
     assert y.shape == want.shape
     assert_bytes_equal(y.cpu().numpy(), want, "stem+pool %s" % ((n, hw, y_type, epi),))
+
+
+@pytest.mark.parametrize("z_odd", [0, 1])
+@pytest.mark.parametrize("n,hw", [(2, (64, 96)), (3, (28, 224))])
+def test_stem_fused_max_pooling_signed_input(n, hw, z_odd):
+    """The image stem as the trunk runs it -- signed input codes, 7 filter rows -- takes
+    the fused kernel whose choices are fixed at compile time, including the odd part of
+    Z_out (both parities here); every pooled byte against the oracle."""
+    torch = require_gpu()
+    from integer_quantized_nn_amd.layers import QConv
+    h, w = hw
+    c = synth.conv_case(5100 + 7 * n + z_odd, n, h, w, 3, 64, 7, 2, 3, I8, I8, U8, RELU)
+    c.z_out = (c.z_out & ~1) | z_odd
+    x, wc, _ = conv_codes(c)
+    conv_ref = oracle_conv(c, x, wc, None)
+    want = to_bytes(O.maxpool2d(conv_ref, 3, 2, 1), U8)
+    xp = np.pad(x, ((0, 0), (3, 3), (3, 3), (0, 1)), constant_values=c.z_in)
+    wp = np.pad(wc, ((0, 0), (0, 0), (0, 0), (0, 1)))
+    conv = QConv(n, h + 6, w + 6, 4, 64, 7, 2, 0, I8, I8, U8, RELU, c.z_in, c.z_out,
+                 to_bytes(wp, I8), c.bias, c.s_in, c.s_w, c.s_out)
+    y = conv.conv_maxpool(torch.from_numpy(to_bytes(xp, I8)).cuda())
+    torch.cuda.synchronize()
+    assert_bytes_equal(y.cpu().numpy(), want, "stem+pool signed input %s" % ((n, hw, z_odd),))
 
 
 # 64-channel 3x3 / stride 1 / pad 1 layers on 56-pixel rows (the direct kernel, forced at
