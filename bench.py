@@ -219,11 +219,14 @@ def make_layer(torch, wl, cfg=None):
         cfg = (19, 0)
     rec = {"peak_ops": PEAK_FP6_OPS if fp6 else PEAK_INT8_OPS, "dtype": "bf6" if fp6 else "int8", "oracle": None}
     conv_wls = ("conv3x3_int8", "conv3x3_4bit", "conv3x3_4bit_fp6", "conv3x3_uint8w", "conv3x3_intrq",
-                "conv3x3_2of4", "resnet50_l3_conv3x3")
+                "conv3x3_2of4", "resnet50_l3_conv3x3", "resnet50_l3_conv3x3_intrq", "conv1x1_int8", "conv1x1_intrq")
     if wl in conv_wls:
-        if wl == "resnet50_l3_conv3x3":   # the trunk's stage-3 3x3 layer: 256 x 14x14, 256 -> 256
+        if wl.startswith("resnet50_l3_conv3x3"):   # the trunk's stage-3 3x3 layer: 256 x 14x14, 256 -> 256
             c = synth.conv_case(31, 256, 14, 14, 256, 256, 3, 1, 1, synth.UINT8, synth.INT8, synth.UINT8,
                                 synth.EPI_RELU, name="l3_conv3x3")
+        elif wl.startswith("conv1x1"):   # the trunk's stage-1 expanding 1x1 layer: 256 x 56x56, 64 -> 256
+            c = synth.conv_case(33, 256, 56, 56, 64, 256, 1, 1, 0, synth.UINT8, synth.INT8, synth.UINT8,
+                                synth.EPI_RELU, name="conv1x1")
         else:
             c = synth.conv3x3_4bit() if wl.startswith("conv3x3_4bit") else synth.conv3x3_int8()
         if wl == "conv3x3_2of4":   # float weights magnitude-pruned to 2:4 along the input channels
@@ -237,14 +240,15 @@ def make_layer(torch, wl, cfg=None):
             wq = quantize(torch.from_numpy(c.w).cuda(), s_w, z_w, w_type).cpu().numpy()
         else:
             wq = quantize(torch.from_numpy(c.w).cuda(), c.s_w, 0, c.w_type, axis=0).cpu().numpy()
-        epi = c.epi | (IB.EPI_INT_REQUANT if wl == "conv3x3_intrq" else 0)
+        epi = c.epi | (IB.EPI_INT_REQUANT if wl.endswith("intrq") else 0)
         lib_w_type = IB.INT8_2OF4 if wl == "conv3x3_2of4" else w_type
-        layer = QConv(n, h, w, ci, co, 3, c.stride, c.pad, c.x_type, lib_w_type, c.y_type, epi, c.z_in, c.z_out,
+        kk = c.w.shape[1]
+        layer = QConv(n, h, w, ci, co, kk, c.stride, c.pad, c.x_type, lib_w_type, c.y_type, epi, c.z_in, c.z_out,
                       wq, c.bias, c.s_in, s_w, c.s_out, res_type=c.res_type, z_res=c.z_res, s_res=c.s_res, z_w=z_w)
         xd = quantize(torch.from_numpy(c.x).cuda(), c.s_in, c.z_in, c.x_type)
         rd = quantize(torch.from_numpy(c.res).cuda(), c.s_res, c.z_res, c.res_type) if c.res is not None else None
         oh, ow = layer.out_shape[1:3]
-        w_bytes = co * 9 * ci // (2 if c.w_type in (synth.UINT4, synth.INT4) else 1)
+        w_bytes = co * kk * kk * ci // (2 if c.w_type in (synth.UINT4, synth.INT4) else 1)
         if wl == "conv3x3_2of4":
             w_bytes = w_bytes * 5 // 8   # kept codes + positions
         y_bytes = n * oh * ow * co // (2 if c.y_type in (synth.UINT4, synth.INT4) else 1)
@@ -572,7 +576,7 @@ def main():
     ap.add_argument("--workload", default="resnet50_trunk",
                     choices=["resnet50_trunk", "resnet50_trunk_2of4", "conv3x3_int8", "conv3x3_2of4", "conv3x3_4bit",
                              "conv3x3_4bit_fp6", "conv3x3_uint8w", "conv3x3_intrq", "resnet50_l3_conv3x3",
-                             "resnet50_stem_pool",
+                             "resnet50_stem_pool", "conv1x1_int8", "conv1x1_intrq", "resnet50_l3_conv3x3_intrq",
                              "vitl_fc1", "vitl_fc1_2of4", "gemm_int8_256"])
     ap.add_argument("--cold", action="store_true",
                     help="single-layer workloads: rotate input/output sets (> 256 MB) so every launch misses the caches")

@@ -102,10 +102,13 @@ typedef enum {
      * floating point ("Quantization" blog, 量化模式: integer (power of two)
      * quantization; FQ-ViT article, LayerNorm code: get_MN).  Prepack writes each
      * M[c] as M_c * 2^-N_c with N_c = clamp(7 - floor(log2 M[c]), 0, 31) and
-     * M_c = clamp(floor(M[c] * 2^N_c), 0, 255) (floor(log2) = the binary exponent);
-     * the kernel computes y = clip(rne((acc + bias) * M_c / 2^N_c) + Z_out) in
-     * integers (rne: half to even; RELU clamps at Z_out).  Not with ADD, ADD_RELU or
-     * RAW_INT32, nor with iqnn_qconv_maxpool_fwd (IQNN_ERR_UNSUPPORTED). */
+     * M_c = clamp(floor(M[c] * 2^N_c), 0, 255) (floor(log2) = the binary exponent)
+     * and stores M_c * 2^-N_c (exact in binary32) in the multiplier slot; the kernel
+     * computes y = clip(rne((acc + bias) * M_c / 2^N_c) + Z_out) (rne: half to even;
+     * RELU clamps at Z_out), exactly: the product is below 2^40 and is formed, scaled
+     * and rounded by one binary64 fused multiply-add, whose single rounding is that
+     * rne.  Not with ADD, ADD_RELU or RAW_INT32, nor with iqnn_qconv_maxpool_fwd
+     * (IQNN_ERR_UNSUPPORTED). */
     IQNN_EPI_INT_REQUANT = 16
 } iqnn_epilogue;
 

@@ -440,11 +440,10 @@ iqnn_status prepack_into(const Layer& L, const void* w_host, const float* bias_h
             const float m = sw_in / s_out;
             if (!normal_ok(m) || m > 1e20f)
                 return fail(IQNN_ERR_INVALID_ARG, "requant multiplier of channel %lld is not a normal float in [FLT_MIN, 1e20]", (long long)oc);
-            if (L.int_rq) {   // the slot holds N << 16 | M instead of the float
+            if (L.int_rq) {   // the slot holds M_c * 2^-N_c, exact in binary32 (8-bit M_c, N_c <= 31)
                 int32_t mi, ni;
                 int_multiplier(m, &mi, &ni);
-                const uint32_t packed = ((uint32_t)ni << 16) | (uint32_t)mi;
-                std::memcpy(&mult[oc], &packed, 4);
+                mult[oc] = std::ldexp((float)mi, -ni);
             } else {
                 mult[oc] = m;
             }

@@ -105,8 +105,9 @@ struct ConvParams {
     // out_fix4 = 0x01010101 and out_fix = 0.
     float t_lo, t_hi, out_magic;
     uint32_t out_fix, out_fix4;
-    // Integer-only requantization: mult[c] holds N << 16 | M (see int_multiplier);
-    // the rounded value is clipped to [q_lo, q_hi] = [t_lo, t_hi] as integers.
+    // Integer-only requantization: mult[c] holds M_c * 2^-N_c exactly (see
+    // int_multiplier); the rounded value is clipped to [q_lo, q_hi] = [t_lo, t_hi] as
+    // integers.
     int32_t int_rq, q_lo, q_hi;
     float res_zf;
     uint32_t res_xor;

@@ -184,15 +184,15 @@ __device__ __forceinline__ uint4 pack_bytes16(const ConvParams& p, const uint32_
 // BIAS: add bias[] here (otherwise the accumulator started from the folded bias).
 // ADDK: 0 = residual add decided by `add` and p.res_type at run time, 1 = always an
 // 8-bit residual, 2 = never a residual, 3 = always a 4-bit residual.
-// INTRQ: integer-only requantization (mult[] holds N << 16 | M); compiled into the
-// register-staged kernel only, so the other kernels' register budgets never see it.
+// INTRQ: integer-only requantization (mult[] holds M_c * 2^-N_c, see below); compiled
+// into the kernels' own integer-requantizing variants only.
 // OUTK: 0 = output type and store width decided at run time; 1 = 8-bit codes, 2 = raw
 // int32, 3 = 4-bit codes, each with 16-channel vector stores (C_out % 16 == 0).  A
 // kernel that keeps most registers busy takes the one branch it needs.
 template <bool BIAS = true, int ADDK = 0, bool INTRQ = false, int OUTK = 0>
 __device__ __forceinline__ void epi_store16(const ConvParams& p, const v16i& acc, const int32_t* bias,
                                             const float* mult, uint32_t rw[4], int ocb, int64_t pix, bool add_rt,
-                                            float m_res) {
+                                            float m_res, bool irq32 = false) {
     const bool add = (ADDK == 1 || ADDK == 3) ? true : (ADDK == 2 ? false : add_rt);
     const int64_t oidx = pix * p.c_out + ocb;   // element index of the first channel
     const bool vec = OUTK != 0 || p.vec_store;
@@ -213,18 +213,44 @@ __device__ __forceinline__ void epi_store16(const ConvParams& p, const v16i& acc
     if constexpr (OUTK == 2) return;
     uint32_t b[16];
     if constexpr (INTRQ) {
-        // integer-only requantization: mult[j] holds N << 16 | M; rne(a * M / 2^N) as
-        // floor((t + 2^(N-1) - 1 + lsb) / 2^N) with lsb the low bit of floor(t / 2^N)
-        // (half to even), clipped in the offset domain, plus Z_out
+        // integer-only requantization: mult[j] = x = M_c * 2^-N_c exactly (8-bit M_c),
+        // and the code is clip(rne(a * M_c / 2^N_c)) + Z_out, rne half to even, with
+        // a = acc + bias.  fma(float(a), x, 1.5 * 2^23) rounds once.  With |a| <= 2^24,
+        // float(a) = a, and for |a x| < 2^22 the result is 1.5 * 2^23 + rne(a x), its
+        // bits those of 1.5 * 2^23 plus the integer; a larger |a x| puts the result at
+        // or beyond 2^24 (at or below 2^23), whose bits lie outside the clip range on
+        // the same side: clipping the bits gives the exact code.  With |a| > 2^24 and
+        // x >= 2^-13 (irq32: the caller checked every channel it stores), |a x| and
+        // |float(a) x| exceed 2^11 with the same sign, and both clip to the same bound.
+        // Otherwise such a lane takes binary64: a * M_c is below 2^40, so the product
+        // and the scaling are exact and the one rounding of the fused add of 1.5 * 2^52
+        // is the rne; the low word of the result is the integer.
+        constexpr int32_t kB = 0x4B400000;   // bits of 1.5 * 2^23
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const uint32_t mn = __builtin_bit_cast(uint32_t, mult[j]);
-            const int64_t t = (int64_t)(acc[j] + (BIAS ? bias[j] : 0)) * (int64_t)(mn & 0xFFFFu);
-            const int n = (int)(mn >> 16);
-            int64_t q = t;
-            if (n > 0) q = (t + (((int64_t)1 << (n - 1)) - 1) + ((t >> n) & 1)) >> n;
-            q = q < p.q_lo ? p.q_lo : (q > p.q_hi ? p.q_hi : q);
-            b[j] = (uint32_t)((int32_t)q + p.z_out);
+            const float r = __builtin_fmaf((float)(acc[j] + (BIAS ? bias[j] : 0)), mult[j], 12582912.0f);
+            b[j] = __builtin_bit_cast(uint32_t, r);
+        }
+        if (!irq32) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int32_t a = acc[j] + (BIAS ? bias[j] : 0);
+                if (a > (1 << 24) || a < -(1 << 24)) {
+                    // the multiplier's conversion stays in this rarely taken block (an
+                    // ordinary conversion would be hoisted above it: 32 more registers
+                    // and conversions on every tile)
+                    double xd;
+                    asm volatile("v_cvt_f64_f32 %0, %1" : "=v"(xd) : "v"(mult[j]));
+                    const double r = __builtin_fma((double)a, xd, 6755399441055744.0);
+                    const int32_t q = (int32_t)(uint32_t)__builtin_bit_cast(uint64_t, r);
+                    b[j] = (uint32_t)(kB + min(max(q, -1024), 1024));
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int32_t q = min(max((int32_t)b[j], kB + p.q_lo), kB + p.q_hi);
+            b[j] = (uint32_t)(q + (p.z_out - kB));
         }
     } else {
         float v[16];
@@ -1094,7 +1120,8 @@ struct StreamCfg {
 // one MFMA per stage accumulates in fp32, which is exact for these integers (a partial
 // sum stays below 2^24); the epilogue converts it to int32 and adds the bias.
 // OUTK: 1 = 8-bit output codes with 16-channel vector stores, fixed at compile time
-// (the requantizing epilogue without run-time type branches); 0 = decided at run time.
+// (the requantizing epilogue without run-time type branches); 4 = the same with the
+// integer-only requantization; 0 = decided at run time.
 // S4: 4-bit activations are INT4 (sign-extended when unpacked), else UINT4.
 // W4: INT4 weights stay packed (two codes per byte, natural K order like an activation
 // row) in the tile-order copy and in LDS: 32 bytes per weight row and stage.  A lane
@@ -1179,6 +1206,17 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
         f6tab[tid] = bf6_code(vlo) | (bf6_code(vhi) << 6);
     }
     __syncthreads();
+    // integer-only requantization: the binary32 evaluation when every multiplier of the
+    // wave's output channels is at least 2^-13 (a wave-uniform choice, see epi_store16)
+    bool irq32 = false;
+    if constexpr (OUTK == 4) {
+        bool ok = true;
+        for (int i = lane; i < C::WOC; i += 64) {
+            const int c = wave_oc * C::WOC + i;
+            ok = ok && (oc0 + c >= p.c_out || cmult[c] >= 0x1p-13f);
+        }
+        irq32 = __all(ok) != 0;
+    }
 
     const int nst = p.kp / kPipeBK;
     constexpr int EXTRA = RES ? 1 : 0;
@@ -1735,10 +1773,11 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
                     epi_store16<true, RES ? 3 : 2>(p, ai, &cbias[ocl], mult, rw, ocb, pix, add, m_res);
                 } else if constexpr (W4) {   // 16 * acc: back to acc, exactly
                     const v16i a = acc[t][u] >> 4;
-                    epi_store16<false, RES ? 3 : 2, false, OUTK>(p, a, nullptr, mult, rw, ocb, pix, add, m_res);
+                    epi_store16<false, RES ? 3 : 2, OUTK == 4, OUTK == 4 ? 1 : OUTK>(p, a, nullptr, mult, rw, ocb,
+                                                                                  pix, add, m_res, irq32);
                 } else {
-                    epi_store16<false, RES ? (B4 ? 3 : 1) : 2, false, OUTK>(p, acc[t][u], nullptr, mult, rw, ocb, pix,
-                                                                            add, m_res);
+                    epi_store16<false, RES ? (B4 ? 3 : 1) : 2, OUTK == 4, OUTK == 4 ? 1 : OUTK>(
+                        p, acc[t][u], nullptr, mult, rw, ocb, pix, add, m_res, irq32);
                 }
             }
         }
@@ -1834,6 +1873,10 @@ bool block_fits_packed(int32_t c_out, int bm) {
     return bm <= kOcPad ? kOcPad % bm == 0 : ocp % bm == 0;
 }
 
+// The block configurations compiled with the integer-only requantization (specialized
+// beside the tile table below).
+template <class C> constexpr bool kIrqTile = false;
+
 template <class C>
 hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bool c4, hipStream_t stream,
                          bool zw = false) {
@@ -1873,6 +1916,16 @@ hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bo
     if (add && !(kResStage && res_prefetch)) return hipErrorInvalidValue;
     // 8-bit codes stored 16 channels at a time: the epilogue compiled for that output
     const bool out8 = p.epi != E_RAW && (p.y_type == T_INT8 || p.y_type == T_UINT8) && p.vec_store;
+    if (p.int_rq) {   // integer-only requantization: Conv / Conv_Relu to 8-bit codes
+        if (!kIrqTile<C> || add || !out8 || c4) return hipErrorInvalidValue;
+        if constexpr (kIrqTile<C>) {
+            if (is_1x1)
+                hipLaunchKernelGGL((qconv_stream<C, true, false, false, false, false, false, false, 4>), g, b, 0, stream, q);
+            else
+                hipLaunchKernelGGL((qconv_stream<C, false, false, false, false, false, false, false, 4>), g, b, 0, stream, q);
+            return hipGetLastError();
+        }
+    }
     if constexpr (kResStage) {
         if (res_prefetch) {
             if (is_1x1 && out8)
@@ -2435,6 +2488,10 @@ __global__ __launch_bounds__(256, 2) void qconv_direct3x3(const ConvParams p, in
             }
         }
     __syncthreads();
+    // integer-only requantization: the binary32 evaluation when every multiplier of the
+    // block's output channels is at least 2^-13 (see epi_store16)
+    bool irq32 = false;
+    if constexpr (INTRQ) irq32 = __all(oc0 + lane >= p.c_out || cmult[lane] >= 0x1p-13f) != 0;
 
     const int h = p.h;
     // Chunk q = (wave + 4j) * 64 + lane of a slab buffer (its bytes 16q..16q+15) is slab
@@ -2574,7 +2631,7 @@ __global__ __launch_bounds__(256, 2) void qconv_direct3x3(const ConvParams p, in
                 // multipliers read from LDS inside the epilogue: no register copy next to
                 // the 144 registers of A fragments
                 epi_store16<false, 2, INTRQ, OUTK>(p, acc[t], nullptr, &cmult[ocl], rw, oc0 + ocl, pix, false,
-                                                   0.0f);
+                                                   0.0f, irq32);
             }
         }
         buf = buf == 2 ? 0 : buf + 1;
@@ -2667,6 +2724,15 @@ using W128x512d3 = StreamCfg<128, 512, 1, 3, 1, kPipeBK, 8>;
 using W256x128d4 = StreamCfg<256, 128, 2, 4, 1, kPipeBK, 8>;
 using W512x128d3 = StreamCfg<512, 128, 4, 3, 1, kPipeBK, 8>;
 
+// the block configurations the automatic tile choice makes for layers without a
+// residual (tiles 8, 10, 11, 16 and 22; 14 runs as 10) carry the integer-only
+// requantization
+template <> constexpr bool kIrqTile<S64x128d6> = true;
+template <> constexpr bool kIrqTile<S128x128d4> = true;
+template <> constexpr bool kIrqTile<S64x256d3> = true;
+template <> constexpr bool kIrqTile<S256x128d3> = true;
+template <> constexpr bool kIrqTile<W256x128d4> = true;
+
 // Automatic tile (per-layer sweeps over the trunk's shapes at batch 256 chose these),
 // mostly on the streaming kernel at two blocks per CU: 256x128 blocks
 // (each wave 128 channels x 64 pixels: 0.75 KB of fragment reads per MFMA) for the
@@ -2704,8 +2770,25 @@ hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_
         tile = -1;
     }
     if (tile < 0 && direct3x3_ok(p, gather, false)) return launch_direct3x3(p, stream);
-    if (p.int_rq) {   // integer-only requantization runs on the register-staged kernel
+    if (p.int_rq) {   // integer-only requantization: the streaming kernel, else the register-staged one
         if (p.zw_red != 0) return hipErrorInvalidValue;
+        const bool out8 = (p.y_type == T_INT8 || p.y_type == T_UINT8) && p.vec_store;
+        if (gather == GATHER_B8 && out8 && pipe_eligible(gather, p.c, p.k) && p.m < ((int64_t)1 << 31) &&
+            (is_1x1 || p.kh * p.kw <= 64)) {
+            // the automatic choice (an explicit tile without the integer variant takes it
+            // too); the 128x128 blocks run two to a CU, whose register budget holds the
+            // integer epilogue (three to a CU would spill)
+            int t = (tile == 8 || tile == 10 || tile == 11 || tile == 16 || tile == 22)
+                        ? tile : pipe_tile_choice(p.m, p.c_out, p.k, false);
+            if (t == 14) t = 10;
+            switch (t) {
+            case 8: return launch_stream<S64x128d6>(p, is_1x1, false, false, stream);
+            case 10: return launch_stream<S128x128d4>(p, is_1x1, false, false, stream);
+            case 11: return launch_stream<S64x256d3>(p, is_1x1, false, false, stream);
+            case 16: return launch_stream<S256x128d3>(p, is_1x1, false, false, stream);
+            default: return launch_stream<W256x128d4>(p, is_1x1, false, false, stream);
+            }
+        }
         if (p.c_out <= 64) return launch_staged<64, 256, 1, 4>(p, gather, is_1x1, stream);
         return launch_staged<128, 128, 2, 2>(p, gather, is_1x1, stream);
     }

@@ -282,8 +282,8 @@ def test_integer_requant_unsupported_combinations(lib, kw):
 
 
 def test_host_prepack_integer_multipliers(lib):
-    # the packed multiplier slot holds N << 16 | M with (M, N) = get_MN(M[c]) (FQ-ViT
-    # article, LayerNorm code), checked against the oracle's get_mn
+    # the packed multiplier slot holds M * 2^-N (exact in binary32) with (M, N) =
+    # get_MN(M[c]) (FQ-ViT article, LayerNorm code), checked against the oracle's get_mn
     rng = np.random.default_rng(21)
     c_out, c_in = 40, 32
     w = rng.integers(-127, 128, size=(c_out, 3, 3, c_in)).astype(np.int32)
@@ -292,9 +292,9 @@ def test_host_prepack_integer_multipliers(lib):
     d = conv_desc(c_in=c_in, c_out=c_out, epilogue=B.EPI_RELU | B.EPI_INT_REQUANT)
     buf = _host_pack(d, w, B.INT8, None, s_in, s_w, s_out)
     ocp = 256
-    slots = buf[4 * ocp:8 * ocp].view(np.uint32)[:c_out]
+    slots = buf[4 * ocp:8 * ocp].view(np.float32)[:c_out]
     want = [O.get_mn(m) for m in O.requant_multiplier(s_in, s_w, s_out)]
-    assert [(int(v) & 0xFFFF, int(v) >> 16) for v in slots] == want
+    assert [float(v) for v in slots] == [float(mm) * 2.0 ** -nn for mm, nn in want]
     assert lib.iqnn_qconv_maxpool_fwd(ctypes.byref(conv_desc(n=2, h=38, w=38, c_in=4, c_out=64, kh=7, kw=7,
                                                              stride_h=2, stride_w=2, pad_h=0, pad_w=0,
                                                              epilogue=B.EPI_RELU | B.EPI_INT_REQUANT)),

@@ -1,9 +1,10 @@
 """GPU parity of the integer-only requantization (IQNN_EPI_INT_REQUANT): every output
 byte equals the oracle's direct accumulator followed by get_mn / requant_int
 ("Quantization" blog, 量化模式: integer (power of two) quantization; FQ-ViT article,
-LayerNorm code: get_MN).  The layers cover the register-staged kernel's gathers:
-8-bit with C_in % 16 == 0 (3x3 and 1x1), the element gather (C_in % 16 != 0, the
-4-channel stem input), 4-bit activations, and a GEMM."""
+LayerNorm code: get_MN).  The layers cover the streaming kernel (8-bit activations
+with whole 64-channel stages, each of its integer-requantizing block configurations),
+the direct 3x3 kernel, and the register-staged kernel's other gathers (the element
+gather for C_in % 16 != 0, the 4-channel stem input, 4-bit activations), and a GEMM."""
 import numpy as np
 import pytest
 
@@ -113,3 +114,55 @@ def test_integer_requant_3x3_workload_full_size():
     want = to_bytes(oracle_int(c, x, wq), c.y_type)
     assert_bytes_equal(y.cpu().numpy(), want, "3x3 workload, integer requant")
     assert len(np.unique(y.cpu().numpy())) >= 64
+
+
+# the streaming kernel's integer-requantizing block configurations (tiles 8, 10, 11, 16
+# and 22; tile 14 runs as 10), 1x1 and 3x3, on 2 x 9 x 13 pixels: several pixel tiles
+# and a ragged tail
+STREAM_TILES = [(8, 1, 64, 64), (8, 3, 64, 64), (10, 1, 128, 128), (10, 3, 64, 192), (11, 1, 64, 64),
+                (11, 3, 128, 64), (14, 1, 256, 128), (14, 3, 128, 128), (16, 1, 256, 256), (16, 3, 64, 256),
+                (22, 1, 256, 512), (22, 3, 64, 512)]
+
+
+@pytest.mark.parametrize("tile,k,ci,co", STREAM_TILES, ids=lambda v: str(v))
+def test_streaming_integer_requant_tiles(tile, k, ci, co):
+    """Every byte of the streaming kernel's integer-only epilogue against the oracle's
+    requant_int, for each block configuration compiled with it."""
+    torch = require_gpu()
+    from integer_quantized_nn_amd.layers import QConv
+    n, h, w = 2, 9, 13
+    c = synth.conv_case(tile * 100 + k * 10 + co, n, h, w, ci, co, k, 1, k // 2, U8, I8, U8, RELU)
+    x, wq, _ = conv_codes(c)
+    want = to_bytes(oracle_int(c, x, wq), U8)
+    conv = QConv(n, h, w, ci, co, k, 1, k // 2, U8, I8, U8, RELU | INT_RQ, c.z_in, c.z_out, to_bytes(wq, I8),
+                 c.bias, c.s_in, c.s_w, c.s_out)
+    y = conv(torch.from_numpy(to_bytes(x, U8)).cuda(), cfg=(tile, 0))
+    torch.cuda.synchronize()
+    assert_bytes_equal(y.cpu().numpy(), want, "integer requant tile %d k=%d co=%d" % (tile, k, co))
+    assert len(np.unique(y.cpu().numpy())) >= 32
+
+
+@pytest.mark.parametrize("mult,y_type,epi", [(0.5, I8, NONE), (0.5, U8, RELU), (3.0, I8, NONE), (2.0 ** -30, U8, RELU)])
+@pytest.mark.parametrize("k", [1, 3])
+def test_integer_requant_exact_rounding(mult, y_type, epi, k):
+    """Scales chosen to fix the multiplier: 0.5 (power-of-two scales; get_MN gives
+    M = 128, N = 8, and every odd accumulator is a tie, rounded half to even), about 3
+    (N = 6 < 8: large products, most codes clipped) and 2^-30 (N clamped to 31,
+    M = 2).  Every byte against the oracle's requant_int, on the streaming kernel."""
+    torch = require_gpu()
+    from integer_quantized_nn_amd.layers import QConv
+    n, h, w, ci, co = 2, 7, 11, 64, 128
+    c = synth.conv_case(int(mult * 1000) + k, n, h, w, ci, co, k, 1, k // 2, U8, I8, y_type, epi)
+    c.s_in = np.float32(2.0 ** -4)
+    c.s_w = np.full(co, 2.0 ** -9, np.float32)
+    c.s_out = np.float32(2.0 ** -13 / mult)
+    x, wq, _ = conv_codes(c)
+    mm = O.requant_multiplier(c.s_in, c.s_w, c.s_out)
+    if mult == 0.5:
+        assert all(O.get_mn(v) == (128, 8) for v in mm)
+    want = to_bytes(oracle_int(c, x, wq), y_type)
+    conv = QConv(n, h, w, ci, co, k, 1, k // 2, U8, I8, y_type, epi | INT_RQ, c.z_in, c.z_out, to_bytes(wq, I8),
+                 c.bias, c.s_in, c.s_w, c.s_out)
+    y = conv(torch.from_numpy(to_bytes(x, U8)).cuda())
+    torch.cuda.synchronize()
+    assert_bytes_equal(y.cpu().numpy(), want, "integer requant mult=%g k=%d" % (mult, k))
