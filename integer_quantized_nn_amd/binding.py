@@ -12,7 +12,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libiqnn.so")
+# IQNN_LIB: another build of the library (the sanitized CPU-hygiene build, say)
+LIB_PATH = os.environ.get("IQNN_LIB") or os.path.join(_HERE, "libiqnn.so")
 
 INT8, UINT8, INT4, UINT4, INT32 = 0, 1, 2, 3, 4
 INT8_2OF4 = 5          # weights only: 2:4-sparse symmetric int8 codes

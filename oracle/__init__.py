@@ -24,7 +24,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libiqo.so")
+# IQO_LIB: another build of the oracle (the sanitized CPU-hygiene build, say)
+_LIB_PATH = os.environ.get("IQO_LIB") or os.path.join(_HERE, "libiqo.so")
 
 INT8, UINT8, INT4, UINT4, INT32 = 0, 1, 2, 3, 4
 EPI_NONE, EPI_RELU, EPI_ADD, EPI_ADD_RELU, EPI_RAW = 0, 1, 2, 3, 4
