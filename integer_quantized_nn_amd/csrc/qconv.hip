@@ -2725,12 +2725,12 @@ using W256x128d4 = StreamCfg<256, 128, 2, 4, 1, kPipeBK, 8>;
 using W512x128d3 = StreamCfg<512, 128, 4, 3, 1, kPipeBK, 8>;
 
 // the block configurations the automatic tile choice makes for layers without a
-// residual (tiles 8, 10, 11, 16 and 22; 14 runs as 10) carry the integer-only
-// requantization
+// residual (tiles 8, 10, 11, 14, 16 and 22) carry the integer-only requantization
 template <> constexpr bool kIrqTile<S64x128d6> = true;
 template <> constexpr bool kIrqTile<S128x128d4> = true;
 template <> constexpr bool kIrqTile<S64x256d3> = true;
 template <> constexpr bool kIrqTile<S256x128d3> = true;
+template <> constexpr bool kIrqTile<S128x128d3o3> = true;
 template <> constexpr bool kIrqTile<W256x128d4> = true;
 
 // Automatic tile (per-layer sweeps over the trunk's shapes at batch 256 chose these),
@@ -2775,13 +2775,11 @@ hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_
         const bool out8 = (p.y_type == T_INT8 || p.y_type == T_UINT8) && p.vec_store;
         if (gather == GATHER_B8 && out8 && pipe_eligible(gather, p.c, p.k) && p.m < ((int64_t)1 << 31) &&
             (is_1x1 || p.kh * p.kw <= 64)) {
-            // the automatic choice (an explicit tile without the integer variant takes it
-            // too); the 128x128 blocks run two to a CU, whose register budget holds the
-            // integer epilogue (three to a CU would spill)
-            int t = (tile == 8 || tile == 10 || tile == 11 || tile == 16 || tile == 22)
-                        ? tile : pipe_tile_choice(p.m, p.c_out, p.k, false);
-            if (t == 14) t = 10;
+            // the automatic choice (an explicit tile without the integer variant takes it too)
+            const int t = (tile == 8 || tile == 10 || tile == 11 || tile == 14 || tile == 16 || tile == 22)
+                              ? tile : pipe_tile_choice(p.m, p.c_out, p.k, false);
             switch (t) {
+            case 14: return launch_stream<S128x128d3o3>(p, is_1x1, false, false, stream);
             case 8: return launch_stream<S64x128d6>(p, is_1x1, false, false, stream);
             case 10: return launch_stream<S128x128d4>(p, is_1x1, false, false, stream);
             case 11: return launch_stream<S64x256d3>(p, is_1x1, false, false, stream);

@@ -116,9 +116,8 @@ def test_integer_requant_3x3_workload_full_size():
     assert len(np.unique(y.cpu().numpy())) >= 64
 
 
-# the streaming kernel's integer-requantizing block configurations (tiles 8, 10, 11, 16
-# and 22; tile 14 runs as 10), 1x1 and 3x3, on 2 x 9 x 13 pixels: several pixel tiles
-# and a ragged tail
+# the streaming kernel's integer-requantizing block configurations (tiles 8, 10, 11, 14,
+# 16 and 22), 1x1 and 3x3, on 2 x 9 x 13 pixels: several pixel tiles and a ragged tail
 STREAM_TILES = [(8, 1, 64, 64), (8, 3, 64, 64), (10, 1, 128, 128), (10, 3, 64, 192), (11, 1, 64, 64),
                 (11, 3, 128, 64), (14, 1, 256, 128), (14, 3, 128, 128), (16, 1, 256, 256), (16, 3, 64, 256),
                 (22, 1, 256, 512), (22, 3, 64, 512)]
