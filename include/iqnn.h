@@ -280,14 +280,19 @@ iqnn_status iqnn_qconv_prepack(const iqnn_conv_desc *desc, const void *w_host,
  * The packed form, with OCP = C_out rounded up to 256 and KP = K rounded up to 64
  * (K = KH*KW*C_in), is:
  *   int32 bias[OCP]     folded bias per physical output channel
- *   float mult[OCP]     requant multiplier M[c] (1.0 for RAW_INT32)
+ *   float mult[OCP]     requant multiplier M[c] (1.0 for RAW_INT32; M_c * 2^-N_c
+ *                       for IQNN_EPI_INT_REQUANT)
  *   256-byte header:    float m_res at +0; 64 bytes holding the input zero-point
  *                       code (the row the kernel reads for padding) at +64; zeros
  *   int8  w[OCP][KP]    weight codes; row packed_row(c) holds channel c, where for
  *                       c = 32b + 16h + 4j + r, packed_row(c) = 32b + 8j + 4h + r;
  *                       for 4-bit activations the K positions inside every group of
  *                       16 are ordered 0,2,4,6,1,3,5,7,8,10,12,14,9,11,13,15
- *                       (the order the kernel unpacks nibbles in); zero padding.
+ *                       (the order the kernel unpacks nibbles in); zero padding;
+ *   then, for layers the streaming kernel runs, regions whose layout is internal to
+ *   the library (a tile-order copy of the weights -- INT4 weights of 4-bit layers
+ *   kept two to a byte there --, the 2:4 blocks, the BF6 copy of the FP6 path);
+ *   iqnn_qconv_packed_size counts them.
  * The kernel contracts a = q_I - s (s = 128 for UINT8 activations, else 0) with the
  * stored weights b = q_W - s_w (s_w = 128 for UINT8 weights, else 0), so
  *   sum_k (q_I - Z_in)(q_W - Z_w) = sum a*b + (s - Z_in) sum_k b + K (s - Z_in)(s_w - Z_w)

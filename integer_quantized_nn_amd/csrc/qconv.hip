@@ -10,9 +10,11 @@
 // activations on the way into LDS, as the MegEngine article describes for its
 // global->shared load (conv 算子優化, after Fig. 5).
 //
-// gfx950 design shared by both kernels below
-//   * Contraction on v_mfma_i32_32x32x32_i8 (signed int8 only; it sustains ~87 % of
-//     the int8 peak on MI355X, more than the 16x16x64 form).  UINT8 activations
+// gfx950 design shared by the kernels below
+//   * Contraction on v_mfma_i32_32x32x32_i8 (signed int8 only; 32 cycles per
+//     instruction, so 5.0 POP/s at 2.4 GHz on 256 CUs -- a register-only loop
+//     reaches 60-95 % of that, depending on the clock a GPU holds under MFMA
+//     load, and iqnn_probe_mfma_rate measures it).  UINT8 activations
 //     enter the MFMA as q - 128 (XOR 0x80); the host folds +128*sum(W) into the
 //     bias.  4-bit activations are unpacked to int8 on chip (UINT4 zero-extended,
 //     INT4 sign-extended): CDNA4 has no 4-bit integer MFMA, so 4-bit data saves HBM
@@ -24,10 +26,12 @@
 //     h the rows 8j+4h+r; the prepacked weight rows are permuted inside every
 //     32-channel block (the column-permutation identity of the article's Fig. 8) so
 //     those 16 values are 16 consecutive channels: one 16-byte store per pixel.
-//   * 256 threads = 4 waves.  Workgroup ids are remapped so consecutive tiles land
-//     on the same XCD (ids are dealt round-robin over 8 XCDs, each with its own L2).
+//   * 4 or 8 waves per workgroup.  Workgroup ids are remapped so consecutive tiles
+//     land on the same XCD (ids are dealt round-robin over 8 XCDs, each with its own
+//     L2).
 //   * The epilogue runs in registers in strict binary32 (no contraction) with
-//     round-half-to-even, then packs and stores.
+//     round-half-to-even, then packs and stores; the integer-only requantization
+//     is evaluated exactly (see epi_store16).
 //
 // qconv_pipe (8-bit activations, C_in % 64 == 0): a 4-deep ring of LDS stages
 //   filled by global_load_lds_dwordx4 (global -> LDS without registers).  The
