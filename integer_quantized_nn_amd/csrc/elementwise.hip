@@ -12,6 +12,7 @@
 // (v_rndne_f32).  Max pooling is passive ("Quantization" blog, 量化激活函数): the
 // max is taken on codes, which keeps scale and zero point.
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include <stdint.h>
 
 #include "iqnn_internal.h"
@@ -223,12 +224,65 @@ __global__ __launch_bounds__(256) void quantize_pad_kernel(const QuantPadParams 
     }
 }
 
+// The image case of quantize_pad_kernel: 3 channels padded to 4, one scale and zero
+// point, W % 4 == 0 and a 16-byte aligned input.  A workgroup of 64 threads per
+// run of a padded row: on an image row, thread g < W/4 quantizes source pixels
+// 4g .. 4g+3 (48 contiguous bytes, three 16-byte loads) into four padded pixels and
+// thread W/4 writes the row's left and right borders; on a border row every thread
+// writes four pixels of zero-point codes.  The arithmetic per element is
+// quantize_pad_kernel's.
+__global__ __launch_bounds__(64) void quantize_pad3_kernel(const QuantPadParams p, int32_t blocks_per_row) {
+    const int hp = p.h + 2 * p.pad, wp = p.w + 2 * p.pad;
+    const int row = (int)blockIdx.x / blocks_per_row;           // n * hp + y
+    const int g = ((int)blockIdx.x - row * blocks_per_row) * 64 + (int)threadIdx.x;
+    const int n = row / hp, y = row - n * hp;
+    const float s = p.scale[0];
+    const int32_t z = p.zp[0];
+    const uint32_t zb = (uint32_t)z & 0xFFu;
+    const uint32_t zword = zb * 0x01010101u;
+    uint32_t* drow = reinterpret_cast<uint32_t*>(p.q) + (int64_t)row * wp;   // one word per padded pixel
+    const int iy = y - p.pad;
+    if (iy < 0 || iy >= p.h) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (4 * g + k < wp) drow[4 * g + k] = zword;
+        return;
+    }
+    const int groups = p.w / 4;
+    if (g < groups) {
+        const float4* src = reinterpret_cast<const float4*>(p.x + ((int64_t)(n * p.h + iy) * p.w + 4 * g) * 3);
+        const float4 a = src[0], b = src[1], c = src[2];
+        const float v[12] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t q0 = (uint32_t)quant_one(v[3 * k], s, z, p.qmin, p.qmax) & 0xFFu;
+            const uint32_t q1 = (uint32_t)quant_one(v[3 * k + 1], s, z, p.qmin, p.qmax) & 0xFFu;
+            const uint32_t q2 = (uint32_t)quant_one(v[3 * k + 2], s, z, p.qmin, p.qmax) & 0xFFu;
+            drow[p.pad + 4 * g + k] = q0 | (q1 << 8) | (q2 << 16) | (zb << 24);
+        }
+    } else if (g == groups) {
+        for (int xo = 0; xo < p.pad; ++xo) {
+            drow[xo] = zword;
+            drow[p.pad + p.w + xo] = zword;
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_quantize_pad(const QuantPadParams& p, hipStream_t stream) {
     const int64_t total = (int64_t)p.n * (p.h + 2 * p.pad) * (p.w + 2 * p.pad);
     if (total == 0) return hipSuccess;
     if (total >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    if (p.c == 3 && p.c_pad == 4 && !p.per_channel && p.w % 4 == 0 && (reinterpret_cast<uintptr_t>(p.x) & 15) == 0) {
+        const int64_t wp = p.w + 2 * p.pad;
+        const int64_t threads = std::max<int64_t>(p.w / 4 + 1, (wp + 3) / 4);   // per padded row
+        const int64_t bpr = (threads + 63) / 64;
+        const int64_t blocks = (int64_t)p.n * (p.h + 2 * p.pad) * bpr;
+        if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(quantize_pad3_kernel, dim3((unsigned)blocks), dim3(64), 0, stream, p, (int32_t)bpr);
+        return hipGetLastError();
+    }
     const int64_t blocks = (total + 255) / 256;
     hipLaunchKernelGGL(quantize_pad_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
