@@ -135,6 +135,33 @@ def test_stem_fused_max_pooling(n, hw, y_type, epi):
     assert_bytes_equal(y.cpu().numpy(), want, "stem+pool %s" % ((n, hw, y_type, epi),))
 
 
+@pytest.mark.parametrize("kh,kw", [(3, 8), (5, 7), (8, 8)])
+def test_stem_fused_max_pooling_other_filter_sizes(kh, kw):
+    """Stride-2 stems with 3x8, 5x7 and 8x8 filters on the 4-channel input (7 taps are
+    widened to 8): the fused kernel's variant that reads the filter-row count at run
+    time, against the oracle's conv and max pooling, every pooled byte.  The 4-channel
+    gather reads 8 taps per filter row, so the fused path takes widths of 7 and 8 only."""
+    torch = require_gpu()
+    from integer_quantized_nn_amd.layers import QConv
+    n = 2
+    # even stem output height and width, an even input width, whole 16-byte units
+    h = next(v for v in range(30, 40) if ((v - kh) // 2 + 1) % 2 == 0)
+    w = next(v for v in range(64, 80) if v % 2 == 0 and ((v - kw) // 2 + 1) % 2 == 0 and (n * h * v) % 4 == 0)
+    c = synth.conv_case(6000 + 10 * kh + kw, n, h, w, 3, 64, 8, 2, 0, U8, I8, U8, RELU)
+    x, wc, _ = conv_codes(c)
+    wc = np.ascontiguousarray(wc[:, :kh, :kw, :])
+    conv_ref = oracle_conv(c, x, wc, None)
+    want = to_bytes(O.maxpool2d(conv_ref, 3, 2, 1), U8)
+    xp = np.pad(x, ((0, 0), (0, 0), (0, 0), (0, 1)), constant_values=c.z_in)
+    wp = np.pad(wc, ((0, 0), (0, 0), (0, 0), (0, 1)))
+    conv = QConv(n, h, w, 4, 64, kh, 2, 0, U8, I8, U8, RELU, c.z_in, c.z_out, to_bytes(wp, I8), c.bias,
+                 c.s_in, c.s_w, c.s_out, kw=kw)
+    y = conv.conv_maxpool(torch.from_numpy(to_bytes(xp, U8)).cuda())
+    torch.cuda.synchronize()
+    assert y.shape == want.shape
+    assert_bytes_equal(y.cpu().numpy(), want, "stem+pool %dx%d" % (kh, kw))
+
+
 @pytest.mark.parametrize("z_odd", [0, 1])
 @pytest.mark.parametrize("n,hw", [(2, (64, 96)), (3, (28, 224))])
 def test_stem_fused_max_pooling_signed_input(n, hw, z_odd):
