@@ -2,8 +2,9 @@
 
 Default workload: the ResNet-50 conv trunk at batch 256 (224x224x3 input), one
 step = quantize the fp32 input (resident in HBM) -> 53 fused quantized convs
-(Conv_Relu / Conv / Conv_Add_Relu; the stem with the max pooling fused) ->
-dequantize the output.  `value` is whole-step throughput in TOPS (2*M*N*K of every
+(Conv_Relu / Conv / Conv_Add_Relu; the stem with the max pooling fused; where a
+64-channel block ends, its last conv and the next block's first conv as one launch)
+-> dequantize the output.  `value` is whole-step throughput in TOPS (2*M*N*K of every
 conv, K = KH*KW*C_in without padding) over exactly --steps timed steps.
 
 The step runs as three HIP graphs (quantize, the convs, dequantize) replayed back
@@ -496,7 +497,7 @@ def bench_trunk(args, torch, cal):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for _ in range(reps):
-                net.launch_layer(i)
+                net.launch_unit(i)
         g.replay()
         torch.cuda.synchronize()
         best = float("inf")
@@ -528,20 +529,21 @@ def bench_trunk(args, torch, cal):
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int8", "data": "synthetic",
         "config": {"workload": wl_name, "batch": args.batch, "image_hw": 224,
-                   "convs": n_conv, "ops_per_step": step_ops,
+                   "convs": len(tr.layers), "conv_launches": n_conv, "ops_per_step": step_ops,
                    "activations": "uint8 asymmetric per-tensor, stored as int8 bytes q - 128 (zero points Z - 128)",
                    "weights": "int8 per-channel symmetric" + (
                        ", 2:4-pruned after the stem (sparse MFMA; ops counted as the dense 2*M*N*K)" if sparse else ""),
-                   "step": "quantize fp32 input, 53 fused convs + max pooling (fused with the stem), "
-                           "dequantize output; three HIP graphs per step"},
+                   "step": "quantize fp32 input, %d fused convs + max pooling (fused with the stem) in %d "
+                           "launches, dequantize output; three HIP graphs per step" % (len(tr.layers), n_conv)},
         "pct_int8_mfma_peak": value * 1e12 / PEAK_INT8_OPS,
         "pct_measured_mfma": value / cal["mfma_int8_tops"],
         "roofline": roof,
         "conv_time_share": float(conv_s.mean() / (ms_per_step * 1e-3)),
         "layer_classes": layer_classes,
         "per_layer_sum_over_conv_graph": float(per_layer.sum() / conv_s.mean()),
-        "per_layer_us_tops": {l.name: [round(per_layer[i] * 1e6, 1), round(conv_ops[i] / per_layer[i] / 1e12, 1)]
-                              for i, l in enumerate(tr.layers)},
+        "per_layer_us_tops": {net.unit_name(i): [round(per_layer[i] * 1e6, 1),
+                                                 round(conv_ops[i] / per_layer[i] / 1e12, 1)]
+                              for i in range(n_conv)},
         "calibration": cal,
     }
     if not args.no_cpu_baseline:

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define IQNN_ABI_VERSION 4
+#define IQNN_ABI_VERSION 5
 
 typedef enum {
     IQNN_OK = 0,
@@ -336,6 +336,26 @@ iqnn_status iqnn_qconv_fwd_cfg(const iqnn_conv_desc *desc, const void *x_dev,
 iqnn_status iqnn_qconv_maxpool_fwd(const iqnn_conv_desc *desc, const void *x_dev,
                                    const void *packed_dev, void *y_dev, int32_t pool_k,
                                    int32_t pool_stride, int32_t pool_pad, void *stream);
+
+/* Two quantized 1x1 convs where the second reads the first's output: y_a =
+ * conv_a(x) (with res_dev for ADD / ADD_RELU) and y_b = conv_b(y_a), bytes equal to
+ * iqnn_qconv_fwd(desc_a) followed by iqnn_qconv_fwd(desc_b) on y_a.  This is the
+ * hand-off between two bottleneck blocks of the ResNet-50 graph (MegEngine 4-bit
+ * article, 算子融合優化, Fig. 3 and 4: the Conv_Add_Relu that ends a block feeds the
+ * next block's first Conv_Relu and its residual add).  desc_b's input must be
+ * desc_a's output: N, H = OH_a, W = OW_a, C_in = C_out_a, x_type = y_type_a, z_in =
+ * z_out_a (IQNN_ERR_INVALID_ARG otherwise).  Both outputs are written; y_a is also the
+ * next block's residual.  One launch keeps y_a's codes in LDS for conv_b instead of
+ * reading them back from HBM when: both convs are 1x1, stride 1, unpadded; conv_a 64
+ * -> 256 channels with an 8-bit residual (ADD / ADD_RELU); conv_b 256 -> 64 or 128
+ * channels (NONE / RELU); 8-bit activations and outputs, INT8 weights, binary32
+ * requantization.  Every other valid pair runs as the two calls, with their errors.
+ * Pointers and alignment as iqnn_qconv_fwd (packed_a_dev, packed_b_dev from
+ * iqnn_qconv_prepack with desc_a, desc_b). */
+iqnn_status iqnn_qconv_pair_fwd(const iqnn_conv_desc *desc_a, const iqnn_conv_desc *desc_b,
+                                const void *x_dev, const void *packed_a_dev, const void *res_dev,
+                                const void *packed_b_dev, void *y_a_dev, void *y_b_dev,
+                                void *stream);
 
 /* ---------------------------------------------------------------------- GEMM */
 

@@ -83,6 +83,7 @@ def lib():
         "iqnn_qconv_fwd": (I, [CD, P, P, P, P, P]),
         "iqnn_qconv_fwd_cfg": (I, [CD, P, P, P, P, KC, P]),
         "iqnn_qconv_maxpool_fwd": (I, [CD, P, P, P, I32, I32, I32, P]),
+        "iqnn_qconv_pair_fwd": (I, [CD, CD, P, P, P, P, P, P, P]),
         "iqnn_qgemm_packed_size": (SZ, [GD]),
         "iqnn_qgemm_prepack": (I, [GD, P, P, F, P, I, F, F, P, SZ, P]),
         "iqnn_qgemm_prepack_host": (I, [GD, P, P, F, P, I, F, F, P, SZ]),
@@ -206,6 +207,11 @@ def _cfg(cfg):
 def iqnn_qconv_maxpool_fwd(desc, x, packed, y, pool_k, pool_stride, pool_pad, stream=None):
     _check(lib().iqnn_qconv_maxpool_fwd(ctypes.byref(desc), _dev(x), _dev(packed), _dev(y), pool_k, pool_stride,
                                         pool_pad, _stream(stream, y)))
+
+
+def iqnn_qconv_pair_fwd(desc_a, desc_b, x, packed_a, res, packed_b, y_a, y_b, stream=None):
+    _check(lib().iqnn_qconv_pair_fwd(ctypes.byref(desc_a), ctypes.byref(desc_b), _dev(x), _dev(packed_a), _dev(res),
+                                     _dev(packed_b), _dev(y_a), _dev(y_b), _stream(stream, y_b)))
 
 
 def iqnn_qgemm_packed_size(desc):

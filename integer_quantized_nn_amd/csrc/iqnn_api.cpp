@@ -653,6 +653,41 @@ iqnn_status forward_pool(const Layer& L, const void* x, const void* packed, void
     return ok();
 }
 
+// Two 1x1 convs, the second reading the first's output (see iqnn_qconv_pair_fwd): one
+// fused launch where the shapes allow, else the two calls one after the other.
+iqnn_status forward_pair(const Layer& A, const Layer& Bl, const void* x, const void* packed_a, const void* res,
+                         const void* packed_b, void* y_a, void* y_b, hipStream_t stream) {
+    if (Bl.gemm || A.gemm || Bl.n != A.n || Bl.h != A.oh || Bl.w != A.ow || Bl.c != A.c_out ||
+        Bl.x_type != A.y_type || Bl.z_in != A.z_out)
+        return fail(IQNN_ERR_INVALID_ARG,
+                    "the second conv's input (N, H, W, C_in, x_type, z_in) must be the first conv's output");
+    // the checks of both calls before anything is launched
+    const bool add = A.epi == E_ADD || A.epi == E_ADD_RELU;
+    if (!x || !packed_a || !packed_b || !y_a || !y_b)
+        return fail(IQNN_ERR_INVALID_ARG, "null input, packed or output pointer");
+    if (add && !res) return fail(IQNN_ERR_INVALID_ARG, "ADD / ADD_RELU epilogue needs a residual");
+    if (!aligned(x, 16) || !aligned(y_a, 16) || !aligned(y_b, 16) || (add && !aligned(res, 16)))
+        return fail(IQNN_ERR_ALIGNMENT, "activation, output and residual pointers must be 16-byte aligned");
+    if (!aligned(packed_a, 256) || !aligned(packed_b, 256))
+        return fail(IQNN_ERR_ALIGNMENT, "packed buffers must be 256-byte aligned");
+    {
+        ConvParams pa, pb;
+        conv_params(A, x, packed_a, res, y_a, pa);
+        conv_params(Bl, y_a, packed_b, nullptr, y_b, pb);
+        pa.w4 = w4_packed(A);
+        pb.w4 = w4_packed(Bl);
+        if (pair_ok(pa, pb)) {
+            hipError_t e = launch_pair(pa, pb, stream);
+            if (e != hipSuccess) return fail(IQNN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+            return ok();
+        }
+    }
+    // every other pair: the two calls in order
+    iqnn_status s = forward(A, x, packed_a, res, y_a, nullptr, stream);
+    if (s != IQNN_OK) return s;
+    return forward(Bl, y_a, packed_b, nullptr, y_b, nullptr, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -804,6 +839,18 @@ iqnn_status iqnn_qconv_maxpool_fwd(const iqnn_conv_desc* desc, const void* x_dev
     iqnn_status s = conv_layer(desc, &L);
     if (s != IQNN_OK) return s;
     return forward_pool(L, x_dev, packed_dev, y_dev, pool_k, pool_stride, pool_pad,
+                        static_cast<hipStream_t>(stream));
+}
+
+iqnn_status iqnn_qconv_pair_fwd(const iqnn_conv_desc* desc_a, const iqnn_conv_desc* desc_b, const void* x_dev,
+                                const void* packed_a_dev, const void* res_dev, const void* packed_b_dev,
+                                void* y_a_dev, void* y_b_dev, void* stream) {
+    Layer A, Bl;
+    iqnn_status s = conv_layer(desc_a, &A);
+    if (s != IQNN_OK) return s;
+    s = conv_layer(desc_b, &Bl);
+    if (s != IQNN_OK) return s;
+    return forward_pair(A, Bl, x_dev, packed_a_dev, res_dev, packed_b_dev, y_a_dev, y_b_dev,
                         static_cast<hipStream_t>(stream));
 }
 

@@ -131,6 +131,11 @@ hipError_t launch_qconv(const ConvParams& p, int gather, bool is_1x1, hipStream_
 bool stem_pool_ok(const ConvParams& p);
 hipError_t launch_stem_pool(const ConvParams& p, uint8_t* yp, hipStream_t stream);
 
+// Two 1x1 convs over the same pixels, the second reading the first's output
+// (y_b = conv_b(y_a)), in one launch: a.y is written and b.x is ignored.
+bool pair_ok(const ConvParams& a, const ConvParams& b);
+hipError_t launch_pair(const ConvParams& a, const ConvParams& b, hipStream_t stream);
+
 struct QuantParams {
     const float* x;
     uint8_t* q;

@@ -193,10 +193,12 @@ __device__ __forceinline__ uint4 pack_bytes16(const ConvParams& p, const uint32_
 // OUTK: 0 = output type and store width decided at run time; 1 = 8-bit codes, 2 = raw
 // int32, 3 = 4-bit codes, each with 16-channel vector stores (C_out % 16 == 0).  A
 // kernel that keeps most registers busy takes the one branch it needs.
+// kept: with OUTK == 1, also receives the 16 stored bytes (a kernel that consumes its
+// own output keeps them in LDS).
 template <bool BIAS = true, int ADDK = 0, bool INTRQ = false, int OUTK = 0>
 __device__ __forceinline__ void epi_store16(const ConvParams& p, const v16i& acc, const int32_t* bias,
                                             const float* mult, uint32_t rw[4], int ocb, int64_t pix, bool add_rt,
-                                            float m_res, bool irq32 = false) {
+                                            float m_res, bool irq32 = false, uint4* kept = nullptr) {
     const bool add = (ADDK == 1 || ADDK == 3) ? true : (ADDK == 2 ? false : add_rt);
     const int64_t oidx = pix * p.c_out + ocb;   // element index of the first channel
     const bool vec = OUTK != 0 || p.vec_store;
@@ -279,6 +281,7 @@ __device__ __forceinline__ void epi_store16(const ConvParams& p, const v16i& acc
         const uint32_t ow[4] = {pk.x, pk.y, pk.z, pk.w};
         if (vec) {
             *reinterpret_cast<uint4*>(p.y + oidx) = pk;
+            if (OUTK == 1 && kept) *kept = pk;
         } else {
             for (int j = 0; j < 16 && ocb + j < p.c_out; ++j) p.y[oidx + j] = (uint8_t)(ow[j >> 2] >> (8 * (j & 3)));
         }
@@ -1800,6 +1803,239 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
     IQNN_WAIT_VM(0);
 }
 
+// ============================================================ fused 1x1 pair
+// Two 1x1 convolutions over the same pixels, the second reading the first's output:
+// y_a = requant(conv_a(x) + residual), the last conv of a bottleneck block (64 -> 256
+// channels, Conv_Add / Conv_Add_Relu), and y_b = requant(conv_b(y_a)), the first conv
+// of the next block (256 -> CC channels, Conv / Conv_Relu).  y_a is stored for the
+// next block's residual and kept in LDS, 64 channels at a time, as conv_b's activation
+// operand, so conv_b never reads it back from HBM.  Per tile of 128 pixels, stages of
+// one ring:
+//   X      the tile's x rows (128 x 64 bytes): all of conv_a's 256 output channels
+//          (weights resident in LDS) into the accumulators;
+//   R_j    residual channels 64j..64j+63 of the tile: their epilogue, the codes stored
+//          to y_a and kept in LDS;
+//   W_j    conv_b's weights for input channels 64j.. (CC rows x 64 bytes of its
+//          tile-order copy): conv_b's K-step over the kept codes.
+// Every stage is two 1 KB DMA instructions per wave (conv_b's 4 KB of weights when
+// CC = 64 are read twice into the slot), so, as in the streaming kernel, "stage g has
+// landed" is vmcnt <= (kPrNST - 2) * 2 with the stages issued kPrNST - 1 ahead.
+constexpr int kPrCa = 64, kPrCb = 256, kPrBN = 128;   // conv_a C_in and C_out; pixels per tile
+constexpr int kPrNST = 6;                             // ring slots
+constexpr int kPrSlot = 8192;                         // bytes per ring slot
+constexpr int kPrChunks = kPrCb / 64;                 // conv_a's channel blocks = conv_b's K-stages
+constexpr int kPrStages = 1 + 2 * kPrChunks;          // stages per tile
+
+template <int CC>
+__global__ __launch_bounds__(256, 2) void qconv_pair(const ConvParams pa, const ConvParams pb, int32_t n_tiles) {
+    constexpr int K_LOADS = 2, D = kPrNST - 1;
+    constexpr int TB = CC / 64;   // conv_b: 32-channel blocks per wave (waves split CC in two)
+    static_assert(CC == 64 || CC == 128, "conv_b's output channels");
+    static_assert(kPrBN * 64 == 4 * K_LOADS * 1024 && CC * 64 <= kPrSlot, "a stage is two KB per wave");
+    __shared__ __attribute__((aligned(1024))) uint8_t wa[kPrCb * 64];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kPrNST * kPrSlot];
+    __shared__ __attribute__((aligned(1024))) uint8_t codes[kPrBN * 64];
+    __shared__ __attribute__((aligned(16))) int32_t biasa[kPrCb];
+    __shared__ __attribute__((aligned(16))) float multa[kPrCb];
+    __shared__ __attribute__((aligned(16))) int32_t biasb[CC];
+    __shared__ __attribute__((aligned(16))) float multb[CC];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wo = wave & 1, wp = wave >> 1;   // channel half, pixel half of the tile
+    const int G = gridDim.x;
+    const int J = ((int)blockIdx.x < n_tiles) ? (n_tiles - (int)blockIdx.x + G - 1) / G : 0;
+    if (J <= 0) return;
+    auto tile_px0 = [&](int i) -> int64_t { return (int64_t)((int)blockIdx.x + i * G) * kPrBN; };
+
+    biasa[tid] = pa.bias[tid];
+    multa[tid] = pa.mult[tid];
+    if (tid < CC) {
+        biasb[tid] = pb.bias[tid];
+        multb[tid] = pb.mult[tid];
+    }
+    __syncthreads();
+    // conv_a's weights: one K-stage, so its tile-order copy is the 16 KB LDS image
+    {
+        const void* src[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) src[i] = pa.w_tiled + (wave * 4 + i) * 1024 + lane * 16;
+        dma16_seq<4>(lds_addr(wa) + wave * 4096, src);
+    }
+
+    // ------------------------------------------------------------ issue side
+    // X and R stages: rows are pixels, lane -> row 16i + lane/4 of the wave's 32, slot
+    // lane%4 holding 16-byte segment slot ^ swz(row) (the fragment reads undo it)
+    const uint32_t ring0 = lds_addr(ring);
+    int is_i = 0, is_k = 0, is_slot = 0;
+    int64_t rowpix[K_LOADS];
+    int seg[K_LOADS];
+    auto set_rows = [&](int i) {
+#pragma unroll
+        for (int ii = 0; ii < K_LOADS; ++ii) {
+            const int row = (wave * K_LOADS + ii) * 16 + (lane >> 2);
+            const int64_t pix = tile_px0(i) + row;
+            rowpix[ii] = pix < pa.m ? pix : pa.m - 1;
+            seg[ii] = ((lane & 3) ^ swz(row)) * 16;
+        }
+    };
+    set_rows(0);
+    auto issue = [&]() {
+        const void* src[K_LOADS];
+        if (is_k == 0) {   // x rows of the tile
+#pragma unroll
+            for (int ii = 0; ii < K_LOADS; ++ii) src[ii] = pa.x + rowpix[ii] * kPrCa + seg[ii];
+        } else {
+            const int j = (is_k - 1) >> 1;
+            if (is_k & 1) {   // residual channels 64j..
+#pragma unroll
+                for (int ii = 0; ii < K_LOADS; ++ii) src[ii] = pa.res + rowpix[ii] * kPrCb + 64 * j + seg[ii];
+            } else {          // conv_b's weight rows for input channels 64j.., 1 KB pieces
+#pragma unroll
+                for (int ii = 0; ii < K_LOADS; ++ii) {
+                    const int q = (wave * K_LOADS + ii) & (CC / 16 - 1);   // piece of the CC x 64 image
+                    src[ii] = pb.w_tiled + ((int64_t)((q >> 2) * kPrChunks + j) * 4096) + (q & 3) * 1024 + lane * 16;
+                }
+            }
+        }
+        dma16_seq<K_LOADS>(ring0 + is_slot * kPrSlot + wave * K_LOADS * 1024, src);
+        is_slot = is_slot + 1 == kPrNST ? 0 : is_slot + 1;
+        // advance; past the last stage the cursor stays there (it is issued again into
+        // the next slot, keeping every stage's DMA count)
+        if (is_k + 1 < kPrStages) {
+            ++is_k;
+        } else if (is_i + 1 < J) {
+            ++is_i;
+            is_k = 0;
+            set_rows(is_i);
+        }
+    };
+    // the LDS stores and reads of a stage stay on their side of its barrier (the DMA's
+    // asm statements after it carry memory clobbers; this one holds the stores before)
+    auto sync = [&]() {
+        asm volatile("" ::: "memory");
+        IQNN_WAIT_VM_LGKM0((D - 1) * K_LOADS);
+        __builtin_amdgcn_s_barrier();
+        issue();
+    };
+
+    // ------------------------------------------------------------ compute side
+    const int frow = lane & 31;
+    const int foff[2] = {frow * 64 + (((lane >> 5) + 0) ^ swz(frow)) * 16,
+                         frow * 64 + (((lane >> 5) + 2) ^ swz(frow)) * 16};
+    const int hl = (lane >> 5) * 16;   // the lane's 16 channels within a 32-channel block
+    v16i acca[kPrChunks][2], accb[TB][2];
+
+    for (int i = 0; i < D; ++i) issue();
+    const float m_res = *pa.m_res;
+    int slot = 0;   // ring slot of the stage being consumed
+    auto next_slot = [&]() { slot = slot + 1 == kPrNST ? 0 : slot + 1; };
+    for (int it = 0; it < J; ++it) {
+        const int64_t px0 = tile_px0(it);
+        sync();   // X: the tile's x rows
+        {
+            const uint8_t* xt = ring + slot * kPrSlot;
+#pragma unroll
+            for (int j = 0; j < kPrChunks; ++j) {
+                const int ca = 64 * j + 32 * wo + hl;
+                v16i b;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) b[q] = biasa[ca + q];
+                acca[j][0] = b;
+                acca[j][1] = b;
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                v4i fb[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    fb[u] = *reinterpret_cast<const v4i*>(xt + (64 * wp + 32 * u) * 64 + foff[kk]);
+                    fb[u][0] ^= pa.x_xor; fb[u][1] ^= pa.x_xor; fb[u][2] ^= pa.x_xor; fb[u][3] ^= pa.x_xor;
+                }
+#pragma unroll
+                for (int j = 0; j < kPrChunks; ++j) {
+                    const v4i fa = *reinterpret_cast<const v4i*>(wa + (64 * j + 32 * wo) * 64 + foff[kk]);
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        acca[j][u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa, fb[u], acca[j][u], 0, 0, 0);
+                }
+            }
+        }
+        next_slot();
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+            const int ob = wo * (CC / 2) + 32 * t + hl;
+            v16i b;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) b[q] = biasb[ob + q];
+            accb[t][0] = b;
+            accb[t][1] = b;
+        }
+#pragma unroll
+        for (int j = 0; j < kPrChunks; ++j) {
+            sync();   // R_j: the residual channels
+            {
+                const uint8_t* rt = ring + slot * kPrSlot;
+                const int ocl = 32 * wo + hl;   // channel within the 64-channel block
+                float mult[16];
+#pragma unroll
+                for (int q = 0; q < 16; ++q) mult[q] = multa[64 * j + ocl + q];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int pl = 64 * wp + 32 * u + frow;
+                    const int64_t pix = px0 + pl;
+                    if (pix < pa.m) {
+                        const uint4 rv = *reinterpret_cast<const uint4*>(rt + pl * 64 + (((ocl >> 4) ^ swz(pl)) << 4));
+                        uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
+                        uint4 pk;
+                        epi_store16<false, 1, false, 1>(pa, acca[j][u], nullptr, mult, rw, 64 * j + ocl, pix, true,
+                                                        m_res, false, &pk);
+                        *reinterpret_cast<uint4*>(codes + pl * 64 + (((ocl >> 4) ^ swz(pl)) << 4)) = pk;
+                    }
+                }
+            }
+            next_slot();
+            sync();   // W_j: conv_b's weights for these 64 input channels; the codes are complete
+            {
+                const uint8_t* wt = ring + slot * kPrSlot;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    v4i fb[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        fb[u] = *reinterpret_cast<const v4i*>(codes + (64 * wp + 32 * u) * 64 + foff[kk]);
+                        fb[u][0] ^= pb.x_xor; fb[u][1] ^= pb.x_xor; fb[u][2] ^= pb.x_xor; fb[u][3] ^= pb.x_xor;
+                    }
+#pragma unroll
+                    for (int t = 0; t < TB; ++t) {
+                        const v4i fa = *reinterpret_cast<const v4i*>(wt + (wo * (CC / 2) + 32 * t) * 64 + foff[kk]);
+#pragma unroll
+                        for (int u = 0; u < 2; ++u)
+                            accb[t][u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa, fb[u], accb[t][u], 0, 0, 0);
+                    }
+                }
+            }
+            next_slot();
+        }
+        // conv_b's epilogue
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+            const int ob = wo * (CC / 2) + 32 * t + hl;
+            float mult[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) mult[q] = multb[ob + q];
+            uint32_t rw[4] = {0, 0, 0, 0};
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int64_t pix = px0 + 64 * wp + 32 * u + frow;
+                if (pix < pb.m) epi_store16<false, 2, false, 1>(pb, accb[t][u], nullptr, mult, rw, ob, pix, false, 0.0f);
+            }
+        }
+    }
+    // no DMA may still be writing this workgroup's LDS when it ends
+    IQNN_WAIT_VM(0);
+}
+
 // Persistent schedule of the streaming kernel over the 8 XCDs (workgroup ids are dealt
 // round-robin, so workgroup i runs on XCD i % 8).  The channel tiles are split into
 // xo_groups groups (1, 2, 4 or 8, dividing the tile count) and the pixel tiles into
@@ -2421,6 +2657,32 @@ hipError_t launch_stem_pool(const ConvParams& p, uint8_t* yp, hipStream_t stream
 #undef IQNN_STEM_POOL_NW
     default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+// The fused 1x1 pair's conditions (see qconv_pair): both 1x1, stride 1, unpadded, over
+// the same pixels (below 2^31); conv_a 64 -> 256 channels with an 8-bit residual
+// (Conv_Add / Conv_Add_Relu), conv_b 256 -> 64 or 128 channels (Conv / Conv_Relu);
+// 8-bit activations and outputs, symmetric dense int8 weights, the binary32
+// requantization.
+bool pair_ok(const ConvParams& a, const ConvParams& b) {
+    auto plain1x1 = [](const ConvParams& p) {
+        return p.kh == 1 && p.kw == 1 && p.sh == 1 && p.sw == 1 && p.ph == 0 && p.pw == 0 && p.vec_store &&
+               p.zw_red == 0 && !p.int_rq && !p.w_idx && !p.w4 && !p.f6 &&
+               (p.y_type == T_INT8 || p.y_type == T_UINT8);
+    };
+    if (!plain1x1(a) || !plain1x1(b) || a.m != b.m || a.m <= 0 || a.m >= ((int64_t)1 << 31)) return false;
+    if (a.c != kPrCa || a.c_out != kPrCb || b.c != kPrCb || (b.c_out != 64 && b.c_out != 128)) return false;
+    if ((a.epi != E_ADD && a.epi != E_ADD_RELU) || (a.res_type != T_INT8 && a.res_type != T_UINT8)) return false;
+    return b.epi == E_NONE || b.epi == E_RELU;
+}
+
+hipError_t launch_pair(const ConvParams& a, const ConvParams& b, hipStream_t stream) {
+    if (!pair_ok(a, b)) return hipErrorInvalidValue;
+    const int64_t n_tiles = (a.m + kPrBN - 1) / kPrBN;
+    const int grid = (int)std::min<int64_t>(n_tiles, 512);   // two workgroups per CU, persistent
+    if (b.c_out == 64) hipLaunchKernelGGL((qconv_pair<64>), dim3(grid), dim3(256), 0, stream, a, b, (int32_t)n_tiles);
+    else hipLaunchKernelGGL((qconv_pair<128>), dim3(grid), dim3(256), 0, stream, a, b, (int32_t)n_tiles);
     return hipGetLastError();
 }
 

@@ -130,6 +130,17 @@ class QConv:
         return out
 
 
+def conv_pair(conv_a, conv_b, x, res=None, out_a=None, out_b=None, stream=None):
+    """y_a = conv_a(x, res) and y_b = conv_b(y_a) in one call (iqnn_qconv_pair_fwd):
+    conv_b's input is conv_a's output.  Returns (y_a, y_b)."""
+    if out_a is None:
+        out_a = empty_codes(conv_a.out_shape, conv_a.y_type, x.device)
+    if out_b is None:
+        out_b = empty_codes(conv_b.out_shape, conv_b.y_type, x.device)
+    B.iqnn_qconv_pair_fwd(conv_a.desc, conv_b.desc, x, conv_a.packed, res, conv_b.packed, out_a, out_b, stream)
+    return out_a, out_b
+
+
 class QGemm:
     """One prepacked quantized GEMM: C[M][N] = epilogue(A[M][K] B[N][K]^T)."""
 

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert B.iqnn_abi_version() == 4
+    assert B.iqnn_abi_version() == 5
     assert lib.iqnn_status_str(0) == b"IQNN_OK"
     assert lib.iqnn_status_str(4) == b"IQNN_ERR_OVERFLOW"
 
