@@ -284,6 +284,30 @@ def make_layer(torch, wl, cfg=None):
         rec.update(ops=c.ops(n, h, w), nbytes=xd.numel() + 64 * 7 * 7 * 4 + int(np.prod(pshape)),
                    ins=[(xd, None)], out_shape=pshape, out_type=synth.INT8,
                    run=lambda i, o: layer.conv_maxpool(rec["ins"][i][0], out=o))
+    elif wl == "resnet50_l1_pair":
+        # the hand-off between two stage-1 bottleneck blocks of the trunk, batch 256 on
+        # 56x56: 1x1 64 -> 256 with the residual add and ReLU, then the next block's 1x1
+        # 256 -> 64 with ReLU on its output, one launch (iqnn_qconv_pair_fwd); the timed
+        # output is the second conv's, the first's is written to its own buffer
+        from integer_quantized_nn_amd.layers import conv_pair, empty_codes
+        U8, I8 = synth.UINT8, synth.INT8
+        a = synth.conv_case(35, 256, 56, 56, 64, 256, 1, 1, 0, U8, I8, U8, synth.EPI_ADD_RELU, res_type=U8,
+                            name="l1_c3")
+        b = synth.conv_case(36, 256, 56, 56, 256, 64, 1, 1, 0, U8, I8, U8, synth.EPI_RELU, name="l1_c1")
+        wa = quantize(torch.from_numpy(a.w).cuda(), a.s_w, 0, I8, axis=0).cpu().numpy()
+        wb = quantize(torch.from_numpy(b.w).cuda(), b.s_w, 0, I8, axis=0).cpu().numpy()
+        conv_a = QConv(256, 56, 56, 64, 256, 1, 1, 0, U8, I8, U8, a.epi, a.z_in, a.z_out, wa, a.bias, a.s_in, a.s_w,
+                       a.s_out, res_type=U8, z_res=a.z_res, s_res=a.s_res)
+        conv_b = QConv(256, 56, 56, 256, 64, 1, 1, 0, U8, I8, U8, b.epi, a.z_out, b.z_out, wb, b.bias, a.s_out,
+                       b.s_w, b.s_out)
+        xd = quantize(torch.from_numpy(a.x).cuda(), a.s_in, a.z_in, U8)
+        rd = quantize(torch.from_numpy(a.res).cuda(), a.s_res, a.z_res, U8)
+        ya = empty_codes(conv_a.out_shape, U8)
+        m = 256 * 56 * 56
+        rec.update(ops=2 * m * 256 * 64 * 2, nbytes=m * (64 + 256 + 256 + 64) + 2 * 256 * 64,
+                   ins=[(xd, rd)], out_shape=conv_b.out_shape, out_type=U8,
+                   run=lambda i, o: conv_pair(conv_a, conv_b, rec["ins"][i][0], res=rec["ins"][i][1], out_a=ya,
+                                              out_b=o))
     elif wl in ("vitl_fc1", "vitl_fc1_2of4", "gemm_int8_256"):
         sparse = wl == "vitl_fc1_2of4"   # weights magnitude-pruned to 2:4 along K, on the sparse MFMA
         g = synth.vitl_fc1(sparse_2of4=sparse) if wl.startswith("vitl") else synth.gemm_int8_256()
@@ -579,7 +603,7 @@ def main():
                     choices=["resnet50_trunk", "resnet50_trunk_2of4", "conv3x3_int8", "conv3x3_2of4", "conv3x3_4bit",
                              "conv3x3_4bit_fp6", "conv3x3_uint8w", "conv3x3_intrq", "resnet50_l3_conv3x3",
                              "resnet50_stem_pool", "conv1x1_int8", "conv1x1_intrq", "resnet50_l3_conv3x3_intrq",
-                             "vitl_fc1", "vitl_fc1_2of4", "gemm_int8_256"])
+                             "resnet50_l1_pair", "vitl_fc1", "vitl_fc1_2of4", "gemm_int8_256"])
     ap.add_argument("--cold", action="store_true",
                     help="single-layer workloads: rotate input/output sets (> 256 MB) so every launch misses the caches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
