@@ -1817,22 +1817,27 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
 //          to y_a and kept in LDS;
 //   W_j    conv_b's weights for input channels 64j.. (CC rows x 64 bytes of its
 //          tile-order copy): conv_b's K-step over the kept codes.
-// Every stage is two 1 KB DMA instructions per wave (conv_b's 4 KB of weights when
-// CC = 64 are read twice into the slot), so, as in the streaming kernel, "stage g has
-// landed" is vmcnt <= (kPrNST - 2) * 2 with the stages issued kPrNST - 1 ahead.
+// With CC = 64 conv_b's 16 KB of weights stay in LDS instead (and conv_a's fragments
+// in registers, 32 per lane, which keeps the LDS at two workgroups per CU), so the ring
+// carries only the X and R stages -- all of them HBM reads -- and a plain barrier hands
+// each block of codes to conv_b.  Every stage is two 1 KB DMA instructions per wave, so,
+// as in the streaming kernel, "stage g has landed" is vmcnt <= (kPrNST - 2) * 2 with the
+// stages issued kPrNST - 1 ahead.
 constexpr int kPrCa = 64, kPrCb = 256, kPrBN = 128;   // conv_a C_in and C_out; pixels per tile
 constexpr int kPrNST = 6;                             // ring slots
 constexpr int kPrSlot = 8192;                         // bytes per ring slot
 constexpr int kPrChunks = kPrCb / 64;                 // conv_a's channel blocks = conv_b's K-stages
-constexpr int kPrStages = 1 + 2 * kPrChunks;          // stages per tile
 
 template <int CC>
 __global__ __launch_bounds__(256, 2) void qconv_pair(const ConvParams pa, const ConvParams pb, int32_t n_tiles) {
     constexpr int K_LOADS = 2, D = kPrNST - 1;
     constexpr int TB = CC / 64;   // conv_b: 32-channel blocks per wave (waves split CC in two)
+    constexpr bool WRES = CC == 64;   // conv_b's weights resident, conv_a's in registers
+    constexpr int STAGES = WRES ? 1 + kPrChunks : 1 + 2 * kPrChunks;   // ring stages per tile
     static_assert(CC == 64 || CC == 128, "conv_b's output channels");
     static_assert(kPrBN * 64 == 4 * K_LOADS * 1024 && CC * 64 <= kPrSlot, "a stage is two KB per wave");
-    __shared__ __attribute__((aligned(1024))) uint8_t wa[kPrCb * 64];
+    __shared__ __attribute__((aligned(1024))) uint8_t wa[WRES ? 16 : kPrCb * 64];
+    __shared__ __attribute__((aligned(1024))) uint8_t wb[WRES ? kPrChunks * CC * 64 : 16];   // [K-stage][CC rows][64]
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kPrNST * kPrSlot];
     __shared__ __attribute__((aligned(1024))) uint8_t codes[kPrBN * 64];
     __shared__ __attribute__((aligned(16))) int32_t biasa[kPrCb];
@@ -1855,12 +1860,14 @@ __global__ __launch_bounds__(256, 2) void qconv_pair(const ConvParams pa, const 
         multb[tid] = pb.mult[tid];
     }
     __syncthreads();
-    // conv_a's weights: one K-stage, so its tile-order copy is the 16 KB LDS image
+    // conv_a's weights have one K-stage, so its tile-order copy is their 16 KB LDS image;
+    // conv_b's (CC = 64: one row block) are four 4 KB blocks, one per K-stage, in order
     {
+        const int8_t* wsrc = WRES ? pb.w_tiled : pa.w_tiled;
         const void* src[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) src[i] = pa.w_tiled + (wave * 4 + i) * 1024 + lane * 16;
-        dma16_seq<4>(lds_addr(wa) + wave * 4096, src);
+        for (int i = 0; i < 4; ++i) src[i] = wsrc + (wave * 4 + i) * 1024 + lane * 16;
+        dma16_seq<4>(lds_addr(WRES ? wb : wa) + wave * 4096, src);
     }
 
     // ------------------------------------------------------------ issue side
@@ -1886,8 +1893,8 @@ __global__ __launch_bounds__(256, 2) void qconv_pair(const ConvParams pa, const 
 #pragma unroll
             for (int ii = 0; ii < K_LOADS; ++ii) src[ii] = pa.x + rowpix[ii] * kPrCa + seg[ii];
         } else {
-            const int j = (is_k - 1) >> 1;
-            if (is_k & 1) {   // residual channels 64j..
+            const int j = WRES ? is_k - 1 : (is_k - 1) >> 1;
+            if (WRES || (is_k & 1)) {   // residual channels 64j..
 #pragma unroll
                 for (int ii = 0; ii < K_LOADS; ++ii) src[ii] = pa.res + rowpix[ii] * kPrCb + 64 * j + seg[ii];
             } else {          // conv_b's weight rows for input channels 64j.., 1 KB pieces
@@ -1902,7 +1909,7 @@ __global__ __launch_bounds__(256, 2) void qconv_pair(const ConvParams pa, const 
         is_slot = is_slot + 1 == kPrNST ? 0 : is_slot + 1;
         // advance; past the last stage the cursor stays there (it is issued again into
         // the next slot, keeping every stage's DMA count)
-        if (is_k + 1 < kPrStages) {
+        if (is_k + 1 < STAGES) {
             ++is_k;
         } else if (is_i + 1 < J) {
             ++is_i;
@@ -1925,6 +1932,15 @@ __global__ __launch_bounds__(256, 2) void qconv_pair(const ConvParams pa, const 
                          frow * 64 + (((lane >> 5) + 2) ^ swz(frow)) * 16};
     const int hl = (lane >> 5) * 16;   // the lane's 16 channels within a 32-channel block
     v16i acca[kPrChunks][2], accb[TB][2];
+    // WRES: conv_a's A fragments, row 64j + 32 wo + frow of its tile-order copy (block j)
+    v4i waf[WRES ? kPrChunks : 1][2];
+    if constexpr (WRES) {
+#pragma unroll
+        for (int j = 0; j < kPrChunks; ++j)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                waf[j][kk] = *reinterpret_cast<const v4i*>(pa.w_tiled + j * 4096 + 32 * wo * 64 + foff[kk]);
+    }
 
     for (int i = 0; i < D; ++i) issue();
     const float m_res = *pa.m_res;
@@ -1954,7 +1970,7 @@ __global__ __launch_bounds__(256, 2) void qconv_pair(const ConvParams pa, const 
                 }
 #pragma unroll
                 for (int j = 0; j < kPrChunks; ++j) {
-                    const v4i fa = *reinterpret_cast<const v4i*>(wa + (64 * j + 32 * wo) * 64 + foff[kk]);
+                    const v4i fa = WRES ? waf[j][kk] : *reinterpret_cast<const v4i*>(wa + (64 * j + 32 * wo) * 64 + foff[kk]);
 #pragma unroll
                     for (int u = 0; u < 2; ++u)
                         acca[j][u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa, fb[u], acca[j][u], 0, 0, 0);
@@ -1995,9 +2011,16 @@ __global__ __launch_bounds__(256, 2) void qconv_pair(const ConvParams pa, const 
                 }
             }
             next_slot();
-            sync();   // W_j: conv_b's weights for these 64 input channels; the codes are complete
+            if constexpr (WRES) {   // the codes are complete: LDS stores done, then the barrier
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt left at their maximum
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+            } else {
+                sync();   // W_j: conv_b's weights for these 64 input channels; the codes are complete
+            }
             {
-                const uint8_t* wt = ring + slot * kPrSlot;
+                const uint8_t* wt = WRES ? wb + j * CC * 64 : ring + slot * kPrSlot;
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
                     v4i fb[2];
@@ -2015,7 +2038,7 @@ __global__ __launch_bounds__(256, 2) void qconv_pair(const ConvParams pa, const 
                     }
                 }
             }
-            next_slot();
+            if constexpr (!WRES) next_slot();
         }
         // conv_b's epilogue
 #pragma unroll
