@@ -121,6 +121,34 @@ def test_fused_conv_pool_rejects_other_shapes_before_launch(lib):
     assert lib.iqnn_qconv_maxpool_fwd(ctypes.byref(stem), P(4096), P(4096), None, 3, 2, 1, None) == 1
 
 
+def test_pair_validated_before_launch(lib):
+    """iqnn_qconv_pair_fwd checks both descriptors, that the second takes the first's
+    output (N, H, W, C_in, type, zero point), and every pointer of both calls before
+    anything is launched (fake device addresses here: a launch would fail otherwise)."""
+    P = ctypes.c_void_p
+    a = conv_desc(n=2, h=7, w=9, c_in=64, c_out=256, kh=1, kw=1, pad_h=0, pad_w=0, epilogue=B.EPI_ADD_RELU,
+                  z_out=5)
+    b = conv_desc(n=2, h=7, w=9, c_in=256, c_out=64, kh=1, kw=1, pad_h=0, pad_w=0, z_in=5)
+    x, pk, r, y = P(4096), P(8192), P(4096), P(4096)
+
+    def call(da, db, *ptrs):
+        return lib.iqnn_qconv_pair_fwd(ctypes.byref(da), ctypes.byref(db), *ptrs, None)
+
+    for bad in (dict(c_in=128), dict(h=8), dict(n=3), dict(z_in=6), dict(x_type=B.INT8)):
+        kb = dict(n=2, h=7, w=9, c_in=256, c_out=64, kh=1, kw=1, pad_h=0, pad_w=0, z_in=5)
+        kb.update(bad)
+        assert call(a, conv_desc(**kb), x, pk, r, pk, y, y) == 1, bad
+        assert "first conv's output" in lib.iqnn_last_error().decode()
+    assert call(a, b, x, pk, None, pk, y, y) == 1                       # ADD_RELU without residual
+    assert call(a, b, x, pk, r, None, y, y) == 1                        # second packed buffer
+    assert call(a, b, x, pk, r, pk, y, None) == 1                       # second output
+    assert call(a, b, P(4100), pk, r, pk, y, y) == 3                    # misaligned x
+    assert call(a, b, x, pk, r, pk, y, P(4104)) == 3                    # misaligned second output
+    assert call(a, b, x, pk, r, P(8208), y, y) == 3                     # second packed not 256-aligned
+    assert call(conv_desc(n=0), b, x, pk, r, pk, y, y) == 1             # invalid first descriptor
+    assert call(a, conv_desc(c_out=0), x, pk, r, pk, y, y) == 1         # invalid second descriptor
+
+
 def test_empty_and_oversized_inputs(lib):
     P = ctypes.c_void_p
     # empty tensors: nothing to read or write, no launch, no pointer needed
