@@ -32,11 +32,11 @@ def _codes(tr):
     return x, w
 
 
-def _run_gpu(tr, x, w, offset=False, sparse=False):
+def _run_gpu(tr, x, w, offset=False, sparse=False, fuse_pairs=True):
     import torch
     from integer_quantized_nn_amd.resnet50 import QuantResNet50Trunk
     net = QuantResNet50Trunk(tr, weight_codes={k: O.pack(v, O.INT8) for k, v in w.items()}, offset_codes=offset,
-                             sparse_2of4=sparse)
+                             sparse_2of4=sparse, fuse_pairs=fuse_pairs)
     # the trunk's input buffer is the image with the stem's border and a 4th channel,
     # all holding the input zero-point code
     p = net.stem_pad
@@ -47,15 +47,18 @@ def _run_gpu(tr, x, w, offset=False, sparse=False):
     return net
 
 
-@pytest.mark.parametrize("offset", [False, True], ids=["uint8", "offset_int8"])
-def test_trunk_every_layer_small_batch(offset):
+@pytest.mark.parametrize("offset,fuse", [(False, True), (True, True), (True, False)],
+                         ids=["uint8", "offset_int8", "offset_int8_unfused"])
+def test_trunk_every_layer_small_batch(offset, fuse):
     """Batch 2 at 224x224: every intermediate tensor of both images, byte for byte.
     With offset codes (uint8 code q stored as the int8 byte q - 128, zero points
-    shifted alike) every buffer holds the uint8 oracle's bytes XOR 0x80."""
+    shifted alike) every buffer holds the uint8 oracle's bytes XOR 0x80.  The trunk
+    runs its block hand-offs fused (one launch per pair) or as separate launches."""
     require_gpu()
     tr = synth.resnet50_trunk(seed=3, batch=2)
     x, w = _codes(tr)
-    net = _run_gpu(tr, x, w, offset)
+    net = _run_gpu(tr, x, w, offset, fuse_pairs=fuse)
+    assert len(net.units) == (50 if fuse else 53)
     ref = oracle_trunk(tr, x, w, [0, 1])
     flip = np.uint8(0x80 if offset else 0)
     for name, buf in net.bufs.items():
