@@ -1137,8 +1137,10 @@ struct StreamCfg {
 // contraction accumulates 16 * acc; the accumulators start from 16 * bias and are
 // shifted right by 4 before the epilogue, which is exact (every term is a multiple
 // of 16).
+// XS: the activation fragments take the uint8 sign flip (XOR with x_xor); false for
+// signed 8-bit codes (x_xor == 0), whose fragments are MFMA operands as they are.
 template <class C, bool IS1X1, bool RES, bool C4, bool B4 = false, bool ZW = false, bool SP = false,
-          bool F6 = false, int OUTK = 0, bool S4 = false, bool W4 = false>
+          bool F6 = false, int OUTK = 0, bool S4 = false, bool W4 = false, bool XS = true>
 __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvParams p) {
     constexpr int BM = C::BM, BN = C::BN, WM = C::WM, NST = C::NST, NW = C::NW;
     constexpr int TM = C::TM, TN = C::TN;
@@ -1174,6 +1176,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
     static_assert(R_INST <= K_LOADS, "a residual tile fits one stage");
     static_assert(!(RES && C4), "the 4-channel gather has no residual stage");
     static_assert(!(ZW && (B4 || C4)), "the per-pixel weight zero-point term needs the 8-bit gather");
+    static_assert(XS || !(B4 || SP || ZW || F6), "signed activations without the sign flip: the dense 8-bit path");
     static_assert(!RES || RROW == 32 || RROW == 64 || RROW == 128, "residual rows of 2, 4 or 8 chunks");
 
     __shared__ __attribute__((aligned(1024))) uint8_t ring[NST * STAGE];
@@ -1517,7 +1520,9 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
                 fb[u][0] = (int)unpack_lo(w0, x_signed4); fb[u][1] = (int)unpack_hi(w0, x_signed4);
                 fb[u][2] = (int)unpack_lo(w1, x_signed4); fb[u][3] = (int)unpack_hi(w1, x_signed4);
             } else {
-                fb[u][0] ^= bxor; fb[u][1] ^= bxor; fb[u][2] ^= bxor; fb[u][3] ^= bxor;
+                if constexpr (XS) {
+                    fb[u][0] ^= bxor; fb[u][1] ^= bxor; fb[u][2] ^= bxor; fb[u][3] ^= bxor;
+                }
                 if constexpr (ZW) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) ssum[u] = __builtin_amdgcn_sdot4(fb[u][i], 0x01010101, ssum[u], false);
@@ -1828,7 +1833,9 @@ constexpr int kPrNST = 6;                             // ring slots
 constexpr int kPrSlot = 8192;                         // bytes per ring slot
 constexpr int kPrChunks = kPrCb / 64;                 // conv_a's channel blocks = conv_b's K-stages
 
-template <int CC>
+// XS: the 8-bit activations (x and the kept codes) take the uint8 sign flip; false when
+// both are signed codes (x_xor == 0 for both convs).
+template <int CC, bool XS>
 __global__ __launch_bounds__(256, 2) void qconv_pair(const ConvParams pa, const ConvParams pb, int32_t n_tiles) {
     constexpr int K_LOADS = 2, D = kPrNST - 1;
     constexpr int TB = CC / 64;   // conv_b: 32-channel blocks per wave (waves split CC in two)
@@ -1966,7 +1973,7 @@ __global__ __launch_bounds__(256, 2) void qconv_pair(const ConvParams pa, const 
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     fb[u] = *reinterpret_cast<const v4i*>(xt + (64 * wp + 32 * u) * 64 + foff[kk]);
-                    fb[u][0] ^= pa.x_xor; fb[u][1] ^= pa.x_xor; fb[u][2] ^= pa.x_xor; fb[u][3] ^= pa.x_xor;
+                    if constexpr (XS) { fb[u][0] ^= pa.x_xor; fb[u][1] ^= pa.x_xor; fb[u][2] ^= pa.x_xor; fb[u][3] ^= pa.x_xor; }
                 }
 #pragma unroll
                 for (int j = 0; j < kPrChunks; ++j) {
@@ -2027,7 +2034,7 @@ __global__ __launch_bounds__(256, 2) void qconv_pair(const ConvParams pa, const 
 #pragma unroll
                     for (int u = 0; u < 2; ++u) {
                         fb[u] = *reinterpret_cast<const v4i*>(codes + (64 * wp + 32 * u) * 64 + foff[kk]);
-                        fb[u][0] ^= pb.x_xor; fb[u][1] ^= pb.x_xor; fb[u][2] ^= pb.x_xor; fb[u][3] ^= pb.x_xor;
+                        if constexpr (XS) { fb[u][0] ^= pb.x_xor; fb[u][1] ^= pb.x_xor; fb[u][2] ^= pb.x_xor; fb[u][3] ^= pb.x_xor; }
                     }
 #pragma unroll
                     for (int t = 0; t < TB; ++t) {
@@ -2186,6 +2193,26 @@ hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bo
                 hipLaunchKernelGGL((qconv_stream<C, true, false, false, false, false, false, false, 4>), g, b, 0, stream, q);
             else
                 hipLaunchKernelGGL((qconv_stream<C, false, false, false, false, false, false, false, 4>), g, b, 0, stream, q);
+            return hipGetLastError();
+        }
+    }
+    // signed 8-bit activations on the automatic choice's configurations: no sign flip
+    if constexpr (kIrqTile<C>) {
+        if (out8 && p.x_xor == 0u && !(add && !kResStage)) {
+            if constexpr (kResStage) {
+                if (add && is_1x1)
+                    hipLaunchKernelGGL((qconv_stream<C, true, true, false, false, false, false, false, 1, false, false, false>),
+                                       g, b, 0, stream, q);
+                else if (add)
+                    hipLaunchKernelGGL((qconv_stream<C, false, true, false, false, false, false, false, 1, false, false, false>),
+                                       g, b, 0, stream, q);
+            }
+            if (!add && is_1x1)
+                hipLaunchKernelGGL((qconv_stream<C, true, false, false, false, false, false, false, 1, false, false, false>),
+                                   g, b, 0, stream, q);
+            else if (!add)
+                hipLaunchKernelGGL((qconv_stream<C, false, false, false, false, false, false, false, 1, false, false, false>),
+                                   g, b, 0, stream, q);
             return hipGetLastError();
         }
     }
@@ -2704,8 +2731,14 @@ hipError_t launch_pair(const ConvParams& a, const ConvParams& b, hipStream_t str
     if (!pair_ok(a, b)) return hipErrorInvalidValue;
     const int64_t n_tiles = (a.m + kPrBN - 1) / kPrBN;
     const int grid = (int)std::min<int64_t>(n_tiles, 512);   // two workgroups per CU, persistent
-    if (b.c_out == 64) hipLaunchKernelGGL((qconv_pair<64>), dim3(grid), dim3(256), 0, stream, a, b, (int32_t)n_tiles);
-    else hipLaunchKernelGGL((qconv_pair<128>), dim3(grid), dim3(256), 0, stream, a, b, (int32_t)n_tiles);
+    const bool xs = a.x_xor != 0u || b.x_xor != 0u;   // signed codes on both sides: no sign flip
+    if (b.c_out == 64) {
+        if (xs) hipLaunchKernelGGL((qconv_pair<64, true>), dim3(grid), dim3(256), 0, stream, a, b, (int32_t)n_tiles);
+        else hipLaunchKernelGGL((qconv_pair<64, false>), dim3(grid), dim3(256), 0, stream, a, b, (int32_t)n_tiles);
+    } else {
+        if (xs) hipLaunchKernelGGL((qconv_pair<128, true>), dim3(grid), dim3(256), 0, stream, a, b, (int32_t)n_tiles);
+        else hipLaunchKernelGGL((qconv_pair<128, false>), dim3(grid), dim3(256), 0, stream, a, b, (int32_t)n_tiles);
+    }
     return hipGetLastError();
 }
 
