@@ -270,6 +270,23 @@ def test_conv_every_tile(tile):
         assert_bytes_equal(y.cpu().numpy(), want, "tile %d four-channel gather" % tile)
 
 
+@pytest.mark.parametrize("tile", list(range(18)) + [20, 21, 22, 23])
+def test_conv_every_tile_signed_codes(tile):
+    """The same layers, and a 3x3 Conv_Add_Relu, with signed 8-bit activations,
+    residuals and outputs: the streaming configurations of the automatic choice run
+    their variant without the activation sign flip on these, the others the flipping
+    one with x_xor = 0; every tile gives the oracle's bytes."""
+    require_gpu()
+    layers = PIPE + [(2, 9, 10, 64, 128, 3, 1, 1, ADD_RELU), (1, 11, 13, 128, 64, 3, 2, 1, ADD)]
+    for i, (n, h, w, ci, co, k, s, p, epi) in enumerate(layers):
+        c = synth.conv_case(2000 + 13 * i, n, h, w, ci, co, k, s, p, I8, I8, I8, epi, res_type=I8)
+        x, wc, res = conv_codes(c)
+        want = to_bytes(oracle_conv(c, x, wc, res), I8)
+        got = gpu_conv(c, x, wc, res, cfg=(tile, 0))
+        assert_bytes_equal(got, want, "tile %d %s" % (tile, layers[i]))
+        assert len(np.unique(got)) >= 32   # the codes span the range
+
+
 # 4-bit activations with C_in % 64 == 0 (the streaming kernel's 4-bit path): both
 # block heights (C_out <= 64 -> 64-channel blocks, 32-byte residual rows; else 128),
 # UINT4 and INT4 codes, 4-bit residuals, stride 2, ragged pixel tails
