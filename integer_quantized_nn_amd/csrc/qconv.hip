@@ -1140,7 +1140,7 @@ struct StreamCfg {
 // XS: the activation fragments take the uint8 sign flip (XOR with x_xor); false for
 // signed 8-bit codes (x_xor == 0), whose fragments are MFMA operands as they are.
 template <class C, bool IS1X1, bool RES, bool C4, bool B4 = false, bool ZW = false, bool SP = false,
-          bool F6 = false, int OUTK = 0, bool S4 = false, bool W4 = false, bool XS = true>
+          bool F6 = false, int OUTK = 0, bool S4 = false, bool W4 = false, bool XS = true, bool SPL = false>
 __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvParams p) {
     constexpr int BM = C::BM, BN = C::BN, WM = C::WM, NST = C::NST, NW = C::NW;
     constexpr int TM = C::TM, TN = C::TN;
@@ -1353,7 +1353,14 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
     int tap = 0, k_ci = 0, k_kx = 0;
     const int64_t row_jump = (int64_t)(p.w_in - p.kw) * p.c;   // end of a filter row -> start of the next
     set_issue_tile(0);
-    auto issue = [&]() {
+    // SPLIT: KxK layers without a residual whose tiles have more than D + 1 stages.  The
+    // issue side then reaches the next tile at a fixed stage of every tile, and the
+    // stage loop is split there, so the per-tile rows and tap masks change only between
+    // the two loops (no per-stage merge of them)
+    static_assert(!SPL || (!IS1X1 && !C4 && !RES && !SP && !F6), "split stage loop: KxK gathers without a residual");
+    constexpr bool split = SPL;
+    bool frozen = false;   // split path: the issue side stays on the last stage of the last tile
+    auto issue = [&](bool in_tile) {
         const uint32_t dst = ring0 + is_off;
         if (RES && is_s == nst) {
             if constexpr (RES) {
@@ -1402,8 +1409,25 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
             }
         }
         is_off = is_off + STAGE == NST * STAGE ? 0 : is_off + STAGE;
-        // advance the cursor; past the end it stays on the last stage
-        if (is_s + 1 < spt) {
+        // advance the cursor; past the end it stays on the last stage.  In the split
+        // path the cursor never leaves its tile here (the loop switches it)
+        if (in_tile) {
+            if (!frozen && is_s + 1 < spt) {
+                ++is_s;
+                if (!IS1X1 && !C4 && is_s < nst) {
+                    tapoff += kPipeBK;
+                    k_ci += kPipeBK;
+                    if (k_ci == p.c) {
+                        k_ci = 0;
+                        ++tap;
+                        if (++k_kx == p.kw) {
+                            k_kx = 0;
+                            tapoff += row_jump;
+                        }
+                    }
+                }
+            }
+        } else if (is_s + 1 < spt) {
             ++is_s;
             if (!IS1X1 && !C4 && is_s < nst) {
                 tapoff += kPipeBK;
@@ -1544,7 +1568,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
     auto sync = [&]() {
         IQNN_WAIT_VM_LGKM0((D - 1) * K_LOADS);
         __builtin_amdgcn_s_barrier();
-        issue();
+        issue(split);
     };
 
     // 2:4 weights: the fragments of one stage (kept codes, positions, both activation
@@ -1627,7 +1651,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
     };
     F6Frag gx, gy;
 
-    for (int i = 0; i < D; ++i) issue();
+    for (int i = 0; i < D; ++i) issue(split);
     uint32_t cur_off = 0;
     auto advance = [&]() { cur_off = cur_off + STAGE == NST * STAGE ? 0 : cur_off + STAGE; };
     sync();
@@ -1693,6 +1717,33 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
         }
     };
 
+    // one stage of the dense path (the body of the plain stage loop below)
+    auto dense_stage = [&](int s, bool last_tile) {
+        const uint8_t* cur = ring + cur_off;
+        shift_b(fb0, 0);
+        unpack_a(fa0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(fa0, fb0, 0, NMF);
+        read_frags(cur, foff1, fa1, fb1);
+#pragma unroll
+        for (int i = 0; i < (NMF < NRD ? NMF : NRD); ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        }
+        if (NMF > NRD) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NRD, 0);
+        if (NRD > NMF) __builtin_amdgcn_sched_group_barrier(0x100, NRD - NMF, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        shift_b(fb1, 1);
+        unpack_a(fa1, 1);
+        mfmas(fa1, fb1, 0, HALF);
+        __builtin_amdgcn_sched_barrier(0);
+        advance();
+        if (!(last_tile && s + 1 == nst && !RES)) sync();
+        if (s + 1 < nst) read_frags(ring + cur_off, foff0, fa0, fb0);
+        mfmas(fa1, fb1, HALF, NMF);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
     for (int j = 0; j < J; ++j) {
         const bool last_tile = j + 1 == J;
         if constexpr (F6) {
@@ -1713,7 +1764,21 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
                     sp_stage(fy, fx, !end1, !(last_tile && end1 && !RES));
                 }
             }
-        } else
+        } else if constexpr (SPL) {
+            // the stage whose sync issues the next tile's first stage
+            const int s_sw = nst - D - 1;
+            for (int s = 0; s < s_sw; ++s) dense_stage(s, last_tile);
+            if (!last_tile) {
+                ++is_j;
+                is_s = 0;
+                tapoff = 0;
+                tap = k_ci = k_kx = 0;
+                set_issue_tile(is_j);
+            } else {
+                frozen = true;
+            }
+            for (int s = s_sw; s < nst; ++s) dense_stage(s, last_tile);
+        } else {
         for (int s = 0; s < nst; ++s) {
             const uint8_t* cur = ring + cur_off;
             shift_b(fb0, 0);
@@ -1738,6 +1803,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
             if (s + 1 < nst) read_frags(ring + cur_off, foff0, fa0, fb0);
             mfmas(fa1, fb1, HALF, NMF);
             __builtin_amdgcn_sched_barrier(0);
+        }
         }
 
         // -------------------------------------------------------- epilogue of tile j
@@ -2196,6 +2262,9 @@ hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bo
             return hipGetLastError();
         }
     }
+    // KxK layers without a residual whose tiles have more than D + 1 stages: the split
+    // stage loop (the issue side's tile switch between two loops)
+    const bool split = !is_1x1 && !c4 && !add && p.kp / kPipeBK > C::NST;
     // signed 8-bit activations on the automatic choice's configurations: no sign flip
     if constexpr (kIrqTile<C>) {
         if (out8 && p.x_xor == 0u && !(add && !kResStage)) {
@@ -2209,6 +2278,9 @@ hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bo
             }
             if (!add && is_1x1)
                 hipLaunchKernelGGL((qconv_stream<C, true, false, false, false, false, false, false, 1, false, false, false>),
+                                   g, b, 0, stream, q);
+            else if (!add && split)
+                hipLaunchKernelGGL((qconv_stream<C, false, false, false, false, false, false, false, 1, false, false, false, true>),
                                    g, b, 0, stream, q);
             else if (!add)
                 hipLaunchKernelGGL((qconv_stream<C, false, false, false, false, false, false, false, 1, false, false, false>),
@@ -2233,6 +2305,9 @@ hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bo
         hipLaunchKernelGGL((qconv_stream<C, true, false, false, false, false, false, false, 1>), g, b, 0, stream, q);
     else if (is_1x1)
         hipLaunchKernelGGL((qconv_stream<C, true, false, false>), g, b, 0, stream, q);
+    else if (out8 && split && kIrqTile<C>)
+        hipLaunchKernelGGL((qconv_stream<C, false, false, false, false, false, false, false, 1, false, false, true, kIrqTile<C>>),
+                           g, b, 0, stream, q);
     else if (out8)
         hipLaunchKernelGGL((qconv_stream<C, false, false, false, false, false, false, false, 1>), g, b, 0, stream, q);
     else
