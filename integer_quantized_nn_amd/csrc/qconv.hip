@@ -47,6 +47,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "iqnn_internal.h"
 
@@ -1270,7 +1271,9 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
     //           its tap is in tmask, else the row of pad codes.
     constexpr int NB = C4 ? 1 : B_INST;
     const uint8_t* prow[NB];
-    uint64_t tmask[NB];
+    // the split variant's layers have at most 32 filter taps (checked by the host)
+    using MaskT = std::conditional_t<SPL, uint32_t, uint64_t>;
+    MaskT tmask[NB];
     constexpr int C4N = C4 ? B_INST : 1;
     int32_t coff[C4N], cky[C4N];
     const uint8_t* rsrc[RES ? R_INST : 1];
@@ -1322,7 +1325,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
                         const uint64_t xm = ((uint64_t)1 << xhi) - ((uint64_t)1 << xlo);
                         for (int ky = ylo; ky < yhi; ++ky) m |= xm << (ky * p.kw);
                     }
-                    tmask[i] = m;
+                    tmask[i] = (MaskT)m;
                 } else {
                     prow[i] = padrow;
                     tmask[i] = 0;
@@ -1353,6 +1356,10 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
     int tap = 0, k_ci = 0, k_kx = 0;
     const int64_t row_jump = (int64_t)(p.w_in - p.kw) * p.c;   // end of a filter row -> start of the next
     set_issue_tile(0);
+    // the pad row's address held in vector registers for the per-lane select (a select
+    // cannot take it from scalar registers next to its condition)
+    const uint8_t* padv = padrow;
+    if constexpr (!IS1X1 && !C4) asm volatile("" : "+v"(padv));
     // SPLIT: KxK layers without a residual whose tiles have more than D + 1 stages.  The
     // issue side then reaches the next tile at a fixed stage of every tile, and the
     // stage loop is split there, so the per-tile rows and tap masks change only between
@@ -1403,7 +1410,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
 #pragma unroll
                 for (int i = 0; i < B_INST; ++i) {
                     if constexpr (IS1X1) bs[i] = prow[i] + (k0 >> SH);
-                    else bs[i] = ((tmask[i] >> tap) & 1) ? prow[i] + (tapoff >> SH) : padrow;
+                    else bs[i] = ((tmask[i] >> tap) & 1) ? prow[i] + (tapoff >> SH) : padv;
                 }
                 dma16_seq<B_INST>(dst + A_BYTES + wave * (BN / NW) * BROW, bs);
             }
@@ -2264,7 +2271,7 @@ hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bo
     }
     // KxK layers without a residual whose tiles have more than D + 1 stages: the split
     // stage loop (the issue side's tile switch between two loops)
-    const bool split = !is_1x1 && !c4 && !add && p.kp / kPipeBK > C::NST;
+    const bool split = !is_1x1 && !c4 && !add && p.kh * p.kw <= 32 && p.kp / kPipeBK > C::NST;
     // signed 8-bit activations on the automatic choice's configurations: no sign flip
     if constexpr (kIrqTile<C>) {
         if (out8 && p.x_xor == 0u && !(add && !kResStage)) {
