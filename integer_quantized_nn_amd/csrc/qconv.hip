@@ -1138,6 +1138,15 @@ struct StreamCfg {
 // contraction accumulates 16 * acc; the accumulators start from 16 * bias and are
 // shifted right by 4 before the epilogue, which is exact (every term is a multiple
 // of 16).
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), unrolled
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
+}
+
 // XS: the activation fragments take the uint8 sign flip (XOR with x_xor); false for
 // signed 8-bit codes (x_xor == 0), whose fragments are MFMA operands as they are.
 template <class C, bool IS1X1, bool RES, bool C4, bool B4 = false, bool ZW = false, bool SP = false,
@@ -1724,9 +1733,11 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
         }
     };
 
-    // one stage of the dense path (the body of the plain stage loop below)
-    auto dense_stage = [&](int s, bool last_tile) {
-        const uint8_t* cur = ring + cur_off;
+    // one stage of the dense path (the body of the plain stage loop below); slot_c: the
+    // stage's ring slot when known at compile time (an integral constant), else -1
+    auto dense_stage_at = [&](auto slot_c, int s, bool last_tile) {
+        constexpr int SLOT = decltype(slot_c)::value;
+        const uint8_t* cur = SLOT >= 0 ? ring + SLOT * STAGE : ring + cur_off;
         shift_b(fb0, 0);
         unpack_a(fa0, 0);
         __builtin_amdgcn_sched_barrier(0);
@@ -1746,9 +1757,14 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
         __builtin_amdgcn_sched_barrier(0);
         advance();
         if (!(last_tile && s + 1 == nst && !RES)) sync();
-        if (s + 1 < nst) read_frags(ring + cur_off, foff0, fa0, fb0);
+        if (s + 1 < nst)
+            read_frags(SLOT >= 0 ? ring + ((SLOT + 1) % NST) * STAGE : ring + cur_off, foff0, fa0, fb0);
         mfmas(fa1, fb1, HALF, NMF);
         __builtin_amdgcn_sched_barrier(0);
+    };
+    // NST stages with their slots 0 .. NST-1 at compile time
+    auto ring_round = [&](int s0, bool last_tile) {
+        static_for<NST>([&](auto q) { dense_stage_at(q, s0 + decltype(q)::value, last_tile); });
     };
 
     for (int j = 0; j < J; ++j) {
@@ -1772,9 +1788,11 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
                 }
             }
         } else if constexpr (SPL) {
-            // the stage whose sync issues the next tile's first stage
+            // the stage whose sync issues the next tile's first stage; nst is a multiple of
+            // NST (checked by the host), so every tile starts in slot 0 and the slots of
+            // its stages are known in rounds of NST
             const int s_sw = nst - D - 1;
-            for (int s = 0; s < s_sw; ++s) dense_stage(s, last_tile);
+            for (int s = 0; s < s_sw; s += NST) ring_round(s, last_tile);
             if (!last_tile) {
                 ++is_j;
                 is_s = 0;
@@ -1784,7 +1802,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
             } else {
                 frozen = true;
             }
-            for (int s = s_sw; s < nst; ++s) dense_stage(s, last_tile);
+            ring_round(s_sw, last_tile);
         } else {
         for (int s = 0; s < nst; ++s) {
             const uint8_t* cur = ring + cur_off;
@@ -2271,7 +2289,8 @@ hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bo
     }
     // KxK layers without a residual whose tiles have more than D + 1 stages: the split
     // stage loop (the issue side's tile switch between two loops)
-    const bool split = !is_1x1 && !c4 && !add && p.kh * p.kw <= 32 && p.kp / kPipeBK > C::NST;
+    const bool split = !is_1x1 && !c4 && !add && p.kh * p.kw <= 32 && p.kp / kPipeBK > C::NST &&
+                       (p.kp / kPipeBK) % C::NST == 0;
     // signed 8-bit activations on the automatic choice's configurations: no sign flip
     if constexpr (kIrqTile<C>) {
         if (out8 && p.x_xor == 0u && !(add && !kResStage)) {
