@@ -2956,11 +2956,23 @@ __global__ __launch_bounds__(256, 2) void qconv_direct3x3(const ConvParams p, in
     const bool px_ok = wave * 32 + frow < 2 * W;
     const uint32_t bxor = XORB ? p.x_xor : 0u;
     const int grid = (int)gridDim.x;
-    int buf = 0;
+    // this lane's fragment offset inside a slab for filter column kx and k-step ks (the
+    // filter row adds ky * SW * 64, a constant), fixed for the launch
+    int boff[3][2];
+#pragma unroll
+    for (int kx = 0; kx < 3; ++kx)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int col = ox + kx;
+            boff[kx][ks] = (r * SW + col) * 64 + (((2 * ks + (lane >> 5)) ^ ((col >> 2) & 3)) << 4);
+        }
     issue(blockIdx.x, 0);
     if ((int)blockIdx.x + grid < n_tiles) issue(blockIdx.x + grid, 1);
     bool stored = false;   // this wave issued the (at least two) stores of its previous tile
-    for (int tile = blockIdx.x; tile < n_tiles; tile += grid) {
+    // one tile in slab buffer BUF (a compile-time constant: the tiles of a workgroup take
+    // the three buffers in turn, so the loop below runs in rounds of three)
+    auto tile_body = [&](auto buf_c, int tile) {
+        constexpr int buf = decltype(buf_c)::value;
         // The memory counter retires loads and stores in issue order, so vmcnt <= N
         // means all but the newest N operations are done.  Issued after this tile's
         // slab: the next tile's slab (CPW DMA, if there is a next tile), the previous
@@ -2978,7 +2990,7 @@ __global__ __launch_bounds__(256, 2) void qconv_direct3x3(const ConvParams p, in
         __builtin_amdgcn_s_barrier();
         {
             const int after = tile + 2 * grid;
-            if (after < n_tiles) issue(after, buf == 0 ? 2 : buf - 1);
+            if (after < n_tiles) issue(after, (buf + 2) % 3);
         }
 
         v16i acc[2];
@@ -2991,16 +3003,13 @@ __global__ __launch_bounds__(256, 2) void qconv_direct3x3(const ConvParams p, in
                 acc[t][4 * q] = bv.x; acc[t][4 * q + 1] = bv.y; acc[t][4 * q + 2] = bv.z; acc[t][4 * q + 3] = bv.w;
             }
         }
-        const uint8_t* sb = &slab[buf][0];
         // B fragment s = (tap, k-step) of this lane's pixel, read one step ahead of its
         // two MFMAs (a scheduling barrier per step keeps the reads from piling up in
         // registers next to the A fragments)
         auto read_b = [&](int s) -> v4i {
             const int tap = s >> 1, ks = s & 1;
             const int ky = tap / 3, kx = tap - 3 * ky;
-            const int col = ox + kx;
-            return *reinterpret_cast<const v4i*>(sb + ((r + ky) * SW + col) * 64 +
-                                                 (((2 * ks + (lane >> 5)) ^ ((col >> 2) & 3)) << 4));
+            return *reinterpret_cast<const v4i*>(&slab[buf][ky * SW * 64] + boff[kx][ks]);
         };
         if constexpr (SP) {
             // one tap per step: its two k-step fragments are the sparse MFMA's B operand
@@ -3057,7 +3066,14 @@ __global__ __launch_bounds__(256, 2) void qconv_direct3x3(const ConvParams p, in
                                                    0.0f, irq32);
             }
         }
-        buf = buf == 2 ? 0 : buf + 1;
+    };
+    for (int tile = blockIdx.x; tile < n_tiles;) {
+        tile_body(std::integral_constant<int, 0>{}, tile);
+        if ((tile += grid) >= n_tiles) break;
+        tile_body(std::integral_constant<int, 1>{}, tile);
+        if ((tile += grid) >= n_tiles) break;
+        tile_body(std::integral_constant<int, 2>{}, tile);
+        tile += grid;
     }
     // no DMA may still be writing this workgroup's LDS when it ends
     IQNN_WAIT_VM(0);
