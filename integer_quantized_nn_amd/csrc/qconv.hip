@@ -1150,7 +1150,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 // XS: the activation fragments take the uint8 sign flip (XOR with x_xor); false for
 // signed 8-bit codes (x_xor == 0), whose fragments are MFMA operands as they are.
 template <class C, bool IS1X1, bool RES, bool C4, bool B4 = false, bool ZW = false, bool SP = false,
-          bool F6 = false, int OUTK = 0, bool S4 = false, bool W4 = false, bool XS = true, bool SPL = false>
+          bool F6 = false, int OUTK = 0, bool S4 = false, bool W4 = false, bool XS = true, int SPL = 0>
 __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvParams p) {
     constexpr int BM = C::BM, BN = C::BN, WM = C::WM, NST = C::NST, NW = C::NW;
     constexpr int TM = C::TM, TN = C::TN;
@@ -1281,7 +1281,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
     constexpr int NB = C4 ? 1 : B_INST;
     const uint8_t* prow[NB];
     // the split variant's layers have at most 32 filter taps (checked by the host)
-    using MaskT = std::conditional_t<SPL, uint32_t, uint64_t>;
+    using MaskT = std::conditional_t<(SPL != 0), uint32_t, uint64_t>;
     MaskT tmask[NB];
     constexpr int C4N = C4 ? B_INST : 1;
     int32_t coff[C4N], cky[C4N];
@@ -1374,7 +1374,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
     // stage loop is split there, so the per-tile rows and tap masks change only between
     // the two loops (no per-stage merge of them)
     static_assert(!SPL || (!IS1X1 && !C4 && !RES && !SP && !F6), "split stage loop: KxK gathers without a residual");
-    constexpr bool split = SPL;
+    constexpr bool split = SPL != 0;   // 2: also nst % NST == 0, the stages run in ring rounds
     bool frozen = false;   // split path: the issue side stays on the last stage of the last tile
     auto issue = [&](bool in_tile) {
         const uint32_t dst = ring0 + is_off;
@@ -1787,10 +1787,23 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
                     sp_stage(fy, fx, !end1, !(last_tile && end1 && !RES));
                 }
             }
-        } else if constexpr (SPL) {
-            // the stage whose sync issues the next tile's first stage; nst is a multiple of
-            // NST (checked by the host), so every tile starts in slot 0 and the slots of
-            // its stages are known in rounds of NST
+        } else if constexpr (SPL == 1) {
+            // the stage whose sync issues the next tile's first stage
+            const int s_sw = nst - D - 1;
+            for (int s = 0; s < s_sw; ++s) dense_stage_at(std::integral_constant<int, -1>{}, s, last_tile);
+            if (!last_tile) {
+                ++is_j;
+                is_s = 0;
+                tapoff = 0;
+                tap = k_ci = k_kx = 0;
+                set_issue_tile(is_j);
+            } else {
+                frozen = true;
+            }
+            for (int s = s_sw; s < nst; ++s) dense_stage_at(std::integral_constant<int, -1>{}, s, last_tile);
+        } else if constexpr (SPL == 2) {
+            // as above; nst is a multiple of NST (checked by the host), so every tile starts
+            // in slot 0 and the slots of its stages are known in rounds of NST
             const int s_sw = nst - D - 1;
             for (int s = 0; s < s_sw; s += NST) ring_round(s, last_tile);
             if (!last_tile) {
@@ -2289,8 +2302,10 @@ hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bo
     }
     // KxK layers without a residual whose tiles have more than D + 1 stages: the split
     // stage loop (the issue side's tile switch between two loops)
-    const bool split = !is_1x1 && !c4 && !add && p.kh * p.kw <= 32 && p.kp / kPipeBK > C::NST &&
-                       (p.kp / kPipeBK) % C::NST == 0;
+    const bool split = !is_1x1 && !c4 && !add && p.kh * p.kw <= 32 && p.kp / kPipeBK > C::NST;
+    // ring rounds: signed codes on rings of at most 4 slots (unrolled with the sign flip,
+    // or over 6 slots, the compiler spills)
+    const bool rounds = split && (p.kp / kPipeBK) % C::NST == 0 && C::NST <= 4;
     // signed 8-bit activations on the automatic choice's configurations: no sign flip
     if constexpr (kIrqTile<C>) {
         if (out8 && p.x_xor == 0u && !(add && !kResStage)) {
@@ -2305,8 +2320,11 @@ hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bo
             if (!add && is_1x1)
                 hipLaunchKernelGGL((qconv_stream<C, true, false, false, false, false, false, false, 1, false, false, false>),
                                    g, b, 0, stream, q);
+            else if (!add && rounds)
+                hipLaunchKernelGGL((qconv_stream<C, false, false, false, false, false, false, false, 1, false, false, false,
+                                                 C::NST <= 4 ? 2 : 1>), g, b, 0, stream, q);
             else if (!add && split)
-                hipLaunchKernelGGL((qconv_stream<C, false, false, false, false, false, false, false, 1, false, false, false, true>),
+                hipLaunchKernelGGL((qconv_stream<C, false, false, false, false, false, false, false, 1, false, false, false, 1>),
                                    g, b, 0, stream, q);
             else if (!add)
                 hipLaunchKernelGGL((qconv_stream<C, false, false, false, false, false, false, false, 1, false, false, false>),
@@ -2332,8 +2350,8 @@ hipError_t launch_stream(const ConvParams& p, bool is_1x1, bool res_prefetch, bo
     else if (is_1x1)
         hipLaunchKernelGGL((qconv_stream<C, true, false, false>), g, b, 0, stream, q);
     else if (out8 && split && kIrqTile<C>)
-        hipLaunchKernelGGL((qconv_stream<C, false, false, false, false, false, false, false, 1, false, false, true, kIrqTile<C>>),
-                           g, b, 0, stream, q);
+        hipLaunchKernelGGL((qconv_stream<C, false, false, false, false, false, false, false, 1, false, false, true,
+                                         kIrqTile<C> ? 1 : 0>), g, b, 0, stream, q);
     else if (out8)
         hipLaunchKernelGGL((qconv_stream<C, false, false, false, false, false, false, false, 1>), g, b, 0, stream, q);
     else
