@@ -1733,8 +1733,8 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
         }
     };
 
-    // one stage of the dense path (the body of the plain stage loop below); slot_c: the
-    // stage's ring slot when known at compile time (an integral constant), else -1
+    // one stage of the dense path; slot_c: the stage's ring slot when known at compile
+    // time (an integral constant), else -1 (the slot is read at run time)
     auto dense_stage_at = [&](auto slot_c, int s, bool last_tile) {
         constexpr int SLOT = decltype(slot_c)::value;
         const uint8_t* cur = SLOT >= 0 ? ring + SLOT * STAGE : ring + cur_off;
@@ -1817,31 +1817,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void qconv_stream(const ConvPar
             }
             ring_round(s_sw, last_tile);
         } else {
-        for (int s = 0; s < nst; ++s) {
-            const uint8_t* cur = ring + cur_off;
-            shift_b(fb0, 0);
-            unpack_a(fa0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            mfmas(fa0, fb0, 0, NMF);
-            read_frags(cur, foff1, fa1, fb1);
-#pragma unroll
-            for (int i = 0; i < (NMF < NRD ? NMF : NRD); ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-            }
-            if (NMF > NRD) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NRD, 0);
-            if (NRD > NMF) __builtin_amdgcn_sched_group_barrier(0x100, NRD - NMF, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            shift_b(fb1, 1);
-            unpack_a(fa1, 1);
-            mfmas(fa1, fb1, 0, HALF);
-            __builtin_amdgcn_sched_barrier(0);
-            advance();
-            if (!(last_tile && s + 1 == nst && !RES)) sync();
-            if (s + 1 < nst) read_frags(ring + cur_off, foff0, fa0, fb0);
-            mfmas(fa1, fb1, HALF, NMF);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+            for (int s = 0; s < nst; ++s) dense_stage_at(std::integral_constant<int, -1>{}, s, last_tile);
         }
 
         // -------------------------------------------------------- epilogue of tile j
