@@ -147,11 +147,13 @@ __device__ __forceinline__ void load_res16(const ConvParams& p, int64_t oidx, in
 
 // The clip / round / zero-point tail of the epilogue below: b[j] holds output code j
 // in its low byte.
-__device__ __forceinline__ void round_codes16(const ConvParams& p, const float v[16], uint32_t b[16]) {
+// FIX_LATER: the odd part of Z_out is left to the byte packer (pack_codes16).
+__device__ __forceinline__ void round_codes16(const ConvParams& p, const float v[16], uint32_t b[16],
+                                              bool fix_later = false) {
 #pragma unroll
     for (int j = 0; j < 16; ++j)
         b[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_fmed3f(v[j], p.t_lo, p.t_hi) + p.out_magic);
-    if (p.out_fix) {
+    if (!fix_later && p.out_fix) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) b[j] += 1u;
     }
@@ -166,6 +168,23 @@ __device__ __forceinline__ uint4 pack_bytes16(const ConvParams& p, const uint32_
         const uint32_t lo2 = __builtin_amdgcn_perm(b[4 * d + 1], b[4 * d], 0x0C0C0400u);
         const uint32_t hi2 = __builtin_amdgcn_perm(b[4 * d + 3], b[4 * d + 2], 0x0C0C0400u);
         ow[d] = (lo2 | (hi2 << 16)) + p.out_fix4;
+    }
+    return make_uint4(ow[0], ow[1], ow[2], ow[3]);
+}
+
+// pack_bytes16 for codes rounded without the odd part of Z_out (round_codes16 with
+// fix_later), adding it here: when a byte may hold 0xFF (p.out_fix = 1) each code is
+// first placed in its own 16-bit lane, so adding 1 to every lane cannot carry into the
+// next code, and a last permute keeps the low bytes -- five instructions per four codes
+// instead of an addition per code.
+__device__ __forceinline__ uint4 pack_codes16(const ConvParams& p, const uint32_t b[16]) {
+    if (!p.out_fix) return pack_bytes16(p, b);
+    uint32_t ow[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t lo2 = __builtin_amdgcn_perm(b[4 * d + 1], b[4 * d], 0x0C040C00u) + 0x00010001u;
+        const uint32_t hi2 = __builtin_amdgcn_perm(b[4 * d + 3], b[4 * d + 2], 0x0C040C00u) + 0x00010001u;
+        ow[d] = __builtin_amdgcn_perm(hi2, lo2, 0x06040200u);
     }
     return make_uint4(ow[0], ow[1], ow[2], ow[3]);
 }
@@ -275,10 +294,10 @@ __device__ __forceinline__ void epi_store16(const ConvParams& p, const v16i& acc
                 v[j] = v[j] + u;
             }
         }
-        round_codes16(p, v, b);
+        round_codes16(p, v, b, OUTK == 1);
     }
     if (OUTK == 1 || (OUTK == 0 && (p.y_type == T_INT8 || p.y_type == T_UINT8))) {
-        const uint4 pk = pack_bytes16(p, b);
+        const uint4 pk = (OUTK == 1 && !INTRQ) ? pack_codes16(p, b) : pack_bytes16(p, b);
         const uint32_t ow[4] = {pk.x, pk.y, pk.z, pk.w};
         if (vec) {
             *reinterpret_cast<uint4*>(p.y + oidx) = pk;
