@@ -287,6 +287,39 @@ def test_conv_every_tile_signed_codes(tile):
         assert len(np.unique(got)) >= 32   # the codes span the range
 
 
+# 3x3 layers without a residual with more pixel tiles per XCD share than a share has
+# persistent blocks, for every configuration (over 64 tiles of 256 pixels per share),
+# so blocks run more than one tile and the streaming kernel's split stage loop hands
+# its issue side over to the next tile inside the loop: 9 and 27 stages per tile,
+# against ring depths that divide them (the loop in rounds) and ones that do not.
+MULTI_TILE = [
+    (64, 48, 48, 64, 64, 3, 1, 1, RELU),      # 147456 pixels, 9 stages
+    (24, 76, 76, 192, 64, 3, 1, 1, NONE),     # 138624 pixels, 27 stages
+]
+_multi_tile_cases = {}
+
+
+def _multi_tile_case(i):
+    if i not in _multi_tile_cases:
+        n, h, w, ci, co, k, s, p, epi = MULTI_TILE[i]
+        c = synth.conv_case(3000 + 7 * i, n, h, w, ci, co, k, s, p, I8, I8, I8, epi)
+        x, wc, _ = conv_codes(c)
+        _multi_tile_cases[i] = (c, x, wc, to_bytes(oracle_conv(c, x, wc, None), I8))
+    return _multi_tile_cases[i]
+
+
+@pytest.mark.parametrize("tile", list(range(18)) + [20, 21, 22, 23])
+def test_conv_every_tile_several_tiles_per_block(tile):
+    """Every block configuration on signed 8-bit codes with several tiles per
+    persistent block; every output byte against the oracle."""
+    require_gpu()
+    for i in range(len(MULTI_TILE)):
+        c, x, wc, want = _multi_tile_case(i)
+        got = gpu_conv(c, x, wc, None, cfg=(tile, 0))
+        assert_bytes_equal(got, want, "tile %d %s" % (tile, MULTI_TILE[i]))
+        assert len(np.unique(got)) >= 32
+
+
 # 4-bit activations with C_in % 64 == 0 (the streaming kernel's 4-bit path): both
 # block heights (C_out <= 64 -> 64-channel blocks, 32-byte residual rows; else 128),
 # UINT4 and INT4 codes, 4-bit residuals, stride 2, ragged pixel tails
