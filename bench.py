@@ -220,11 +220,14 @@ def make_layer(torch, wl, cfg=None):
         cfg = (19, 0)
     rec = {"peak_ops": PEAK_FP6_OPS if fp6 else PEAK_INT8_OPS, "dtype": "bf6" if fp6 else "int8", "oracle": None}
     conv_wls = ("conv3x3_int8", "conv3x3_4bit", "conv3x3_4bit_fp6", "conv3x3_uint8w", "conv3x3_intrq",
-                "conv3x3_2of4", "resnet50_l3_conv3x3", "resnet50_l3_conv3x3_intrq", "conv1x1_int8", "conv1x1_intrq")
+                "conv3x3_2of4", "resnet50_l3_conv3x3", "resnet50_l3_conv3x3_intrq", "resnet50_l3_conv3x3_s8",
+                "conv1x1_int8", "conv1x1_intrq")
     if wl in conv_wls:
         if wl.startswith("resnet50_l3_conv3x3"):   # the trunk's stage-3 3x3 layer: 256 x 14x14, 256 -> 256
-            c = synth.conv_case(31, 256, 14, 14, 256, 256, 3, 1, 1, synth.UINT8, synth.INT8, synth.UINT8,
-                                synth.EPI_RELU, name="l3_conv3x3")
+            # _s8: signed 8-bit activation and output codes, the trunk's stored form (no sign flip)
+            t8 = synth.INT8 if wl.endswith("_s8") else synth.UINT8
+            c = synth.conv_case(31, 256, 14, 14, 256, 256, 3, 1, 1, t8, synth.INT8, t8, synth.EPI_RELU,
+                                name="l3_conv3x3")
         elif wl.startswith("conv1x1"):   # the trunk's stage-1 expanding 1x1 layer: 256 x 56x56, 64 -> 256
             c = synth.conv_case(33, 256, 56, 56, 64, 256, 1, 1, 0, synth.UINT8, synth.INT8, synth.UINT8,
                                 synth.EPI_RELU, name="conv1x1")
@@ -603,6 +606,7 @@ def main():
                     choices=["resnet50_trunk", "resnet50_trunk_2of4", "conv3x3_int8", "conv3x3_2of4", "conv3x3_4bit",
                              "conv3x3_4bit_fp6", "conv3x3_uint8w", "conv3x3_intrq", "resnet50_l3_conv3x3",
                              "resnet50_stem_pool", "conv1x1_int8", "conv1x1_intrq", "resnet50_l3_conv3x3_intrq",
+                             "resnet50_l3_conv3x3_s8",
                              "resnet50_l1_pair", "vitl_fc1", "vitl_fc1_2of4", "gemm_int8_256"])
     ap.add_argument("--cold", action="store_true",
                     help="single-layer workloads: rotate input/output sets (> 256 MB) so every launch misses the caches")
